@@ -1,0 +1,397 @@
+"""Pins of the CPU oracle against facts that do not come from the oracle itself:
+hand-derived examples, exact integer arithmetic, library routines (PyTorch's
+float8/bf16 casts, scaled_dot_product_attention, rms_norm), closed forms and
+invariants.  CPU only."""
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import dsa_oracle as O
+import synth
+
+GOLD = os.path.join(os.path.dirname(__file__), "golden")
+
+
+# ----------------------------------------------------------------------------- formats
+
+def test_e4m3_decode_all_codes_vs_torch():
+    codes = np.arange(256, dtype=np.uint8)
+    ref = torch.from_numpy(codes).view(torch.float8_e4m3fn).to(torch.float64).numpy()
+    got = O.decode_e4m3(codes)
+    nan = np.isnan(ref)
+    assert np.array_equal(nan, np.isnan(got))
+    assert np.array_equal(ref[~nan], got[~nan])
+    assert O.decode_e4m3(np.array([0x7E], np.uint8))[0] == 448.0
+    assert O.decode_e4m3(np.array([0x01], np.uint8))[0] == 2.0 ** -9
+
+
+def test_e4m3_encode_vs_torch_sweep_and_midpoints():
+    g = np.random.default_rng(7)
+    x = np.concatenate([
+        g.standard_normal(20000).astype(np.float32) * 30,
+        g.uniform(-448, 448, 20000).astype(np.float32),
+        (g.standard_normal(5000) * 1e-3).astype(np.float32),
+    ])
+    mags = O.decode_e4m3(np.arange(127, dtype=np.uint8))
+    mids = ((mags[:-1] + mags[1:]) / 2).astype(np.float32)    # exact in fp32
+    x = np.concatenate([x, mids, -mids, mags.astype(np.float32)])
+    ref = torch.from_numpy(x).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    got = O.encode_e4m3(x)
+    # torch maps -0.0 to 0x80 as well; compare everything
+    assert np.array_equal(ref, got)
+
+
+def test_e4m3_encode_saturates():
+    x = np.array([448.0, 460.0, 1e4, 3e38, -500.0, -1e9], np.float32)
+    got = O.encode_e4m3(x)
+    assert list(got) == [0x7E, 0x7E, 0x7E, 0x7E, 0xFE, 0xFE]
+
+
+def test_bf16_decode_and_round_vs_torch():
+    g = np.random.default_rng(3)
+    x = (g.standard_normal(4000) * np.exp2(g.integers(-130, 100, 4000))).astype(np.float32)
+    ref = torch.from_numpy(x).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    assert np.array_equal(O.round_to_bf16(x.astype(np.float64)), ref)
+    back = torch.from_numpy(ref.view(np.int16)).view(torch.bfloat16).to(torch.float64).numpy()
+    assert np.array_equal(O.decode_bf16(ref), back)
+
+
+def test_bf16_round_is_single_rounding_from_fp64():
+    # 1 + 2^-8 + 2^-30 lies above the midpoint between 1 and 1+2^-7; rounding
+    # through fp32 first would land exactly on the midpoint and go to 1.0.
+    v = 1.0 + 2.0 ** -8 + 2.0 ** -30
+    assert O.round_to_bf16(np.array([v]))[0] == 0x3F81
+    assert O.round_to_bf16(np.array([1.0 + 2.0 ** -8]))[0] == 0x3F80   # tie -> even
+    assert O.round_to_bf16(np.array([-0.0]))[0] == 0x8000
+
+
+# ----------------------------------------------------------------------------- indexer
+
+def test_indexer_hand_example():
+    g = json.load(open(os.path.join(GOLD, "indexer_topk_tiny.json")))
+    s = O.indexer_scores(np.array(g["q"], float), np.array(g["w"], float),
+                         np.array(g["k"], float), g["pos0"])
+    assert np.array_equal(s, np.array(g["scores"]))
+    idx, cnt = O.topk_indices(s, g["pos0"], 2)
+    assert idx.tolist() == g["top2"] and cnt.tolist() == [2]
+    idx, _ = O.topk_indices(s, g["pos0"], 3)
+    assert idx.tolist() == g["top3"]
+
+
+def test_indexer_integer_config_is_exact():
+    """Integer q/k and w on a 1/256 grid: 256*I is an integer computed exactly in int64."""
+    inp = synth.dsa_config("tiny", seed=1, L=512)
+    q = O.decode_bf16(inp.q_idx)
+    k = O.decode_bf16(inp.k_idx)
+    w = inp.w_idx.astype(np.float64)
+    s = O.indexer_scores(q, w, k, inp.pos0)
+    qi = q.astype(np.int64)
+    ki = k.astype(np.int64)
+    wi = np.rint(w * 256).astype(np.int64)
+    assert np.array_equal(wi, w * 256)
+    d = np.einsum("thd,sd->ths", qi, ki)
+    exact = np.einsum("th,ths->ts", wi, np.maximum(d, 0))
+    assert np.array_equal(s * 256, exact.astype(np.float64))
+
+
+def test_indexer_causal_mask_and_fp8_scale():
+    T, L = 3, 40
+    g = np.random.default_rng(5)
+    q = g.standard_normal((T, 16, 64))
+    w = g.random((T, 16))
+    kf = g.standard_normal((L, 64)).astype(np.float32)
+    codes, scale = synth.to_e4m3_rows(kf)
+    rows = O.dequant_rows(codes, "fp8", scale)
+    s = O.indexer_scores(q, w, rows, L - T)
+    for t in range(T):
+        assert np.all(np.isneginf(s[t, L - T + t + 1:]))
+        assert np.all(np.isfinite(s[t, :L - T + t + 1]))
+    # scaled rows: scale * (q . code) == q . (scale * code); a positive scale commutes with relu
+    unscaled = O.indexer_scores(q, w, O.decode_e4m3(codes), L - T)
+    vis = np.isfinite(s)
+    np.testing.assert_allclose(s[vis], (unscaled * scale[None, :])[vis], rtol=1e-12)
+
+
+# ----------------------------------------------------------------------------- top-k
+
+def _brute_topk(scores, pos0, k):
+    T = scores.shape[0]
+    out = []
+    for t in range(T):
+        vis = pos0 + t + 1
+        ranked = sorted(range(vis), key=lambda s: (-float(scores[t, s]), s))
+        sel = sorted(ranked[:min(k, vis)])
+        out.append(sel + [-1] * (k - len(sel)))
+    return np.array(out, np.int32)
+
+
+@pytest.mark.parametrize("seed", range(6))
+def test_topk_vs_brute_force_with_ties(seed):
+    g = np.random.default_rng(seed)
+    T, L, k = 4, 48, 9
+    scores = g.integers(0, 6, size=(T, L)).astype(np.float64)   # many ties
+    scores[:, ::7] *= -1
+    idx, cnt = O.topk_indices(scores, L - T, k)
+    assert np.array_equal(idx, _brute_topk(scores, L - T, k))
+    assert list(cnt) == [k] * T
+
+
+def test_topk_golden_tie_case_and_all_equal():
+    g = json.load(open(os.path.join(GOLD, "indexer_topk_tiny.json")))["tie_case"]
+    s = np.array(g["scores"], float)
+    assert O.topk_indices(s, g["pos0"], 2)[0].tolist() == g["top2"]
+    assert O.topk_indices(s, g["pos0"], 4)[0].tolist() == g["top4"]
+    eq = np.full((2, 100), 3.25)
+    idx, _ = O.topk_indices(eq, 98, 10)
+    assert idx.tolist() == [list(range(10))] * 2
+
+
+def test_topk_negative_zero_ties_positive_zero():
+    s = np.array([[0.0, -0.0, 0.0, -1.0]])
+    idx, _ = O.topk_indices(s, 3, 2)
+    assert idx.tolist() == [[0, 1]]
+
+
+def test_topk_visible_at_most_k_selects_all():
+    g = np.random.default_rng(1)
+    T, L, k = 3, 10, 16
+    s = g.standard_normal((T, L))
+    idx, cnt = O.topk_indices(s, L - T, k)
+    for t in range(T):
+        vis = L - T + t + 1
+        assert cnt[t] == vis
+        assert idx[t, :vis].tolist() == list(range(vis))
+        assert np.all(idx[t, vis:] == -1)
+
+
+def test_topk_permutation_invariance_tie_free():
+    g = np.random.default_rng(2)
+    L, k = 300, 37
+    s = g.standard_normal((1, L))           # continuous: no ties
+    perm = g.permutation(L)
+    idx, _ = O.topk_indices(s, L - 1, k)
+    idx_p, _ = O.topk_indices(s[:, perm], L - 1, k)
+    assert sorted(perm[idx_p[0]].tolist()) == idx[0].tolist()
+
+
+# ----------------------------------------------------------------------------- attention
+
+def _sdpa_causal(q, K, V, pos0, sm_scale):
+    """Dense causal attention via torch's library routine (fp64, CPU)."""
+    T, H, D = q.shape
+    L = K.shape[0]
+    qt = torch.from_numpy(q).permute(1, 0, 2)[None]              # [1,H,T,D]
+    kt = torch.from_numpy(K)[None, None].expand(1, H, L, D)
+    vt = torch.from_numpy(V)[None, None].expand(1, H, L, D)
+    mask = torch.zeros(T, L, dtype=torch.bool)
+    for t in range(T):
+        mask[t, :pos0 + t + 1] = True
+    o = torch.nn.functional.scaled_dot_product_attention(qt, kt, vt, attn_mask=mask, scale=sm_scale)
+    return o[0].permute(1, 0, 2).numpy()
+
+
+def test_attention_hand_example():
+    g = json.load(open(os.path.join(GOLD, "indexer_topk_tiny.json")))["attention_case"]
+    out = O.attend_rows(np.array(g["q"]), np.array(g["K"]), np.array(g["V"]), 1.0)
+    np.testing.assert_allclose(out, np.array(g["out"]), rtol=1e-14)
+
+
+def test_sparse_attention_equals_dense_when_visible_le_k():
+    g = np.random.default_rng(4)
+    T, H, D, L, k = 4, 8, 128, 60, 2048
+    q = g.standard_normal((T, H, D))
+    K = g.standard_normal((L, D))
+    V = g.standard_normal((L, D))
+    scores = g.standard_normal((T, L))
+    idx, _ = O.topk_indices(scores, L - T, k)
+    got = O.sparse_attention(q, K, V, idx, 1 / math.sqrt(D))
+    ref = _sdpa_causal(q, K, V, L - T, 1 / math.sqrt(D))
+    np.testing.assert_allclose(got, ref, rtol=1e-10, atol=1e-12)
+
+
+def test_attention_closed_forms():
+    g = np.random.default_rng(6)
+    H, D = 8, 128
+    q = g.standard_normal((H, D))
+    K = g.standard_normal((5, D))
+    V = g.standard_normal((5, D))
+    one = O.attend_rows(q, K[:1], V[:1], 0.1)
+    np.testing.assert_allclose(one, np.broadcast_to(V[0], (H, D)), rtol=1e-14)
+    Vc = np.broadcast_to(V[2], (5, D))
+    np.testing.assert_allclose(O.attend_rows(q, K, Vc, 0.1), np.broadcast_to(V[2], (H, D)), rtol=1e-13)
+    # sink: constant V scaled by 1 - p_sink
+    sink = g.standard_normal(H)
+    z = 0.1 * q @ K.T
+    p_sink = np.exp(sink) / (np.exp(z).sum(axis=1) + np.exp(sink))
+    got = O.attend_rows(q, K, Vc, 0.1, sink)
+    np.testing.assert_allclose(got, (1 - p_sink)[:, None] * V[2][None, :], rtol=1e-12)
+    # sink of -inf is no sink
+    np.testing.assert_allclose(O.attend_rows(q, K, V, 0.1, np.full(H, -np.inf)),
+                               O.attend_rows(q, K, V, 0.1), rtol=0, atol=0)
+    # order of the index list does not matter (up to fp64 rounding)
+    idx = np.array([[3, 0, 4, 1]])
+    a = O.sparse_attention(q[None], K, V, idx, 0.1)
+    b = O.sparse_attention(q[None], K, V, idx[:, ::-1], 0.1)
+    assert np.max(np.abs(a - b)) <= 1e-12
+    # skipped entries and an empty list
+    c = O.sparse_attention(q[None], K, V, np.array([[3, -1, 0, 99, 4, 1]]), 0.1)
+    np.testing.assert_array_equal(a, c)
+    assert np.all(O.sparse_attention(q[None], K, V, np.array([[-1, -1]]), 0.1) == 0)
+
+
+def test_swa_equals_dense_when_window_covers_context_and_w1_is_self():
+    g = np.random.default_rng(8)
+    T, H, D, L = 5, 8, 128, 40
+    q = g.standard_normal((T, H, D))
+    K = g.standard_normal((L, D))
+    V = g.standard_normal((L, D))
+    cap = 64
+    Kr = np.zeros((cap, D)); Vr = np.zeros((cap, D))
+    for p in range(L):
+        Kr[p % cap] = K[p]; Vr[p % cap] = V[p]
+    got = O.swa_attention(q, Kr, Vr, cap, L - T, 128, 1 / math.sqrt(D))
+    ref = _sdpa_causal(q, K, V, L - T, 1 / math.sqrt(D))
+    np.testing.assert_allclose(got, ref, rtol=1e-10, atol=1e-12)
+    w1 = O.swa_attention(q, Kr, Vr, cap, L - T, 1, 1 / math.sqrt(D))
+    for t in range(T):
+        np.testing.assert_allclose(w1[t], np.broadcast_to(V[L - T + t], (H, D)), rtol=1e-14)
+
+
+# ----------------------------------------------------------------------------- layer stages
+
+def test_rmsnorm_vs_torch_and_constant():
+    g = np.random.default_rng(9)
+    x = g.standard_normal((8, 4096))
+    gam = g.standard_normal(4096)
+    ref = torch.nn.functional.rms_norm(torch.from_numpy(x), (4096,), torch.from_numpy(gam), eps=1e-6)
+    np.testing.assert_allclose(O.rmsnorm(x, gam, 1e-6), ref.numpy(), rtol=1e-13)
+    c = 0.37
+    y = O.rmsnorm(np.full((1, 16), c), np.ones(16), 1e-6)
+    np.testing.assert_allclose(y, c / math.sqrt(c * c + 1e-6), rtol=1e-14)
+
+
+def test_rope_closed_forms_and_invariants():
+    d = 128
+    theta = 1e6
+    # pos 0 is the identity
+    g = np.random.default_rng(10)
+    x = g.standard_normal((1, 3, d))
+    assert np.array_equal(O.rope(x, [0], theta), x)
+    # unit vector e_i rotates in the (i, i + d/2) plane by pos * theta^(-2i/d)
+    for i in (0, 5, 63):
+        e = np.zeros((1, 1, d)); e[0, 0, i] = 1.0
+        p = 1000003
+        out = O.rope(e, [p], theta)[0, 0]
+        ang = p * theta ** (-2.0 * i / d)
+        assert abs(out[i] - math.cos(ang)) < 1e-7
+        assert abs(out[i + d // 2] - math.sin(ang)) < 1e-7
+        assert np.count_nonzero(out) <= 2
+    # complex formulation: (a + ib) * exp(i*angle)
+    pos = np.array([3, 77, 1048575])
+    x = g.standard_normal((3, 2, d))
+    c, s = O.rope_cos_sin(pos, d, theta)
+    z = (x[..., :d // 2] + 1j * x[..., d // 2:]) * (c + 1j * s)[:, None, :]
+    ref = np.concatenate([z.real, z.imag], axis=-1)
+    np.testing.assert_allclose(O.rope(x, pos, theta), ref, rtol=1e-13, atol=1e-13)
+    # norm and relative position (cos/sin are fp32-rounded, so 1e-6)
+    y = O.rope(x, pos, theta)
+    np.testing.assert_allclose(np.linalg.norm(y, axis=-1), np.linalg.norm(x, axis=-1), rtol=1e-6)
+    qv = g.standard_normal((1, 1, d)); kv = g.standard_normal((1, 1, d))
+    a = np.sum(O.rope(qv, [500], theta) * O.rope(kv, [200], theta))
+    b = np.sum(O.rope(qv, [900500], theta) * O.rope(kv, [900200], theta))
+    assert abs(a - b) <= 1e-5 * (np.linalg.norm(qv) * np.linalg.norm(kv))
+
+
+def test_quantize_rows_vs_torch_cast_and_bounds():
+    g = np.random.default_rng(11)
+    rows = O.bf16_round_trip(g.standard_normal((64, 64)) * 3)
+    rows[5] = 0.0
+    codes, scale = O.quantize_rows_e4m3(rows)
+    assert scale[5] == 1.0 and np.all(codes[5] & 0x7F == 0)
+    amax = np.max(np.abs(rows), axis=1)
+    np.testing.assert_array_equal(scale[amax > 0], (amax[amax > 0] / 448.0).astype(np.float32))
+    # the division and cast done by the library give the same codes
+    xs = (torch.from_numpy(rows.astype(np.float32)) / torch.from_numpy(scale)[:, None])
+    ref = xs.to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    np.testing.assert_array_equal(codes, ref)
+    # the largest magnitude of each nonzero row maps to +-448
+    deq = O.dequant_rows(codes, "fp8", scale)
+    nz = amax > 0
+    assert np.all(np.max(np.abs(O.decode_e4m3(codes[nz])), axis=1) == 448.0)
+    # relative error of normal codes <= 2^-4
+    big = np.abs(rows) >= (2.0 ** -6) * scale[:, None]
+    assert np.all(np.abs(deq - rows)[big] <= 2.0 ** -4 * np.abs(rows)[big])
+
+
+def test_project_with_permutation_weights_is_exact_selection():
+    g = np.random.default_rng(12)
+    y = O.bf16_round_trip(g.standard_normal((8, 32)))
+    perm = g.permutation(32)[:20]
+    W = np.zeros((20, 32)); W[np.arange(20), perm] = 1.0
+    assert np.array_equal(O.project(y, W), y[:, perm])
+
+
+# ----------------------------------------------------------------------------- layer step
+
+def _small_dsa_layer(seed, L, T, w_std=0.02, top_k=2048):
+    lay = synth.layer_inputs("dsa", 0, L, T, seed=seed, w_std=w_std)
+    cache = {"k": lay.k.copy(), "v": lay.v.copy(), "k_idx": lay.k_idx.copy(),
+             "k_idx_scale": lay.k_idx_scale.copy()}
+    return lay, cache
+
+
+def test_layer_step_zero_output_projection_is_residual():
+    T, L = 2, 64
+    lay, cache = _small_dsa_layer(0, L, T)
+    x = synth.module_x(0, T)
+    w_o = np.zeros_like(lay.w_o)
+    r = O.layer_step("dsa", x, lay.gamma, lay.w_qkvi, w_o, cache, L - T, top_k=16)
+    np.testing.assert_array_equal(r["x_out"], O.decode_bf16(x))
+
+
+def test_layer_step_zero_query_projection_averages_selected_values():
+    """Q weights 0 => every logit 0 => each head's output is the plain mean of
+    the selected V rows (rounded to bf16)."""
+    T, L, k = 3, 200, 32
+    lay, cache = _small_dsa_layer(1, L, T)
+    w = lay.w_qkvi.copy()
+    w[:1024] = 0
+    x = synth.module_x(1, T)
+    r = O.layer_step("dsa", x, lay.gamma, w, lay.w_o, cache, L - T, top_k=k)
+    V = O.decode_bf16(cache["v"])
+    for t in range(T):
+        sel = r["idx"][t][r["idx"][t] >= 0]
+        assert len(sel) == k
+        mean = V[sel].mean(axis=0)
+        ref = O.bf16_round_trip(np.tile(mean, 8))
+        np.testing.assert_array_equal(r["attn"][t], ref)
+
+
+def test_layer_step_dsa_with_short_context_is_dense_attention():
+    T, L = 4, 50
+    lay, cache = _small_dsa_layer(2, L, T)
+    x = synth.module_x(2, T)
+    r = O.layer_step("dsa", x, lay.gamma, lay.w_qkvi, lay.w_o, cache, L - T, top_k=2048)
+    q = r["qkv"][:, :1024].reshape(T, 8, 128)
+    K = O.decode_bf16(cache["k"][:L]); V = O.decode_bf16(cache["v"][:L])
+    dense = _sdpa_causal(q, K, V, L - T, 1 / math.sqrt(128)).reshape(T, 1024)
+    np.testing.assert_array_equal(r["attn"], O.bf16_round_trip(dense))
+    # the new rows were appended before attention and quantised indexer keys written
+    assert np.array_equal(cache["k"][L - T:L], O.round_to_bf16(r["qkv"][:, 1024:1152]))
+    assert np.array_equal(cache["k_idx"][L - T:L], r["k_idx_codes"])
+
+
+def test_layer_step_swa_small_context_is_dense():
+    T, L = 3, 20
+    lay = synth.layer_inputs("swa", 0, L, T, seed=3, ring_cap=160)
+    cache = {"k": lay.k.copy(), "v": lay.v.copy(), "ring_cap": 160}
+    x = synth.module_x(3, T)
+    r = O.layer_step("swa", x, lay.gamma, lay.w_qkvi, lay.w_o, cache, L - T)
+    q = r["qkv"][:, :1024].reshape(T, 8, 128)
+    K = O.decode_bf16(cache["k"][:L]); V = O.decode_bf16(cache["v"][:L])
+    dense = _sdpa_causal(q, K, V, L - T, 1 / math.sqrt(128)).reshape(T, 1024)
+    np.testing.assert_array_equal(r["attn"], O.bf16_round_trip(dense))

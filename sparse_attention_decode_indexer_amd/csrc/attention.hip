@@ -1,0 +1,287 @@
+// Split-K GQA attention over a list of cache rows, for gfx950.
+//
+// Method: NaiveAI, "Naive-N0.5-Flash: Building Frontier AI with AI".
+//   §Model Architecture: attention runs only over the positions the indexer selected.
+//   §Hybrid SWA-DSA Architecture: GQA (eight query heads of this GPU share one KV head),
+//     a 128-token sliding window for SWA layers, a sink bias in both attention types.
+//   §Optimizing inside the kernel: the selected K/V rows are staged on chip split by split
+//     before the math; the eight heads are mapped so the matrix unit is not padded by
+//     heads (here: heads are the N side of a 16x16x32 MFMA, rows the M side).
+//
+// One workgroup = one (token, split of 64 list entries).  It stages the split's K and V
+// rows in LDS with 16-byte coalesced loads, computes S = K q^T on the matrix cores,
+// runs the softmax of the split in fp32 (base-2 exponentials of log2e-scaled logits),
+// accumulates P V, and writes (m, l, acc) to the workspace.  The last workgroup of a
+// token (atomic counter) merges the splits in split order, so the result does not
+// depend on which workgroup merges or on timing.
+#include "dsa_common.h"
+#include "dsa_kernels.h"
+
+namespace dsa {
+
+constexpr int kAttnThreads = 256;
+constexpr int kSplitRows = 64;
+constexpr int kPartStride = 132;  // floats per (token, split, head): m, l, pad x2, acc[128]
+
+struct AttnParams {
+  const uint16_t* q;      // [T][8][128] bf16
+  const uint8_t* kc;      // cache rows (bf16: 256 B, e4m3: 128 B)
+  const uint8_t* vc;
+  const float* ks;        // [rows] fp32 (e4m3 only)
+  const float* vs;
+  const int32_t* idx;     // MODE 0: [T][k]
+  int k;
+  int T;
+  int64_t L;              // MODE 0: valid row range [0, L)
+  int64_t ring_cap;       // MODE 1
+  int64_t pos0;           // MODE 1
+  int window;             // MODE 1
+  float sm_log2;          // sm_scale * log2(e)
+  const float* sink;      // [8] natural-log logits or nullptr
+  void* out;
+  int out_f32;
+  float* part;            // [T][nsplit][8][kPartStride]
+  uint32_t* ctr;          // [T] counters, stride 64 words
+  int nsplit;
+};
+
+template <int KVDT>
+struct AttnShared {
+  static constexpr int RB = KVDT == 0 ? 256 : 128;   // bytes per cache row
+  static constexpr int KSTRIDE = RB + 16;            // padded K row stride
+  int64_t rows[kSplitRows];
+  alignas(16) uint8_t kst[kSplitRows * KSTRIDE];
+  alignas(16) uint8_t vst[kSplitRows * RB];
+  float kscl[kSplitRows];
+  float vscl[kSplitRows];
+  float s[kHq][kSplitRows];
+  uint32_t last;
+};
+
+template <int KVDT, int MODE>
+__global__ void __launch_bounds__(kAttnThreads) attn_kernel(AttnParams p) {
+  using SH = AttnShared<KVDT>;
+  __shared__ SH sh;
+  constexpr int RB = SH::RB;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int split = blockIdx.x;
+  const int t = blockIdx.y;
+  // ---- row list of this split
+  if (tid < kSplitRows) {
+    const int e = split * kSplitRows + tid;
+    int64_t r = -1;
+    if (MODE == 0) {
+      if (e < p.k) {
+        const int32_t v = p.idx[(size_t)t * p.k + e];
+        if (v >= 0 && (int64_t)v < p.L) r = v;
+      }
+    } else {
+      const int64_t pos = p.pos0 + t - p.window + 1 + e;
+      if (e < p.window && pos >= 0) r = pos % p.ring_cap;
+    }
+    sh.rows[tid] = r;
+    if (KVDT == 1) {
+      sh.kscl[tid] = r >= 0 ? p.ks[r] : 0.0f;
+      sh.vscl[tid] = r >= 0 ? p.vs[r] : 0.0f;
+    }
+  }
+  __syncthreads();
+  // ---- stage K and V rows (16-byte chunks, one row per RB/16 consecutive threads)
+  {
+    constexpr int CPR = RB / 16;
+    for (int c = tid; c < kSplitRows * CPR; c += kAttnThreads) {
+      const int row = c / CPR, col = c % CPR;
+      const int64_t r = sh.rows[row];
+      uint4 kv = make_uint4(0u, 0u, 0u, 0u), vv = kv;
+      if (r >= 0) {
+        kv = *reinterpret_cast<const uint4*>(p.kc + r * RB + col * 16);
+        vv = *reinterpret_cast<const uint4*>(p.vc + r * RB + col * 16);
+      }
+      *reinterpret_cast<uint4*>(&sh.kst[row * SH::KSTRIDE + col * 16]) = kv;
+      *reinterpret_cast<uint4*>(&sh.vst[row * RB + col * 16]) = vv;
+    }
+  }
+  // ---- q^T operand (heads on the N side): lane l -> head l%16 (< 8 real), dims kb*32 + (l/16)*8
+  Frag8 qb[4];
+  {
+    const int h = lane & 15;
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb) {
+      if (h < kHq)
+        qb[kb].u = *reinterpret_cast<const uint4*>(p.q + ((size_t)t * kHq + h) * kD + kb * 32 + (lane >> 4) * 8);
+      else
+        qb[kb].u = make_uint4(0u, 0u, 0u, 0u);
+    }
+  }
+  __syncthreads();
+  // ---- S = K q^T: wave w owns rows 16w .. 16w+15
+  {
+    f32x4_t acc = {};
+    const int row = wave * 16 + (lane & 15);
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb) {
+      Frag8 a;
+      const int d0 = kb * 32 + (lane >> 4) * 8;
+      if constexpr (KVDT == 0) {
+        a.u = *reinterpret_cast<const uint4*>(&sh.kst[row * SH::KSTRIDE + d0 * 2]);
+      } else {
+        const uint2 raw = *reinterpret_cast<const uint2*>(&sh.kst[row * SH::KSTRIDE + d0]);
+        bf16x2_t x0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)raw.x, 1.0f, false);
+        bf16x2_t x1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)raw.x, 1.0f, true);
+        bf16x2_t x2 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)raw.y, 1.0f, false);
+        bf16x2_t x3 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)raw.y, 1.0f, true);
+        a.v = bf16x8_t{x0[0], x0[1], x1[0], x1[1], x2[0], x2[1], x3[0], x3[1]};
+      }
+      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a.v, qb[kb].v, acc, 0, 0, 0);
+    }
+    const int h = lane & 15;
+    if (h < kHq) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int rr = wave * 16 + (lane >> 4) * 4 + i;
+        float z = acc[i];
+        if (KVDT == 1) z *= sh.kscl[rr];
+        sh.s[h][rr] = (sh.rows[rr] >= 0) ? z * p.sm_log2 : -__builtin_inff();
+      }
+    }
+  }
+  __syncthreads();
+  // ---- softmax of the split: thread (h = tid/32, j = tid%32) holds rows j and j+32
+  const int h = tid >> 5;
+  const int jj = tid & 31;
+  float m, l;
+  {
+    const float z0 = sh.s[h][jj], z1 = sh.s[h][jj + 32];
+    m = fmaxf(z0, z1);
+#pragma unroll
+    for (int d = 16; d >= 1; d >>= 1) m = fmaxf(m, __shfl_xor(m, d, 64));
+    float p0 = 0.0f, p1 = 0.0f;
+    if (m != -__builtin_inff()) {
+      p0 = exp2f(z0 - m);
+      p1 = exp2f(z1 - m);
+    }
+    l = p0 + p1;
+#pragma unroll
+    for (int d = 16; d >= 1; d >>= 1) l += __shfl_xor(l, d, 64);
+    if (KVDT == 1) {
+      p0 *= sh.vscl[jj];
+      p1 *= sh.vscl[jj + 32];
+    }
+    sh.s[h][jj] = p0;
+    sh.s[h][jj + 32] = p1;
+  }
+  __syncthreads();
+  // ---- acc[h][d4..d4+3] = sum_j p[h][j] * V[j][d4..d4+3]
+  const int d4 = jj * 4;
+  float acc[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+  for (int j = 0; j < kSplitRows; ++j) {
+    const float pj = sh.s[h][j];
+    float v[4];
+    if constexpr (KVDT == 0) {
+      const uint2 raw = *reinterpret_cast<const uint2*>(&sh.vst[j * RB + d4 * 2]);
+      v[0] = __uint_as_float(raw.x << 16);
+      v[1] = __uint_as_float(raw.x & 0xffff0000u);
+      v[2] = __uint_as_float(raw.y << 16);
+      v[3] = __uint_as_float(raw.y & 0xffff0000u);
+    } else {
+      const uint32_t raw = *reinterpret_cast<const uint32_t*>(&sh.vst[j * RB + d4]);
+      auto lo = __builtin_amdgcn_cvt_pk_f32_fp8((int)raw, false);
+      auto hi = __builtin_amdgcn_cvt_pk_f32_fp8((int)raw, true);
+      v[0] = lo[0]; v[1] = lo[1]; v[2] = hi[0]; v[3] = hi[1];
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) acc[i] = fmaf(pj, v[i], acc[i]);
+  }
+  // ---- publish the split's partial
+  float* part = p.part + (((size_t)t * p.nsplit + split) * kHq + h) * kPartStride;
+  if (jj == 0) {
+    astf(part + 0, m);
+    astf(part + 1, l);
+  }
+#pragma unroll
+  for (int i = 0; i < 4; ++i) astf(part + 4 + d4 + i, acc[i]);
+  vm_wait_all();
+  __syncthreads();
+  if (tid == 0) sh.last = (aadd(p.ctr + 64 * t, 1u) == (uint32_t)p.nsplit - 1u) ? 1u : 0u;
+  __syncthreads();
+  if (!sh.last) return;
+  // ---- merge of all splits of token t, in split order
+  const float* pt = p.part + (size_t)t * p.nsplit * kHq * kPartStride;
+  float M = -__builtin_inff();
+  for (int s = 0; s < p.nsplit; ++s) M = fmaxf(M, aldf(pt + ((size_t)s * kHq + h) * kPartStride));
+  float sink2 = -__builtin_inff();
+  if (p.sink) sink2 = p.sink[h] * 1.4426950408889634f;
+  M = fmaxf(M, sink2);
+  float den = 0.0f;
+  float o[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+  if (M != -__builtin_inff()) {
+    for (int s = 0; s < p.nsplit; ++s) {
+      const float* ps = pt + ((size_t)s * kHq + h) * kPartStride;
+      const float ms = aldf(ps);
+      if (ms == -__builtin_inff()) continue;
+      const float sc = exp2f(ms - M);
+      den = fmaf(aldf(ps + 1), sc, den);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) o[i] = fmaf(aldf(ps + 4 + d4 + i), sc, o[i]);
+    }
+    if (sink2 != -__builtin_inff()) den += exp2f(sink2 - M);
+  }
+#pragma unroll
+  for (int i = 0; i < 4; ++i) o[i] = den > 0.0f ? o[i] / den : 0.0f;
+  const size_t ob = ((size_t)t * kHq + h) * kD + d4;
+  if (p.out_f32) {
+    float* of = static_cast<float*>(p.out) + ob;
+    *reinterpret_cast<float4*>(of) = make_float4(o[0], o[1], o[2], o[3]);
+  } else {
+    uint16_t* ob16 = static_cast<uint16_t*>(p.out) + ob;
+    const uint32_t w0 = (uint32_t)f32_to_bf16(o[0]) | ((uint32_t)f32_to_bf16(o[1]) << 16);
+    const uint32_t w1 = (uint32_t)f32_to_bf16(o[2]) | ((uint32_t)f32_to_bf16(o[3]) << 16);
+    *reinterpret_cast<uint2*>(ob16) = make_uint2(w0, w1);
+  }
+  if (tid == 0) ast(p.ctr + 64 * t, 0u);
+}
+
+size_t attn_workspace_bytes(int T, int nsplit) {
+  return ctl::kBytes + (size_t)T * nsplit * kHq * kPartStride * sizeof(float);
+}
+
+int attn_splits(int list_len) { return (list_len + kSplitRows - 1) / kSplitRows; }
+
+hipError_t launch_attention(int mode, int kvdt, const void* q, const void* kc, const void* vc,
+                            const float* ks, const float* vs, const int32_t* idx, int k, int T,
+                            int64_t L, int64_t ring_cap, int64_t pos0, int window, float sm_scale,
+                            const float* sink, void* out, int out_f32, void* ws, hipStream_t st) {
+  AttnParams p{};
+  p.q = static_cast<const uint16_t*>(q);
+  p.kc = static_cast<const uint8_t*>(kc);
+  p.vc = static_cast<const uint8_t*>(vc);
+  p.ks = ks;
+  p.vs = vs;
+  p.idx = idx;
+  p.k = k;
+  p.T = T;
+  p.L = L;
+  p.ring_cap = ring_cap;
+  p.pos0 = pos0;
+  p.window = window;
+  p.sm_log2 = sm_scale * 1.4426950408889634f;
+  p.sink = sink;
+  p.out = out;
+  p.out_f32 = out_f32;
+  p.nsplit = attn_splits(mode == 0 ? k : window);
+  uint8_t* w8 = static_cast<uint8_t*>(ws);
+  p.ctr = reinterpret_cast<uint32_t*>(w8) + ctl::kDone;
+  p.part = reinterpret_cast<float*>(w8 + ctl::kBytes);
+  const dim3 grid(p.nsplit, T), block(kAttnThreads);
+  if (mode == 0) {
+    if (kvdt == 0) hipLaunchKernelGGL((attn_kernel<0, 0>), grid, block, 0, st, p);
+    else hipLaunchKernelGGL((attn_kernel<1, 0>), grid, block, 0, st, p);
+  } else {
+    hipLaunchKernelGGL((attn_kernel<0, 1>), grid, block, 0, st, p);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace dsa

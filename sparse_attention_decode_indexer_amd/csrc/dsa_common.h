@@ -1,0 +1,253 @@
+// Device-side building blocks shared by the gfx950 kernels: number formats, the
+// MFMA operand types, order-preserving keys, block scans and the grid barrier.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace dsa {
+
+#define DSA_DEV __device__ __forceinline__
+
+constexpr int kHq = 8;       // query heads per GPU share
+constexpr int kD = 128;      // head width
+constexpr int kHI = 16;      // indexer heads
+constexpr int kDI = 64;      // indexer head width
+constexpr int kMaxT = 8;     // verify block
+constexpr int kMaxTopK = 2048;
+constexpr int kHidden = 4096;
+constexpr int kNProjDSA = kHq * kD + 2 * kD + kHI * kDI + kDI + kHI;  // 2384
+constexpr int kNProjSWA = kHq * kD + 2 * kD;                          // 1280
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+
+union Frag8 {           // eight bf16 = one MFMA A/B operand of the K=16/K=32 shapes
+  bf16x8_t v;
+  uint4 u;
+  uint32_t w[4];
+};
+
+// ----------------------------------------------------------------------------- formats
+
+DSA_DEV float bf16_to_f32(uint16_t b) { return __uint_as_float((uint32_t)b << 16); }
+
+// fp32 -> bf16, round to nearest even (NaN kept quiet)
+DSA_DEV uint16_t f32_to_bf16(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7f800000u) == 0x7f800000u && (u & 0x7fffffu)) return (uint16_t)((u >> 16) | 0x40);
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return (uint16_t)(u >> 16);
+}
+
+DSA_DEV float round_bf16(float f) { return bf16_to_f32(f32_to_bf16(f)); }
+
+// OCP e4m3fn code -> fp32, exact (integer construction of the IEEE bits)
+DSA_DEV float e4m3_to_f32(uint32_t c) {
+  uint32_t s = (c & 0x80u) << 24;
+  uint32_t e = (c >> 3) & 0xFu;
+  uint32_t m = c & 7u;
+  if (e == 15u && m == 7u) return __uint_as_float(0x7fc00000u | s);
+  if (e == 0u) {                       // subnormal: m * 2^-9, exact in fp32
+    float v = (float)m * 0x1p-9f;
+    return __uint_as_float(__float_as_uint(v) | s);
+  }
+  return __uint_as_float(s | ((e + 120u) << 23) | (m << 20));
+}
+
+// fp32 -> e4m3fn code: nearest, ties to even, saturating at +-448; sign kept (also for 0).
+DSA_DEV uint32_t f32_to_e4m3(float x) {
+  uint32_t u = __float_as_uint(x);
+  uint32_t s = (u >> 24) & 0x80u;
+  float a = fminf(fabsf(x), 448.0f);
+  uint32_t au = __float_as_uint(a);
+  int e = (int)(au >> 23) - 127;       // unbiased exponent of a (a > 0)
+  if (a == 0.0f) return s;
+  uint32_t code;
+  if (e < -6) {
+    // subnormal range: quantum 2^-9; a * 2^9 in [0, 8), exact scaling
+    float r = a * 512.0f;
+    float f = floorf(r);
+    float rem = r - f;                 // exact
+    uint32_t q = (uint32_t)f;
+    if (rem > 0.5f || (rem == 0.5f && (q & 1u))) q += 1u;
+    code = q;                          // q == 8 is the smallest normal (code 8) -- consistent
+  } else {
+    // normal: 3 mantissa bits; round the 23-bit fraction to 3 bits
+    uint32_t mant = au & 0x7fffffu;
+    uint32_t keep = mant >> 20;
+    uint32_t rest = mant & 0xfffffu;
+    uint32_t half = 0x80000u;
+    uint32_t q = ((uint32_t)(e + 7) << 3) | keep;
+    if (rest > half || (rest == half && (q & 1u))) q += 1u;
+    code = q;                          // a <= 448 so q <= 126 after rounding
+  }
+  return s | code;
+}
+
+// ----------------------------------------------------------------------------- keys
+
+// Order-preserving map fp32 -> uint32 (larger score <=> larger key); -0 maps like +0.
+DSA_DEV uint32_t order_key(float f) {
+  uint32_t u = __float_as_uint(f);
+  if (u == 0x80000000u) u = 0u;
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+// ----------------------------------------------------------------------------- scans
+
+// Inclusive prefix sum across one wavefront (64 lanes).
+DSA_DEV uint32_t wave_incl_scan(uint32_t v) {
+  const int lane = threadIdx.x & 63;
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    uint32_t o = __shfl_up(v, d, 64);
+    if (lane >= d) v += o;
+  }
+  return v;
+}
+
+DSA_DEV uint32_t wave_sum(uint32_t v) {
+#pragma unroll
+  for (int d = 32; d >= 1; d >>= 1) v += __shfl_xor(v, d, 64);
+  return v;
+}
+
+DSA_DEV uint32_t wave_max_u32(uint32_t v) {
+#pragma unroll
+  for (int d = 32; d >= 1; d >>= 1) v = max(v, (uint32_t)__shfl_xor(v, d, 64));
+  return v;
+}
+
+DSA_DEV uint32_t wave_min_u32(uint32_t v) {
+#pragma unroll
+  for (int d = 32; d >= 1; d >>= 1) v = min(v, (uint32_t)__shfl_xor(v, d, 64));
+  return v;
+}
+
+DSA_DEV float wave_max_f32(float v) {
+#pragma unroll
+  for (int d = 32; d >= 1; d >>= 1) v = fmaxf(v, __shfl_xor(v, d, 64));
+  return v;
+}
+
+// Exclusive prefix sum across the block; `scratch` holds >= nwaves+1 words of LDS.
+// Returns the exclusive prefix; *total receives the block sum.  All threads must call.
+template <int NT>
+DSA_DEV uint32_t block_excl_scan(uint32_t v, uint32_t* scratch, uint32_t* total) {
+  constexpr int NW = NT / 64;
+  const int lane = threadIdx.x & 63;
+  const int wid = threadIdx.x >> 6;
+  uint32_t inc = wave_incl_scan(v);
+  if (lane == 63) scratch[wid] = inc;
+  __syncthreads();
+  if (wid == 0) {
+    uint32_t t = (lane < NW) ? scratch[lane] : 0u;
+    uint32_t ti = wave_incl_scan(t);
+    if (lane < NW) scratch[lane] = ti - t;   // exclusive wave offsets
+    if (lane == NW - 1) scratch[NW] = ti;
+  }
+  __syncthreads();
+  uint32_t res = scratch[wid] + inc - v;
+  *total = scratch[NW];
+  __syncthreads();
+  return res;
+}
+
+template <int NT>
+DSA_DEV uint32_t block_max_u32(uint32_t v, uint32_t* scratch) {
+  constexpr int NW = NT / 64;
+  v = wave_max_u32(v);
+  if ((threadIdx.x & 63) == 0) scratch[threadIdx.x >> 6] = v;
+  __syncthreads();
+  uint32_t r = scratch[0];
+#pragma unroll
+  for (int i = 1; i < NW; ++i) r = max(r, scratch[i]);
+  __syncthreads();
+  return r;
+}
+
+template <int NT>
+DSA_DEV uint32_t block_min_u32(uint32_t v, uint32_t* scratch) {
+  constexpr int NW = NT / 64;
+  v = wave_min_u32(v);
+  if ((threadIdx.x & 63) == 0) scratch[threadIdx.x >> 6] = v;
+  __syncthreads();
+  uint32_t r = scratch[0];
+#pragma unroll
+  for (int i = 1; i < NW; ++i) r = min(r, scratch[i]);
+  __syncthreads();
+  return r;
+}
+
+// ----------------------------------------------------------------------------- coherent access
+
+// Data that crosses workgroups inside one launch is written and read only through these
+// agent-scope relaxed atomics (sc1 loads/stores on gfx950: coherent across the XCDs' L2s
+// without writing back or invalidating whole caches).  A producer orders its stores
+// before a later signal with vm_wait_all() (all of its own vector memory operations done).
+DSA_DEV uint32_t ald(const uint32_t* p) { return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT); }
+DSA_DEV uint64_t ald64(const uint64_t* p) { return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT); }
+DSA_DEV float aldf(const float* p) { return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT); }
+DSA_DEV void ast(uint32_t* p, uint32_t v) { __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT); }
+DSA_DEV void ast64(uint64_t* p, uint64_t v) { __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT); }
+DSA_DEV void astf(float* p, float v) { __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT); }
+DSA_DEV uint32_t aadd(uint32_t* p, uint32_t v) { return __hip_atomic_fetch_add(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT); }
+DSA_DEV uint32_t amax(uint32_t* p, uint32_t v) { return __hip_atomic_fetch_max(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT); }
+DSA_DEV void vm_wait_all() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
+// Control words of a workspace (uint32 index; every counter on its own 256-byte line).
+namespace ctl {
+constexpr int kGroup = 0;        // 8 arrival counters, stride 64
+constexpr int kTop = 512;        // group arrivals
+constexpr int kGen = 576;        // barrier generation
+constexpr int kError = 640;      // sticky error word (1 = a wait timed out)
+constexpr int kTau = 704;        // [8] ~tau per token
+constexpr int kDone = 1024;      // [8] per-token completion counters, stride 64
+constexpr int kWords = 1536;
+constexpr size_t kBytes = 8192;
+}  // namespace ctl
+
+constexpr uint64_t kSpinLimit = 20000000ull;   // 0.2 s of the 100 MHz real-time counter
+
+// Grid barrier for `nblocks` co-resident workgroups: two-level arrival (eight groups by
+// blockIdx % 8, i.e. by XCD, then one top counter), release by a generation word.
+// Counters return to zero at every release.  A wait longer than kSpinLimit sets the
+// sticky error word and gives up, so a launch whose workgroups are not all resident
+// ends instead of hanging.  Only data exchanged through the coherent accessors above
+// is guaranteed visible after the barrier.
+DSA_DEV void grid_barrier(uint32_t* c, uint32_t nblocks) {
+  vm_wait_all();
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    const uint32_t g0 = ald(c + ctl::kGen);
+    const uint32_t grp = blockIdx.x & 7u;
+    const uint32_t gsize = (nblocks >> 3) + (grp < (nblocks & 7u) ? 1u : 0u);
+    const uint32_t ngroups = nblocks < 8u ? nblocks : 8u;
+    bool last = false;
+    if (aadd(c + ctl::kGroup + 64 * grp, 1u) == gsize - 1u) {
+      ast(c + ctl::kGroup + 64 * grp, 0u);
+      if (aadd(c + ctl::kTop, 1u) == ngroups - 1u) {
+        ast(c + ctl::kTop, 0u);
+        last = true;
+      }
+    }
+    if (last) {
+      vm_wait_all();
+      aadd(c + ctl::kGen, 1u);
+    } else {
+      const uint64_t t0 = __builtin_amdgcn_s_memrealtime();
+      while (ald(c + ctl::kGen) == g0) {
+        __builtin_amdgcn_s_sleep(1);
+        if (__builtin_amdgcn_s_memrealtime() - t0 > kSpinLimit) {
+          ast(c + ctl::kError, 1u);
+          break;
+        }
+      }
+    }
+  }
+  __syncthreads();
+}
+
+}  // namespace dsa

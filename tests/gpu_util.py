@@ -1,0 +1,52 @@
+"""Helpers for the GPU parity tests: uploads of synthetic inputs and comparison rules."""
+import numpy as np
+import torch
+
+DEV = "cuda:0"
+
+
+def up(a, dtype=None):
+    """numpy -> device tensor (bf16 bit patterns travel as int16, e4m3 codes as uint8)."""
+    a = np.ascontiguousarray(a)
+    if a.dtype == np.uint16:
+        a = a.view(np.int16)
+    t = torch.from_numpy(a).to(DEV)
+    return t if dtype is None else t.to(dtype)
+
+
+def down(t):
+    return t.detach().cpu().numpy()
+
+
+def bf16_bits(t):
+    """device int16/bfloat16 tensor -> numpy uint16 bit patterns"""
+    if t.dtype == torch.bfloat16:
+        t = t.view(torch.int16)
+    return down(t).view(np.uint16)
+
+
+def tie_band_ok(idx_gpu, idx_ref, scores_ref, mag_ref, pos0, k, rel=2.0 ** -16):
+    """Index sets may differ only in positions whose exact score is within the
+    rounding band of the k-th score.  Returns (ok, number of differing positions)."""
+    T = idx_gpu.shape[0]
+    ndiff = 0
+    for t in range(T):
+        g = set(int(x) for x in idx_gpu[t] if x >= 0)
+        r = set(int(x) for x in idx_ref[t] if x >= 0)
+        if len(g) != len(r):
+            return False, -1
+        sym = g ^ r
+        if not sym:
+            continue
+        ndiff += len(sym)
+        vis = pos0 + t + 1
+        s = scores_ref[t, :vis]
+        order = np.lexsort((np.arange(vis), -s))
+        kk = min(k, vis)
+        s_theta = order[kk - 1]
+        theta = s[s_theta]
+        for p in sym:
+            band = rel * max(mag_ref[t, p], mag_ref[t, s_theta])
+            if abs(s[p] - theta) > band:
+                return False, ndiff
+    return True, ndiff

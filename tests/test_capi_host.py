@@ -1,0 +1,96 @@
+"""Host-side checks of the C ABI (no GPU needed): the library loads, exports every
+symbol include/dsa.h declares, sizes workspaces, and rejects bad arguments before
+launching anything."""
+import ctypes as C
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HDR = os.path.join(ROOT, "include", "dsa.h")
+
+
+def _declared():
+    txt = open(HDR).read()
+    pat = r"^(?:dsa_status_t|size_t|int64_t|const char\s*\*)\s*(\w+)\s*\("
+    return sorted(set(re.findall(pat, txt, flags=re.M)))
+
+
+def test_library_exports_every_declared_symbol():
+    import sparse_attention_decode_indexer_amd as dsa
+    names = _declared()
+    assert set(dsa.EXPORTS) == set(names), names
+    lib = C.CDLL(dsa.LIB_PATH)
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_status_strings():
+    import sparse_attention_decode_indexer_amd as dsa
+    for s in range(8):
+        assert dsa.dsa_status_string(s)
+    assert dsa.dsa_status_string(0) == "ok"
+
+
+def test_workspace_sizes_are_monotone_and_cover_candidates():
+    import sparse_attention_decode_indexer_amd as dsa
+    small = dsa.dsa_workspace_bytes(dsa.WS_INDEX_TOPK, 8, 65536, 2048)
+    big = dsa.dsa_workspace_bytes(dsa.WS_INDEX_TOPK, 8, 1 << 20, 2048)
+    assert 0 < small < big
+    assert big >= 8 * (1 << 20) * 8            # every position can be a candidate
+    assert dsa.dsa_workspace_bytes(dsa.WS_SPARSE_ATTN, 8, 1 << 20, 2048) >= 8 * 32 * 8 * 130 * 4
+    assert dsa.dsa_workspace_bytes(dsa.WS_LAYER_DSA, 8, 1 << 20, 2048) > big
+    assert dsa.dsa_workspace_bytes(dsa.WS_LAYER_SWA, 8, 1 << 20, 128) > 0
+    assert dsa.dsa_workspace_bytes(dsa.WS_TOPK, 0, 100, 10) == 0
+
+
+FAKE = 0x10000          # aligned, never dereferenced: every call below fails validation first
+MIS = 0x10004           # misaligned
+
+
+def test_validation_errors_without_launch():
+    import sparse_attention_decode_indexer_amd as dsa
+    E = {v: k for k, v in dsa.STATUS.items()}
+    f = lambda *a, **k: dsa.dsa_indexer_scores(*a, stream=0, raise_on_error=False, **k)
+    assert f(None, FAKE, FAKE, None, dsa.BF16, 1, 100, 99, FAKE, 100) == E["DSA_ERR_NULL"]
+    assert f(FAKE, FAKE, FAKE, None, 7, 1, 100, 99, FAKE, 100) == E["DSA_ERR_DTYPE"]
+    assert f(FAKE, FAKE, FAKE, None, dsa.FP8_E4M3, 1, 100, 99, FAKE, 100) == E["DSA_ERR_DTYPE"]
+    assert f(FAKE, FAKE, FAKE, FAKE, dsa.BF16, 1, 100, 99, FAKE, 100) == E["DSA_ERR_DTYPE"]
+    assert f(FAKE, FAKE, FAKE, None, dsa.BF16, 9, 100, 90, FAKE, 100) == E["DSA_ERR_SHAPE"]
+    assert f(FAKE, FAKE, FAKE, None, dsa.BF16, 0, 100, 90, FAKE, 100) == E["DSA_ERR_SHAPE"]
+    assert f(FAKE, FAKE, FAKE, None, dsa.BF16, 2, 100, 99, FAKE, 100) == E["DSA_ERR_SHAPE"]   # pos0+T > L
+    assert f(FAKE, FAKE, FAKE, None, dsa.BF16, 1, 100, 99, FAKE, 98) == E["DSA_ERR_SHAPE"]    # ld < L
+    assert f(FAKE, FAKE, FAKE, None, dsa.BF16, 1, 100, 99, FAKE, 102) == E["DSA_ERR_SHAPE"]   # ld % 4
+    assert f(MIS, FAKE, FAKE, None, dsa.BF16, 1, 100, 99, FAKE, 100) == E["DSA_ERR_ALIGN"]
+    t = lambda *a: dsa.dsa_topk(*a, stream=0, raise_on_error=False)
+    assert t(FAKE, 1, 100, 100, 99, 0, FAKE, None, FAKE, 1 << 30) == E["DSA_ERR_SHAPE"]        # k = 0
+    assert t(FAKE, 1, 100, 100, 99, 2049, FAKE, None, FAKE, 1 << 30) == E["DSA_ERR_SHAPE"]
+    assert t(FAKE, 1, 100, 100, 99, 16, FAKE, None, FAKE, 16) == E["DSA_ERR_WORKSPACE"]
+    assert t(FAKE, 1, 100, 100, 99, 16, None, None, FAKE, 1 << 30) == E["DSA_ERR_NULL"]
+    too_long = dsa.dsa_max_context() + 8
+    assert t(FAKE, 1, too_long, too_long, too_long - 1, 16, FAKE, None, FAKE, 1 << 40) == E["DSA_ERR_SHAPE"]
+    a = lambda *x: dsa.dsa_sparse_attn(*x, stream=0, raise_on_error=False)
+    assert a(FAKE, FAKE, FAKE, None, None, dsa.FP8_E4M3, FAKE, 16, 1, 100, 0.1, None, FAKE, dsa.FP32,
+             FAKE, 1 << 30) == E["DSA_ERR_DTYPE"]
+    assert a(FAKE, FAKE, FAKE, None, None, dsa.BF16, FAKE, 16, 1, 100, 0.1, None, FAKE, 5,
+             FAKE, 1 << 30) == E["DSA_ERR_DTYPE"]
+    assert a(FAKE, FAKE, FAKE, None, None, dsa.BF16, FAKE, 16, 1, 100, 0.1, None, FAKE, dsa.FP32,
+             FAKE, 8) == E["DSA_ERR_WORKSPACE"]
+    s = lambda *x: dsa.swa_attn(*x, stream=0, raise_on_error=False)
+    assert s(FAKE, FAKE, FAKE, 130, 8, 500, 128, 0.1, None, FAKE, dsa.FP32, FAKE, 1 << 30) == E["DSA_ERR_SHAPE"]
+    assert s(FAKE, FAKE, FAKE, 135, 8, 500, 128, 0.1, None, FAKE, dsa.FP32, None, 1 << 30) == E["DSA_ERR_WORKSPACE"]
+    cfg = dsa.layer_config(dsa.LAYER_DSA)
+    w = dsa.LayerWeights(FAKE, FAKE, FAKE)
+    c = dsa.LayerCache(FAKE, FAKE, FAKE, FAKE, 1000)
+    L = lambda **kw: dsa.dsa_layer_step(cfg, w, c, FAKE, FAKE + 0x1000, 8, 100, ws=FAKE, ws_bytes=16,
+                                        stream=0, raise_on_error=False, **kw)
+    assert L() == E["DSA_ERR_WORKSPACE"]
+    c.capacity = 100
+    assert L() == E["DSA_ERR_SHAPE"]          # pos0 + T > capacity
+    cfg.hidden = 2048
+    c.capacity = 1000
+    assert L() == E["DSA_ERR_SHAPE"]
+    cfg.hidden = 4096
+    c.k_idx = None
+    assert L() == E["DSA_ERR_NULL"]

@@ -1,0 +1,351 @@
+"""GPU parity of every entry point against the CPU oracle (through the C ABI).
+
+Tolerances (derived from the arithmetic):
+* indexer scores: products of bf16 operands are exact in fp32; the 64-term dot, the
+  16-term weighted head sum and the scale multiply each add at most n*2^-24 relative
+  error of the absolute sum S = sum_h |w| sum_d |q k|, so |gpu - exact| <= 2^-16 * S.
+  Integer-valued inputs are exact in fp32 under any order: bit-exact there.
+* top-k on given scores: bit-exact (integer radix on order-preserving keys).
+* fused scan + top-k: bit-identical to top-k of the materialised GPU scores; against
+  the fp64 scores the index sets may differ only inside the 2^-16 * S rounding band.
+* attention: fp32 output ||g - r||_inf <= 1e-5 ||r||_inf per (token, head) row;
+  bf16 output max-abs <= 2e-2.
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import synth
+from oracle import dsa_oracle as O
+from tests.gpu_util import DEV, up, down, bf16_bits, tie_band_ok
+
+pytestmark = pytest.mark.gpu
+
+SM = 1.0 / math.sqrt(128)
+
+
+@pytest.fixture(scope="module")
+def dsa():
+    import sparse_attention_decode_indexer_amd as m
+    assert torch.cuda.is_available()
+    return m
+
+
+def _kdt(dsa, inp):
+    return dsa.BF16 if inp.k_idx_dtype == "bf16" else dsa.FP8_E4M3
+
+
+def _gpu_scores(dsa, inp, T=None, L=None, pos0=None):
+    T = T or inp.T
+    L = L or inp.L
+    pos0 = inp.pos0 if pos0 is None else pos0
+    ld = (L + 3) // 4 * 4
+    sc = torch.full((T, ld), float("nan"), dtype=torch.float32, device=DEV)
+    kscale = up(inp.k_idx_scale) if inp.k_idx_scale is not None else None
+    dsa.dsa_indexer_scores(up(inp.q_idx), up(inp.w_idx), up(inp.k_idx), kscale, _kdt(dsa, inp), T, L,
+                           pos0, sc, ld)
+    torch.cuda.synchronize()
+    return down(sc)[:, :L]
+
+
+def _oracle_scores(inp, with_abs=True):
+    krows = O.dequant_rows(inp.k_idx, inp.k_idx_dtype, inp.k_idx_scale)
+    return O.indexer_scores(O.decode_bf16(inp.q_idx), inp.w_idx, krows, inp.pos0, with_abs=with_abs)
+
+
+# ----------------------------------------------------------------------------- indexer
+
+@pytest.mark.parametrize("tie", [False, True])
+def test_indexer_scores_integer_config_bit_exact(dsa, tie):
+    inp = synth.dsa_config("tiny", seed=0, tie_stress=tie)
+    g = _gpu_scores(dsa, inp)
+    r = _oracle_scores(inp, with_abs=False)
+    assert np.array_equal(g.astype(np.float64), r)
+
+
+@pytest.mark.parametrize("name,L,T", [("verify64k", 5000, 8), ("verify64k", 4099, 5),
+                                      ("verify256k_fp8", 9001, 8), ("verify256k_fp8", 300, 3),
+                                      ("verify1m", 20000, 8)])
+def test_indexer_scores_within_rounding_band(dsa, name, L, T):
+    inp = synth.dsa_config(name, seed=1, L=L, T=T)
+    g = _gpu_scores(dsa, inp)
+    r, S = _oracle_scores(inp)
+    vis = np.isfinite(r)
+    assert np.array_equal(vis, np.isfinite(g)), "causal mask differs"
+    assert np.all(np.isneginf(g[~vis]))
+    err = np.abs(g[vis] - r[vis])
+    assert np.all(err <= 2.0 ** -16 * S[vis] + 1e-30), float(np.max(err / (S[vis] + 1e-30)))
+
+
+def test_indexer_fp8_decode_all_codes(dsa):
+    """Each key row holds one e4m3 code in dim 0; q = +-e_0 on head 0 with weight 1
+    recovers relu(+-value * scale) exactly for all 256 codes (NaN codes skipped)."""
+    codes = np.array([c for c in range(256) if (c & 0x7F) != 0x7F], np.uint8)
+    L = len(codes)
+    k = np.zeros((L, 64), np.uint8)
+    k[:, 0] = codes
+    scale = np.full(L, 0.5, np.float32)
+    vals = O.decode_e4m3(codes) * 0.5
+    for sign in (1.0, -1.0):
+        q = np.zeros((1, 16, 64), np.float32)
+        q[0, 0, 0] = sign
+        w = np.zeros((1, 16), np.float32)
+        w[0, 0] = 1.0
+        sc = torch.zeros((1, L + (-L) % 4), dtype=torch.float32, device=DEV)
+        dsa.dsa_indexer_scores(up(synth.to_bf16_bits(q)), up(w), up(k), up(scale), dsa.FP8_E4M3, 1, L,
+                               L - 1, sc, sc.shape[1])
+        torch.cuda.synchronize()
+        g = down(sc)[0, :L].astype(np.float64)
+        assert np.array_equal(g, np.maximum(sign * vals, 0.0))
+
+
+def test_indexer_full_context_sampled(dsa):
+    """1M-position workload at its full size: GPU scores checked on sampled columns."""
+    inp = synth.dsa_config("verify1m", seed=0)
+    g = _gpu_scores(dsa, inp)
+    rng = np.random.default_rng(0)
+    cols = np.unique(np.concatenate([rng.choice(inp.L, 4000, replace=False),
+                                     np.arange(inp.L - 64, inp.L), inp.planted[:500]]))
+    krows = O.dequant_rows(inp.k_idx[cols], "fp8", inp.k_idx_scale[cols])
+    q = O.decode_bf16(inp.q_idx)
+    for t in range(inp.T):
+        d = q[t] @ krows.T
+        r = inp.w_idx[t].astype(np.float64) @ np.maximum(d, 0)
+        S = np.abs(inp.w_idx[t].astype(np.float64)) @ (np.abs(q[t]) @ np.abs(krows).T)
+        vis = cols <= inp.pos0 + t
+        assert np.all(np.abs(g[t, cols[vis]] - r[vis]) <= 2.0 ** -16 * S[vis] + 1e-30)
+        assert np.all(np.isneginf(g[t, cols[~vis]]))
+
+
+# ----------------------------------------------------------------------------- top-k
+
+def _gpu_topk(dsa, scores, pos0, k):
+    T, L = scores.shape
+    ld = (L + 3) // 4 * 4
+    s = np.full((T, ld), -np.inf, np.float32)
+    s[:, :L] = scores
+    idx = torch.full((T, k), -7, dtype=torch.int32, device=DEV)
+    cnt = torch.full((T,), -7, dtype=torch.int32, device=DEV)
+    ws = dsa.workspace(dsa.WS_TOPK, T, L, k)
+    dsa.dsa_topk(up(s), T, L, ld, pos0, k, idx, cnt, ws)
+    torch.cuda.synchronize()
+    return down(idx), down(cnt)
+
+
+TOPK_CASES = [
+    # (name, T, L, k, generator)
+    ("ints-ties", 8, 5000, 2048, lambda g, T, L: g.integers(-3, 30, (T, L)).astype(np.float32)),
+    ("all-equal", 3, 3000, 100, lambda g, T, L: np.full((T, L), 1.5, np.float32)),
+    ("neg-zero", 2, 600, 37, lambda g, T, L: np.where(g.random((T, L)) < 0.5, -0.0, 0.0).astype(np.float32)),
+    ("normal", 8, 70000, 2048, lambda g, T, L: g.standard_normal((T, L)).astype(np.float32)),
+    ("vis-le-k", 8, 1000, 2048, lambda g, T, L: g.standard_normal((T, L)).astype(np.float32)),
+    ("small-k", 5, 9999, 7, lambda g, T, L: g.standard_normal((T, L)).astype(np.float32)),
+    ("k1", 1, 130, 1, lambda g, T, L: g.integers(0, 3, (T, L)).astype(np.float32)),
+    ("tiny-L", 8, 8, 4, lambda g, T, L: g.integers(0, 3, (T, L)).astype(np.float32)),
+    ("negatives", 4, 20000, 512, lambda g, T, L: -np.abs(g.standard_normal((T, L))).astype(np.float32)),
+    ("sparse-big", 8, 262144, 2048,
+     lambda g, T, L: np.where(g.random((T, L)) < 0.003, 100 + g.random((T, L)), g.random((T, L))).astype(np.float32)),
+]
+
+
+@pytest.mark.parametrize("case", TOPK_CASES, ids=[c[0] for c in TOPK_CASES])
+def test_topk_bit_exact_on_given_scores(dsa, case):
+    name, T, L, k, gen = case
+    g = np.random.default_rng(3)
+    s = gen(g, T, L)
+    pos0 = L - T
+    idx, cnt = _gpu_topk(dsa, s, pos0, k)
+    ridx, rcnt = O.topk_indices(s.astype(np.float64), pos0, k)
+    assert np.array_equal(cnt, rcnt)
+    assert np.array_equal(idx, ridx)
+
+
+def test_topk_full_context(dsa):
+    T, L, k = 8, 1 << 20, 2048
+    g = np.random.default_rng(5)
+    s = g.standard_normal((T, L)).astype(np.float32)
+    s[:, g.choice(L - T, 20000, replace=False)] = 7.0    # a large tie block across the boundary
+    idx, cnt = _gpu_topk(dsa, s, L - T, k)
+    ridx, rcnt = O.topk_indices(s.astype(np.float64), L - T, k)
+    assert np.array_equal(cnt, rcnt) and np.array_equal(idx, ridx)
+
+
+# ----------------------------------------------------------------------------- fused scan + top-k
+
+@pytest.mark.parametrize("name,L,T,seed", [("tiny", None, None, 0), ("verify64k", 65536, 8, 0),
+                                           ("verify256k_fp8", 40000, 8, 1), ("verify1m", 100000, 7, 2)])
+def test_index_topk_matches_materialised_path_and_oracle(dsa, name, L, T, seed):
+    inp = synth.dsa_config(name, seed=seed, L=L, T=T)
+    T, L, k = inp.T, inp.L, inp.top_k
+    idx = torch.full((T, k), -7, dtype=torch.int32, device=DEV)
+    cnt = torch.zeros(T, dtype=torch.int32, device=DEV)
+    ws = dsa.workspace(dsa.WS_INDEX_TOPK, T, L, k)
+    kscale = up(inp.k_idx_scale) if inp.k_idx_scale is not None else None
+    dsa.dsa_index_topk(up(inp.q_idx), up(inp.w_idx), up(inp.k_idx), kscale, _kdt(dsa, inp), T, L, inp.pos0,
+                       k, idx, cnt, ws)
+    torch.cuda.synchronize()
+    fused = down(idx)
+    g = _gpu_scores(dsa, inp)
+    ridx_same, rcnt = O.topk_indices(g.astype(np.float64), inp.pos0, k)
+    assert np.array_equal(fused, ridx_same), "fused selection differs from top-k of the GPU scores"
+    assert np.array_equal(down(cnt), rcnt)
+    r, S = _oracle_scores(inp)
+    ridx, _ = O.topk_indices(r, inp.pos0, k)
+    ok, ndiff = tie_band_ok(fused, ridx, r, S, inp.pos0, k)
+    assert ok, f"selection differs outside the rounding band ({ndiff})"
+    if name == "tiny":
+        assert np.array_equal(fused, ridx)
+
+
+def test_index_topk_full_context_planted(dsa):
+    inp = synth.dsa_config("verify1m", seed=0)
+    T, L, k = inp.T, inp.L, inp.top_k
+    idx = torch.full((T, k), -7, dtype=torch.int32, device=DEV)
+    ws = dsa.workspace(dsa.WS_INDEX_TOPK, T, L, k)
+    dsa.dsa_index_topk(up(inp.q_idx), up(inp.w_idx), up(inp.k_idx), up(inp.k_idx_scale), dsa.FP8_E4M3, T, L,
+                       inp.pos0, k, idx, None, ws)
+    torch.cuda.synchronize()
+    fused = down(idx)
+    g = _gpu_scores(dsa, inp)
+    ridx_same, _ = O.topk_indices(g.astype(np.float64), inp.pos0, k)
+    assert np.array_equal(fused, ridx_same)
+    r, S = _oracle_scores(inp)
+    ridx, _ = O.topk_indices(r, inp.pos0, k)
+    ok, ndiff = tie_band_ok(fused, ridx, r, S, inp.pos0, k)
+    assert ok, ndiff
+    # planted rows dominate the selection
+    assert np.isin(fused[0], inp.planted).mean() > 0.99
+    # run-to-run bitwise
+    idx2 = torch.full((T, k), -9, dtype=torch.int32, device=DEV)
+    dsa.dsa_index_topk(up(inp.q_idx), up(inp.w_idx), up(inp.k_idx), up(inp.k_idx_scale), dsa.FP8_E4M3, T, L,
+                       inp.pos0, k, idx2, None, ws)
+    torch.cuda.synchronize()
+    assert np.array_equal(down(idx2), fused)
+
+
+# ----------------------------------------------------------------------------- attention
+
+def _attn_inputs(inp):
+    if inp.kv_dtype == "bf16":
+        return O.decode_bf16(inp.k), O.decode_bf16(inp.v)
+    return O.dequant_rows(inp.k, "fp8", inp.k_scale), O.dequant_rows(inp.v, "fp8", inp.v_scale)
+
+
+def _run_sparse(dsa, inp, idx, k, out_dtype, sink=None):
+    T, L = inp.T, inp.L
+    f32 = out_dtype == "f32"
+    out = torch.full((T, 8, 128), float("nan"), dtype=torch.float32 if f32 else torch.bfloat16, device=DEV)
+    ws = dsa.workspace(dsa.WS_SPARSE_ATTN, T, L, k)
+    fp8 = inp.kv_dtype == "fp8"
+    dsa.dsa_sparse_attn(up(inp.q), up(inp.k), up(inp.v), up(inp.k_scale) if fp8 else None,
+                        up(inp.v_scale) if fp8 else None, dsa.FP8_E4M3 if fp8 else dsa.BF16, up(idx), k, T, L,
+                        SM, None if sink is None else up(sink), out, dsa.FP32 if f32 else dsa.BF16, ws)
+    torch.cuda.synchronize()
+    if f32:
+        return down(out).astype(np.float64)
+    return O.decode_bf16(bf16_bits(out))
+
+
+def _check_attn(got, ref, out_dtype):
+    if out_dtype == "f32":
+        T, H, _ = ref.shape
+        for t in range(T):
+            for h in range(H):
+                den = max(np.max(np.abs(ref[t, h])), 1e-30)
+                assert np.max(np.abs(got[t, h] - ref[t, h])) / den <= 1e-5, (t, h)
+    else:
+        assert np.max(np.abs(got - ref)) <= 2e-2
+
+
+@pytest.mark.parametrize("name,L,out_dtype,with_sink", [
+    ("tiny", None, "f32", False), ("verify64k", 20000, "f32", False), ("verify64k", 20000, "bf16", False),
+    ("verify256k_fp8", 30000, "f32", False), ("verify256k_fp8", 30000, "bf16", True),
+    ("verify64k", 3000, "f32", True)])
+def test_sparse_attention_vs_oracle(dsa, name, L, out_dtype, with_sink):
+    inp = synth.dsa_config(name, seed=2, L=L)
+    k = inp.top_k
+    g = np.random.default_rng(9)
+    idx = np.full((inp.T, k), -1, np.int32)
+    for t in range(inp.T):
+        vis = inp.pos0 + t + 1
+        n = min(k, vis)
+        idx[t, :n] = np.sort(g.choice(vis, n, replace=False))
+    sink = synth.sink_logits(2) if with_sink else None
+    got = _run_sparse(dsa, inp, idx, k, out_dtype, sink)
+    K, V = _attn_inputs(inp)
+    ref = O.sparse_attention(O.decode_bf16(inp.q), K, V, idx, SM, sink)
+    _check_attn(got, ref, out_dtype)
+
+
+def test_sparse_attention_ragged_lists(dsa):
+    """Skipped entries (-1, >= L), duplicates, a short list, an empty token row."""
+    inp = synth.dsa_config("verify64k", seed=4, L=2000, T=4)
+    k = 150
+    g = np.random.default_rng(1)
+    idx = g.integers(0, inp.L, (inp.T, k)).astype(np.int32)
+    idx[0, ::3] = -1
+    idx[1, ::5] = inp.L + 7
+    idx[2, :] = 11                        # one row repeated
+    idx[3, :] = -1                        # nothing to attend
+    got = _run_sparse(dsa, inp, idx, k, "f32")
+    K, V = _attn_inputs(inp)
+    ref = O.sparse_attention(O.decode_bf16(inp.q), K, V, idx, SM)
+    np.testing.assert_allclose(got[3], 0.0)
+    _check_attn(got[:3], ref[:3], "f32")
+    # a -inf sink is no sink
+    got2 = _run_sparse(dsa, inp, idx, k, "f32", np.full(8, -np.inf, np.float32))
+    assert np.array_equal(got, got2)
+
+
+def test_sparse_attention_fp8_values_all_codes(dsa):
+    """A single selected row: the output is that row's decoded V exactly (fp32)."""
+    codes = np.array([c for c in range(256) if (c & 0x7F) != 0x7F], np.uint8)
+    rows = (len(codes) + 127) // 128
+    L = rows
+    V = np.zeros((L, 128), np.uint8)
+    V.reshape(-1)[:len(codes)] = codes
+    K = np.zeros((L, 128), np.uint8)
+    vs = np.full(L, 0.25, np.float32)
+    ks = np.ones(L, np.float32)
+    q = synth.to_bf16_bits(np.ones((L, 8, 128), np.float32))
+    idx = np.arange(L, dtype=np.int32)[:, None].repeat(1, axis=1)
+    out = torch.zeros((L, 8, 128), dtype=torch.float32, device=DEV)
+    ws = dsa.workspace(dsa.WS_SPARSE_ATTN, L, L, 1)
+    dsa.dsa_sparse_attn(up(q), up(K), up(V), up(ks), up(vs), dsa.FP8_E4M3, up(idx), 1, L, L, SM, None, out,
+                        dsa.FP32, ws)
+    torch.cuda.synchronize()
+    got = down(out)
+    want = O.decode_e4m3(V) * 0.25
+    for t in range(L):
+        for h in range(8):
+            assert np.array_equal(got[t, h].astype(np.float64), want[t])
+
+
+@pytest.mark.parametrize("pos0,T,window,cap", [(5000, 8, 128, 135), (3, 4, 128, 140), (1000, 1, 1, 8),
+                                               (70, 8, 128, 256)])
+def test_swa_vs_oracle(dsa, pos0, T, window, cap):
+    g = np.random.default_rng(pos0)
+    Kr = synth.to_bf16_bits(g.standard_normal((cap, 128)).astype(np.float32))
+    Vr = synth.to_bf16_bits(g.standard_normal((cap, 128)).astype(np.float32))
+    q = synth.to_bf16_bits(g.standard_normal((T, 8, 128)).astype(np.float32))
+    for sink in (None, synth.sink_logits(5)):
+        out = torch.full((T, 8, 128), float("nan"), dtype=torch.float32, device=DEV)
+        ws = dsa.workspace(dsa.WS_SWA_ATTN, T, pos0 + T, window)
+        dsa.swa_attn(up(q), up(Kr), up(Vr), cap, T, pos0, window, SM, None if sink is None else up(sink), out,
+                     dsa.FP32, ws)
+        torch.cuda.synchronize()
+        ref = O.swa_attention(O.decode_bf16(q), O.decode_bf16(Kr), O.decode_bf16(Vr), cap, pos0, window, SM, sink)
+        _check_attn(down(out).astype(np.float64), ref, "f32")
+
+
+def test_attention_run_to_run_bitwise(dsa):
+    inp = synth.dsa_config("verify64k", seed=6, L=30000)
+    k = inp.top_k
+    g = np.random.default_rng(2)
+    idx = np.sort(np.stack([g.choice(inp.pos0 + 1, k, replace=False) for _ in range(inp.T)]), axis=1)
+    a = _run_sparse(dsa, inp, idx.astype(np.int32), k, "f32")
+    for _ in range(3):
+        b = _run_sparse(dsa, inp, idx.astype(np.int32), k, "f32")
+        assert np.array_equal(a, b)

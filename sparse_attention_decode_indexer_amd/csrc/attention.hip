@@ -55,6 +55,8 @@ struct AttnShared {
   float kscl[kSplitRows];
   float vscl[kSplitRows];
   float s[kHq][kSplitRows];
+  float ms[kHq * 32];     // split maxima / sums of the merging workgroup
+  float ls[kHq * 32];
   uint32_t last;
 };
 
@@ -83,24 +85,34 @@ __global__ void __launch_bounds__(kAttnThreads) attn_kernel(AttnParams p) {
     }
     sh.rows[tid] = r;
     if (KVDT == 1) {
-      sh.kscl[tid] = r >= 0 ? p.ks[r] : 0.0f;
-      sh.vscl[tid] = r >= 0 ? p.vs[r] : 0.0f;
+      const float ksv = p.ks[r >= 0 ? r : 0], vsv = p.vs[r >= 0 ? r : 0];
+      sh.kscl[tid] = r >= 0 ? ksv : 0.0f;
+      sh.vscl[tid] = r >= 0 ? vsv : 0.0f;
     }
   }
   __syncthreads();
   // ---- stage K and V rows (16-byte chunks, one row per RB/16 consecutive threads)
   {
+    // every load is issued before any is consumed; invalid rows read row 0 and are zeroed
     constexpr int CPR = RB / 16;
-    for (int c = tid; c < kSplitRows * CPR; c += kAttnThreads) {
+    constexpr int NCH = kSplitRows * CPR / kAttnThreads;
+    uint4 kv[NCH], vv[NCH];
+#pragma unroll
+    for (int u = 0; u < NCH; ++u) {
+      const int c = tid + u * kAttnThreads;
       const int row = c / CPR, col = c % CPR;
       const int64_t r = sh.rows[row];
-      uint4 kv = make_uint4(0u, 0u, 0u, 0u), vv = kv;
-      if (r >= 0) {
-        kv = *reinterpret_cast<const uint4*>(p.kc + r * RB + col * 16);
-        vv = *reinterpret_cast<const uint4*>(p.vc + r * RB + col * 16);
-      }
-      *reinterpret_cast<uint4*>(&sh.kst[row * SH::KSTRIDE + col * 16]) = kv;
-      *reinterpret_cast<uint4*>(&sh.vst[row * RB + col * 16]) = vv;
+      const int64_t rr = r >= 0 ? r : 0;
+      kv[u] = *reinterpret_cast<const uint4*>(p.kc + rr * RB + col * 16);
+      vv[u] = *reinterpret_cast<const uint4*>(p.vc + rr * RB + col * 16);
+    }
+#pragma unroll
+    for (int u = 0; u < NCH; ++u) {
+      const int c = tid + u * kAttnThreads;
+      const int row = c / CPR, col = c % CPR;
+      const bool ok = sh.rows[row] >= 0;
+      *reinterpret_cast<uint4*>(&sh.kst[row * SH::KSTRIDE + col * 16]) = ok ? kv[u] : make_uint4(0u, 0u, 0u, 0u);
+      *reinterpret_cast<uint4*>(&sh.vst[row * RB + col * 16]) = ok ? vv[u] : make_uint4(0u, 0u, 0u, 0u);
     }
   }
   // ---- q^T operand (heads on the N side): lane l -> head l%16 (< 8 real), dims kb*32 + (l/16)*8
@@ -196,35 +208,57 @@ __global__ void __launch_bounds__(kAttnThreads) attn_kernel(AttnParams p) {
   }
   // ---- publish the split's partial
   float* part = p.part + (((size_t)t * p.nsplit + split) * kHq + h) * kPartStride;
-  if (jj == 0) {
-    astf(part + 0, m);
-    astf(part + 1, l);
-  }
-#pragma unroll
-  for (int i = 0; i < 4; ++i) astf(part + 4 + d4 + i, acc[i]);
+  if (jj == 0)
+    ast64(reinterpret_cast<uint64_t*>(part), (uint64_t)__float_as_uint(m) | ((uint64_t)__float_as_uint(l) << 32));
+  ast64(reinterpret_cast<uint64_t*>(part + 4 + d4),
+        (uint64_t)__float_as_uint(acc[0]) | ((uint64_t)__float_as_uint(acc[1]) << 32));
+  ast64(reinterpret_cast<uint64_t*>(part + 6 + d4),
+        (uint64_t)__float_as_uint(acc[2]) | ((uint64_t)__float_as_uint(acc[3]) << 32));
   vm_wait_all();
   __syncthreads();
   if (tid == 0) sh.last = (aadd(p.ctr + 64 * t, 1u) == (uint32_t)p.nsplit - 1u) ? 1u : 0u;
   __syncthreads();
   if (!sh.last) return;
-  // ---- merge of all splits of token t, in split order
+  // ---- merge of all splits of token t, in split order.  Split statistics first (one
+  // coherent load per thread), then each thread's accumulators with 16 loads in flight.
   const float* pt = p.part + (size_t)t * p.nsplit * kHq * kPartStride;
+  if (tid < p.nsplit * kHq) {
+    const uint64_t ml = ald64(reinterpret_cast<const uint64_t*>(pt + (size_t)tid * kPartStride));
+    sh.ms[tid] = __uint_as_float((uint32_t)ml);
+    sh.ls[tid] = __uint_as_float((uint32_t)(ml >> 32));
+  }
+  __syncthreads();
   float M = -__builtin_inff();
-  for (int s = 0; s < p.nsplit; ++s) M = fmaxf(M, aldf(pt + ((size_t)s * kHq + h) * kPartStride));
+  for (int s = 0; s < p.nsplit; ++s) M = fmaxf(M, sh.ms[s * kHq + h]);
   float sink2 = -__builtin_inff();
   if (p.sink) sink2 = p.sink[h] * 1.4426950408889634f;
   M = fmaxf(M, sink2);
   float den = 0.0f;
   float o[4] = {0.0f, 0.0f, 0.0f, 0.0f};
   if (M != -__builtin_inff()) {
-    for (int s = 0; s < p.nsplit; ++s) {
-      const float* ps = pt + ((size_t)s * kHq + h) * kPartStride;
-      const float ms = aldf(ps);
-      if (ms == -__builtin_inff()) continue;
-      const float sc = exp2f(ms - M);
-      den = fmaf(aldf(ps + 1), sc, den);
+    constexpr int U = 8;
+    for (int s0 = 0; s0 < p.nsplit; s0 += U) {
+      uint64_t va[U], vb[U];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) o[i] = fmaf(aldf(ps + 4 + d4 + i), sc, o[i]);
+      for (int u = 0; u < U; ++u) {
+        const int sc = s0 + u < p.nsplit ? s0 + u : p.nsplit - 1;   // clamped: unconditional loads
+        const uint64_t* ps = reinterpret_cast<const uint64_t*>(pt + ((size_t)sc * kHq + h) * kPartStride + 4 + d4);
+        va[u] = ald64(ps);
+        vb[u] = ald64(ps + 1);
+      }
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int s = s0 + u;
+        if (s >= p.nsplit) break;
+        const float ms = sh.ms[s * kHq + h];
+        if (ms == -__builtin_inff()) continue;
+        const float sc = exp2f(ms - M);
+        den = fmaf(sh.ls[s * kHq + h], sc, den);
+        o[0] = fmaf(__uint_as_float((uint32_t)va[u]), sc, o[0]);
+        o[1] = fmaf(__uint_as_float((uint32_t)(va[u] >> 32)), sc, o[1]);
+        o[2] = fmaf(__uint_as_float((uint32_t)vb[u]), sc, o[2]);
+        o[3] = fmaf(__uint_as_float((uint32_t)(vb[u] >> 32)), sc, o[3]);
+      }
     }
     if (sink2 != -__builtin_inff()) den += exp2f(sink2 - M);
   }

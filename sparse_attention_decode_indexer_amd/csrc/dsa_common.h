@@ -35,10 +35,8 @@ DSA_DEV float bf16_to_f32(uint16_t b) { return __uint_as_float((uint32_t)b << 16
 
 // fp32 -> bf16, round to nearest even (NaN kept quiet)
 DSA_DEV uint16_t f32_to_bf16(float f) {
-  uint32_t u = __float_as_uint(f);
-  if ((u & 0x7f800000u) == 0x7f800000u && (u & 0x7fffffu)) return (uint16_t)((u >> 16) | 0x40);
-  u += 0x7fffu + ((u >> 16) & 1u);
-  return (uint16_t)(u >> 16);
+  const __bf16 b = (__bf16)f;                 // v_cvt_pk_bf16_f32: round to nearest even
+  return __builtin_bit_cast(uint16_t, b);
 }
 
 DSA_DEV float round_bf16(float f) { return bf16_to_f32(f32_to_bf16(f)); }
@@ -208,6 +206,15 @@ constexpr int kDone = 1024;      // [8] per-token completion counters, stride 64
 constexpr int kWords = 1536;
 constexpr size_t kBytes = 8192;
 }  // namespace ctl
+
+// Phase timestamps (100 MHz real-time counter) for profiling builds only (-DDSA_TRACE):
+// thread 0 of each workgroup records slot `s` (< 16) of its row in a caller buffer.
+#ifdef DSA_TRACE
+#define DSA_MARK(buf, s) \
+  do { if ((buf) && threadIdx.x == 0) (buf)[blockIdx.x * 16 + (s)] = __builtin_amdgcn_s_memrealtime(); } while (0)
+#else
+#define DSA_MARK(buf, s) do { } while (0)
+#endif
 
 constexpr uint64_t kSpinLimit = 20000000ull;   // 0.2 s of the 100 MHz real-time counter
 

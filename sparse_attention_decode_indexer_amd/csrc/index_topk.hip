@@ -15,13 +15,15 @@
 // Selection is one launch of one workgroup per chunk of C keys, all resident at once:
 //   P1  scores of the chunk (computed, or read from memory) stay in LDS; each
 //       workgroup derives a lower bound tau_wg of its m-th largest visible score from
-//       per-group maxima and publishes min(tau) with an integer atomic;
+//       per-group maxima and publishes it in its own slot;
+//   --  grid barrier; tau = min over the slots;
 //   P2  every workgroup writes its visible scores >= tau, in position order, as
 //       (order key, position) candidates;
-//   P3  the last workgroup to publish a token's candidates runs an exact radix select
-//       over them and writes the selected positions in ascending order.
-// P1 and P2 are separated by one grid barrier; inter-workgroup data moves only through
-// agent-scope atomic loads/stores, so no cache writeback or invalidation is needed.
+//   --  grid barrier;
+//   P3  workgroup t runs an exact radix select over token t's candidates and writes
+//       the selected positions in ascending order.
+// Inter-workgroup data moves only through agent-scope atomic loads/stores, so no cache
+// writeback or invalidation is needed at the barriers.
 // Because at least m scores of each of n_part workgroups are >= tau and
 // m * n_part >= k, the candidates always contain the k best; the result is exact and
 // independent of tau.  All cross-workgroup arithmetic is integer, so the result is
@@ -31,12 +33,14 @@
 
 namespace dsa {
 
-constexpr int kTile = 32;        // keys per MFMA column tile
-constexpr int kSelThreads = 256; // threads of the selection kernel
+constexpr int kTile = 32;          // keys per MFMA column tile
+constexpr int kSelThreads = 512;   // 8 waves: wave pairs (w, w+4) share key tiles
 constexpr int kSelWaves = kSelThreads / 64;
-constexpr int kGroups = 32 * kSelWaves;   // score groups per workgroup and token
-constexpr int kMaxChunk = 4096;  // keys per workgroup held in LDS
+constexpr int kPairs = kSelWaves / 2;
+constexpr int kMaxChunk = 4096;    // keys per workgroup held in LDS
 constexpr int kTauMaxM = 32;
+constexpr int kPrefetch = 4;       // key tiles in flight per wave
+constexpr int kMaxWG = 1024;
 
 // ----------------------------------------------------------------------------- tile math
 
@@ -47,8 +51,8 @@ struct KeyTile {
 };
 
 // Lane l loads dims [32*(l>>5), +32) of key s0 + (l & 31); rows past L are clamped
-// (their scores are masked by the caller).
-template <int KDT>
+// (their scores are never used).
+template <int KDT, bool WITH_SCALE = true>
 DSA_DEV void load_key_tile(const uint8_t* __restrict__ kbase, const float* __restrict__ kscale,
                            int64_t L, int64_t s0, KeyTile<KDT>& kt) {
   const int l = threadIdx.x & 63;
@@ -66,53 +70,60 @@ DSA_DEV void load_key_tile(const uint8_t* __restrict__ kbase, const float* __res
     const uint4* p = reinterpret_cast<const uint4*>(kbase + s * 64 + half * 32);
     kt.raw[0] = p[0];
     kt.raw[1] = p[1];
-    kt.scale = kscale[s];
+    if constexpr (WITH_SCALE) kt.scale = kscale[s];
   }
 }
 
-// A operands: row tile r, k-step j.  Lane l: row (l & 31) -> token 2r + ((l&31)>>4),
-// head (l & 15); dims 32*(l>>5) + 8j .. +8 (the same dims the key operand uses).
-template <int RT>
-DSA_DEV void load_q_frags(const uint16_t* __restrict__ q_idx, int T, Frag8 (&qa)[RT][4]) {
+// A operands of row tiles rt0 .. rt0+RTW-1, k-step j.  Lane l: row (l & 31) -> token
+// 2r + ((l&31)>>4), head (l & 15); dims 32*(l>>5) + 8j .. +8 (the key operand's dims).
+template <int RTW>
+DSA_DEV void load_q_frags(const uint16_t* __restrict__ q_idx, int T, int rt0, Frag8 (&qa)[RTW][4]) {
   const int l = threadIdx.x & 63;
   const int half = l >> 5;
   const int row = l & 31;
 #pragma unroll
-  for (int r = 0; r < RT; ++r) {
-    const int tt = 2 * r + (row >> 4);
+  for (int r = 0; r < RTW; ++r) {
+    const int tt = 2 * (rt0 + r) + (row >> 4);
+    const int tc = tt < T ? tt : T - 1;          // clamped: loads stay unconditional
     const int hh = row & 15;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      if (tt < T) {
-        qa[r][j].u = *reinterpret_cast<const uint4*>(q_idx + (tt * kHI + hh) * kDI + half * 32 + 8 * j);
-      } else {
-        qa[r][j].u = make_uint4(0u, 0u, 0u, 0u);
-      }
-    }
+    for (int j = 0; j < 4; ++j)
+      qa[r][j].u = *reinterpret_cast<const uint4*>(q_idx + (tc * kHI + hh) * kDI + half * 32 + 8 * j);
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      if (tt >= T) qa[r][j].u = make_uint4(0u, 0u, 0u, 0u);
   }
 }
 
-// Head weights for this lane's accumulator elements.  Element e of the 32x32 output
-// holds row 8*(e>>2) + 4*half + (e&3): token 2r + (e>>3), head 8*((e>>2)&1) + 4*half + (e&3).
-template <int RT>
-DSA_DEV void load_w(const float* __restrict__ w_idx, int T, float (&wv)[RT][16]) {
+// Head weights of this lane's accumulator elements.  Element e of the 32x32 output holds
+// row 8*(e>>2) + 4*half + (e&3): token 2r + (e>>3), head 8*((e>>2)&1) + 4*half + (e&3).
+template <int RTW>
+DSA_DEV void load_w(const float* __restrict__ w_idx, int T, int rt0, float (&wv)[RTW][16]) {
   const int half = (threadIdx.x & 63) >> 5;
 #pragma unroll
-  for (int r = 0; r < RT; ++r) {
+  for (int r = 0; r < RTW; ++r) {
 #pragma unroll
     for (int e = 0; e < 16; ++e) {
-      const int tt = 2 * r + (e >> 3);
+      const int tt = 2 * (rt0 + r) + (e >> 3);
       const int hh = 8 * ((e >> 2) & 1) + 4 * half + (e & 3);
-      wv[r][e] = (tt < T) ? w_idx[tt * kHI + hh] : 0.0f;
+      const float v = w_idx[(tt < T ? tt : T - 1) * kHI + hh];
+      wv[r][e] = (tt < T) ? v : 0.0f;
     }
   }
 }
 
-// Scores of one 32-key tile: out[r] is the score of token 2r + (lane>>5) for key
-// s0 + (lane & 31).  Fixed arithmetic order (the same in every kernel that calls it).
-template <int KDT, int RT>
-DSA_DEV void score_tile(const KeyTile<KDT>& kt, const Frag8 (&qa)[RT][4], const float (&wv)[RT][16],
-                        float (&out)[RT]) {
+// relu by integer max on the bit pattern: non-negative floats (sign 0) are non-negative
+// integers, negative floats (and -0) are negative integers, so max(bits, 0) is relu(x)
+// without a NaN canonicalisation.
+DSA_DEV float relu_bits(float x) { return __int_as_float(max(__float_as_int(x), 0)); }
+
+// Scores of one 32-key tile for RTW row tiles: out[r] is the score of token
+// 2(rt0+r) + (lane>>5) for key s0 + (lane & 31).  The arithmetic and its order are fixed
+// (products and sums in fp32: head sum over 8 heads per lane in element order, then the
+// partner lane's 8, then the row scale), the same in every kernel that calls it.
+template <int KDT, int RTW>
+DSA_DEV void score_tile(const KeyTile<KDT>& kt, const Frag8 (&qa)[RTW][4], const float (&wv)[RTW][16],
+                        float (&out)[RTW]) {
   Frag8 kb[4];
   if constexpr (KDT == 0) {
 #pragma unroll
@@ -130,18 +141,21 @@ DSA_DEV void score_tile(const KeyTile<KDT>& kt, const Frag8 (&qa)[RT][4], const 
   }
   const int half = (threadIdx.x & 63) >> 5;
 #pragma unroll
-  for (int r = 0; r < RT; ++r) {
+  for (int r = 0; r < RTW; ++r) {
     f32x16_t acc = {};
 #pragma unroll
     for (int j = 0; j < 4; ++j)
       acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa[r][j].v, kb[j].v, acc, 0, 0, 0);
     float p0 = 0.0f, p1 = 0.0f;
 #pragma unroll
-    for (int e = 0; e < 8; ++e) p0 = fmaf(wv[r][e], fmaxf(acc[e], 0.0f), p0);
+    for (int e = 0; e < 8; ++e) p0 = fmaf(wv[r][e], relu_bits(acc[e]), p0);
 #pragma unroll
-    for (int e = 8; e < 16; ++e) p1 = fmaf(wv[r][e], fmaxf(acc[e], 0.0f), p1);
+    for (int e = 8; e < 16; ++e) p1 = fmaf(wv[r][e], relu_bits(acc[e]), p1);
+    // lanes l and l+32 hold the same (token pair, key) over complementary heads: lane l
+    // keeps token 2r (p0) and sends p1; lane l+32 keeps token 2r+1 (p1) and sends p0.
     const float send = half ? p0 : p1;
-    const float recv = __shfl_xor(send, 32, 64);
+    const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(send), __float_as_uint(send), false, false);
+    const float recv = __uint_as_float(half ? sw[0] : sw[1]);
     const float tot = (half ? p1 : p0) + recv;
     out[r] = (KDT == 1) ? tot * kt.scale : tot;
   }
@@ -159,29 +173,31 @@ indexer_scores_kernel(const uint16_t* __restrict__ q_idx, const float* __restric
                       int T, int64_t L, int64_t pos0, float* __restrict__ scores, int64_t ld) {
   Frag8 qa[RT][4];
   float wv[RT][16];
-  load_q_frags<RT>(q_idx, T, qa);
-  load_w<RT>(w_idx, T, wv);
+  load_q_frags<RT>(q_idx, T, 0, qa);
+  load_w<RT>(w_idx, T, 0, wv);
   const int lane = threadIdx.x & 63;
   const int half = lane >> 5;
   const int wave = threadIdx.x >> 6;
   const int64_t ntiles = (L + kTile - 1) / kTile;
   const int64_t tile0 = ((int64_t)blockIdx.x * (kScoreThreads / 64) + wave) * kScoreTilesPerWave;
-  KeyTile<KDT> cur, nxt;
-  if (tile0 < ntiles) load_key_tile<KDT>(k_idx, k_scale, L, tile0 * kTile, cur);
+  KeyTile<KDT> buf[kScoreTilesPerWave];
+#pragma unroll
+  for (int i = 0; i < kScoreTilesPerWave; ++i) {
+    const int64_t ti = tile0 + i < ntiles ? tile0 + i : ntiles - 1;
+    load_key_tile<KDT>(k_idx, k_scale, L, ti * kTile, buf[i]);
+  }
+#pragma unroll
   for (int i = 0; i < kScoreTilesPerWave; ++i) {
     const int64_t tile = tile0 + i;
     if (tile >= ntiles) break;
-    if (i + 1 < kScoreTilesPerWave && tile + 1 < ntiles)
-      load_key_tile<KDT>(k_idx, k_scale, L, (tile + 1) * kTile, nxt);
     float out[RT];
-    score_tile<KDT, RT>(cur, qa, wv, out);
+    score_tile<KDT, RT>(buf[i], qa, wv, out);
     const int64_t s = tile * kTile + (lane & 31);
 #pragma unroll
     for (int r = 0; r < RT; ++r) {
       const int tt = 2 * r + half;
       if (tt < T && s < L) scores[tt * ld + s] = (s <= pos0 + tt) ? out[r] : -__builtin_inff();
     }
-    cur = nxt;
   }
 }
 
@@ -200,7 +216,7 @@ struct SelParams {
   int k;
   int64_t L;
   int64_t pos0;
-  int chunk;             // keys per workgroup (multiple of 128, <= kMaxChunk)
+  int chunk;             // keys per workgroup (multiple of 512, <= kMaxChunk)
   int nwg;               // workgroups (>= T)
   int m;                 // tau rank; 0 disables tau
   int n_part;            // workgroups [0, n_part) publish tau
@@ -210,48 +226,68 @@ struct SelParams {
   // workspace
   uint32_t* ctl;         // control words (see namespace ctl)
   uint32_t* cnt;         // [T][nwg] candidate counts
+  uint32_t* tauv;        // [T][kMaxWG] per-workgroup tau bounds
   uint64_t* cand;        // [T][nwg][chunk] (position << 32 | order key)
+  uint64_t* trace;       // profiling builds: [nwg][16] phase timestamps
 };
 
 struct SelShared {
   float sc[kMaxT][kMaxChunk];        // chunk scores (P1/P2); resolver scratch (P3)
-  uint32_t gmax[kMaxT][kGroups];     // per-group maxima (order keys)
+  float kscale[kMaxChunk];           // row scales of the chunk (e4m3 keys)
   uint32_t tau[kMaxT];
-  uint32_t resolve[kMaxT];
+  uint64_t scan64[32];
   uint32_t scan[32];
 };
 
-// m-th largest of the kGroups group maxima of one token, computed by one wave.
-DSA_DEV uint32_t mth_largest_wave(const uint32_t* g, int m) {
+// Exclusive prefix sum of 64-bit values across the block (fields packed by the caller).
+template <int NT>
+DSA_DEV uint64_t block_excl_scan64(uint64_t v, uint64_t* scratch, uint64_t* total) {
+  constexpr int NW = NT / 64;
   const int lane = threadIdx.x & 63;
-  constexpr int PER = kGroups / 64;
-  uint32_t v[PER];
+  const int wid = threadIdx.x >> 6;
+  uint64_t inc = v;
 #pragma unroll
-  for (int i = 0; i < PER; ++i) v[i] = g[lane * PER + i];
-  uint32_t cur = 0;
-  for (int it = 0; it < m; ++it) {
-    uint32_t mx = v[0];
-#pragma unroll
-    for (int i = 1; i < PER; ++i) mx = max(mx, v[i]);
-    cur = wave_max_u32(mx);
-    // remove one occurrence (lowest lane, lowest slot)
-    bool has = false;
-#pragma unroll
-    for (int i = 0; i < PER; ++i) has |= (v[i] == cur);
-    const uint64_t bal = __ballot(has);
-    const int first = __builtin_ctzll(bal);
-    if (lane == first) {
-      bool done = false;
-#pragma unroll
-      for (int i = 0; i < PER; ++i)
-        if (!done && v[i] == cur) { v[i] = 0u; done = true; }
-    }
+  for (int d = 1; d < 64; d <<= 1) {
+    const uint64_t o = __shfl_up(inc, d, 64);
+    if (lane >= d) inc += o;
   }
-  return cur;
+  if (lane == 63) scratch[wid] = inc;
+  __syncthreads();
+  if (wid == 0) {
+    uint64_t t = (lane < NW) ? scratch[lane] : 0ull;
+    uint64_t ti = t;
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) {
+      const uint64_t o = __shfl_up(ti, d, 64);
+      if (lane >= d) ti += o;
+    }
+    if (lane < NW) scratch[lane] = ti - t;
+    if (lane == NW - 1) scratch[NW] = ti;
+  }
+  __syncthreads();
+  const uint64_t res = scratch[wid] + inc - v;
+  *total = scratch[NW];
+  __syncthreads();
+  return res;
+}
+
+// m-th largest of the 64 values held by the lanes of one wave (1 <= m <= 64): each
+// lane counts the values ranked above its own (larger, or equal in a lower lane); the
+// lane of rank m-1 holds the answer.
+DSA_DEV uint32_t mth_largest_lanes(uint32_t v, int m) {
+  const int lane = threadIdx.x & 63;
+  int rank = 0;
+#pragma unroll
+  for (int o = 0; o < 64; ++o) {
+    const uint32_t w = __builtin_amdgcn_readlane(v, o);
+    rank += (w > v) || (w == v && o < lane);
+  }
+  const uint64_t bal = __ballot(rank == m - 1);
+  return __builtin_amdgcn_readlane(v, __builtin_ctzll(bal));
 }
 
 // Exact selection of the kk best candidates of token t.  Runs in one workgroup after
-// every workgroup has published its candidates for t.
+// every workgroup has published its candidates (after the second grid barrier).
 DSA_DEV void resolve_token(const SelParams& p, int t, SelShared& sh) {
   uint32_t* pre = reinterpret_cast<uint32_t*>(&sh.sc[0][0]);         // [nwg + 1]
   uint32_t* hist = pre + 1040;                                        // [2048]
@@ -263,7 +299,8 @@ DSA_DEV void resolve_token(const SelParams& p, int t, SelShared& sh) {
   uint32_t carry = 0;
   for (int base = 0; base < nwg; base += kSelThreads) {
     const int w = base + tid;
-    const uint32_t c = (w < nwg) ? ald(cnt_t + w) : 0u;
+    const uint32_t cv = ald(cnt_t + (w < nwg ? w : nwg - 1));
+    const uint32_t c = (w < nwg) ? cv : 0u;
     uint32_t tot;
     const uint32_t ex = block_excl_scan<kSelThreads>(c, sh.scan, &tot);
     if (w < nwg) pre[w] = carry + ex;
@@ -276,12 +313,50 @@ DSA_DEV void resolve_token(const SelParams& p, int t, SelShared& sh) {
   uint32_t kk = (uint32_t)((int64_t)p.k < vis ? p.k : vis);
   if (kk > nc) kk = nc;   // cannot happen when the bound holds; keeps reads in range
   const uint64_t* base = p.cand + (size_t)t * nwg * p.chunk;
+  // Bring the candidates on chip when they fit: many independent coherent loads in
+  // flight per thread, then every pass below reads LDS.
+  uint64_t* lc = reinterpret_cast<uint64_t*>(misc + 16);              // 8-byte aligned
+  const uint32_t lds_cap = (uint32_t)((sizeof(sh.sc) - (1040 + 2048 + 16) * 4) / 8);
+  const bool in_lds = nc > 0 && nc <= lds_cap;
+  if (in_lds) {
+    constexpr int U = 8;
+    for (uint32_t g0b = 0; g0b < nc; g0b += kSelThreads * U) {
+      uint64_t v[U];
+      uint32_t gi[U];
+      size_t off[U];
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        gi[u] = g0b + u * kSelThreads + tid;
+        const uint32_t g = gi[u] < nc ? gi[u] : nc - 1;     // clamped: loads stay unconditional
+        int lo = 0, hi = nwg - 1;
+        while (lo < hi) {
+          const int mid = (lo + hi + 1) >> 1;
+          if (pre[mid] <= g) lo = mid; else hi = mid - 1;
+        }
+        off[u] = (size_t)lo * p.chunk + (g - pre[lo]);
+      }
+#pragma unroll
+      for (int u = 0; u < U; ++u) v[u] = ald64(base + off[u]);
+#pragma unroll
+      for (int u = 0; u < U; ++u)
+        if (gi[u] < nc) lc[gi[u]] = v[u];
+    }
+    __syncthreads();
+  }
+  DSA_MARK(p.trace, 9);
   // contiguous run of candidates per thread, visited in position order
   const uint32_t run = (nc + kSelThreads - 1) / kSelThreads;
   const uint32_t g0 = min(nc, (uint32_t)tid * run);
   const uint32_t g1 = min(nc, g0 + run);
   auto visit = [&](auto&& fn) {
     if (g0 >= g1) return;
+    if (in_lds) {
+      for (uint32_t g = g0; g < g1; ++g) {
+        const uint64_t e = lc[g];
+        fn((uint32_t)e, (uint32_t)(e >> 32));
+      }
+      return;
+    }
     int lo = 0, hi = nwg - 1;            // largest w with pre[w] <= g0
     while (lo < hi) {
       const int mid = (lo + hi + 1) >> 1;
@@ -300,6 +375,7 @@ DSA_DEV void resolve_token(const SelParams& p, int t, SelShared& sh) {
   visit([&](uint32_t key, uint32_t) { kmin = min(kmin, key); kmax = max(kmax, key); });
   kmin = block_min_u32<kSelThreads>(kmin, sh.scan);
   kmax = block_max_u32<kSelThreads>(kmax, sh.scan);
+  DSA_MARK(p.trace, 10);
   uint32_t kstar;
   uint32_t take_eq;
   if (kk == nc) {
@@ -350,6 +426,7 @@ DSA_DEV void resolve_token(const SelParams& p, int t, SelShared& sh) {
     kstar = known;
     take_eq = need;
   }
+  DSA_MARK(p.trace, 11);
   // compaction in position order: keys above kstar, then the first take_eq equal to it
   uint32_t my_eq = 0;
   visit([&](uint32_t key, uint32_t) { my_eq += (key == kstar); });
@@ -377,16 +454,14 @@ DSA_DEV void resolve_token(const SelParams& p, int t, SelShared& sh) {
       }
     });
   }
+  DSA_MARK(p.trace, 12);
   for (int i = (int)kk + tid; i < p.k; i += kSelThreads) out[i] = -1;
-  if (tid == 0) {
-    if (p.count) p.count[t] = (int32_t)kk;
-    ast(p.ctl + ctl::kTau + t, 0u);
-    ast(p.ctl + ctl::kDone + 64 * t, 0u);
-  }
+  if (tid == 0 && p.trace) p.trace[blockIdx.x * 16 + 13] = nc;
+  if (tid == 0 && p.count) p.count[t] = (int32_t)kk;
   __syncthreads();
 }
 
-template <int SRC, int KDT, int RT>
+template <int SRC, int KDT, int RTW>
 __global__ void __launch_bounds__(kSelThreads, 1) select_kernel(SelParams p) {
   __shared__ SelShared sh;
   const int tid = threadIdx.x;
@@ -396,108 +471,180 @@ __global__ void __launch_bounds__(kSelThreads, 1) select_kernel(SelParams p) {
   const int wg = blockIdx.x;
   const int64_t c0 = (int64_t)wg * p.chunk;
   const int T = p.T;
-  // ---------------- P1: scores of this chunk into LDS, group maxima
-  int64_t nkeys = p.L - c0;
-  nkeys = nkeys < 0 ? 0 : (nkeys > p.chunk ? p.chunk : nkeys);
+  DSA_MARK(p.trace, 0);
+  // ---------------- P1: scores of this chunk into LDS
+  int64_t nk64 = p.L - c0;
+  nk64 = nk64 < 0 ? 0 : (nk64 > p.chunk ? p.chunk : nk64);
+  const int nkeys = (int)nk64;
   if constexpr (SRC == 0) {
-    Frag8 qa[RT][4];
-    float wv[RT][16];
-    load_q_frags<RT>(p.q_idx, T, qa);
-    load_w<RT>(p.w_idx, T, wv);
-    uint32_t gm[RT];
+    // waves w and w+4 take the same key tiles and different row tiles
+    const int pair = wave & (kPairs - 1);
+    const int rt0 = (wave >= kPairs) ? RTW : 0;
+    Frag8 qa[RTW][4];
+    float wv[RTW][16];
+    load_q_frags<RTW>(p.q_idx, T, rt0, qa);
+    load_w<RTW>(p.w_idx, T, rt0, wv);
+    const bool active = 2 * rt0 < T;
+    const int ntiles = (nkeys + kTile - 1) / kTile;
+    const int nmine = ntiles > pair ? (ntiles - pair + kPairs - 1) / kPairs : 0;   // tiles pair, pair+kPairs, ...
+    if constexpr (KDT == 1) {
+      // the chunk's row scales, one bulk load into LDS
+      constexpr int PERS = kMaxChunk / kSelThreads;
+      float sv[PERS];
 #pragma unroll
-    for (int r = 0; r < RT; ++r) gm[r] = 0u;
-    const int ntiles = (int)((nkeys + kTile - 1) / kTile);
-    KeyTile<KDT> cur, nxt;
-    int tile = wave;
-    if (tile < ntiles) load_key_tile<KDT>(p.k_idx, p.k_scale, p.L, c0 + (int64_t)tile * kTile, cur);
-    for (; tile < ntiles; tile += kSelWaves) {
-      const int tn = tile + kSelWaves;
-      if (tn < ntiles) load_key_tile<KDT>(p.k_idx, p.k_scale, p.L, c0 + (int64_t)tn * kTile, nxt);
-      float out[RT];
-      score_tile<KDT, RT>(cur, qa, wv, out);
-      const int sl = tile * kTile + (lane & 31);
-      const int64_t s = c0 + sl;
+      for (int q = 0; q < PERS; ++q) {
+        const int i = tid + q * kSelThreads;
+        sv[q] = p.k_scale[c0 + (i < nkeys ? i : (nkeys > 0 ? nkeys - 1 : 0))];
+      }
 #pragma unroll
-      for (int r = 0; r < RT; ++r) {
-        const int tt = 2 * r + half;
-        if (tt < T) {
-          sh.sc[tt][sl] = out[r];
-          if (s < p.L && s <= p.pos0 + tt) gm[r] = max(gm[r], order_key(out[r]));
+      for (int q = 0; q < PERS; ++q) sh.kscale[tid + q * kSelThreads] = sv[q];
+      __syncthreads();
+    }
+    DSA_MARK(p.trace, 1);
+    KeyTile<KDT> buf[kPrefetch];
+    if (active && nmine > 0) {
+      // Loads are unconditional (tile index clamped to the last tile, which is then
+      // already cached) so the compiler keeps kPrefetch tiles in flight without
+      // draining the memory counter at branch merges.
+      auto tile_of = [&](int j) { return c0 + (int64_t)(pair + (j < nmine ? j : nmine - 1) * kPairs) * kTile; };
+#pragma unroll
+      for (int i = 0; i < kPrefetch; ++i) load_key_tile<KDT, false>(p.k_idx, p.k_scale, p.L, tile_of(i), buf[i]);
+      for (int base = 0; base < nmine; base += kPrefetch) {
+#pragma unroll
+        for (int i = 0; i < kPrefetch; ++i) {
+          const int j = base + i;
+          const int sl = (pair + j * kPairs) * kTile + (lane & 31);
+          if constexpr (KDT == 1) buf[i].scale = sh.kscale[sl & (kMaxChunk - 1)];
+          float out[RTW];
+          score_tile<KDT, RTW>(buf[i], qa, wv, out);
+          load_key_tile<KDT, false>(p.k_idx, p.k_scale, p.L, tile_of(j + kPrefetch), buf[i]);
+          if (j < nmine) {
+#pragma unroll
+            for (int r = 0; r < RTW; ++r) sh.sc[2 * (rt0 + r) + half][sl] = out[r];
+          }
         }
       }
-      cur = nxt;
-    }
-#pragma unroll
-    for (int r = 0; r < RT; ++r) {
-      const int tt = 2 * r + half;
-      if (tt < T) sh.gmax[tt][wave * 32 + (lane & 31)] = gm[r];
     }
   } else {
-    // scores from memory: coalesced reads, group g = elements g, g + kGroups, ...
+    constexpr int PER = kMaxChunk / kSelThreads;
     for (int t = 0; t < T; ++t) {
       const float* src = p.scores + (size_t)t * p.ld + c0;
-      for (int i = tid; i < nkeys; i += kSelThreads) sh.sc[t][i] = src[i];
-    }
-    __syncthreads();
-    for (int t = 0; t < T; ++t) {
-      if (tid < kGroups) {
-        uint32_t g = 0u;
-        for (int i = tid; i < nkeys; i += kGroups) {
-          const int64_t s = c0 + i;
-          if (s <= p.pos0 + t) g = max(g, order_key(sh.sc[t][i]));
-        }
-        sh.gmax[t][tid] = g;
+      float v[PER];
+#pragma unroll
+      for (int q = 0; q < PER; ++q) {
+        const int i = tid + q * kSelThreads;
+        v[q] = src[i < nkeys ? i : (nkeys > 0 ? nkeys - 1 : 0)];
+      }
+#pragma unroll
+      for (int q = 0; q < PER; ++q) {
+        const int i = tid + q * kSelThreads;
+        if (i < nkeys) sh.sc[t][i] = v[q];
       }
     }
   }
   __syncthreads();
-  // tau of this workgroup (one wave per token)
+  DSA_MARK(p.trace, 2);
+  // ---------------- tau bound: wave t takes token t; lane g holds the maximum of the
+  // visible scores g, g+64, ...; the m-th largest of those 64 maxima is <= the m-th
+  // largest visible score of the chunk.
   if (p.m > 0 && wg < p.n_part) {
     for (int t = wave; t < T; t += kSelWaves) {
-      const uint32_t tw = mth_largest_wave(sh.gmax[t], p.m);
-      if (lane == 0) amax(p.ctl + ctl::kTau + t, ~tw);
-    }
-  }
-  grid_barrier(p.ctl, p.nwg);
-  // ---------------- P2: candidates >= tau in position order; the last workgroup to
-  // publish a token's candidates resolves that token
-  if (tid < T) {
-    sh.tau[tid] = (p.m > 0) ? ~ald(p.ctl + ctl::kTau + tid) : 0u;
-    sh.resolve[tid] = 0u;
-  }
-  __syncthreads();
-  {
-    const int per = (p.chunk + kSelThreads - 1) / kSelThreads;
-    const int i0 = tid * per;
-    for (int tt = 0; tt < T; ++tt) {
-      const int t = (tt + wg) % T;            // rotate so different workgroups finish different tokens last
-      const uint32_t tau = sh.tau[t];
-      const int64_t lim = p.pos0 + t - c0;    // visible local indices: i <= lim and i < nkeys
-      uint32_t c = 0;
-      for (int i = i0; i < i0 + per; ++i)
-        if (i < nkeys && i <= lim && order_key(sh.sc[t][i]) >= tau) ++c;
-      uint32_t tot;
-      uint32_t o = block_excl_scan<kSelThreads>(c, sh.scan, &tot);
-      uint64_t* dst = p.cand + ((size_t)t * p.nwg + wg) * p.chunk;
-      for (int i = i0; i < i0 + per; ++i) {
-        if (i < nkeys && i <= lim) {
-          const uint32_t key = order_key(sh.sc[t][i]);
-          if (key >= tau) ast64(dst + o++, ((uint64_t)(uint32_t)(c0 + i) << 32) | key);
+      const int64_t lim = p.pos0 + t - c0;
+      uint32_t g = 0u;
+      for (int i0 = 0; i0 < nkeys; i0 += 512) {
+        float v[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) v[u] = sh.sc[t][(i0 + u * 64 + lane) & (kMaxChunk - 1)];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+          const int i = i0 + u * 64 + lane;
+          if (i < nkeys && i <= lim) g = max(g, order_key(v[u]));
         }
       }
-      if (tid == 0) ast(p.cnt + (size_t)t * p.nwg + wg, tot);
-      vm_wait_all();
-      __syncthreads();
-      if (tid == 0) {
-        if (aadd(p.ctl + ctl::kDone + 64 * t, 1u) == (uint32_t)p.nwg - 1u) sh.resolve[t] = 1u;
-      }
+      const uint32_t tw = mth_largest_lanes(g, p.m);
+      if (lane == 0) ast(p.tauv + (size_t)t * kMaxWG + wg, tw);
     }
   }
+  DSA_MARK(p.trace, 3);
+  grid_barrier(p.ctl, p.nwg);
+  DSA_MARK(p.trace, 4);
+  // ---------------- P2: tau = min of the published bounds; candidates >= tau in
+  // position order
+  for (int t = wave; t < T; t += kSelWaves) {
+    uint32_t tm = 0xffffffffu;
+    if (p.m > 0) {
+      uint32_t v[kMaxWG / 64];
+      const int nl = (p.n_part + 63) / 64;
+#pragma unroll
+      for (int i = 0; i < kMaxWG / 64; ++i) {
+        const int w = lane + 64 * i;
+        const int wc = w < p.n_part ? w : p.n_part - 1;
+        v[i] = i < nl ? ald(p.tauv + (size_t)t * kMaxWG + wc) : 0xffffffffu;
+      }
+#pragma unroll
+      for (int i = 0; i < kMaxWG / 64; ++i) tm = min(tm, (lane + 64 * i < p.n_part) ? v[i] : 0xffffffffu);
+      tm = wave_min_u32(tm);
+    } else {
+      tm = 0u;
+    }
+    if (lane == 0) sh.tau[t] = tm;
+  }
   __syncthreads();
-  // ---------------- P3: exact selection of the tokens this workgroup completed
-  for (int t = 0; t < T; ++t)
-    if (sh.resolve[t]) resolve_token(p, t, sh);
+  DSA_MARK(p.trace, 5);
+  {
+    constexpr int PER = kMaxChunk / kSelThreads;     // positions per thread (chunk <= 4096)
+    const int per = p.chunk / kSelThreads;
+    const int i0 = tid * per;
+    uint32_t cnt[kMaxT];
+#pragma unroll
+    for (int t = 0; t < kMaxT; ++t) {
+      cnt[t] = 0;
+      if (t < T) {
+        const uint32_t tau = sh.tau[t];
+        const int64_t lim = p.pos0 + t - c0;
+#pragma unroll
+        for (int q = 0; q < PER; ++q) {
+          const int i = i0 + q;
+          if (q < per && i < nkeys && i <= lim && order_key(sh.sc[t][i]) >= tau) ++cnt[t];
+        }
+      }
+    }
+    uint64_t tot_lo, tot_hi;
+    const uint64_t ex_lo = block_excl_scan64<kSelThreads>(
+        (uint64_t)cnt[0] | ((uint64_t)cnt[1] << 16) | ((uint64_t)cnt[2] << 32) | ((uint64_t)cnt[3] << 48),
+        sh.scan64, &tot_lo);
+    const uint64_t ex_hi = block_excl_scan64<kSelThreads>(
+        (uint64_t)cnt[4] | ((uint64_t)cnt[5] << 16) | ((uint64_t)cnt[6] << 32) | ((uint64_t)cnt[7] << 48),
+        sh.scan64, &tot_hi);
+    DSA_MARK(p.trace, 6);
+#pragma unroll
+    for (int t = 0; t < kMaxT; ++t) {
+      if (t < T && cnt[t]) {
+        uint32_t o = (uint32_t)(((t < 4 ? ex_lo : ex_hi) >> (16 * (t & 3))) & 0xffffu);
+        const uint32_t tau = sh.tau[t];
+        const int64_t lim = p.pos0 + t - c0;
+        uint64_t* dst = p.cand + ((size_t)t * p.nwg + wg) * p.chunk;
+#pragma unroll
+        for (int q = 0; q < PER; ++q) {
+          const int i = i0 + q;
+          if (q < per && i < nkeys && i <= lim) {
+            const uint32_t key = order_key(sh.sc[t][i]);
+            if (key >= tau) ast64(dst + o++, ((uint64_t)(uint32_t)(c0 + i) << 32) | key);
+          }
+        }
+      }
+    }
+    if (tid < T) {
+      const uint32_t tot = (uint32_t)(((tid < 4 ? tot_lo : tot_hi) >> (16 * (tid & 3))) & 0xffffu);
+      ast(p.cnt + (size_t)tid * p.nwg + wg, tot);
+    }
+  }
+  DSA_MARK(p.trace, 7);
+  grid_barrier(p.ctl, p.nwg);
+  DSA_MARK(p.trace, 8);
+  // ---------------- P3: workgroup t selects token t
+  if (wg < T) resolve_token(p, wg, sh);
+  DSA_MARK(p.trace, 15);
 }
 
 // ----------------------------------------------------------------------------- host launchers
@@ -528,13 +675,13 @@ hipError_t launch_indexer_scores(const void* q_idx, const float* w_idx, const vo
 SelGeometry select_geometry(int T, int64_t L, int64_t pos0, int k, int num_cu) {
   SelGeometry g{};
   int64_t per = (L + num_cu - 1) / num_cu;
-  int64_t chunk = ((per + 127) / 128) * 128;
-  if (chunk < 128) chunk = 128;
+  int64_t chunk = ((per + kSelThreads - 1) / kSelThreads) * kSelThreads;
+  if (chunk < kSelThreads) chunk = kSelThreads;
   g.chunk = (int)chunk;
   int64_t nwg = (L + chunk - 1) / chunk;
   if (nwg < T) nwg = T;
   g.nwg = (int)nwg;
-  g.fits = chunk <= kMaxChunk && nwg <= 1024;
+  g.fits = chunk <= kMaxChunk && nwg <= kMaxWG;
   g.n_part = (int)(pos0 / chunk);
   const int64_t kmax = (int64_t)k < L ? k : L;
   g.m = 0;
@@ -547,10 +694,15 @@ SelGeometry select_geometry(int T, int64_t L, int64_t pos0, int k, int num_cu) {
 
 size_t select_workspace_bytes(int T, int64_t L, int k, int num_cu) {
   SelGeometry g = select_geometry(T, L, L - T, k, num_cu);
-  return ctl::kBytes + (size_t)kMaxT * 1024 * 4 + (size_t)kMaxT * g.nwg * g.chunk * sizeof(uint64_t);
+  return ctl::kBytes + 2 * (size_t)kMaxT * kMaxWG * 4 + (size_t)kMaxT * g.nwg * g.chunk * sizeof(uint64_t);
 }
 
 int64_t select_max_context(int num_cu) { return (int64_t)num_cu * kMaxChunk; }
+
+#ifdef DSA_TRACE
+static uint64_t* g_trace = nullptr;
+extern "C" void dsa_trace_set(void* buf) { g_trace = static_cast<uint64_t*>(buf); }
+#endif
 
 hipError_t launch_select(int src, const void* q_idx, const float* w_idx, const void* k_idx,
                          const float* k_scale, int kdt, const float* scores, int64_t ld, int T,
@@ -574,22 +726,21 @@ hipError_t launch_select(int src, const void* q_idx, const float* w_idx, const v
   p.n_part = g.n_part;
   p.idx = idx;
   p.count = count;
+#ifdef DSA_TRACE
+  p.trace = g_trace;
+#endif
   uint8_t* w8 = static_cast<uint8_t*>(ws);
   p.ctl = reinterpret_cast<uint32_t*>(w8);
   p.cnt = reinterpret_cast<uint32_t*>(w8 + ctl::kBytes);
-  p.cand = reinterpret_cast<uint64_t*>(w8 + ctl::kBytes + (size_t)kMaxT * 1024 * 4);
+  p.tauv = reinterpret_cast<uint32_t*>(w8 + ctl::kBytes + (size_t)kMaxT * kMaxWG * 4);
+  p.cand = reinterpret_cast<uint64_t*>(w8 + ctl::kBytes + 2 * (size_t)kMaxT * kMaxWG * 4);
   void* args[] = {&p};
-  const int rt = row_tiles(T);
+  // row tiles per wave: the two waves of a pair split ceil(T/2) row tiles
+  const int rtw = row_tiles(T) <= 2 ? 1 : 2;
   void* fn = nullptr;
-  if (src == 1) {
-    fn = (void*)select_kernel<1, 0, 1>;
-  } else if (kdt == 0) {
-    fn = rt == 1 ? (void*)select_kernel<0, 0, 1> : rt == 2 ? (void*)select_kernel<0, 0, 2>
-       : rt == 3 ? (void*)select_kernel<0, 0, 3> : (void*)select_kernel<0, 0, 4>;
-  } else {
-    fn = rt == 1 ? (void*)select_kernel<0, 1, 1> : rt == 2 ? (void*)select_kernel<0, 1, 2>
-       : rt == 3 ? (void*)select_kernel<0, 1, 3> : (void*)select_kernel<0, 1, 4>;
-  }
+  if (src == 1) fn = (void*)select_kernel<1, 0, 1>;
+  else if (kdt == 0) fn = rtw == 1 ? (void*)select_kernel<0, 0, 1> : (void*)select_kernel<0, 0, 2>;
+  else fn = rtw == 1 ? (void*)select_kernel<0, 1, 1> : (void*)select_kernel<0, 1, 2>;
   // every workgroup must be resident at once (one per CU by the LDS footprint)
   int per_cu = 0;
   hipError_t e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, fn, kSelThreads, 0);

@@ -1,0 +1,155 @@
+"""dsa_layer_step on the GPU against the oracle's layer step.
+
+Stage checks are teacher-forced: the oracle consumes the GPU's own rotated projection
+(qkv_out) and selected indices, so each stage is compared on identical inputs:
+* projection + RoPE: within one bf16 ulp of the fp64 result (fp32 accumulation);
+* cache append: K/V rows equal the exported rotated rows bit for bit; the e4m3 indexer
+  rows and scales equal the oracle's quantisation of the exported k_I bit for bit;
+* selection: within the 2^-16 * S rounding band of the fp64 indexer scores;
+* layer output: |gpu - ref| <= 2e-2 * max(1, |ref|) (bf16 storage of large values).
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import synth
+from oracle import dsa_oracle as O
+from tests.gpu_util import DEV, up, down, bf16_bits, tie_band_ok
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def dsa():
+    import sparse_attention_decode_indexer_amd as m
+    return m
+
+
+def _within_ulp(g, r, kind="dsa"):
+    """Projection outputs: one bf16 ulp of the value for plain columns; for rotated
+    columns the inputs of the rotation carry one-ulp differences each, so the bound is
+    two ulps of the rotation pair's norm (which the rotation preserves)."""
+    scale = np.abs(r).copy()
+    segs = [(0, 1024, 128), (1024, 128, 128)]
+    if kind == "dsa":
+        segs += [(1280, 1024, 64), (2304, 64, 64)]
+    for off, n, d in segs:
+        blk = r[:, off:off + n].reshape(r.shape[0], -1, d)
+        a, b = blk[..., : d // 2], blk[..., d // 2:]
+        nrm = np.sqrt(a * a + b * b)
+        scale[:, off:off + n] = np.concatenate([nrm, nrm], axis=-1).reshape(r.shape[0], n) * 2.0
+    tol = 2.0 ** -7 * np.maximum(scale, 2.0 ** -30)
+    return np.abs(g - r) <= tol
+
+
+def _run_layer(dsa, kind, lay, x_bits, T, pos0, top_k=2048, window=128, sink=None):
+    n_proj = synth.N_PROJ_DSA if kind == "dsa" else synth.N_PROJ_SWA
+    cfg = dsa.layer_config(dsa.LAYER_DSA if kind == "dsa" else dsa.LAYER_SWA, top_k=top_k, window=window,
+                           sink=sink)
+    g_gamma, g_w, g_wo = up(lay.gamma), up(lay.w_qkvi), up(lay.w_o)
+    kc, vc = up(lay.k), up(lay.v)
+    ki = up(lay.k_idx) if kind == "dsa" else None
+    ks = up(lay.k_idx_scale) if kind == "dsa" else None
+    cache = dsa.LayerCache(kc.data_ptr(), vc.data_ptr(), ki.data_ptr() if ki is not None else None,
+                           ks.data_ptr() if ks is not None else None, lay.capacity)
+    w = dsa.LayerWeights(g_gamma.data_ptr(), g_w.data_ptr(), g_wo.data_ptr())
+    x = up(x_bits)
+    xo = torch.zeros_like(x)
+    qkv = torch.zeros((T, n_proj), dtype=torch.int16, device=DEV)
+    idx = torch.full((T, top_k), -7, dtype=torch.int32, device=DEV) if kind == "dsa" else None
+    ws = dsa.workspace(dsa.WS_LAYER_DSA if kind == "dsa" else dsa.WS_LAYER_SWA, T, pos0 + T,
+                       top_k if kind == "dsa" else window)
+    dsa.dsa_layer_step(cfg, w, cache, x, xo, T, pos0, idx_out=idx, qkv_out=qkv, ws=ws)
+    torch.cuda.synchronize()
+    out = {"x_out": bf16_bits(xo), "qkv": bf16_bits(qkv), "k": bf16_bits(kc), "v": bf16_bits(vc)}
+    if kind == "dsa":
+        out["idx"] = down(idx)
+        out["k_idx"] = down(ki)
+        out["k_idx_scale"] = down(ks)
+    return out
+
+
+@pytest.mark.parametrize("L,T,top_k", [(3000, 8, 2048), (40000, 8, 2048), (777, 3, 64)])
+def test_dsa_layer_step_stages(dsa, L, T, top_k):
+    pos0 = L - T
+    lay = synth.layer_inputs("dsa", 0, L, T, seed=L)
+    x = synth.module_x(L, T)
+    g = _run_layer(dsa, "dsa", lay, x, T, pos0, top_k=top_k)
+    # free-running oracle for the projection
+    cache0 = {"k": lay.k.copy(), "v": lay.v.copy(), "k_idx": lay.k_idx.copy(), "k_idx_scale": lay.k_idx_scale.copy()}
+    free = O.layer_step("dsa", x, lay.gamma, lay.w_qkvi, lay.w_o, cache0, pos0, top_k=top_k)
+    gq = O.decode_bf16(g["qkv"])
+    ok = _within_ulp(gq, free["qkv"])
+    assert ok.mean() == 1.0, f"{(~ok).sum()} projection values beyond one bf16 ulp"
+    # teacher-forced oracle
+    cache = {"k": lay.k.copy(), "v": lay.v.copy(), "k_idx": lay.k_idx.copy(), "k_idx_scale": lay.k_idx_scale.copy()}
+    tf = O.layer_step("dsa", x, lay.gamma, lay.w_qkvi, lay.w_o, cache, pos0, top_k=top_k,
+                      teacher={"qkv": g["qkv"], "idx": g["idx"]})
+    # appended rows
+    assert np.array_equal(g["k"][pos0:L], g["qkv"][:, 1024:1152])
+    assert np.array_equal(g["v"][pos0:L], g["qkv"][:, 1152:1280])
+    assert np.array_equal(g["k_idx"][pos0:L], cache["k_idx"][pos0:L])
+    assert np.array_equal(g["k_idx_scale"][pos0:L], cache["k_idx_scale"][pos0:L])
+    # untouched rows stay untouched
+    assert np.array_equal(g["k"][:pos0], lay.k[:pos0]) and np.array_equal(g["k_idx"][:pos0], lay.k_idx[:pos0])
+    # selection vs the fp64 scores of the same rotated queries and cache
+    krows = O.dequant_rows(cache["k_idx"][:L], "fp8", cache["k_idx_scale"][:L])
+    qi = O.decode_bf16(g["qkv"][:, 1280:2304]).reshape(T, 16, 64)
+    wi = O.decode_bf16(g["qkv"][:, 2368:2384])
+    r, S = O.indexer_scores(qi, wi, krows, pos0, with_abs=True)
+    ridx, _ = O.topk_indices(r, pos0, top_k)
+    okb, nd = tie_band_ok(g["idx"], ridx, r, S, pos0, top_k)
+    assert okb, nd
+    # layer output (teacher-forced and free-running)
+    gx = O.decode_bf16(g["x_out"])
+    for ref in (tf["x_out"], free["x_out"]):
+        assert np.all(np.abs(gx - ref) <= 2e-2 * np.maximum(1.0, np.abs(ref)))
+
+
+@pytest.mark.parametrize("pos0,T", [(5000, 8), (100, 8), (0, 1)])
+def test_swa_layer_step_stages(dsa, pos0, T):
+    cap = 256
+    L = pos0 + T
+    lay = synth.layer_inputs("swa", 1, L, T, seed=7, ring_cap=cap)
+    x = synth.module_x(7, T)
+    g = _run_layer(dsa, "swa", lay, x, T, pos0)
+    c0 = {"k": lay.k.copy(), "v": lay.v.copy(), "ring_cap": cap}
+    free = O.layer_step("swa", x, lay.gamma, lay.w_qkvi, lay.w_o, c0, pos0)
+    assert _within_ulp(O.decode_bf16(g["qkv"]), free["qkv"], "swa").all()
+    c1 = {"k": lay.k.copy(), "v": lay.v.copy(), "ring_cap": cap}
+    tf = O.layer_step("swa", x, lay.gamma, lay.w_qkvi, lay.w_o, c1, pos0, teacher={"qkv": g["qkv"]})
+    for t in range(T):
+        assert np.array_equal(g["k"][(pos0 + t) % cap], g["qkv"][t, 1024:1152])
+    gx = O.decode_bf16(g["x_out"])
+    for ref in (tf["x_out"], free["x_out"]):
+        assert np.all(np.abs(gx - ref) <= 2e-2 * np.maximum(1.0, np.abs(ref)))
+
+
+def test_layer_step_run_to_run_bitwise(dsa):
+    L, T = 20000, 8
+    lay = synth.layer_inputs("dsa", 0, L, T, seed=11)
+    x = synth.module_x(11, T)
+    a = _run_layer(dsa, "dsa", lay, x, T, L - T)
+    for _ in range(2):
+        b = _run_layer(dsa, "dsa", lay, x, T, L - T)
+        for key in a:
+            assert np.array_equal(a[key], b[key]), key
+
+
+def test_layer_step_with_sink_matches_oracle_attention(dsa):
+    """Sink logits through the layer: compare against the oracle fed the GPU's
+    rotated projection and indices, attention recomputed with the sink."""
+    L, T = 5000, 4
+    lay = synth.layer_inputs("dsa", 0, L, T, seed=13)
+    x = synth.module_x(13, T)
+    sink = up(synth.sink_logits(13, std=2.0))
+    g = _run_layer(dsa, "dsa", lay, x, T, L - T, sink=sink)
+    q = O.decode_bf16(g["qkv"][:, :1024]).reshape(T, 8, 128)
+    Kc = O.decode_bf16(g["k"][:L]); Vc = O.decode_bf16(g["v"][:L])
+    attn = O.sparse_attention(q, Kc, Vc, g["idx"], 1 / math.sqrt(128), down(sink).astype(np.float64))
+    attn = O.bf16_round_trip(attn.reshape(T, 1024))
+    ref = O.project(attn, O.decode_bf16(lay.w_o)) + O.decode_bf16(x)
+    gx = O.decode_bf16(g["x_out"])
+    assert np.all(np.abs(gx - ref) <= 2e-2 * np.maximum(1.0, np.abs(ref)))

@@ -95,7 +95,7 @@ DSA_DEV void load_q_frags(const uint16_t* __restrict__ q_idx, int T, int rt0, Fr
   }
 }
 
-// Head weights of this lane's accumulator elements.  Element e of the 32x32 output holds
+// Half head weights (w/2) of this lane's accumulator elements.  Element e of the 32x32 output holds
 // row 8*(e>>2) + 4*half + (e&3): token 2r + (e>>3), head 8*((e>>2)&1) + 4*half + (e&3).
 template <int RTW>
 DSA_DEV void load_w(const float* __restrict__ w_idx, int T, int rt0, float (&wv)[RTW][16]) {
@@ -107,9 +107,73 @@ DSA_DEV void load_w(const float* __restrict__ w_idx, int T, int rt0, float (&wv)
       const int tt = 2 * (rt0 + r) + (e >> 3);
       const int hh = 8 * ((e >> 2) & 1) + 4 * half + (e & 3);
       const float v = w_idx[(tt < T ? tt : T - 1) * kHI + hh];
-      wv[r][e] = (tt < T) ? v : 0.0f;
+      wv[r][e] = (tt < T) ? 0.5f * v : 0.0f;
     }
   }
+}
+
+// Linear part of the score.  relu(x) = (x + |x|) / 2, so
+//   I[t,s] = sum_h (w_h/2) |q_h . k_s|  +  k_s . qlin_t,   qlin_t = sum_h (w_h/2) q_h.
+// qlin is formed once per launch in fp32 (fixed order h = 0..15) and stored as three
+// bf16 parts hi + mid + lo (each the round-to-nearest-even of the remainder), which
+// carry its 24 bits; the key contraction with the parts runs on the matrix cores.
+// ql: [3][kMaxT][kDI] bf16 in LDS; rows of tokens >= T are zero.
+template <int NT>
+DSA_DEV void build_qlin(const uint16_t* __restrict__ q_idx, const float* __restrict__ w_idx, int T,
+                        uint16_t* ql) {
+  for (int i = threadIdx.x; i < kMaxT * kDI; i += NT) {
+    const int t = i / kDI, d = i % kDI;
+    const int tc = t < T ? t : T - 1;
+    float wq[kHI], qv[kHI];
+#pragma unroll
+    for (int h = 0; h < kHI; ++h) {
+      wq[h] = w_idx[tc * kHI + h];
+      qv[h] = bf16_to_f32(q_idx[(tc * kHI + h) * kDI + d]);
+    }
+    float acc = 0.0f;
+#pragma unroll
+    for (int h = 0; h < kHI; ++h) acc = fmaf(0.5f * wq[h], qv[h], acc);
+    acc = (t < T) ? acc : 0.0f;
+    const uint16_t hi = f32_to_bf16(acc);
+    const float r1 = acc - bf16_to_f32(hi);
+    const uint16_t mid = f32_to_bf16(r1);
+    const uint16_t lo = f32_to_bf16(r1 - bf16_to_f32(mid));
+    ql[(0 * kMaxT + t) * kDI + d] = hi;
+    ql[(1 * kMaxT + t) * kDI + d] = mid;
+    ql[(2 * kMaxT + t) * kDI + d] = lo;
+  }
+}
+
+// A operand of the linear tile for row tiles rt0 .. rt0+RTW-1: row 8r + 4c + p holds part
+// p (< 3) of qlin for token 2(rt0+r) + c, so accumulator element 4r + p of a lane in half c
+// is part p of the token whose score that lane ends up holding.  Other rows are zero.
+template <int RTW>
+DSA_DEV void load_qlin_frags(const uint16_t* ql, int rt0, Frag8 (&qf)[4]) {
+  const int l = threadIdx.x & 63;
+  const int half = l >> 5;
+  const int row = l & 31;
+  const int r = row >> 3, c = (row >> 2) & 1, pp = row & 3;
+  const int t = 2 * (rt0 + r) + c;
+  const bool ok = (r < RTW) & (pp < 3) & (t < kMaxT);
+  const int pc = pp < 3 ? pp : 2, tcl = t < kMaxT ? t : kMaxT - 1;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const uint4 v = *reinterpret_cast<const uint4*>(ql + (pc * kMaxT + tcl) * kDI + half * 32 + 8 * j);
+    qf[j].u = ok ? v : make_uint4(0u, 0u, 0u, 0u);
+  }
+}
+
+// Order key without the -0 canonicalisation (3 instructions).  Only used where -0 may
+// rank below +0 harmlessly (the tau lower bound).
+DSA_DEV uint32_t order_key_fast(float f) {
+  const uint32_t u = __float_as_uint(f);
+  return u ^ ((uint32_t)((int32_t)u >> 31) | 0x80000000u);
+}
+
+// Inverse of order_key on canonical keys: the float with that key (key 0 -> -inf side
+// handled by the caller).
+DSA_DEV float key_to_float(uint32_t k) {
+  return __uint_as_float((k & 0x80000000u) ? (k & 0x7fffffffu) : ~k);
 }
 
 // relu by integer max on the bit pattern: non-negative floats (sign 0) are non-negative
@@ -118,12 +182,14 @@ DSA_DEV void load_w(const float* __restrict__ w_idx, int T, int rt0, float (&wv)
 DSA_DEV float relu_bits(float x) { return __int_as_float(max(__float_as_int(x), 0)); }
 
 // Scores of one 32-key tile for RTW row tiles: out[r] is the score of token
-// 2(rt0+r) + (lane>>5) for key s0 + (lane & 31).  The arithmetic and its order are fixed
-// (products and sums in fp32: head sum over 8 heads per lane in element order, then the
-// partner lane's 8, then the row scale), the same in every kernel that calls it.
+// 2(rt0+r) + (lane>>5) for key s0 + (lane & 31).  The arithmetic and its order are fixed,
+// the same in every kernel that calls it: per head a = q_h . k (MFMA, fp32); per lane
+// sum_e (w/2)|a_e| over its 8 heads of each token of the row tile, in element order; the
+// two lanes of a (token pair, key) exchange and add; then + ((hi + mid) + lo) of the
+// linear tile; then x the row scale for e4m3 keys.
 template <int KDT, int RTW>
-DSA_DEV void score_tile(const KeyTile<KDT>& kt, const Frag8 (&qa)[RTW][4], const float (&wv)[RTW][16],
-                        float (&out)[RTW]) {
+DSA_DEV void score_tile(const KeyTile<KDT>& kt, const Frag8 (&qa)[RTW][4], const Frag8 (&qf)[4],
+                        const float (&wv)[RTW][16], float (&out)[RTW]) {
   Frag8 kb[4];
   if constexpr (KDT == 0) {
 #pragma unroll
@@ -139,7 +205,9 @@ DSA_DEV void score_tile(const KeyTile<KDT>& kt, const Frag8 (&qa)[RTW][4], const
       kb[j].v = bf16x8_t{a[0], a[1], b[0], b[1], c[0], c[1], d[0], d[1]};
     }
   }
-  const int half = (threadIdx.x & 63) >> 5;
+  f32x16_t lacc = {};
+#pragma unroll
+  for (int j = 0; j < 4; ++j) lacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qf[j].v, kb[j].v, lacc, 0, 0, 0);
 #pragma unroll
   for (int r = 0; r < RTW; ++r) {
     f32x16_t acc = {};
@@ -148,16 +216,17 @@ DSA_DEV void score_tile(const KeyTile<KDT>& kt, const Frag8 (&qa)[RTW][4], const
       acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa[r][j].v, kb[j].v, acc, 0, 0, 0);
     float p0 = 0.0f, p1 = 0.0f;
 #pragma unroll
-    for (int e = 0; e < 8; ++e) p0 = fmaf(wv[r][e], relu_bits(acc[e]), p0);
+    for (int e = 0; e < 8; ++e) p0 = fmaf(wv[r][e], fabsf(acc[e]), p0);
 #pragma unroll
-    for (int e = 8; e < 16; ++e) p1 = fmaf(wv[r][e], relu_bits(acc[e]), p1);
-    // lanes l and l+32 hold the same (token pair, key) over complementary heads: lane l
-    // keeps token 2r (p0) and sends p1; lane l+32 keeps token 2r+1 (p1) and sends p0.
-    const float send = half ? p0 : p1;
-    const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(send), __float_as_uint(send), false, false);
-    const float recv = __uint_as_float(half ? sw[0] : sw[1]);
-    const float tot = (half ? p1 : p0) + recv;
-    out[r] = (KDT == 1) ? tot * kt.scale : tot;
+    for (int e = 8; e < 16; ++e) p1 = fmaf(wv[r][e], fabsf(acc[e]), p1);
+    // lanes l and l+32 hold the same (token pair, key) over complementary heads: one
+    // swap of p0's upper half with p1's lower half leaves token 2r's two partial sums
+    // side by side in lane l and token 2r+1's in lane l+32.
+    const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(p0), __float_as_uint(p1), false, false);
+    const float tot = __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
+    const float lin = (lacc[4 * r] + lacc[4 * r + 1]) + lacc[4 * r + 2];
+    const float v = tot + lin;
+    out[r] = (KDT == 1) ? v * kt.scale : v;
   }
 }
 
@@ -171,10 +240,15 @@ __global__ void __launch_bounds__(kScoreThreads)
 indexer_scores_kernel(const uint16_t* __restrict__ q_idx, const float* __restrict__ w_idx,
                       const uint8_t* __restrict__ k_idx, const float* __restrict__ k_scale,
                       int T, int64_t L, int64_t pos0, float* __restrict__ scores, int64_t ld) {
+  __shared__ uint16_t ql[3 * kMaxT * kDI];
+  build_qlin<kScoreThreads>(q_idx, w_idx, T, ql);
   Frag8 qa[RT][4];
   float wv[RT][16];
   load_q_frags<RT>(q_idx, T, 0, qa);
   load_w<RT>(w_idx, T, 0, wv);
+  __syncthreads();
+  Frag8 qf[4];
+  load_qlin_frags<RT>(ql, 0, qf);
   const int lane = threadIdx.x & 63;
   const int half = lane >> 5;
   const int wave = threadIdx.x >> 6;
@@ -191,7 +265,7 @@ indexer_scores_kernel(const uint16_t* __restrict__ q_idx, const float* __restric
     const int64_t tile = tile0 + i;
     if (tile >= ntiles) break;
     float out[RT];
-    score_tile<KDT, RT>(buf[i], qa, wv, out);
+    score_tile<KDT, RT>(buf[i], qa, qf, wv, out);
     const int64_t s = tile * kTile + (lane & 31);
 #pragma unroll
     for (int r = 0; r < RT; ++r) {
@@ -234,42 +308,10 @@ struct SelParams {
 struct SelShared {
   float sc[kMaxT][kMaxChunk];        // chunk scores (P1/P2); resolver scratch (P3)
   float kscale[kMaxChunk];           // row scales of the chunk (e4m3 keys)
-  uint32_t tau[kMaxT];
-  uint64_t scan64[32];
+  uint16_t ql[3 * kMaxT * kDI];      // linear-part query, three bf16 parts
+  uint32_t wcnt[2 * kSelWaves];      // resolver: per-wave counts
   uint32_t scan[32];
 };
-
-// Exclusive prefix sum of 64-bit values across the block (fields packed by the caller).
-template <int NT>
-DSA_DEV uint64_t block_excl_scan64(uint64_t v, uint64_t* scratch, uint64_t* total) {
-  constexpr int NW = NT / 64;
-  const int lane = threadIdx.x & 63;
-  const int wid = threadIdx.x >> 6;
-  uint64_t inc = v;
-#pragma unroll
-  for (int d = 1; d < 64; d <<= 1) {
-    const uint64_t o = __shfl_up(inc, d, 64);
-    if (lane >= d) inc += o;
-  }
-  if (lane == 63) scratch[wid] = inc;
-  __syncthreads();
-  if (wid == 0) {
-    uint64_t t = (lane < NW) ? scratch[lane] : 0ull;
-    uint64_t ti = t;
-#pragma unroll
-    for (int d = 1; d < 64; d <<= 1) {
-      const uint64_t o = __shfl_up(ti, d, 64);
-      if (lane >= d) ti += o;
-    }
-    if (lane < NW) scratch[lane] = ti - t;
-    if (lane == NW - 1) scratch[NW] = ti;
-  }
-  __syncthreads();
-  const uint64_t res = scratch[wid] + inc - v;
-  *total = scratch[NW];
-  __syncthreads();
-  return res;
-}
 
 // m-th largest of the 64 values held by the lanes of one wave (1 <= m <= 64): each
 // lane counts the values ranked above its own (larger, or equal in a lower lane); the
@@ -286,98 +328,33 @@ DSA_DEV uint32_t mth_largest_lanes(uint32_t v, int m) {
   return __builtin_amdgcn_readlane(v, __builtin_ctzll(bal));
 }
 
-// Exact selection of the kk best candidates of token t.  Runs in one workgroup after
-// every workgroup has published its candidates (after the second grid barrier).
-DSA_DEV void resolve_token(const SelParams& p, int t, SelShared& sh) {
-  uint32_t* pre = reinterpret_cast<uint32_t*>(&sh.sc[0][0]);         // [nwg + 1]
-  uint32_t* hist = pre + 1040;                                        // [2048]
-  uint32_t* misc = hist + 2048;                                       // small
+constexpr int kRegPer = 16;                                  // candidates per lane
+constexpr uint32_t kRegCands = kSelThreads * kRegPer;        // register-resident limit
+
+// Register-resident tail of the selection for nc <= kRegCands candidates already in LDS
+// (position order): wave w holds elements [w*R, (w+1)*R) as 64-element blocks (lane =
+// element), so ballots give position-ordered ranks.  Radix passes histogram the
+// registers; the compaction counts (above, equal) per wave in one pass and writes in a
+// second.
+DSA_DEV void resolve_regs(const SelParams& p, int t, SelShared& sh, const uint64_t* lc,
+                          uint32_t nc, uint32_t kk, uint32_t kmin, uint32_t kmax,
+                          uint32_t* hist, uint32_t* misc) {
   const int tid = threadIdx.x;
-  const int nwg = p.nwg;
-  const uint32_t* cnt_t = p.cnt + (size_t)t * nwg;
-  // prefix over workgroup counts
-  uint32_t carry = 0;
-  for (int base = 0; base < nwg; base += kSelThreads) {
-    const int w = base + tid;
-    const uint32_t cv = ald(cnt_t + (w < nwg ? w : nwg - 1));
-    const uint32_t c = (w < nwg) ? cv : 0u;
-    uint32_t tot;
-    const uint32_t ex = block_excl_scan<kSelThreads>(c, sh.scan, &tot);
-    if (w < nwg) pre[w] = carry + ex;
-    carry += tot;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const uint32_t R = ((nc + kSelWaves - 1) / kSelWaves + 63) & ~63u;   // <= 64 * kRegPer
+  const uint32_t w0 = min(nc, (uint32_t)wave * R), w1 = min(nc, w0 + R);
+  const uint32_t nmine = (w1 > w0 + lane) ? (w1 - w0 - lane + 63u) / 64u : 0u;
+  uint64_t e[kRegPer];
+#pragma unroll
+  for (int i = 0; i < kRegPer; ++i) {
+    const uint32_t g = w0 + 64u * i + lane;
+    e[i] = lc[g < nc ? g : nc - 1];
   }
-  if (tid == 0) pre[nwg] = carry;
-  __syncthreads();
-  const uint32_t nc = carry;
-  const int64_t vis = p.pos0 + t + 1;
-  uint32_t kk = (uint32_t)((int64_t)p.k < vis ? p.k : vis);
-  if (kk > nc) kk = nc;   // cannot happen when the bound holds; keeps reads in range
-  const uint64_t* base = p.cand + (size_t)t * nwg * p.chunk;
-  // Bring the candidates on chip when they fit: many independent coherent loads in
-  // flight per thread, then every pass below reads LDS.
-  uint64_t* lc = reinterpret_cast<uint64_t*>(misc + 16);              // 8-byte aligned
-  const uint32_t lds_cap = (uint32_t)((sizeof(sh.sc) - (1040 + 2048 + 16) * 4) / 8);
-  const bool in_lds = nc > 0 && nc <= lds_cap;
-  if (in_lds) {
-    constexpr int U = 8;
-    for (uint32_t g0b = 0; g0b < nc; g0b += kSelThreads * U) {
-      uint64_t v[U];
-      uint32_t gi[U];
-      size_t off[U];
-#pragma unroll
-      for (int u = 0; u < U; ++u) {
-        gi[u] = g0b + u * kSelThreads + tid;
-        const uint32_t g = gi[u] < nc ? gi[u] : nc - 1;     // clamped: loads stay unconditional
-        int lo = 0, hi = nwg - 1;
-        while (lo < hi) {
-          const int mid = (lo + hi + 1) >> 1;
-          if (pre[mid] <= g) lo = mid; else hi = mid - 1;
-        }
-        off[u] = (size_t)lo * p.chunk + (g - pre[lo]);
-      }
-#pragma unroll
-      for (int u = 0; u < U; ++u) v[u] = ald64(base + off[u]);
-#pragma unroll
-      for (int u = 0; u < U; ++u)
-        if (gi[u] < nc) lc[gi[u]] = v[u];
-    }
-    __syncthreads();
-  }
-  DSA_MARK(p.trace, 9);
-  // contiguous run of candidates per thread, visited in position order
-  const uint32_t run = (nc + kSelThreads - 1) / kSelThreads;
-  const uint32_t g0 = min(nc, (uint32_t)tid * run);
-  const uint32_t g1 = min(nc, g0 + run);
-  auto visit = [&](auto&& fn) {
-    if (g0 >= g1) return;
-    if (in_lds) {
-      for (uint32_t g = g0; g < g1; ++g) {
-        const uint64_t e = lc[g];
-        fn((uint32_t)e, (uint32_t)(e >> 32));
-      }
-      return;
-    }
-    int lo = 0, hi = nwg - 1;            // largest w with pre[w] <= g0
-    while (lo < hi) {
-      const int mid = (lo + hi + 1) >> 1;
-      if (pre[mid] <= g0) lo = mid; else hi = mid - 1;
-    }
-    int w = lo;
-    uint32_t j = g0 - pre[w];
-    for (uint32_t g = g0; g < g1; ++g) {
-      while (g >= pre[w + 1]) { ++w; j = 0; }
-      const uint64_t e = ald64(base + (size_t)w * p.chunk + j);
-      fn((uint32_t)e, (uint32_t)(e >> 32));
-      ++j;
-    }
-  };
-  uint32_t kmin = 0xffffffffu, kmax = 0u;
-  visit([&](uint32_t key, uint32_t) { kmin = min(kmin, key); kmax = max(kmax, key); });
   kmin = block_min_u32<kSelThreads>(kmin, sh.scan);
   kmax = block_max_u32<kSelThreads>(kmax, sh.scan);
   DSA_MARK(p.trace, 10);
-  uint32_t kstar;
-  uint32_t take_eq;
+  uint32_t kstar, take_eq;
   if (kk == nc) {
     kstar = kmin;
     take_eq = 0xffffffffu;
@@ -391,12 +368,14 @@ DSA_DEV void resolve_token(const SelParams& p, int t, SelShared& sh) {
       const int dbits = hi < 11 ? hi : 11;
       const int lo = hi - dbits;
       const uint32_t nb = 1u << dbits;
-      for (int b = tid; b < 2048; b += kSelThreads) hist[b] = 0u;
+      for (int b2 = tid; b2 < 2048; b2 += kSelThreads) hist[b2] = 0u;
       __syncthreads();
       const uint32_t pmask = hi >= 32 ? 0u : ~((1u << hi) - 1u);
-      visit([&](uint32_t key, uint32_t) {
-        if ((key & pmask) == known) atomicAdd(&hist[(key >> lo) & (nb - 1u)], 1u);
-      });
+#pragma unroll
+      for (int i = 0; i < kRegPer; ++i) {
+        const uint32_t key = (uint32_t)e[i];
+        if (((uint32_t)i < nmine) & ((key & pmask) == known)) atomicAdd(&hist[(key >> lo) & (nb - 1u)], 1u);
+      }
       __syncthreads();
       // largest digit d with count(digit >= d) >= need
       constexpr int PER = 2048 / kSelThreads;
@@ -421,38 +400,299 @@ DSA_DEV void resolve_token(const SelParams& p, int t, SelShared& sh) {
       need -= misc[1];
       known |= d << lo;
       hi = lo;
+      const uint32_t in_bin = hist[d];
       __syncthreads();
+      if (need == in_bin && hi > 0) {
+        // the whole boundary bin is taken: the cut is its smallest key
+        const uint32_t pm = ~((1u << hi) - 1u);
+        uint32_t bmin = 0xffffffffu;
+#pragma unroll
+        for (int i = 0; i < kRegPer; ++i) {
+          const uint32_t key = (uint32_t)e[i];
+          if (((uint32_t)i < nmine) & ((key & pm) == known)) bmin = min(bmin, key);
+        }
+        known = block_min_u32<kSelThreads>(bmin, sh.scan);
+        need = 0xffffffffu;      // every key equal to the cut is taken
+        hi = 0;
+      }
     }
     kstar = known;
     take_eq = need;
   }
   DSA_MARK(p.trace, 11);
-  // compaction in position order: keys above kstar, then the first take_eq equal to it
-  uint32_t my_eq = 0;
-  visit([&](uint32_t key, uint32_t) { my_eq += (key == kstar); });
-  uint32_t tot;
-  const uint32_t eq_base = block_excl_scan<kSelThreads>(my_eq, sh.scan, &tot);
-  uint32_t my_sel = 0;
+  // per-wave counts of keys above and equal to the cut
+  uint32_t cgt = 0, ceq = 0;
+#pragma unroll
+  for (int i = 0; i < kRegPer; ++i) {
+    const uint32_t key = (uint32_t)e[i];
+    const bool v = (uint32_t)i < nmine;
+    cgt += (uint32_t)__builtin_popcountll(__ballot(v & (key > kstar)));
+    ceq += (uint32_t)__builtin_popcountll(__ballot(v & (key == kstar)));
+  }
+  uint32_t* wq = sh.wcnt;           // [8] above counts, then [8] equal counts
+  if (lane == 0) { wq[wave] = cgt; wq[kSelWaves + wave] = ceq; }
+  __syncthreads();
+  uint32_t eq_base = 0, sel_base = 0, eb = 0;
+#pragma unroll
+  for (int j = 0; j < kSelWaves; ++j) {
+    const uint32_t gj = wq[j], ej = wq[kSelWaves + j];
+    const uint32_t rem = take_eq > eb ? take_eq - eb : 0u;
+    const uint32_t sj = gj + (ej < rem ? ej : rem);
+    if (j < wave) { eq_base += ej; sel_base += sj; }
+    eb += ej;
+  }
+  int32_t* out = p.idx + (size_t)t * p.k;
+  const uint64_t lt = (1ull << lane) - 1ull;
+  uint32_t er = eq_base, o = sel_base;
+#pragma unroll
+  for (int i = 0; i < kRegPer; ++i) {
+    const uint32_t key = (uint32_t)e[i];
+    const bool v = (uint32_t)i < nmine;
+    const bool eq = v & (key == kstar);
+    const uint64_t me = __ballot(eq);
+    const bool sel = v & ((key > kstar) | (eq & (er + (uint32_t)__builtin_popcountll(me & lt) < take_eq)));
+    const uint64_t ms = __ballot(sel);
+    const uint32_t oo = o + (uint32_t)__builtin_popcountll(ms & lt);
+    if (sel & (oo < kk)) out[oo] = (int32_t)(e[i] >> 32);
+    er += (uint32_t)__builtin_popcountll(me);
+    o += (uint32_t)__builtin_popcountll(ms);
+  }
+  DSA_MARK(p.trace, 12);
+  for (int i = (int)kk + tid; i < p.k; i += kSelThreads) out[i] = -1;
+  if (tid == 0 && p.trace) p.trace[blockIdx.x * 16 + 13] = nc;
+  if (tid == 0 && p.count) p.count[t] = (int32_t)kk;
+  __syncthreads();
+}
+
+// Exact selection of the kk best candidates of token t.  Runs in one workgroup after
+// every workgroup has published its candidates (after the second grid barrier).
+// Candidates arrive in position order; the selection is: every key above the cut key
+// K*, then the first `take_eq` (in position order) of the keys equal to K*.
+DSA_DEV void resolve_token(const SelParams& p, int t, SelShared& sh) {
+  uint32_t* pre = reinterpret_cast<uint32_t*>(&sh.sc[0][0]);         // [nwg + 1]
+  uint32_t* hist = pre + 1040;                                        // [2048]
+  uint32_t* misc = hist + 2048;                                       // small
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int nwg = p.nwg;
+  const uint32_t* cnt_t = p.cnt + (size_t)t * nwg;
+  // prefix over workgroup counts
+  uint32_t carry = 0;
+  for (int base = 0; base < nwg; base += kSelThreads) {
+    const int w = base + tid;
+    const uint32_t cv = ald(cnt_t + (w < nwg ? w : nwg - 1));
+    const uint32_t c = (w < nwg) ? cv : 0u;
+    uint32_t tot;
+    const uint32_t ex = block_excl_scan<kSelThreads>(c, sh.scan, &tot);
+    if (w < nwg) pre[w] = carry + ex;
+    carry += tot;
+  }
+  if (tid == 0) pre[nwg] = carry;
+  __syncthreads();
+  const uint32_t nc = carry;
+  const int64_t vis = p.pos0 + t + 1;
+  uint32_t kk = (uint32_t)((int64_t)p.k < vis ? p.k : vis);
+  if (kk > nc) kk = nc;   // cannot happen when the bound holds; keeps reads in range
+  const uint64_t* base = p.cand + (size_t)t * nwg * p.chunk;
+  // Bring the candidates on chip when they fit: wave w copies source segments w, w+8,
+  // ..., lane = element, so each load instruction reads one contiguous run; 16 segments
+  // are in flight per wave.
+  uint64_t* lc = reinterpret_cast<uint64_t*>(misc + 16);              // 8-byte aligned
+  const uint32_t lds_cap = (uint32_t)((sizeof(sh.sc) - (1040 + 2048 + 16) * 4) / 8);
+  const bool in_lds = nc > 0 && nc <= lds_cap;
+  uint32_t kmin = 0xffffffffu, kmax = 0u;
+  if (in_lds) {
+    constexpr int U = 16;
+    for (int s0 = wave; s0 < nwg; s0 += kSelWaves * U) {
+      uint64_t v[U];
+      uint32_t b0[U], n[U];
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int sgi = s0 + kSelWaves * u;
+        const int sc = sgi < nwg ? sgi : nwg - 1;
+        b0[u] = pre[sc];
+        n[u] = sgi < nwg ? pre[sc + 1] - b0[u] : 0u;
+        // slot 0 of every segment exists, so the clamped read stays in the workspace
+        v[u] = ald64(base + (size_t)sc * p.chunk + ((uint32_t)lane < n[u] ? (uint32_t)lane : 0u));
+      }
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        if ((uint32_t)lane < n[u]) {
+          lc[b0[u] + lane] = v[u];
+          kmin = min(kmin, (uint32_t)v[u]);
+          kmax = max(kmax, (uint32_t)v[u]);
+        }
+      }
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        if (n[u] > 64u) {                // long segments (few): the rest, 64 at a time
+          const uint64_t* src = base + (size_t)(s0 + kSelWaves * u) * p.chunk;
+          for (uint32_t j = 64u + lane; j < n[u]; j += 64u) {
+            const uint64_t x = ald64(src + j);
+            lc[b0[u] + j] = x;
+            kmin = min(kmin, (uint32_t)x);
+            kmax = max(kmax, (uint32_t)x);
+          }
+        }
+      }
+    }
+    __syncthreads();
+    DSA_MARK(p.trace, 9);
+    if (nc <= kRegCands) {
+      resolve_regs(p, t, sh, lc, nc, kk, kmin, kmax, hist, misc);
+      return;
+    }
+  }
+  // element g of the position-ordered candidate list (LDS, or the workspace slots)
+  auto elem = [&](uint32_t g) -> uint64_t {
+    if (in_lds) return lc[g];
+    int lo = 0, hi = nwg - 1;
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (pre[mid] <= g) lo = mid; else hi = mid - 1;
+    }
+    return ald64(base + (size_t)lo * p.chunk + (g - pre[lo]));
+  };
+  // order-free passes read element g = tid, tid + 512, ... (conflict-free in LDS)
+  if (!in_lds) {
+    for (uint32_t g = tid; g < nc; g += kSelThreads) {
+      const uint32_t key = (uint32_t)elem(g);
+      kmin = min(kmin, key);
+      kmax = max(kmax, key);
+    }
+  }
+  kmin = block_min_u32<kSelThreads>(kmin, sh.scan);
+  kmax = block_max_u32<kSelThreads>(kmax, sh.scan);
+  DSA_MARK(p.trace, 10);
+  uint32_t kstar;
+  uint32_t take_eq;
+  if (kk == nc) {
+    kstar = kmin;
+    take_eq = 0xffffffffu;
+  } else {
+    // MSB-first radix select on the bits where candidate keys differ
+    const uint32_t diff = kmin ^ kmax;
+    int hi = diff ? 32 - __builtin_clz(diff) : 0;
+    uint32_t known = hi >= 32 ? 0u : (kmax & ~((1u << hi) - 1u));
+    uint32_t need = kk;
+    while (hi > 0) {
+      const int dbits = hi < 11 ? hi : 11;
+      const int lo = hi - dbits;
+      const uint32_t nb = 1u << dbits;
+      for (int b2 = tid; b2 < 2048; b2 += kSelThreads) hist[b2] = 0u;
+      __syncthreads();
+      const uint32_t pmask = hi >= 32 ? 0u : ~((1u << hi) - 1u);
+      for (uint32_t g0 = tid; g0 < nc; g0 += 4 * kSelThreads) {
+        uint32_t key[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          const uint32_t g = g0 + u * kSelThreads;
+          key[u] = (uint32_t)elem(g < nc ? g : nc - 1);
+        }
+#pragma unroll
+        for (int u = 0; u < 4; ++u)
+          if ((g0 + u * kSelThreads < nc) & ((key[u] & pmask) == known))
+            atomicAdd(&hist[(key[u] >> lo) & (nb - 1u)], 1u);
+      }
+      __syncthreads();
+      // largest digit d with count(digit >= d) >= need
+      constexpr int PER = 2048 / kSelThreads;
+      const int rb = kSelThreads - 1 - tid;           // reversed thread order
+      uint32_t loc = 0;
+#pragma unroll
+      for (int i = 0; i < PER; ++i) loc += hist[rb * PER + i];
+      uint32_t tot;
+      const uint32_t above = block_excl_scan<kSelThreads>(loc, sh.scan, &tot);
+      uint32_t run_c = above;
+#pragma unroll
+      for (int i = PER - 1; i >= 0; --i) {
+        const uint32_t h = hist[rb * PER + i];
+        if (run_c < need && run_c + h >= need) {
+          misc[0] = (uint32_t)(rb * PER + i);
+          misc[1] = run_c;
+        }
+        run_c += h;
+      }
+      __syncthreads();
+      const uint32_t d = misc[0];
+      need -= misc[1];
+      known |= d << lo;
+      hi = lo;
+      const uint32_t in_bin = hist[d];
+      __syncthreads();
+      if (need == in_bin && hi > 0) {
+        // the whole boundary bin is taken: the cut is its smallest key
+        const uint32_t pm = ~((1u << hi) - 1u);
+        uint32_t bmin = 0xffffffffu;
+        for (uint32_t g = tid; g < nc; g += kSelThreads) {
+          const uint32_t key = (uint32_t)elem(g);
+          if ((key & pm) == known) bmin = min(bmin, key);
+        }
+        known = block_min_u32<kSelThreads>(bmin, sh.scan);
+        need = 0xffffffffu;      // every key equal to the cut is taken
+        hi = 0;
+      }
+    }
+    kstar = known;
+    take_eq = need;
+  }
+  DSA_MARK(p.trace, 11);
+  // Position-ordered compaction: wave w owns elements [w*R, (w+1)*R) in 64-element
+  // segments (lane = element), so ballots give in-order ranks.  Pass 1 counts keys equal
+  // to K* per wave; pass 2 (knowing each wave's first equal-key rank) counts selected
+  // elements; pass 3 writes.
+  const uint32_t R = ((nc + kSelWaves - 1) / kSelWaves + 63) & ~63u;
+  const uint32_t w0 = min(nc, wave * R), w1 = min(nc, w0 + R);
+  const uint64_t lt = (1ull << lane) - 1ull;
+  uint32_t* wq = sh.wcnt;           // [8] equal counts, then [8] selected counts
+  uint32_t cnt_eq = 0;
+  for (uint32_t g0 = w0; g0 < w1; g0 += 64) {
+    const uint32_t g = g0 + lane;
+    const uint32_t key = (uint32_t)elem(g < w1 ? g : w1 - 1);
+    const bool e = (g < w1) & (key == kstar);
+    cnt_eq += (uint32_t)__builtin_popcountll(__ballot(e));
+  }
+  if (lane == 0) wq[wave] = cnt_eq;
+  __syncthreads();
+  uint32_t eq_base = 0;
+  for (int j = 0; j < wave; ++j) eq_base += wq[j];
+  uint32_t cnt_sel = 0;
   {
     uint32_t er = eq_base;
-    visit([&](uint32_t key, uint32_t) {
-      if (key > kstar) ++my_sel;
-      else if (key == kstar) { if (er < take_eq) ++my_sel; ++er; }
-    });
+    for (uint32_t g0 = w0; g0 < w1; g0 += 64) {
+      const uint32_t g = g0 + lane;
+      const uint32_t key = (uint32_t)elem(g < w1 ? g : w1 - 1);
+      const bool in = g < w1;
+      const bool e = in & (key == kstar);
+      const uint64_t me = __ballot(e);
+      const bool sel = in & ((key > kstar) | (e & (er + (uint32_t)__builtin_popcountll(me & lt) < take_eq)));
+      cnt_sel += (uint32_t)__builtin_popcountll(__ballot(sel));
+      er += (uint32_t)__builtin_popcountll(me);
+    }
   }
-  const uint32_t sel_base = block_excl_scan<kSelThreads>(my_sel, sh.scan, &tot);
+  __syncthreads();
+  if (lane == 0) wq[8 + wave] = cnt_sel;
+  __syncthreads();
+  uint32_t sel_base = 0;
+  for (int j = 0; j < wave; ++j) sel_base += wq[8 + j];
   int32_t* out = p.idx + (size_t)t * p.k;
   {
     uint32_t er = eq_base, o = sel_base;
-    visit([&](uint32_t key, uint32_t pos) {
-      bool s = false;
-      if (key > kstar) s = true;
-      else if (key == kstar) { s = er < take_eq; ++er; }
-      if (s) {
-        if (o < kk) out[o] = (int32_t)pos;
-        ++o;
-      }
-    });
+    for (uint32_t g0 = w0; g0 < w1; g0 += 64) {
+      const uint32_t g = g0 + lane;
+      const uint64_t ev = elem(g < w1 ? g : w1 - 1);
+      const uint32_t key = (uint32_t)ev;
+      const bool in = g < w1;
+      const bool e = in & (key == kstar);
+      const uint64_t me = __ballot(e);
+      const bool sel = in & ((key > kstar) | (e & (er + (uint32_t)__builtin_popcountll(me & lt) < take_eq)));
+      const uint64_t ms = __ballot(sel);
+      const uint32_t oo = o + (uint32_t)__builtin_popcountll(ms & lt);
+      if (sel && oo < kk) out[oo] = (int32_t)(ev >> 32);
+      er += (uint32_t)__builtin_popcountll(me);
+      o += (uint32_t)__builtin_popcountll(ms);
+    }
   }
   DSA_MARK(p.trace, 12);
   for (int i = (int)kk + tid; i < p.k; i += kSelThreads) out[i] = -1;
@@ -476,6 +716,10 @@ __global__ void __launch_bounds__(kSelThreads, 1) select_kernel(SelParams p) {
   int64_t nk64 = p.L - c0;
   nk64 = nk64 < 0 ? 0 : (nk64 > p.chunk ? p.chunk : nk64);
   const int nkeys = (int)nk64;
+  // running maximum of this lane's scores per row tile (the tau bound's group maxima)
+  float gmax[RTW];
+#pragma unroll
+  for (int r = 0; r < RTW; ++r) gmax[r] = -__builtin_inff();
   if constexpr (SRC == 0) {
     // waves w and w+4 take the same key tiles and different row tiles
     const int pair = wave & (kPairs - 1);
@@ -484,6 +728,7 @@ __global__ void __launch_bounds__(kSelThreads, 1) select_kernel(SelParams p) {
     float wv[RTW][16];
     load_q_frags<RTW>(p.q_idx, T, rt0, qa);
     load_w<RTW>(p.w_idx, T, rt0, wv);
+    build_qlin<kSelThreads>(p.q_idx, p.w_idx, T, sh.ql);
     const bool active = 2 * rt0 < T;
     const int ntiles = (nkeys + kTile - 1) / kTile;
     const int nmine = ntiles > pair ? (ntiles - pair + kPairs - 1) / kPairs : 0;   // tiles pair, pair+kPairs, ...
@@ -498,8 +743,10 @@ __global__ void __launch_bounds__(kSelThreads, 1) select_kernel(SelParams p) {
       }
 #pragma unroll
       for (int q = 0; q < PERS; ++q) sh.kscale[tid + q * kSelThreads] = sv[q];
-      __syncthreads();
     }
+    __syncthreads();
+    Frag8 qf[4];
+    load_qlin_frags<RTW>(sh.ql, rt0, qf);
     DSA_MARK(p.trace, 1);
     KeyTile<KDT> buf[kPrefetch];
     if (active && nmine > 0) {
@@ -513,10 +760,13 @@ __global__ void __launch_bounds__(kSelThreads, 1) select_kernel(SelParams p) {
 #pragma unroll
         for (int i = 0; i < kPrefetch; ++i) {
           const int j = base + i;
-          const int sl = (pair + j * kPairs) * kTile + (lane & 31);
+          const int jc = j < nmine ? j : nmine - 1;      // the tile actually loaded (clamped)
+          const int sl = (pair + jc * kPairs) * kTile + (lane & 31);
           if constexpr (KDT == 1) buf[i].scale = sh.kscale[sl & (kMaxChunk - 1)];
           float out[RTW];
-          score_tile<KDT, RTW>(buf[i], qa, wv, out);
+          score_tile<KDT, RTW>(buf[i], qa, qf, wv, out);
+#pragma unroll
+          for (int r = 0; r < RTW; ++r) gmax[r] = fmaxf(gmax[r], out[r]);   // clamped repeats are harmless
           load_key_tile<KDT, false>(p.k_idx, p.k_scale, p.L, tile_of(j + kPrefetch), buf[i]);
           if (j < nmine) {
 #pragma unroll
@@ -544,34 +794,55 @@ __global__ void __launch_bounds__(kSelThreads, 1) select_kernel(SelParams p) {
   }
   __syncthreads();
   DSA_MARK(p.trace, 2);
-  // ---------------- tau bound: wave t takes token t; lane g holds the maximum of the
-  // visible scores g, g+64, ...; the m-th largest of those 64 maxima is <= the m-th
-  // largest visible score of the chunk.
+  // ---------------- tau bound.  Any split of the chunk's (visible) scores into at least
+  // m non-empty groups gives one: the m-th largest group maximum is <= the m-th largest
+  // score.  Computed scores use 64 groups per token: the keys at one position mod 32
+  // whose tile index mod 4 is in {p, p+2} (p = 0, 1); loaded scores use 64 groups of
+  // stride 64.  Only workgroups whose chunk lies entirely before pos0 publish, so every
+  // score of the chunk is visible to every token.
   if (p.m > 0 && wg < p.n_part) {
-    for (int t = wave; t < T; t += kSelWaves) {
-      const int64_t lim = p.pos0 + t - c0;
-      uint32_t g = 0u;
-      for (int i0 = 0; i0 < nkeys; i0 += 512) {
-        float v[8];
+    if constexpr (SRC == 0) {
+      // group (token, pair, key lane) maxima -> LDS (the row-scale area is free now);
+      // wave t then merges pairs (2q, 2q+1) per lane: 64 groups of the token
+      float* gm = sh.kscale;                                        // [kMaxT][128]
+      const int pair = wave & (kPairs - 1);
+      const int rt0 = (wave >= kPairs) ? RTW : 0;
 #pragma unroll
-        for (int u = 0; u < 8; ++u) v[u] = sh.sc[t][(i0 + u * 64 + lane) & (kMaxChunk - 1)];
-#pragma unroll
-        for (int u = 0; u < 8; ++u) {
-          const int i = i0 + u * 64 + lane;
-          if (i < nkeys && i <= lim) g = max(g, order_key(v[u]));
-        }
+      for (int r = 0; r < RTW; ++r) {
+        const int tt = 2 * (rt0 + r) + half;
+        if (tt < T) gm[tt * 128 + pair * 32 + (lane & 31)] = gmax[r];
       }
-      const uint32_t tw = mth_largest_lanes(g, p.m);
-      if (lane == 0) ast(p.tauv + (size_t)t * kMaxWG + wg, tw);
+      __syncthreads();
+      for (int t = wave; t < T; t += kSelWaves) {
+        const uint32_t g = max(order_key_fast(gm[t * 128 + lane]), order_key_fast(gm[t * 128 + 64 + lane]));
+        const uint32_t tw = mth_largest_lanes(g, p.m);
+        if (lane == 0) ast(p.tauv + (size_t)t * kMaxWG + wg, tw);
+      }
+    } else {
+      for (int t = wave; t < T; t += kSelWaves) {
+        uint32_t g = 0u;
+        for (int i0 = 0; i0 < nkeys; i0 += 512) {
+          float v[8];
+#pragma unroll
+          for (int u = 0; u < 8; ++u) v[u] = sh.sc[t][(i0 + u * 64 + lane) & (kMaxChunk - 1)];
+#pragma unroll
+          for (int u = 0; u < 8; ++u)
+            if (i0 + u * 64 + lane < nkeys) g = max(g, order_key_fast(v[u]));
+        }
+        const uint32_t tw = mth_largest_lanes(g, p.m);
+        if (lane == 0) ast(p.tauv + (size_t)t * kMaxWG + wg, tw);
+      }
     }
   }
   DSA_MARK(p.trace, 3);
   grid_barrier(p.ctl, p.nwg);
   DSA_MARK(p.trace, 4);
-  // ---------------- P2: tau = min of the published bounds; candidates >= tau in
-  // position order
-  for (int t = wave; t < T; t += kSelWaves) {
-    uint32_t tm = 0xffffffffu;
+  // ---------------- P2: wave t takes token t: tau = min of the published bounds, then
+  // the chunk's visible scores >= tau go out in position order (one ballot per 64
+  // positions, running offset) and the wave publishes their count.
+  if (wave < T) {
+    const int t = wave;
+    uint32_t tm = 0u;
     if (p.m > 0) {
       uint32_t v[kMaxWG / 64];
       const int nl = (p.n_part + 63) / 64;
@@ -581,63 +852,40 @@ __global__ void __launch_bounds__(kSelThreads, 1) select_kernel(SelParams p) {
         const int wc = w < p.n_part ? w : p.n_part - 1;
         v[i] = i < nl ? ald(p.tauv + (size_t)t * kMaxWG + wc) : 0xffffffffu;
       }
+      tm = 0xffffffffu;
 #pragma unroll
       for (int i = 0; i < kMaxWG / 64; ++i) tm = min(tm, (lane + 64 * i < p.n_part) ? v[i] : 0xffffffffu);
       tm = wave_min_u32(tm);
-    } else {
-      tm = 0u;
     }
-    if (lane == 0) sh.tau[t] = tm;
-  }
-  __syncthreads();
-  DSA_MARK(p.trace, 5);
-  {
-    constexpr int PER = kMaxChunk / kSelThreads;     // positions per thread (chunk <= 4096)
-    const int per = p.chunk / kSelThreads;
-    const int i0 = tid * per;
-    uint32_t cnt[kMaxT];
+    DSA_MARK(p.trace, 5);
+    // score >= tau as a float compare (equal keys <=> equal floats, -0 == +0)
+    const float tauf = tm ? key_to_float(tm) : -__builtin_inff();
+    const int64_t lim64 = p.pos0 + t - c0;
+    const int lim = (int)(lim64 < nkeys - 1 ? lim64 : nkeys - 1);      // last visible local index
+    const int nseg = p.chunk / 64;                                        // a multiple of 8
+    const int seg_vis = lim >= 0 ? ((lim >> 6) + 8) & ~7 : 0;            // segments up to lim, rounded to 8
+    const int nloop = seg_vis < nseg ? seg_vis : nseg;
+    uint64_t* dst = p.cand + ((size_t)t * p.nwg + wg) * p.chunk;
+    const float* row = sh.sc[t];
+    const uint64_t lt = (1ull << lane) - 1ull;
+    uint32_t off = 0;
+    for (int s0 = 0; s0 < nloop; s0 += 8) {
+      float v[8];
 #pragma unroll
-    for (int t = 0; t < kMaxT; ++t) {
-      cnt[t] = 0;
-      if (t < T) {
-        const uint32_t tau = sh.tau[t];
-        const int64_t lim = p.pos0 + t - c0;
+      for (int u = 0; u < 8; ++u) v[u] = row[(s0 + u) * 64 + lane];
 #pragma unroll
-        for (int q = 0; q < PER; ++q) {
-          const int i = i0 + q;
-          if (q < per && i < nkeys && i <= lim && order_key(sh.sc[t][i]) >= tau) ++cnt[t];
-        }
+      for (int u = 0; u < 8; ++u) {
+        const int i = (s0 + u) * 64 + lane;
+        const bool q = (i <= lim) & (v[u] >= tauf);
+        const uint64_t m = __ballot(q);
+        if (q)
+          ast64(dst + off + (uint32_t)__builtin_popcountll(m & lt),
+                ((uint64_t)(uint32_t)(c0 + i) << 32) | order_key(v[u]));
+        off += (uint32_t)__builtin_popcountll(m);
       }
     }
-    uint64_t tot_lo, tot_hi;
-    const uint64_t ex_lo = block_excl_scan64<kSelThreads>(
-        (uint64_t)cnt[0] | ((uint64_t)cnt[1] << 16) | ((uint64_t)cnt[2] << 32) | ((uint64_t)cnt[3] << 48),
-        sh.scan64, &tot_lo);
-    const uint64_t ex_hi = block_excl_scan64<kSelThreads>(
-        (uint64_t)cnt[4] | ((uint64_t)cnt[5] << 16) | ((uint64_t)cnt[6] << 32) | ((uint64_t)cnt[7] << 48),
-        sh.scan64, &tot_hi);
+    if (lane == 0) ast(p.cnt + (size_t)t * p.nwg + wg, off);
     DSA_MARK(p.trace, 6);
-#pragma unroll
-    for (int t = 0; t < kMaxT; ++t) {
-      if (t < T && cnt[t]) {
-        uint32_t o = (uint32_t)(((t < 4 ? ex_lo : ex_hi) >> (16 * (t & 3))) & 0xffffu);
-        const uint32_t tau = sh.tau[t];
-        const int64_t lim = p.pos0 + t - c0;
-        uint64_t* dst = p.cand + ((size_t)t * p.nwg + wg) * p.chunk;
-#pragma unroll
-        for (int q = 0; q < PER; ++q) {
-          const int i = i0 + q;
-          if (q < per && i < nkeys && i <= lim) {
-            const uint32_t key = order_key(sh.sc[t][i]);
-            if (key >= tau) ast64(dst + o++, ((uint64_t)(uint32_t)(c0 + i) << 32) | key);
-          }
-        }
-      }
-    }
-    if (tid < T) {
-      const uint32_t tot = (uint32_t)(((tid < 4 ? tot_lo : tot_hi) >> (16 * (tid & 3))) & 0xffffu);
-      ast(p.cnt + (size_t)tid * p.nwg + wg, tot);
-    }
   }
   DSA_MARK(p.trace, 7);
   grid_barrier(p.ctl, p.nwg);

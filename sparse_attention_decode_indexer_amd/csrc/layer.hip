@@ -5,9 +5,11 @@
 //   §A DSA layer: from 29 kernels to one: input RMSNorm, Q/K/V projections, RoPE,
 //     KV-cache writes, ..., output projection.
 //   §Optimizing inside the kernel: projection weights do not depend on the normalised
-//     input, so every workgroup issues all of its weight loads first and computes the
-//     RMSNorm of the whole input locally while they are in flight (no global
-//     synchronisation between the norm and the projection).
+//     input.  On gfx950 a wave64 vector instruction holds its SIMD for four cycles, so
+//     having every projection workgroup recompute the RMSNorm of the whole block (as
+//     the pages' CTAs do) costs more than it saves; instead one small kernel normalises
+//     the block once and builds the rotary tables, and every projection workgroup
+//     issues its activation and weight loads at entry.
 //   §GPU Memory Optimization: positional-encoding precision at 1M context -- rotary
 //     angles are formed in fp64.
 //
@@ -15,8 +17,8 @@
 // of W (RPW = 4, 8 or 16, chosen so the launch covers the chip) over the full K; its
 // eight waves split K.  A v_mfma_f32_16x16x32_bf16 tile takes the rows on the M side
 // (rows >= RPW are zero) and the tokens on the N side (padded to 16).  Each lane streams
-// a contiguous k range of one weight row straight into registers; the normalised
-// activations sit in LDS.  The eight partial tiles are summed in wave order.
+// its k chunks of one weight row straight into registers; the normalised activations
+// sit in LDS.  The eight partial tiles are summed in wave order.
 #include "dsa_common.h"
 #include "dsa_kernels.h"
 
@@ -102,16 +104,20 @@ struct ProjParams {
   float* kidx_scale;
   uint32_t* kictr;          // counter of finished k_I blocks
   float* kistage;           // [T][64] rotated k_I values
+  const uint16_t* y;        // [T][4096] bf16 normalised input (from norm_rope_kernel)
+  const float2* rope128;    // [T][64] (cos, sin) for width-128 heads
+  const float2* rope64;     // [T][32] (cos, sin) for width-64 indexer heads
   // OUT
   const uint16_t* o;        // [T][1024] bf16 attention output
   uint16_t* xout;           // [T][4096]
 };
 
+constexpr int kXsStride = kHidden + 8;      // padded LDS row: rows fall in different banks
+
 struct ProjShared {
-  alignas(16) uint16_t xs[kMaxT][kHidden];   // activations (normalised in place for QKV)
+  alignas(16) uint16_t xs[kMaxT][kXsStride];  // normalised activations (QKV) or attention output (OUT)
   float red[kProjWaves][16][16];
   float tile[16][16];
-  float rsq[kMaxT];
   float rc[kMaxT][8];
   float rs[kMaxT][8];
   uint32_t last;
@@ -125,9 +131,8 @@ __global__ void __launch_bounds__(kProjThreads) proj_kernel(ProjParams p) {
   const int wave = tid >> 6;
   const int b = blockIdx.x;
   const int K = p.K;
-  const int Kw = K / kProjWaves;             // per wave
-  const int sub = Kw / 4;                    // per lane group (= NSTEP * 8)
-  const int kl = wave * Kw + (lane >> 4) * sub;
+  const int Kw = K / kProjWaves;             // per wave (= NSTEP * 32)
+  const int kw0 = wave * Kw;
   const int T = p.T;
   const int rpw = p.rpw;
   const int lrow = lane & 15;
@@ -140,31 +145,34 @@ __global__ void __launch_bounds__(kProjThreads) proj_kernel(ProjParams p) {
   } else {
     wrow = b * rpw + (lrow < rpw ? lrow : 0);
   }
-  // 1) weights first: they do not depend on the norm (rows >= rpw are zero)
+  // 1) activation loads first (needed first, and small), then all weight loads: the
+  //    weights do not depend on the norm and stream in while it is computed.  Lane group
+  //    g takes k chunk 4i+g of the wave's range at step i, so each load instruction reads
+  //    64 contiguous bytes of every row.
+  const uint16_t* src = MODE == 0 ? p.y : p.o;
+  constexpr int NCH = kMaxT * (MODE == 0 ? kHidden : kHq * kD) / 8 / kProjThreads;   // uint4 chunks per thread
+  const int chunks = kMaxT * K / 8;
+  uint4 v[NCH];
+#pragma unroll
+  for (int u = 0; u < NCH; ++u) {
+    const int c = tid + u * kProjThreads;
+    const int cc = c < chunks ? c : chunks - 1;
+    const int t = cc / (K / 8), kk = (cc % (K / 8)) * 8;
+    const int tc = t < T ? t : T - 1;
+    v[u] = *reinterpret_cast<const uint4*>(src + (size_t)tc * K + kk);
+  }
   Frag8 wf[NSTEP];
   {
-    const uint4* wp = reinterpret_cast<const uint4*>(p.w + (size_t)wrow * K + kl);
+    const uint4* wp = reinterpret_cast<const uint4*>(p.w + (size_t)wrow * K + kw0) + (lane >> 4);
 #pragma unroll
-    for (int i = 0; i < NSTEP; ++i) wf[i].u = wp[i];
+    for (int i = 0; i < NSTEP; ++i) wf[i].u = wp[4 * i];
     if (lrow >= rpw) {
 #pragma unroll
       for (int i = 0; i < NSTEP; ++i) wf[i].u = make_uint4(0u, 0u, 0u, 0u);
     }
   }
-  // 2) activations into LDS: every load issued before any is stored
-  const uint16_t* src = MODE == 0 ? p.x : p.o;
+  // 2) activations into LDS
   {
-    constexpr int NCH = kMaxT * (MODE == 0 ? kHidden : kHq * kD) / 8 / kProjThreads;   // uint4 chunks per thread
-    const int chunks = kMaxT * K / 8;
-    uint4 v[NCH];
-#pragma unroll
-    for (int u = 0; u < NCH; ++u) {
-      const int c = tid + u * kProjThreads;
-      const int cc = c < chunks ? c : chunks - 1;
-      const int t = cc / (K / 8), kk = (cc % (K / 8)) * 8;
-      const int tc = t < T ? t : T - 1;
-      v[u] = *reinterpret_cast<const uint4*>(src + (size_t)tc * K + kk);
-    }
 #pragma unroll
     for (int u = 0; u < NCH; ++u) {
       const int c = tid + u * kProjThreads;
@@ -174,62 +182,16 @@ __global__ void __launch_bounds__(kProjThreads) proj_kernel(ProjParams p) {
       }
     }
   }
-  // rotary cos/sin of this block's pairs at the block's positions (fp64 angles)
+  // rotary cos/sin of this block's pairs at the block's positions (table from norm_rope_kernel)
   if (MODE == 0 && bi.rot_d && tid < 8 * kMaxT) {
     const int t = tid >> 3, r = tid & 7;
     if (t < T && r < rpw / 2) {
-      const double inv = pow((double)p.theta, -2.0 * (double)(bi.i0 + r) / (double)bi.rot_d);
-      const double ang = (double)(p.pos0 + t) * inv;
-      sh.rc[t][r] = (float)cos(ang);
-      sh.rs[t][r] = (float)sin(ang);
+      const float2 cs = bi.rot_d == kD ? p.rope128[t * (kD / 2) + bi.i0 + r] : p.rope64[t * (kDI / 2) + bi.i0 + r];
+      sh.rc[t][r] = cs.x;
+      sh.rs[t][r] = cs.y;
     }
   }
   __syncthreads();
-  if (MODE == 0) {
-    // RMSNorm: wave t sums token t's squares (lane l: elements l*64 .. l*64+63 in order,
-    // then a fixed butterfly), then every thread normalises its 8 columns of each row
-    {
-      const int t = wave;
-      float ss = 0.0f;
-      if (t < T) {
-        const uint4* xr = reinterpret_cast<const uint4*>(&sh.xs[t][lane * 64]);
-#pragma unroll
-        for (int c = 0; c < 8; ++c) {
-          const uint4 v = xr[c];
-          const uint32_t w4[4] = {v.x, v.y, v.z, v.w};
-#pragma unroll
-          for (int q = 0; q < 4; ++q) {
-            const float a = __uint_as_float(w4[q] << 16), bb = __uint_as_float(w4[q] & 0xffff0000u);
-            ss = fmaf(a, a, ss);
-            ss = fmaf(bb, bb, ss);
-          }
-        }
-      }
-#pragma unroll
-      for (int d = 32; d >= 1; d >>= 1) ss += __shfl_xor(ss, d, 64);
-      if (lane == 0) sh.rsq[t] = (t < T) ? 1.0f / sqrtf(ss / (float)kHidden + p.eps) : 0.0f;
-    }
-    const uint4 gv = reinterpret_cast<const uint4*>(p.gamma)[tid];   // gamma[8*tid .. 8*tid+8)
-    __syncthreads();
-    {
-      const uint32_t g4[4] = {gv.x, gv.y, gv.z, gv.w};
-      for (int t = 0; t < T; ++t) {
-        uint4* xp = reinterpret_cast<uint4*>(&sh.xs[t][8 * tid]);
-        const uint4 v = *xp;
-        const uint32_t x4[4] = {v.x, v.y, v.z, v.w};
-        uint32_t o4[4];
-        const float r = sh.rsq[t];
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const float y0 = (__uint_as_float(x4[q] << 16) * r) * __uint_as_float(g4[q] << 16);
-          const float y1 = (__uint_as_float(x4[q] & 0xffff0000u) * r) * __uint_as_float(g4[q] & 0xffff0000u);
-          o4[q] = (uint32_t)f32_to_bf16(y0) | ((uint32_t)f32_to_bf16(y1) << 16);
-        }
-        *xp = make_uint4(o4[0], o4[1], o4[2], o4[3]);
-      }
-    }
-    __syncthreads();
-  }
   // 3) MFMA over this wave's k range
   f32x4_t acc = {};
   {
@@ -237,7 +199,7 @@ __global__ void __launch_bounds__(kProjThreads) proj_kernel(ProjParams p) {
 #pragma unroll
     for (int i = 0; i < NSTEP; ++i) {
       Frag8 bfr;
-      bfr.u = *reinterpret_cast<const uint4*>(&sh.xs[tok & 7][kl + i * 8]);
+      bfr.u = *reinterpret_cast<const uint4*>(&sh.xs[tok & 7][kw0 + (4 * i + (lane >> 4)) * 8]);
       if (tok >= kMaxT) bfr.u = make_uint4(0u, 0u, 0u, 0u);
       acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wf[i].v, bfr.v, acc, 0, 0, 0);
     }
@@ -335,6 +297,68 @@ __global__ void __launch_bounds__(kProjThreads) proj_kernel(ProjParams p) {
   if (tid == 0) ast(p.kictr, 0u);
 }
 
+// Input RMSNorm of the block (one workgroup per token) and the rotary tables (one more
+// workgroup): y[t] = bf16(x[t] * rsqrt(mean(x[t]^2) + eps) * gamma); cos/sin of
+// (pos0 + t) * theta^(-2i/d) with the angle formed in fp64.  Every projection workgroup
+// then reads y and the tables instead of recomputing them.
+__global__ void __launch_bounds__(kProjThreads) norm_rope_kernel(const uint16_t* __restrict__ x,
+                                                                 const uint16_t* __restrict__ gamma, int T,
+                                                                 float eps, float theta, int64_t pos0,
+                                                                 uint16_t* __restrict__ y, float2* rope128,
+                                                                 float2* rope64) {
+  __shared__ float part[kProjWaves];
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
+  const int t = blockIdx.x;
+  if (t < T) {
+    const uint4 xv = reinterpret_cast<const uint4*>(x + (size_t)t * kHidden)[tid];   // 8 elements
+    const uint4 gv = reinterpret_cast<const uint4*>(gamma)[tid];
+    const uint32_t x4[4] = {xv.x, xv.y, xv.z, xv.w};
+    const uint32_t g4[4] = {gv.x, gv.y, gv.z, gv.w};
+    float ss = 0.0f;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const float a = __uint_as_float(x4[q] << 16), b = __uint_as_float(x4[q] & 0xffff0000u);
+      ss = fmaf(a, a, ss);
+      ss = fmaf(b, b, ss);
+    }
+#pragma unroll
+    for (int d = 32; d >= 1; d >>= 1) ss += __shfl_xor(ss, d, 64);
+    if (lane == 0) part[wave] = ss;
+    __syncthreads();
+    float tot = part[0];
+#pragma unroll
+    for (int w = 1; w < kProjWaves; ++w) tot += part[w];
+    const float r = 1.0f / sqrtf(tot / (float)kHidden + eps);
+    uint32_t o4[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const float y0 = (__uint_as_float(x4[q] << 16) * r) * __uint_as_float(g4[q] << 16);
+      const float y1 = (__uint_as_float(x4[q] & 0xffff0000u) * r) * __uint_as_float(g4[q] & 0xffff0000u);
+      o4[q] = (uint32_t)f32_to_bf16(y0) | ((uint32_t)f32_to_bf16(y1) << 16);
+    }
+    reinterpret_cast<uint4*>(y + (size_t)t * kHidden)[tid] = make_uint4(o4[0], o4[1], o4[2], o4[3]);
+  } else {
+    for (int e = tid; e < T * (kD / 2 + kDI / 2); e += kProjThreads) {
+      const int tt = e / (kD / 2 + kDI / 2), j = e % (kD / 2 + kDI / 2);
+      const bool wide = j < kD / 2;
+      const int i = wide ? j : j - kD / 2;
+      const double inv = pow((double)theta, -2.0 * (double)i / (double)(wide ? kD : kDI));
+      const double ang = (double)(pos0 + tt) * inv;
+      const float2 cs = make_float2((float)cos(ang), (float)sin(ang));
+      if (wide) rope128[tt * (kD / 2) + i] = cs;
+      else rope64[tt * (kDI / 2) + i] = cs;
+    }
+  }
+}
+
+// workspace layout of the projection stage
+constexpr size_t kWsKiStage = ctl::kBytes;
+constexpr size_t kWsY = kWsKiStage + (size_t)kMaxT * kDI * sizeof(float);
+constexpr size_t kWsRope128 = kWsY + (size_t)kMaxT * kHidden * 2;
+constexpr size_t kWsRope64 = kWsRope128 + (size_t)kMaxT * (kD / 2) * sizeof(float2);
+constexpr size_t kWsProjEnd = kWsRope64 + (size_t)kMaxT * (kDI / 2) * sizeof(float2);
+
 hipError_t launch_proj_qkv(int kind, const void* x, const void* gamma, const void* w, int T,
                            float eps, float theta, int64_t pos0, void* qkv, void* q_att,
                            void* q_idx, float* w_idx, void* kcache, void* vcache,
@@ -348,7 +372,13 @@ hipError_t launch_proj_qkv(int kind, const void* x, const void* gamma, const voi
   p.rpw = kind == 0 ? 8 : 4;                 // DSA: 298 workgroups, SWA: 320
   uint8_t* w8 = static_cast<uint8_t*>(ws);
   p.kictr = reinterpret_cast<uint32_t*>(w8) + ctl::kDone;
-  p.kistage = reinterpret_cast<float*>(w8 + ctl::kBytes);
+  p.kistage = reinterpret_cast<float*>(w8 + kWsKiStage);
+  uint16_t* y = reinterpret_cast<uint16_t*>(w8 + kWsY);
+  float2* r128 = reinterpret_cast<float2*>(w8 + kWsRope128);
+  float2* r64 = reinterpret_cast<float2*>(w8 + kWsRope64);
+  p.y = y;
+  p.rope128 = r128;
+  p.rope64 = r64;
   p.gamma = static_cast<const uint16_t*>(gamma);
   p.eps = eps;
   p.theta = theta;
@@ -363,6 +393,10 @@ hipError_t launch_proj_qkv(int kind, const void* x, const void* gamma, const voi
   p.ring_cap = ring_cap;
   p.kidx = static_cast<uint8_t*>(kidx);
   p.kidx_scale = kidx_scale;
+  hipLaunchKernelGGL(norm_rope_kernel, dim3(T + 1), dim3(kProjThreads), 0, st, p.x, p.gamma, T, eps, theta,
+                     pos0, y, r128, r64);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
   const dim3 grid(proj_blocks(kind, p.rpw)), block(kProjThreads);
   // per-lane fragments: K / 8 waves / 4 lane groups / 8 = 16
   hipLaunchKernelGGL((proj_kernel<0, 16>), grid, block, 0, st, p);
@@ -386,6 +420,6 @@ hipError_t launch_proj_out(const void* o, const void* w_o, const void* x, void* 
   return hipGetLastError();
 }
 
-size_t proj_workspace_bytes() { return ctl::kBytes + (size_t)kMaxT * kDI * sizeof(float); }
+size_t proj_workspace_bytes() { return kWsProjEnd; }
 
 }  // namespace dsa

@@ -145,6 +145,9 @@ TOPK_CASES = [
     ("k1", 1, 130, 1, lambda g, T, L: g.integers(0, 3, (T, L)).astype(np.float32)),
     ("tiny-L", 8, 8, 4, lambda g, T, L: g.integers(0, 3, (T, L)).astype(np.float32)),
     ("negatives", 4, 20000, 512, lambda g, T, L: -np.abs(g.standard_normal((T, L))).astype(np.float32)),
+    # candidate counts around the register-resident limit of the selection tail (8192)
+    ("reg-edge", 3, 8194, 2048, lambda g, T, L: g.standard_normal((T, L)).astype(np.float32)),
+    ("mid-nc", 2, 12000, 2048, lambda g, T, L: g.standard_normal((T, L)).astype(np.float32)),
     ("sparse-big", 8, 262144, 2048,
      lambda g, T, L: np.where(g.random((T, L)) < 0.003, 100 + g.random((T, L)), g.random((T, L))).astype(np.float32)),
 ]

@@ -268,13 +268,49 @@ def main():
             "peak": HBM_PEAK_GBPS,
             "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBPS, 4),
-            "traffic": None,
+            "traffic": measured_traffic(L, T),
             "avg_us": round(sel_avg, 2),
             "algorithmic_bytes": int(sel_bytes),
         },
         "cpu_baseline": cpu,
     }
     print(json.dumps(out))
+
+
+KERNEL_SOURCES = ("sparse_attention_decode_indexer_amd/csrc/index_topk.hip",
+                  "sparse_attention_decode_indexer_amd/csrc/dsa_common.h")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "select_kernel_traffic_1m.txt")
+
+
+def kernel_source_sha():
+    """sha256 of the selection kernel's sources with // comments and blank lines removed."""
+    import hashlib
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, f), encoding="utf-8") as fh:
+            for line in fh:
+                code = line.split("//", 1)[0].strip()
+                if code:
+                    h.update(code.encode() + b"\n")
+    return h.hexdigest()
+
+
+def measured_traffic(L, T):
+    """HBM bytes per select_kernel launch from the committed FETCH_SIZE/WRITE_SIZE summary
+    (1M context, T = 8 only), or None when the kernel changed since the counters were taken."""
+    if L != (1 << 20) or T != 8 or not os.path.exists(TRAFFIC_FILE):
+        return None
+    vals = {}
+    with open(TRAFFIC_FILE, encoding="utf-8") as fh:
+        for line in fh:
+            key, _, val = line.partition(":")
+            vals[key.strip()] = val.strip()
+    if vals.get("source_sha256") != kernel_source_sha():
+        return None
+    try:
+        return int(vals["traffic_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
 
 
 def cpu_baseline(host_layers, x_host, L, T, bytes_step):

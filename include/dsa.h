@@ -2,8 +2,7 @@
  * dsa.h -- C ABI of a single-GPU decode/verify step of a DeepSeek-Sparse-Attention
  * (DSA) layer and its sliding-window (SWA) sibling, for AMD Instinct MI355X (gfx950).
  *
- * Source of the method: NaiveAI, "Naive-N0.5-Flash: Building Frontier AI with AI"
- * (naive.ai research page).
+ * Source of the method: NaiveAI research page on Naive-N0.5-Flash (naive.ai/en/research).
  *   - §Model Architecture: a lightweight indexer scores the full history while the
  *     backbone attends only a selected subset of positions; the full KV cache is kept.
  *   - §Hybrid SWA-DSA Architecture: DSA keeps the top 2,048 positions, SWA a 128-token

@@ -5,8 +5,7 @@ TEST INFRASTRUCTURE.  Only ``tests/``, ``__graft_entry__.smoke()`` and the
 library's product path never touches it, and it shares no code, table or
 helper with the HIP kernels.
 
-What it computes follows NaiveAI, "Naive-N0.5-Flash: Building Frontier AI with
-AI" (naive.ai research page):
+What it computes follows NaiveAI research page on Naive-N0.5-Flash (naive.ai/en/research):
 
 * §Model Architecture: a lightweight indexer scores the whole history; the
   backbone attends only a selected subset of positions.

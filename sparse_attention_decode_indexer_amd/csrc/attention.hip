@@ -1,6 +1,6 @@
 // Split-K GQA attention over a list of cache rows, for gfx950.
 //
-// Method: NaiveAI, "Naive-N0.5-Flash: Building Frontier AI with AI".
+// Method: NaiveAI research page on Naive-N0.5-Flash (naive.ai/en/research).
 //   §Model Architecture: attention runs only over the positions the indexer selected.
 //   §Hybrid SWA-DSA Architecture: GQA (eight query heads of this GPU share one KV head),
 //     a 128-token sliding window for SWA layers, a sink bias in both attention types.

@@ -1,6 +1,7 @@
 // Indexer scan and exact top-k selection for gfx950.
 //
-// Method: NaiveAI, "Naive-N0.5-Flash: Building Frontier AI with AI", §Model Architecture
+// Method: NaiveAI research page on Naive-N0.5-Flash (naive.ai/en/research),
+// §Model Architecture
 // (the indexer scores the full history, the backbone attends a selected subset) and
 // §Hybrid SWA-DSA Architecture (16 indexer heads, top 2,048 positions).
 //

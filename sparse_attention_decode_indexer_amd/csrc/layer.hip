@@ -1,7 +1,7 @@
 // Layer-step projections for gfx950: input RMSNorm + fused QKV/indexer projection with
 // RoPE and cache append, and the output projection with the residual add.
 //
-// Method: NaiveAI, "Naive-N0.5-Flash: Building Frontier AI with AI".
+// Method: NaiveAI research page on Naive-N0.5-Flash (naive.ai/en/research).
 //   §A DSA layer: from 29 kernels to one: input RMSNorm, Q/K/V projections, RoPE,
 //     KV-cache writes, ..., output projection.
 //   §Optimizing inside the kernel: projection weights do not depend on the normalised

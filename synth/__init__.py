@@ -14,8 +14,8 @@ lives here.
 
 Workloads (one GPU's share of a Naive-N0.5-Flash DSA layer: 8 query heads
 sharing one KV head of width 128, a 16-head indexer of width 64, top-2048;
-NaiveAI, "Naive-N0.5-Flash: Building Frontier AI with AI", §Hybrid SWA-DSA
-Architecture and §Optimizing inside the kernel):
+NaiveAI research page on Naive-N0.5-Flash (naive.ai/en/research),
+§Hybrid SWA-DSA Architecture and §Optimizing inside the kernel):
 
   tiny      L=4096,  T=1, indexer q/k integers in [-4,4], w on a 1/256 grid
   verify64k L=65536, T=8, indexer q/k ~N(0,1/64), bf16 everything

@@ -197,14 +197,11 @@ DSA_DEV void vm_wait_all() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
 // Control words of a workspace (uint32 index; every counter on its own 256-byte line).
 namespace ctl {
-constexpr int kGroup = 0;        // 8 arrival counters, stride 64
-constexpr int kTop = 512;        // group arrivals
-constexpr int kGen = 576;        // barrier generation
 constexpr int kError = 640;      // sticky error word (1 = a wait timed out)
-constexpr int kTau = 704;        // [8] ~tau per token
+constexpr int kEpoch = 768;      // launch counter (tags of the tagged slots)
 constexpr int kDone = 1024;      // [8] per-token completion counters, stride 64
-constexpr int kWords = 1536;
-constexpr size_t kBytes = 8192;
+constexpr int kWords = 3072;
+constexpr size_t kBytes = 16384;
 }  // namespace ctl
 
 // Phase timestamps (100 MHz real-time counter) for profiling builds only (-DDSA_TRACE):
@@ -218,43 +215,48 @@ constexpr size_t kBytes = 8192;
 
 constexpr uint64_t kSpinLimit = 20000000ull;   // 0.2 s of the 100 MHz real-time counter
 
-// Grid barrier for `nblocks` co-resident workgroups: two-level arrival (eight groups by
-// blockIdx % 8, i.e. by XCD, then one top counter), release by a generation word.
-// Counters return to zero at every release.  A wait longer than kSpinLimit sets the
-// sticky error word and gives up, so a launch whose workgroups are not all resident
-// ends instead of hanging.  Only data exchanged through the coherent accessors above
-// is guaranteed visible after the barrier.
-DSA_DEV void grid_barrier(uint32_t* c, uint32_t nblocks) {
-  vm_wait_all();
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    const uint32_t g0 = ald(c + ctl::kGen);
-    const uint32_t grp = blockIdx.x & 7u;
-    const uint32_t gsize = (nblocks >> 3) + (grp < (nblocks & 7u) ? 1u : 0u);
-    const uint32_t ngroups = nblocks < 8u ? nblocks : 8u;
-    bool last = false;
-    if (aadd(c + ctl::kGroup + 64 * grp, 1u) == gsize - 1u) {
-      ast(c + ctl::kGroup + 64 * grp, 0u);
-      if (aadd(c + ctl::kTop, 1u) == ngroups - 1u) {
-        ast(c + ctl::kTop, 0u);
-        last = true;
-      }
+// Cross-workgroup hand-offs inside one launch use tagged slots instead of barriers: a
+// producer writes (tag << 32 | value) into its own 64-bit slot after its data has landed,
+// and a consumer polls the slots it needs until all carry the launch's tag, receiving the
+// values with the same loads.  The tag is a launch counter + 1: the counter is read at
+// kernel start and advanced by one workgroup once every workgroup has published (so
+// every read of it has completed).  It runs through [0, 2^31) and wraps, so a tag is
+// never 0 (the value of a cleared workspace).
+DSA_DEV uint32_t next_epoch(uint32_t e) { return (e + 1u) & 0x7fffffffu; }
+
+// Wave-wide wait for slots[0 .. n) (n >= 1, n <= 64 * N) to carry `tag`; returns the
+// minimum of their values.  A wait longer than kSpinLimit sets the sticky error word and
+// gives up, so a launch whose workgroups are not all resident ends instead of hanging.
+template <int N>
+DSA_DEV uint32_t wait_tagged_min(const uint64_t* slots, int n, uint32_t tag, uint32_t* ctl_words) {
+  const int lane = threadIdx.x & 63;
+  uint64_t v[N];
+#pragma unroll
+  for (int i = 0; i < N; ++i) {
+    const int w = lane + 64 * i;
+    v[i] = ald64(slots + (w < n ? w : n - 1));
+  }
+  const uint64_t t0 = __builtin_amdgcn_s_memrealtime();
+  while (true) {
+    bool ok = true;
+#pragma unroll
+    for (int i = 0; i < N; ++i) ok = ok & ((uint32_t)(v[i] >> 32) == tag);
+    if (__ballot(!ok) == 0ull) break;
+    __builtin_amdgcn_s_sleep(1);
+    if (__builtin_amdgcn_s_memrealtime() - t0 > kSpinLimit) {
+      if (lane == 0) ast(ctl_words + ctl::kError, 1u);
+      break;
     }
-    if (last) {
-      vm_wait_all();
-      aadd(c + ctl::kGen, 1u);
-    } else {
-      const uint64_t t0 = __builtin_amdgcn_s_memrealtime();
-      while (ald(c + ctl::kGen) == g0) {
-        __builtin_amdgcn_s_sleep(1);
-        if (__builtin_amdgcn_s_memrealtime() - t0 > kSpinLimit) {
-          ast(c + ctl::kError, 1u);
-          break;
-        }
-      }
+#pragma unroll
+    for (int i = 0; i < N; ++i) {
+      const int w = lane + 64 * i;
+      v[i] = ald64(slots + (w < n ? w : n - 1));
     }
   }
-  __syncthreads();
+  uint32_t m = 0xffffffffu;
+#pragma unroll
+  for (int i = 0; i < N; ++i) m = min(m, (lane + 64 * i < n) ? (uint32_t)v[i] : 0xffffffffu);
+  return wave_min_u32(m);
 }
 
 }  // namespace dsa

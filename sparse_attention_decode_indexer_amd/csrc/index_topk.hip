@@ -17,14 +17,14 @@
 //   P1  scores of the chunk (computed, or read from memory) stay in LDS; each
 //       workgroup derives a lower bound tau_wg of its m-th largest visible score from
 //       per-group maxima and publishes it in its own slot;
-//   --  grid barrier; tau = min over the slots;
+//   --  tau = min over the slots (waiting until each carries this launch's tag);
 //   P2  every workgroup writes its visible scores >= tau, in position order, as
-//       (order key, position) candidates;
-//   --  grid barrier;
-//   P3  workgroup t runs an exact radix select over token t's candidates and writes
-//       the selected positions in ascending order.
-// Inter-workgroup data moves only through agent-scope atomic loads/stores, so no cache
-// writeback or invalidation is needed at the barriers.
+//       (order key, position) candidates, then its count tagged with the launch;
+//   P3  workgroup t waits until every count of token t carries this launch's tag,
+//       runs an exact radix select over token t's candidates and writes the selected
+//       positions in ascending order.
+// There is no grid barrier: inter-workgroup data moves only through agent-scope atomic
+// loads/stores of tagged slots, so no cache writeback or invalidation is needed.
 // Because at least m scores of each of n_part workgroups are >= tau and
 // m * n_part >= k, the candidates always contain the k best; the result is exact and
 // independent of tau.  All cross-workgroup arithmetic is integer, so the result is
@@ -300,8 +300,8 @@ struct SelParams {
   int32_t* count;
   // workspace
   uint32_t* ctl;         // control words (see namespace ctl)
-  uint32_t* cnt;         // [T][nwg] candidate counts
-  uint32_t* tauv;        // [T][kMaxWG] per-workgroup tau bounds
+  uint64_t* cnt;         // [T][nwg] (launch tag << 32 | candidate count)
+  uint64_t* tauv;        // [T][kMaxWG] (launch tag << 32 | tau bound) per workgroup
   uint64_t* cand;        // [T][nwg][chunk] (position << 32 | order key)
   uint64_t* trace;       // profiling builds: [nwg][16] phase timestamps
 };
@@ -469,7 +469,7 @@ DSA_DEV void resolve_regs(const SelParams& p, int t, SelShared& sh, const uint64
 // every workgroup has published its candidates (after the second grid barrier).
 // Candidates arrive in position order; the selection is: every key above the cut key
 // K*, then the first `take_eq` (in position order) of the keys equal to K*.
-DSA_DEV void resolve_token(const SelParams& p, int t, SelShared& sh) {
+DSA_DEV void resolve_token(const SelParams& p, int t, SelShared& sh, uint32_t epoch) {
   uint32_t* pre = reinterpret_cast<uint32_t*>(&sh.sc[0][0]);         // [nwg + 1]
   uint32_t* hist = pre + 1040;                                        // [2048]
   uint32_t* misc = hist + 2048;                                       // small
@@ -477,13 +477,47 @@ DSA_DEV void resolve_token(const SelParams& p, int t, SelShared& sh) {
   const int lane = tid & 63;
   const int wave = tid >> 6;
   const int nwg = p.nwg;
-  const uint32_t* cnt_t = p.cnt + (size_t)t * nwg;
+  const uint64_t* cnt_t = p.cnt + (size_t)t * nwg;
+  // Each workgroup publishes its count, tagged with this launch, after its candidates;
+  // waiting for all tags replaces a grid barrier and delivers the counts at once.
+  constexpr int kCntPer = kMaxWG / kSelThreads;
+  const uint32_t tag = epoch + 1u;
+  uint32_t cw[kCntPer];
+  {
+    uint64_t v[kCntPer];
+#pragma unroll
+    for (int j = 0; j < kCntPer; ++j) {
+      const int w = tid + j * kSelThreads;
+      v[j] = ald64(cnt_t + (w < nwg ? w : nwg - 1));
+    }
+    const uint64_t t0 = __builtin_amdgcn_s_memrealtime();
+#pragma unroll
+    for (int j = 0; j < kCntPer; ++j) {
+      const int w = tid + j * kSelThreads;
+      while ((uint32_t)(v[j] >> 32) != tag) {
+        __builtin_amdgcn_s_sleep(1);
+        if (__builtin_amdgcn_s_memrealtime() - t0 > kSpinLimit) {
+          ast(p.ctl + ctl::kError, 1u);
+          v[j] = 0;
+          break;
+        }
+        v[j] = ald64(cnt_t + (w < nwg ? w : nwg - 1));
+      }
+      cw[j] = (w < nwg) ? (uint32_t)v[j] : 0u;
+    }
+  }
+  __syncthreads();
+  DSA_MARK(p.trace, 8);
+  // every workgroup has published, so every workgroup has read the launch counter
+  if (t == 0 && tid == 0) ast(p.ctl + ctl::kEpoch, next_epoch(epoch));
   // prefix over workgroup counts
   uint32_t carry = 0;
-  for (int base = 0; base < nwg; base += kSelThreads) {
+#pragma unroll
+  for (int j = 0; j < kCntPer; ++j) {
+    const int base = j * kSelThreads;
+    if (base >= nwg) break;
     const int w = base + tid;
-    const uint32_t cv = ald(cnt_t + (w < nwg ? w : nwg - 1));
-    const uint32_t c = (w < nwg) ? cv : 0u;
+    const uint32_t c = cw[j];
     uint32_t tot;
     const uint32_t ex = block_excl_scan<kSelThreads>(c, sh.scan, &tot);
     if (w < nwg) pre[w] = carry + ex;
@@ -713,6 +747,8 @@ __global__ void __launch_bounds__(kSelThreads, 1) select_kernel(SelParams p) {
   const int64_t c0 = (int64_t)wg * p.chunk;
   const int T = p.T;
   DSA_MARK(p.trace, 0);
+  const uint32_t epoch = ald(p.ctl + ctl::kEpoch);
+  const uint32_t tag = epoch + 1u;                       // this launch's slot tag
   // ---------------- P1: scores of this chunk into LDS
   int64_t nk64 = p.L - c0;
   nk64 = nk64 < 0 ? 0 : (nk64 > p.chunk ? p.chunk : nk64);
@@ -725,23 +761,34 @@ __global__ void __launch_bounds__(kSelThreads, 1) select_kernel(SelParams p) {
     // waves w and w+4 take the same key tiles and different row tiles
     const int pair = wave & (kPairs - 1);
     const int rt0 = (wave >= kPairs) ? RTW : 0;
-    Frag8 qa[RTW][4];
-    float wv[RTW][16];
-    load_q_frags<RTW>(p.q_idx, T, rt0, qa);
-    load_w<RTW>(p.w_idx, T, rt0, wv);
-    build_qlin<kSelThreads>(p.q_idx, p.w_idx, T, sh.ql);
     const bool active = 2 * rt0 < T;
     const int ntiles = (nkeys + kTile - 1) / kTile;
     const int nmine = ntiles > pair ? (ntiles - pair + kPairs - 1) / kPairs : 0;   // tiles pair, pair+kPairs, ...
+    const int jlast = nmine > 0 ? nmine - 1 : 0;
+    // Loads are unconditional (tile index clamped to the wave's last tile, which is then
+    // already cached; rows past L are clamped inside) so the compiler keeps kPrefetch
+    // tiles in flight without draining the memory counter at branch merges.
+    auto tile_of = [&](int j) { return c0 + (int64_t)(pair + (j < jlast ? j : jlast) * kPairs) * kTile; };
+    // the first key tiles and the chunk's row scales go out before anything else, so
+    // their latency overlaps the query set-up below
+    KeyTile<KDT> buf[kPrefetch];
+#pragma unroll
+    for (int i = 0; i < kPrefetch; ++i) load_key_tile<KDT, false>(p.k_idx, p.k_scale, p.L, tile_of(i), buf[i]);
+    constexpr int PERS = kMaxChunk / kSelThreads;
+    float sv[PERS];
     if constexpr (KDT == 1) {
-      // the chunk's row scales, one bulk load into LDS
-      constexpr int PERS = kMaxChunk / kSelThreads;
-      float sv[PERS];
 #pragma unroll
       for (int q = 0; q < PERS; ++q) {
         const int i = tid + q * kSelThreads;
         sv[q] = p.k_scale[c0 + (i < nkeys ? i : (nkeys > 0 ? nkeys - 1 : 0))];
       }
+    }
+    Frag8 qa[RTW][4];
+    float wv[RTW][16];
+    load_q_frags<RTW>(p.q_idx, T, rt0, qa);
+    load_w<RTW>(p.w_idx, T, rt0, wv);
+    build_qlin<kSelThreads>(p.q_idx, p.w_idx, T, sh.ql);
+    if constexpr (KDT == 1) {
 #pragma unroll
       for (int q = 0; q < PERS; ++q) sh.kscale[tid + q * kSelThreads] = sv[q];
     }
@@ -749,14 +796,7 @@ __global__ void __launch_bounds__(kSelThreads, 1) select_kernel(SelParams p) {
     Frag8 qf[4];
     load_qlin_frags<RTW>(sh.ql, rt0, qf);
     DSA_MARK(p.trace, 1);
-    KeyTile<KDT> buf[kPrefetch];
     if (active && nmine > 0) {
-      // Loads are unconditional (tile index clamped to the last tile, which is then
-      // already cached) so the compiler keeps kPrefetch tiles in flight without
-      // draining the memory counter at branch merges.
-      auto tile_of = [&](int j) { return c0 + (int64_t)(pair + (j < nmine ? j : nmine - 1) * kPairs) * kTile; };
-#pragma unroll
-      for (int i = 0; i < kPrefetch; ++i) load_key_tile<KDT, false>(p.k_idx, p.k_scale, p.L, tile_of(i), buf[i]);
       for (int base = 0; base < nmine; base += kPrefetch) {
 #pragma unroll
         for (int i = 0; i < kPrefetch; ++i) {
@@ -817,7 +857,7 @@ __global__ void __launch_bounds__(kSelThreads, 1) select_kernel(SelParams p) {
       for (int t = wave; t < T; t += kSelWaves) {
         const uint32_t g = max(order_key_fast(gm[t * 128 + lane]), order_key_fast(gm[t * 128 + 64 + lane]));
         const uint32_t tw = mth_largest_lanes(g, p.m);
-        if (lane == 0) ast(p.tauv + (size_t)t * kMaxWG + wg, tw);
+        if (lane == 0) ast64(p.tauv + (size_t)t * kMaxWG + wg, ((uint64_t)tag << 32) | tw);
       }
     } else {
       for (int t = wave; t < T; t += kSelWaves) {
@@ -831,32 +871,21 @@ __global__ void __launch_bounds__(kSelThreads, 1) select_kernel(SelParams p) {
             if (i0 + u * 64 + lane < nkeys) g = max(g, order_key_fast(v[u]));
         }
         const uint32_t tw = mth_largest_lanes(g, p.m);
-        if (lane == 0) ast(p.tauv + (size_t)t * kMaxWG + wg, tw);
+        if (lane == 0) ast64(p.tauv + (size_t)t * kMaxWG + wg, ((uint64_t)tag << 32) | tw);
       }
     }
   }
   DSA_MARK(p.trace, 3);
-  grid_barrier(p.ctl, p.nwg);
-  DSA_MARK(p.trace, 4);
   // ---------------- P2: wave t takes token t: tau = min of the published bounds, then
   // the chunk's visible scores >= tau go out in position order (one ballot per 64
   // positions, running offset) and the wave publishes their count.
   if (wave < T) {
     const int t = wave;
     uint32_t tm = 0u;
-    if (p.m > 0) {
-      uint32_t v[kMaxWG / 64];
-      const int nl = (p.n_part + 63) / 64;
-#pragma unroll
-      for (int i = 0; i < kMaxWG / 64; ++i) {
-        const int w = lane + 64 * i;
-        const int wc = w < p.n_part ? w : p.n_part - 1;
-        v[i] = i < nl ? ald(p.tauv + (size_t)t * kMaxWG + wc) : 0xffffffffu;
-      }
-      tm = 0xffffffffu;
-#pragma unroll
-      for (int i = 0; i < kMaxWG / 64; ++i) tm = min(tm, (lane + 64 * i < p.n_part) ? v[i] : 0xffffffffu);
-      tm = wave_min_u32(tm);
+    if (p.m > 0) {                       // wait for every participating bound of token t
+      const uint64_t* slots = p.tauv + (size_t)t * kMaxWG;
+      tm = p.n_part <= 256 ? wait_tagged_min<4>(slots, p.n_part, tag, p.ctl)
+                           : wait_tagged_min<16>(slots, p.n_part, tag, p.ctl);
     }
     DSA_MARK(p.trace, 5);
     // score >= tau as a float compare (equal keys <=> equal floats, -0 == +0)
@@ -879,20 +908,21 @@ __global__ void __launch_bounds__(kSelThreads, 1) select_kernel(SelParams p) {
         const int i = (s0 + u) * 64 + lane;
         const bool q = (i <= lim) & (v[u] >= tauf);
         const uint64_t m = __ballot(q);
-        if (q)
-          ast64(dst + off + (uint32_t)__builtin_popcountll(m & lt),
-                ((uint64_t)(uint32_t)(c0 + i) << 32) | order_key(v[u]));
-        off += (uint32_t)__builtin_popcountll(m);
+        if (m != 0ull) {                 // wave-uniform: most segments hold no candidate
+          if (q)
+            ast64(dst + off + (uint32_t)__builtin_popcountll(m & lt),
+                  ((uint64_t)(uint32_t)(c0 + i) << 32) | order_key(v[u]));
+          off += (uint32_t)__builtin_popcountll(m);
+        }
       }
     }
-    if (lane == 0) ast(p.cnt + (size_t)t * p.nwg + wg, off);
+    vm_wait_all();                       // candidates land before their count
+    if (lane == 0) ast64(p.cnt + (size_t)t * p.nwg + wg, ((uint64_t)tag << 32) | off);
     DSA_MARK(p.trace, 6);
   }
   DSA_MARK(p.trace, 7);
-  grid_barrier(p.ctl, p.nwg);
-  DSA_MARK(p.trace, 8);
-  // ---------------- P3: workgroup t selects token t
-  if (wg < T) resolve_token(p, wg, sh);
+  // ---------------- P3: workgroup t selects token t once every count of the token is in
+  if (wg < T) resolve_token(p, wg, sh, epoch);
   DSA_MARK(p.trace, 15);
 }
 
@@ -943,7 +973,7 @@ SelGeometry select_geometry(int T, int64_t L, int64_t pos0, int k, int num_cu) {
 
 size_t select_workspace_bytes(int T, int64_t L, int k, int num_cu) {
   SelGeometry g = select_geometry(T, L, L - T, k, num_cu);
-  return ctl::kBytes + 2 * (size_t)kMaxT * kMaxWG * 4 + (size_t)kMaxT * g.nwg * g.chunk * sizeof(uint64_t);
+  return ctl::kBytes + (size_t)kMaxT * kMaxWG * (8 + 8) + (size_t)kMaxT * g.nwg * g.chunk * sizeof(uint64_t);
 }
 
 int64_t select_max_context(int num_cu) { return (int64_t)num_cu * kMaxChunk; }
@@ -980,9 +1010,9 @@ hipError_t launch_select(int src, const void* q_idx, const float* w_idx, const v
 #endif
   uint8_t* w8 = static_cast<uint8_t*>(ws);
   p.ctl = reinterpret_cast<uint32_t*>(w8);
-  p.cnt = reinterpret_cast<uint32_t*>(w8 + ctl::kBytes);
-  p.tauv = reinterpret_cast<uint32_t*>(w8 + ctl::kBytes + (size_t)kMaxT * kMaxWG * 4);
-  p.cand = reinterpret_cast<uint64_t*>(w8 + ctl::kBytes + 2 * (size_t)kMaxT * kMaxWG * 4);
+  p.cnt = reinterpret_cast<uint64_t*>(w8 + ctl::kBytes);
+  p.tauv = reinterpret_cast<uint64_t*>(w8 + ctl::kBytes + (size_t)kMaxT * kMaxWG * 8);
+  p.cand = reinterpret_cast<uint64_t*>(w8 + ctl::kBytes + (size_t)kMaxT * kMaxWG * 16);
   void* args[] = {&p};
   // row tiles per wave: the two waves of a pair split ceil(T/2) row tiles
   const int rtw = row_tiles(T) <= 2 ? 1 : 2;

@@ -45,24 +45,41 @@ struct AttnParams {
   int nsplit;
 };
 
-template <int KVDT>
+template <int KVDT, int ROWS>
 struct AttnShared {
   static constexpr int RB = KVDT == 0 ? 256 : 128;   // bytes per cache row
   static constexpr int KSTRIDE = RB + 16;            // padded K row stride
-  int64_t rows[kSplitRows];
-  alignas(16) uint8_t kst[kSplitRows * KSTRIDE];
-  alignas(16) uint8_t vst[kSplitRows * RB];
-  float kscl[kSplitRows];
-  float vscl[kSplitRows];
-  float s[kHq][kSplitRows];
+  int64_t rows[ROWS];
+  alignas(16) uint8_t kst[ROWS * KSTRIDE];
+  alignas(16) uint8_t vst[ROWS * RB];
+  float kscl[ROWS];
+  float vscl[ROWS];
+  float s[kHq][ROWS];
   float ms[kHq * 32];     // split maxima / sums of the merging workgroup
   float ls[kHq * 32];
   uint32_t last;
 };
 
-template <int KVDT, int MODE>
+// out[t][h][d4 .. d4+3] = o / den (0 for an empty list), fp32 or bf16
+DSA_DEV void store_out(const AttnParams& p, int t, int h, int d4, float (&o)[4], float den) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) o[i] = den > 0.0f ? o[i] / den : 0.0f;
+  const size_t ob = ((size_t)t * kHq + h) * kD + d4;
+  if (p.out_f32) {
+    float* of = static_cast<float*>(p.out) + ob;
+    *reinterpret_cast<float4*>(of) = make_float4(o[0], o[1], o[2], o[3]);
+  } else {
+    uint16_t* ob16 = static_cast<uint16_t*>(p.out) + ob;
+    const uint32_t w0 = (uint32_t)f32_to_bf16(o[0]) | ((uint32_t)f32_to_bf16(o[1]) << 16);
+    const uint32_t w1 = (uint32_t)f32_to_bf16(o[2]) | ((uint32_t)f32_to_bf16(o[3]) << 16);
+    *reinterpret_cast<uint2*>(ob16) = make_uint2(w0, w1);
+  }
+}
+
+template <int KVDT, int MODE, int ROWS>
 __global__ void __launch_bounds__(kAttnThreads) attn_kernel(AttnParams p) {
-  using SH = AttnShared<KVDT>;
+  static_assert(ROWS % 64 == 0 && ROWS <= kAttnThreads, "64-row blocks, one list entry per thread");
+  using SH = AttnShared<KVDT, ROWS>;
   __shared__ SH sh;
   constexpr int RB = SH::RB;
   const int tid = threadIdx.x;
@@ -71,8 +88,8 @@ __global__ void __launch_bounds__(kAttnThreads) attn_kernel(AttnParams p) {
   const int split = blockIdx.x;
   const int t = blockIdx.y;
   // ---- row list of this split
-  if (tid < kSplitRows) {
-    const int e = split * kSplitRows + tid;
+  if (tid < ROWS) {
+    const int e = split * ROWS + tid;
     int64_t r = -1;
     if (MODE == 0) {
       if (e < p.k) {
@@ -95,7 +112,7 @@ __global__ void __launch_bounds__(kAttnThreads) attn_kernel(AttnParams p) {
   {
     // every load is issued before any is consumed; invalid rows read row 0 and are zeroed
     constexpr int CPR = RB / 16;
-    constexpr int NCH = kSplitRows * CPR / kAttnThreads;
+    constexpr int NCH = ROWS * CPR / kAttnThreads;
     uint4 kv[NCH], vv[NCH];
 #pragma unroll
     for (int u = 0; u < NCH; ++u) {
@@ -128,10 +145,11 @@ __global__ void __launch_bounds__(kAttnThreads) attn_kernel(AttnParams p) {
     }
   }
   __syncthreads();
-  // ---- S = K q^T: wave w owns rows 16w .. 16w+15
-  {
+  // ---- S = K q^T: wave w owns rows 64b + 16w .. +15 of each 64-row block b
+#pragma unroll
+  for (int rb = 0; rb < ROWS / 64; ++rb) {
     f32x4_t acc = {};
-    const int row = wave * 16 + (lane & 15);
+    const int row = rb * 64 + wave * 16 + (lane & 15);
 #pragma unroll
     for (int kb = 0; kb < 4; ++kb) {
       Frag8 a;
@@ -152,7 +170,7 @@ __global__ void __launch_bounds__(kAttnThreads) attn_kernel(AttnParams p) {
     if (h < kHq) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const int rr = wave * 16 + (lane >> 4) * 4 + i;
+        const int rr = rb * 64 + wave * 16 + (lane >> 4) * 4 + i;
         float z = acc[i];
         if (KVDT == 1) z *= sh.kscl[rr];
         sh.s[h][rr] = (sh.rows[rr] >= 0) ? z * p.sm_log2 : -__builtin_inff();
@@ -160,35 +178,43 @@ __global__ void __launch_bounds__(kAttnThreads) attn_kernel(AttnParams p) {
     }
   }
   __syncthreads();
-  // ---- softmax of the split: thread (h = tid/32, j = tid%32) holds rows j and j+32
+  // ---- softmax of the split: thread (h = tid/32, j = tid%32) holds rows j, j+32, ...
+  constexpr int RPT = ROWS / 32;
   const int h = tid >> 5;
   const int jj = tid & 31;
   float m, l;
   {
-    const float z0 = sh.s[h][jj], z1 = sh.s[h][jj + 32];
-    m = fmaxf(z0, z1);
+    float z[RPT];
+#pragma unroll
+    for (int i = 0; i < RPT; ++i) z[i] = sh.s[h][jj + 32 * i];
+    m = z[0];
+#pragma unroll
+    for (int i = 1; i < RPT; ++i) m = fmaxf(m, z[i]);
 #pragma unroll
     for (int d = 16; d >= 1; d >>= 1) m = fmaxf(m, __shfl_xor(m, d, 64));
-    float p0 = 0.0f, p1 = 0.0f;
+    float pz[RPT];
+#pragma unroll
+    for (int i = 0; i < RPT; ++i) pz[i] = 0.0f;
     if (m != -__builtin_inff()) {
-      p0 = exp2f(z0 - m);
-      p1 = exp2f(z1 - m);
+#pragma unroll
+      for (int i = 0; i < RPT; ++i) pz[i] = exp2f(z[i] - m);
     }
-    l = p0 + p1;
+    l = pz[0];
+#pragma unroll
+    for (int i = 1; i < RPT; ++i) l += pz[i];
 #pragma unroll
     for (int d = 16; d >= 1; d >>= 1) l += __shfl_xor(l, d, 64);
-    if (KVDT == 1) {
-      p0 *= sh.vscl[jj];
-      p1 *= sh.vscl[jj + 32];
+#pragma unroll
+    for (int i = 0; i < RPT; ++i) {
+      if (KVDT == 1) pz[i] *= sh.vscl[jj + 32 * i];
+      sh.s[h][jj + 32 * i] = pz[i];
     }
-    sh.s[h][jj] = p0;
-    sh.s[h][jj + 32] = p1;
   }
   __syncthreads();
   // ---- acc[h][d4..d4+3] = sum_j p[h][j] * V[j][d4..d4+3]
   const int d4 = jj * 4;
   float acc[4] = {0.0f, 0.0f, 0.0f, 0.0f};
-  for (int j = 0; j < kSplitRows; ++j) {
+  for (int j = 0; j < ROWS; ++j) {
     const float pj = sh.s[h][j];
     float v[4];
     if constexpr (KVDT == 0) {
@@ -205,6 +231,25 @@ __global__ void __launch_bounds__(kAttnThreads) attn_kernel(AttnParams p) {
     }
 #pragma unroll
     for (int i = 0; i < 4; ++i) acc[i] = fmaf(pj, v[i], acc[i]);
+  }
+  float sink2 = -__builtin_inff();
+  if (p.sink) sink2 = p.sink[h] * 1.4426950408889634f;
+  if (p.nsplit == 1) {
+    // the whole list in one workgroup: normalise here (same operations as the merge)
+    const float M = fmaxf(m, sink2);
+    float den = 0.0f;
+    float o[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+    if (M != -__builtin_inff()) {
+      if (m != -__builtin_inff()) {
+        const float sc = exp2f(m - M);
+        den = fmaf(l, sc, den);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) o[i] = fmaf(acc[i], sc, o[i]);
+      }
+      if (sink2 != -__builtin_inff()) den += exp2f(sink2 - M);
+    }
+    store_out(p, t, h, d4, o, den);
+    return;
   }
   // ---- publish the split's partial
   float* part = p.part + (((size_t)t * p.nsplit + split) * kHq + h) * kPartStride;
@@ -230,8 +275,6 @@ __global__ void __launch_bounds__(kAttnThreads) attn_kernel(AttnParams p) {
   __syncthreads();
   float M = -__builtin_inff();
   for (int s = 0; s < p.nsplit; ++s) M = fmaxf(M, sh.ms[s * kHq + h]);
-  float sink2 = -__builtin_inff();
-  if (p.sink) sink2 = p.sink[h] * 1.4426950408889634f;
   M = fmaxf(M, sink2);
   float den = 0.0f;
   float o[4] = {0.0f, 0.0f, 0.0f, 0.0f};
@@ -262,18 +305,7 @@ __global__ void __launch_bounds__(kAttnThreads) attn_kernel(AttnParams p) {
     }
     if (sink2 != -__builtin_inff()) den += exp2f(sink2 - M);
   }
-#pragma unroll
-  for (int i = 0; i < 4; ++i) o[i] = den > 0.0f ? o[i] / den : 0.0f;
-  const size_t ob = ((size_t)t * kHq + h) * kD + d4;
-  if (p.out_f32) {
-    float* of = static_cast<float*>(p.out) + ob;
-    *reinterpret_cast<float4*>(of) = make_float4(o[0], o[1], o[2], o[3]);
-  } else {
-    uint16_t* ob16 = static_cast<uint16_t*>(p.out) + ob;
-    const uint32_t w0 = (uint32_t)f32_to_bf16(o[0]) | ((uint32_t)f32_to_bf16(o[1]) << 16);
-    const uint32_t w1 = (uint32_t)f32_to_bf16(o[2]) | ((uint32_t)f32_to_bf16(o[3]) << 16);
-    *reinterpret_cast<uint2*>(ob16) = make_uint2(w0, w1);
-  }
+  store_out(p, t, h, d4, o, den);
   if (tid == 0) ast(p.ctr + 64 * t, 0u);
 }
 
@@ -281,7 +313,13 @@ size_t attn_workspace_bytes(int T, int nsplit) {
   return ctl::kBytes + (size_t)T * nsplit * kHq * kPartStride * sizeof(float);
 }
 
-int attn_splits(int list_len) { return (list_len + kSplitRows - 1) / kSplitRows; }
+// DSA lists (k up to 2048) split in 64-row pieces (enough workgroups to fill the chip);
+// a sliding window of up to 128 rows runs in one workgroup per token (no merge).
+constexpr int kSwaRows = 128;
+int attn_splits(int mode, int list_len) {
+  const int rows = mode == 0 ? kSplitRows : kSwaRows;
+  return (list_len + rows - 1) / rows;
+}
 
 hipError_t launch_attention(int mode, int kvdt, const void* q, const void* kc, const void* vc,
                             const float* ks, const float* vs, const int32_t* idx, int k, int T,
@@ -304,16 +342,16 @@ hipError_t launch_attention(int mode, int kvdt, const void* q, const void* kc, c
   p.sink = sink;
   p.out = out;
   p.out_f32 = out_f32;
-  p.nsplit = attn_splits(mode == 0 ? k : window);
+  p.nsplit = attn_splits(mode, mode == 0 ? k : window);
   uint8_t* w8 = static_cast<uint8_t*>(ws);
   p.ctr = reinterpret_cast<uint32_t*>(w8) + ctl::kDone;
   p.part = reinterpret_cast<float*>(w8 + ctl::kBytes);
   const dim3 grid(p.nsplit, T), block(kAttnThreads);
   if (mode == 0) {
-    if (kvdt == 0) hipLaunchKernelGGL((attn_kernel<0, 0>), grid, block, 0, st, p);
-    else hipLaunchKernelGGL((attn_kernel<1, 0>), grid, block, 0, st, p);
+    if (kvdt == 0) hipLaunchKernelGGL((attn_kernel<0, 0, kSplitRows>), grid, block, 0, st, p);
+    else hipLaunchKernelGGL((attn_kernel<1, 0, kSplitRows>), grid, block, 0, st, p);
   } else {
-    hipLaunchKernelGGL((attn_kernel<0, 1>), grid, block, 0, st, p);
+    hipLaunchKernelGGL((attn_kernel<0, 1, kSwaRows>), grid, block, 0, st, p);
   }
   return hipGetLastError();
 }

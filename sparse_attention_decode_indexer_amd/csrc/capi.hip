@@ -61,7 +61,7 @@ LayerWs layer_ws(int kind, int T, int64_t L, int k, int window, int ncu) {
   w.attn_out = o; o = align_up(o + (size_t)dsa::kMaxT * dsa::kHq * dsa::kD * 2);
   const int list = kind == DSA_LAYER_DSA ? k : window;
   w.idx = o; o = align_up(o + (kind == DSA_LAYER_DSA ? (size_t)dsa::kMaxT * k * 4 : 0));
-  w.attn = o; o = align_up(o + dsa::attn_workspace_bytes(dsa::kMaxT, dsa::attn_splits(list)));
+  w.attn = o; o = align_up(o + dsa::attn_workspace_bytes(dsa::kMaxT, dsa::attn_splits(kind == DSA_LAYER_DSA ? 0 : 1, list)));
   w.sel = o;
   if (kind == DSA_LAYER_DSA) o = align_up(o + dsa::select_workspace_bytes(T, L, k, ncu));
   w.total = o;
@@ -98,9 +98,9 @@ size_t dsa_workspace_bytes(int kind, int T, int64_t L, int k) {
     case DSA_WS_INDEX_TOPK:
       return dsa::select_workspace_bytes(T, L, k, ncu);
     case DSA_WS_SPARSE_ATTN:
-      return dsa::attn_workspace_bytes(T, dsa::attn_splits(k));
+      return dsa::attn_workspace_bytes(T, dsa::attn_splits(0, k));
     case DSA_WS_SWA_ATTN:
-      return dsa::attn_workspace_bytes(T, dsa::attn_splits(k));
+      return dsa::attn_workspace_bytes(T, dsa::attn_splits(1, k));
     case DSA_WS_LAYER_DSA:
       return layer_ws(DSA_LAYER_DSA, T, L, k, 0, ncu).total;
     case DSA_WS_LAYER_SWA:
@@ -189,7 +189,7 @@ dsa_status_t dsa_sparse_attn(const void* q, const void* k_cache, const void* v_c
   if (fp8 != (k_scale != nullptr) || fp8 != (v_scale != nullptr)) return DSA_ERR_DTYPE;
   if (out_dtype != DSA_BF16 && out_dtype != DSA_FP32) return DSA_ERR_DTYPE;
   if (T < 1 || T > dsa::kMaxT || k < 1 || k > dsa::kMaxTopK || L < 1 || L > kMaxL) return DSA_ERR_SHAPE;
-  const size_t need = dsa::attn_workspace_bytes(T, dsa::attn_splits(k));
+  const size_t need = dsa::attn_workspace_bytes(T, dsa::attn_splits(0, k));
   if (!ws || ws_bytes < need) return DSA_ERR_WORKSPACE;
   if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) || !aligned16(out) || !aligned16(ws) ||
       (sink && !aligned16(sink)))
@@ -206,7 +206,7 @@ dsa_status_t swa_attn(const void* q, const void* k_ring, const void* v_ring, int
   if (out_dtype != DSA_BF16 && out_dtype != DSA_FP32) return DSA_ERR_DTYPE;
   if (T < 1 || T > dsa::kMaxT || window < 1 || window > dsa::kMaxTopK || pos0 < 0) return DSA_ERR_SHAPE;
   if (ring_cap < (int64_t)window + T - 1 || ring_cap > kMaxL) return DSA_ERR_SHAPE;
-  const size_t need = dsa::attn_workspace_bytes(T, dsa::attn_splits(window));
+  const size_t need = dsa::attn_workspace_bytes(T, dsa::attn_splits(1, window));
   if (!ws || ws_bytes < need) return DSA_ERR_WORKSPACE;
   if (!aligned16(q) || !aligned16(k_ring) || !aligned16(v_ring) || !aligned16(out) || !aligned16(ws) ||
       (sink && !aligned16(sink)))

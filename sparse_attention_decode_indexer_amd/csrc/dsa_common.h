@@ -209,8 +209,11 @@ constexpr size_t kBytes = 16384;
 #ifdef DSA_TRACE
 #define DSA_MARK(buf, s) \
   do { if ((buf) && threadIdx.x == 0) (buf)[blockIdx.x * 16 + (s)] = __builtin_amdgcn_s_memrealtime(); } while (0)
+#define DSA_MARK_CLK(buf, s) \
+  do { if ((buf) && threadIdx.x == 0) (buf)[blockIdx.x * 16 + (s)] = __builtin_amdgcn_s_memtime(); } while (0)
 #else
 #define DSA_MARK(buf, s) do { } while (0)
+#define DSA_MARK_CLK(buf, s) do { } while (0)
 #endif
 
 constexpr uint64_t kSpinLimit = 20000000ull;   // 0.2 s of the 100 MHz real-time counter

@@ -28,7 +28,7 @@ hipError_t launch_select(int src, const void* q_idx, const float* w_idx, const v
                          int num_cu, hipStream_t st);
 
 size_t attn_workspace_bytes(int T, int nsplit);
-int attn_splits(int list_len);
+int attn_splits(int mode, int list_len);   // mode 0: index list, 1: sliding window
 // mode 0: sparse list idx; mode 1: sliding window over a ring
 hipError_t launch_attention(int mode, int kvdt, const void* q, const void* kc, const void* vc,
                             const float* ks, const float* vs, const int32_t* idx, int k, int T,
@@ -45,5 +45,9 @@ hipError_t launch_proj_out(const void* o, const void* w_o, const void* x, void* 
                            void* ws, hipStream_t st);
 
 hipError_t launch_zero(void* p, size_t bytes, hipStream_t st);
+
+#ifdef DSA_TRACE
+uint64_t* dsa_trace_buffer();   // profiling builds: phase-timestamp buffer (or null)
+#endif
 
 }  // namespace dsa

@@ -182,16 +182,15 @@ DSA_DEV float key_to_float(uint32_t k) {
 // without a NaN canonicalisation.
 DSA_DEV float relu_bits(float x) { return __int_as_float(max(__float_as_int(x), 0)); }
 
-// Scores of one 32-key tile for RTW row tiles: out[r] is the score of token
-// 2(rt0+r) + (lane>>5) for key s0 + (lane & 31).  The arithmetic and its order are fixed,
-// the same in every kernel that calls it: per head a = q_h . k (MFMA, fp32); per lane
+// Building blocks of a tile's scores.  Their arithmetic and its order are fixed and the
+// same in every kernel that uses them: per head a = q_h . k (MFMA, fp32); per lane
 // sum_e (w/2)|a_e| over its 8 heads of each token of the row tile, in element order; the
 // two lanes of a (token pair, key) exchange and add; then + ((hi + mid) + lo) of the
 // linear tile; then x the row scale for e4m3 keys.
-template <int KDT, int RTW>
-DSA_DEV void score_tile(const KeyTile<KDT>& kt, const Frag8 (&qa)[RTW][4], const Frag8 (&qf)[4],
-                        const float (&wv)[RTW][16], float (&out)[RTW]) {
-  Frag8 kb[4];
+
+// e4m3 or bf16 key tile -> the four bf16 B operands (e4m3 -> bf16 is exact)
+template <int KDT>
+DSA_DEV void keys_to_bf16(const KeyTile<KDT>& kt, Frag8 (&kb)[4]) {
   if constexpr (KDT == 0) {
 #pragma unroll
     for (int j = 0; j < 4; ++j) kb[j].u = kt.raw[j];
@@ -206,29 +205,49 @@ DSA_DEV void score_tile(const KeyTile<KDT>& kt, const Frag8 (&qa)[RTW][4], const
       kb[j].v = bf16x8_t{a[0], a[1], b[0], b[1], c[0], c[1], d[0], d[1]};
     }
   }
-  f32x16_t lacc = {};
+}
+
+// one 32-row tile against the key tile: K = 64 in four steps
+DSA_DEV f32x16_t mma_k64(const Frag8 (&a)[4], const Frag8 (&kb)[4]) {
+  f32x16_t acc = {};
 #pragma unroll
-  for (int j = 0; j < 4; ++j) lacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qf[j].v, kb[j].v, lacc, 0, 0, 0);
+  for (int j = 0; j < 4; ++j) acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[j].v, kb[j].v, acc, 0, 0, 0);
+  return acc;
+}
+
+// linear part of row tile r (accumulator elements 4r .. 4r+2 of the linear tile)
+template <int R>
+DSA_DEV float lin_part(const f32x16_t& lacc) { return (lacc[4 * R] + lacc[4 * R + 1]) + lacc[4 * R + 2]; }
+
+// score of token 2r + (lane>>5) for key lane & 31 from the row tile's accumulator
+template <int KDT>
+DSA_DEV float row_score(const f32x16_t& acc, const float (&w)[16], float lin, float scale) {
+  float p0 = 0.0f, p1 = 0.0f;
 #pragma unroll
-  for (int r = 0; r < RTW; ++r) {
-    f32x16_t acc = {};
+  for (int e = 0; e < 8; ++e) p0 = fmaf(w[e], fabsf(acc[e]), p0);
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
-      acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa[r][j].v, kb[j].v, acc, 0, 0, 0);
-    float p0 = 0.0f, p1 = 0.0f;
-#pragma unroll
-    for (int e = 0; e < 8; ++e) p0 = fmaf(wv[r][e], fabsf(acc[e]), p0);
-#pragma unroll
-    for (int e = 8; e < 16; ++e) p1 = fmaf(wv[r][e], fabsf(acc[e]), p1);
-    // lanes l and l+32 hold the same (token pair, key) over complementary heads: one
-    // swap of p0's upper half with p1's lower half leaves token 2r's two partial sums
-    // side by side in lane l and token 2r+1's in lane l+32.
-    const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(p0), __float_as_uint(p1), false, false);
-    const float tot = __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
-    const float lin = (lacc[4 * r] + lacc[4 * r + 1]) + lacc[4 * r + 2];
-    const float v = tot + lin;
-    out[r] = (KDT == 1) ? v * kt.scale : v;
-  }
+  for (int e = 8; e < 16; ++e) p1 = fmaf(w[e], fabsf(acc[e]), p1);
+  // lanes l and l+32 hold the same (token pair, key) over complementary heads: one swap
+  // of p0's upper half with p1's lower half leaves token 2r's two partial sums side by
+  // side in lane l and token 2r+1's in lane l+32.
+  const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(p0), __float_as_uint(p1), false, false);
+  const float tot = __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
+  const float v = tot + lin;
+  return (KDT == 1) ? v * scale : v;
+}
+
+// Scores of one 32-key tile for RTW row tiles: out[r] is the score of token
+// 2(rt0+r) + (lane>>5) for key s0 + (lane & 31).
+template <int KDT, int RTW>
+DSA_DEV void score_tile(const KeyTile<KDT>& kt, const Frag8 (&qa)[RTW][4], const Frag8 (&qf)[4],
+                        const float (&wv)[RTW][16], float (&out)[RTW]) {
+  Frag8 kb[4];
+  keys_to_bf16<KDT>(kt, kb);
+  const f32x16_t lacc = mma_k64(qf, kb);
+  out[0] = row_score<KDT>(mma_k64(qa[0], kb), wv[0], lin_part<0>(lacc), kt.scale);
+  if constexpr (RTW > 1) out[1] = row_score<KDT>(mma_k64(qa[1], kb), wv[1], lin_part<1>(lacc), kt.scale);
+  if constexpr (RTW > 2) out[2] = row_score<KDT>(mma_k64(qa[2], kb), wv[2], lin_part<2>(lacc), kt.scale);
+  if constexpr (RTW > 3) out[3] = row_score<KDT>(mma_k64(qa[3], kb), wv[3], lin_part<3>(lacc), kt.scale);
 }
 
 // ----------------------------------------------------------------------------- scores kernel
@@ -311,6 +330,7 @@ struct SelShared {
   float kscale[kMaxChunk];           // row scales of the chunk (e4m3 keys)
   uint16_t ql[3 * kMaxT * kDI];      // linear-part query, three bf16 parts
   uint32_t wcnt[2 * kSelWaves];      // resolver: per-wave counts
+  float dump[64];                    // target of scores that are not kept (clamped tiles)
   uint32_t scan[32];
 };
 
@@ -738,6 +758,7 @@ DSA_DEV void resolve_token(const SelParams& p, int t, SelShared& sh, uint32_t ep
 
 template <int SRC, int KDT, int RTW>
 __global__ void __launch_bounds__(kSelThreads, 1) select_kernel(SelParams p) {
+  static_assert(RTW == 1 || RTW == 2, "a wave holds one or two row tiles");
   __shared__ SelShared sh;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -796,25 +817,50 @@ __global__ void __launch_bounds__(kSelThreads, 1) select_kernel(SelParams p) {
     Frag8 qf[4];
     load_qlin_frags<RTW>(sh.ql, rt0, qf);
     DSA_MARK(p.trace, 1);
+    DSA_MARK_CLK(p.trace, 14);
     if (active && nmine > 0) {
+      // Software pipeline: the last row tile's epilogue of tile j-1 runs on the vector
+      // units while the matrix cores work on tile j, and each earlier row tile's
+      // epilogue runs under the next row tile's MFMAs.  Scores of clamped repeats go to
+      // a dump slot (selected by address, so no branch splits the schedule).
+      f32x16_t accp = {};
+      float linp = -__builtin_inff(), scp = 1.0f;      // the first "pending" row scores -inf
+      float* dstp = &sh.dump[lane];
       for (int base = 0; base < nmine; base += kPrefetch) {
 #pragma unroll
         for (int i = 0; i < kPrefetch; ++i) {
           const int j = base + i;
           const int jc = j < nmine ? j : nmine - 1;      // the tile actually loaded (clamped)
           const int sl = (pair + jc * kPairs) * kTile + (lane & 31);
-          if constexpr (KDT == 1) buf[i].scale = sh.kscale[sl & (kMaxChunk - 1)];
-          float out[RTW];
-          score_tile<KDT, RTW>(buf[i], qa, qf, wv, out);
-#pragma unroll
-          for (int r = 0; r < RTW; ++r) gmax[r] = fmaxf(gmax[r], out[r]);   // clamped repeats are harmless
+          const float scale = (KDT == 1) ? sh.kscale[sl & (kMaxChunk - 1)] : 1.0f;
+          const bool keep = j < nmine;
+          Frag8 kb[4];
+          keys_to_bf16<KDT>(buf[i], kb);
           load_key_tile<KDT, false>(p.k_idx, p.k_scale, p.L, tile_of(j + kPrefetch), buf[i]);
-          if (j < nmine) {
-#pragma unroll
-            for (int r = 0; r < RTW; ++r) sh.sc[2 * (rt0 + r) + half][sl] = out[r];
+          const f32x16_t lacc = mma_k64(qf, kb);
+          {
+            const float o = row_score<KDT>(accp, wv[RTW - 1], linp, scp);
+            gmax[RTW - 1] = fmaxf(gmax[RTW - 1], o);
+            *dstp = o;
           }
+          f32x16_t acc = mma_k64(qa[0], kb);
+          if constexpr (RTW == 2) {
+            const f32x16_t acc1 = mma_k64(qa[1], kb);
+            const float o = row_score<KDT>(acc, wv[0], lin_part<0>(lacc), scale);
+            gmax[0] = fmaxf(gmax[0], o);
+            float* d = keep ? &sh.sc[2 * rt0 + half][sl] : &sh.dump[lane];
+            *d = o;
+            acc = acc1;
+          }
+          accp = acc;
+          linp = lin_part<RTW - 1>(lacc);
+          scp = scale;
+          dstp = keep ? &sh.sc[2 * (rt0 + RTW - 1) + half][sl] : &sh.dump[lane];
         }
       }
+      const float o = row_score<KDT>(accp, wv[RTW - 1], linp, scp);
+      gmax[RTW - 1] = fmaxf(gmax[RTW - 1], o);
+      *dstp = o;
     }
   } else {
     constexpr int PER = kMaxChunk / kSelThreads;
@@ -835,6 +881,7 @@ __global__ void __launch_bounds__(kSelThreads, 1) select_kernel(SelParams p) {
   }
   __syncthreads();
   DSA_MARK(p.trace, 2);
+  if (wg >= T) DSA_MARK_CLK(p.trace, 13);     // core clock over P1 (profiling builds)
   // ---------------- tau bound.  Any split of the chunk's (visible) scores into at least
   // m non-empty groups gives one: the m-th largest group maximum is <= the m-th largest
   // score.  Computed scores use 64 groups per token: the keys at one position mod 32
@@ -981,6 +1028,7 @@ int64_t select_max_context(int num_cu) { return (int64_t)num_cu * kMaxChunk; }
 #ifdef DSA_TRACE
 static uint64_t* g_trace = nullptr;
 extern "C" void dsa_trace_set(void* buf) { g_trace = static_cast<uint64_t*>(buf); }
+uint64_t* dsa_trace_buffer() { return g_trace; }
 #endif
 
 hipError_t launch_select(int src, const void* q_idx, const float* w_idx, const void* k_idx,

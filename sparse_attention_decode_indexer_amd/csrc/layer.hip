@@ -5,11 +5,9 @@
 //   §A DSA layer: from 29 kernels to one: input RMSNorm, Q/K/V projections, RoPE,
 //     KV-cache writes, ..., output projection.
 //   §Optimizing inside the kernel: projection weights do not depend on the normalised
-//     input.  On gfx950 a wave64 vector instruction holds its SIMD for four cycles, so
-//     having every projection workgroup recompute the RMSNorm of the whole block (as
-//     the pages' CTAs do) costs more than it saves; instead one small kernel normalises
-//     the block once and builds the rotary tables, and every projection workgroup
-//     issues its activation and weight loads at entry.
+//     input, so every projection workgroup issues its input and weight loads at entry
+//     and normalises the block (and builds its rotary factors) while the weights stream
+//     in.  Only the lanes of real weight rows issue weight loads.
 //   §GPU Memory Optimization: positional-encoding precision at 1M context -- rotary
 //     angles are formed in fp64.
 //
@@ -104,12 +102,10 @@ struct ProjParams {
   float* kidx_scale;
   uint32_t* kictr;          // counter of finished k_I blocks
   float* kistage;           // [T][64] rotated k_I values
-  const uint16_t* y;        // [T][4096] bf16 normalised input (from norm_rope_kernel)
-  const float2* rope128;    // [T][64] (cos, sin) for width-128 heads
-  const float2* rope64;     // [T][32] (cos, sin) for width-64 indexer heads
   // OUT
   const uint16_t* o;        // [T][1024] bf16 attention output
   uint16_t* xout;           // [T][4096]
+  uint64_t* trace;          // profiling builds: [blocks][16] phase timestamps
 };
 
 constexpr int kXsStride = kHidden + 8;      // padded LDS row: rows fall in different banks
@@ -120,6 +116,7 @@ struct ProjShared {
   float tile[16][16];
   float rc[kMaxT][8];
   float rs[kMaxT][8];
+  float rnorm[kMaxT];                          // 1 / rms of each token
   uint32_t last;
 };
 
@@ -149,7 +146,11 @@ __global__ void __launch_bounds__(kProjThreads) proj_kernel(ProjParams p) {
   //    weights do not depend on the norm and stream in while it is computed.  Lane group
   //    g takes k chunk 4i+g of the wave's range at step i, so each load instruction reads
   //    64 contiguous bytes of every row.
-  const uint16_t* src = MODE == 0 ? p.y : p.o;
+  uint64_t* trace = MODE == 0 ? p.trace : nullptr;
+  (void)trace;
+  DSA_MARK(trace, 0);
+  // QKV: the layer input x (normalised below); OUT: the attention output
+  const uint16_t* src = MODE == 0 ? p.x : p.o;
   constexpr int NCH = kMaxT * (MODE == 0 ? kHidden : kHq * kD) / 8 / kProjThreads;   // uint4 chunks per thread
   const int chunks = kMaxT * K / 8;
   uint4 v[NCH];
@@ -161,18 +162,68 @@ __global__ void __launch_bounds__(kProjThreads) proj_kernel(ProjParams p) {
     const int tc = t < T ? t : T - 1;
     v[u] = *reinterpret_cast<const uint4*>(src + (size_t)tc * K + kk);
   }
+  uint4 gv = make_uint4(0u, 0u, 0u, 0u);
+  if (MODE == 0) gv = reinterpret_cast<const uint4*>(p.gamma)[tid];   // gamma[8 tid .. 8 tid + 8)
+  // only the lanes of real rows load weights (the MFMA's unused rows stay zero)
   Frag8 wf[NSTEP];
-  {
+  if (lrow < rpw) {
     const uint4* wp = reinterpret_cast<const uint4*>(p.w + (size_t)wrow * K + kw0) + (lane >> 4);
 #pragma unroll
     for (int i = 0; i < NSTEP; ++i) wf[i].u = wp[4 * i];
-    if (lrow >= rpw) {
+  } else {
 #pragma unroll
-      for (int i = 0; i < NSTEP; ++i) wf[i].u = make_uint4(0u, 0u, 0u, 0u);
+    for (int i = 0; i < NSTEP; ++i) wf[i].u = make_uint4(0u, 0u, 0u, 0u);
+  }
+  DSA_MARK(trace, 1);
+  if (MODE == 0) {
+    // Input RMSNorm while the weights stream in: thread tid holds elements
+    // [8 tid, 8 tid + 8) of every token.  Per token: squares summed in element order per
+    // thread; thread partials go through LDS (the activation area, not yet in use) and
+    // wave t adds token t's: lane j takes threads 8j .. 8j+7 in order, then an xor
+    // butterfly over the wave.  y = bf16(x * (1 / sqrt(mean + eps)) * gamma).
+    static_assert(kProjWaves == kMaxT, "one wave per token for the norm reduction");
+    float* scr = reinterpret_cast<float*>(&sh.xs[0][0]);          // [kMaxT][kProjThreads]
+#pragma unroll
+    for (int t = 0; t < kMaxT; ++t) {
+      const uint32_t x4[4] = {v[t].x, v[t].y, v[t].z, v[t].w};
+      float a2 = 0.0f;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const float a = __uint_as_float(x4[q] << 16), bb = __uint_as_float(x4[q] & 0xffff0000u);
+        a2 = fmaf(a, a, a2);
+        a2 = fmaf(bb, bb, a2);
+      }
+      scr[t * kProjThreads + tid] = a2;
+    }
+    __syncthreads();
+    {
+      const float4 q0 = *reinterpret_cast<const float4*>(&scr[wave * kProjThreads + lane * 8]);
+      const float4 q1 = *reinterpret_cast<const float4*>(&scr[wave * kProjThreads + lane * 8 + 4]);
+      float a = ((((((q0.x + q0.y) + q0.z) + q0.w) + q1.x) + q1.y) + q1.z) + q1.w;
+#pragma unroll
+      for (int d = 32; d >= 1; d >>= 1) a += __shfl_xor(a, d, 64);
+      if (lane == 0) sh.rnorm[wave] = 1.0f / sqrtf(a / (float)kHidden + p.eps);
+    }
+    __syncthreads();
+    const uint32_t g4[4] = {gv.x, gv.y, gv.z, gv.w};
+#pragma unroll
+    for (int t = 0; t < kMaxT; ++t) {
+      const float r = sh.rnorm[t];
+      const uint32_t x4[4] = {v[t].x, v[t].y, v[t].z, v[t].w};
+      uint32_t o4[4];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const float y0 = (__uint_as_float(x4[q] << 16) * r) * __uint_as_float(g4[q] << 16);
+        const float y1 = (__uint_as_float(x4[q] & 0xffff0000u) * r) * __uint_as_float(g4[q] & 0xffff0000u);
+        o4[q] = (uint32_t)f32_to_bf16(y0) | ((uint32_t)f32_to_bf16(y1) << 16);
+      }
+      *reinterpret_cast<uint4*>(&sh.xs[t][8 * tid]) = t < T ? make_uint4(o4[0], o4[1], o4[2], o4[3])
+                                                            : make_uint4(0u, 0u, 0u, 0u);
+      __builtin_amdgcn_sched_barrier(0);   // one token at a time: keeps register use low
     }
   }
-  // 2) activations into LDS
-  {
+  // 2) activations into LDS (QKV: already stored, normalised)
+  if (MODE == 1) {
 #pragma unroll
     for (int u = 0; u < NCH; ++u) {
       const int c = tid + u * kProjThreads;
@@ -182,16 +233,20 @@ __global__ void __launch_bounds__(kProjThreads) proj_kernel(ProjParams p) {
       }
     }
   }
-  // rotary cos/sin of this block's pairs at the block's positions (table from norm_rope_kernel)
+  // rotary cos/sin of this block's pairs at the block's positions: angle
+  // (pos0 + t) * theta^(-2i/d) formed in fp64, cos/sin rounded to fp32
   if (MODE == 0 && bi.rot_d && tid < 8 * kMaxT) {
     const int t = tid >> 3, r = tid & 7;
     if (t < T && r < rpw / 2) {
-      const float2 cs = bi.rot_d == kD ? p.rope128[t * (kD / 2) + bi.i0 + r] : p.rope64[t * (kDI / 2) + bi.i0 + r];
-      sh.rc[t][r] = cs.x;
-      sh.rs[t][r] = cs.y;
+      const int i = bi.i0 + r;
+      const double inv = pow((double)p.theta, -2.0 * (double)i / (double)bi.rot_d);
+      const double ang = (double)(p.pos0 + t) * inv;
+      sh.rc[t][r] = (float)cos(ang);
+      sh.rs[t][r] = (float)sin(ang);
     }
   }
   __syncthreads();
+  DSA_MARK(trace, 2);
   // 3) MFMA over this wave's k range
   f32x4_t acc = {};
   {
@@ -216,6 +271,7 @@ __global__ void __launch_bounds__(kProjThreads) proj_kernel(ProjParams p) {
     sh.tile[r][c] = v;
   }
   __syncthreads();
+  DSA_MARK(trace, 3);
   // 4) epilogue
   if (MODE == 1) {
     // x_out[t][n] = bf16(x[t][n] + acc)
@@ -228,6 +284,7 @@ __global__ void __launch_bounds__(kProjThreads) proj_kernel(ProjParams p) {
     return;
   }
   // QKV: round, rotate pairs (r, r + rpw/2) at position pos0 + t, round, store
+  DSA_MARK(trace, 4);
   const int hp = rpw / 2;
   if (tid < hp * kMaxT) {
     const int t = tid / hp, r = tid % hp;
@@ -297,67 +354,9 @@ __global__ void __launch_bounds__(kProjThreads) proj_kernel(ProjParams p) {
   if (tid == 0) ast(p.kictr, 0u);
 }
 
-// Input RMSNorm of the block (one workgroup per token) and the rotary tables (one more
-// workgroup): y[t] = bf16(x[t] * rsqrt(mean(x[t]^2) + eps) * gamma); cos/sin of
-// (pos0 + t) * theta^(-2i/d) with the angle formed in fp64.  Every projection workgroup
-// then reads y and the tables instead of recomputing them.
-__global__ void __launch_bounds__(kProjThreads) norm_rope_kernel(const uint16_t* __restrict__ x,
-                                                                 const uint16_t* __restrict__ gamma, int T,
-                                                                 float eps, float theta, int64_t pos0,
-                                                                 uint16_t* __restrict__ y, float2* rope128,
-                                                                 float2* rope64) {
-  __shared__ float part[kProjWaves];
-  const int tid = threadIdx.x;
-  const int lane = tid & 63, wave = tid >> 6;
-  const int t = blockIdx.x;
-  if (t < T) {
-    const uint4 xv = reinterpret_cast<const uint4*>(x + (size_t)t * kHidden)[tid];   // 8 elements
-    const uint4 gv = reinterpret_cast<const uint4*>(gamma)[tid];
-    const uint32_t x4[4] = {xv.x, xv.y, xv.z, xv.w};
-    const uint32_t g4[4] = {gv.x, gv.y, gv.z, gv.w};
-    float ss = 0.0f;
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const float a = __uint_as_float(x4[q] << 16), b = __uint_as_float(x4[q] & 0xffff0000u);
-      ss = fmaf(a, a, ss);
-      ss = fmaf(b, b, ss);
-    }
-#pragma unroll
-    for (int d = 32; d >= 1; d >>= 1) ss += __shfl_xor(ss, d, 64);
-    if (lane == 0) part[wave] = ss;
-    __syncthreads();
-    float tot = part[0];
-#pragma unroll
-    for (int w = 1; w < kProjWaves; ++w) tot += part[w];
-    const float r = 1.0f / sqrtf(tot / (float)kHidden + eps);
-    uint32_t o4[4];
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const float y0 = (__uint_as_float(x4[q] << 16) * r) * __uint_as_float(g4[q] << 16);
-      const float y1 = (__uint_as_float(x4[q] & 0xffff0000u) * r) * __uint_as_float(g4[q] & 0xffff0000u);
-      o4[q] = (uint32_t)f32_to_bf16(y0) | ((uint32_t)f32_to_bf16(y1) << 16);
-    }
-    reinterpret_cast<uint4*>(y + (size_t)t * kHidden)[tid] = make_uint4(o4[0], o4[1], o4[2], o4[3]);
-  } else {
-    for (int e = tid; e < T * (kD / 2 + kDI / 2); e += kProjThreads) {
-      const int tt = e / (kD / 2 + kDI / 2), j = e % (kD / 2 + kDI / 2);
-      const bool wide = j < kD / 2;
-      const int i = wide ? j : j - kD / 2;
-      const double inv = pow((double)theta, -2.0 * (double)i / (double)(wide ? kD : kDI));
-      const double ang = (double)(pos0 + tt) * inv;
-      const float2 cs = make_float2((float)cos(ang), (float)sin(ang));
-      if (wide) rope128[tt * (kD / 2) + i] = cs;
-      else rope64[tt * (kDI / 2) + i] = cs;
-    }
-  }
-}
-
 // workspace layout of the projection stage
 constexpr size_t kWsKiStage = ctl::kBytes;
-constexpr size_t kWsY = kWsKiStage + (size_t)kMaxT * kDI * sizeof(float);
-constexpr size_t kWsRope128 = kWsY + (size_t)kMaxT * kHidden * 2;
-constexpr size_t kWsRope64 = kWsRope128 + (size_t)kMaxT * (kD / 2) * sizeof(float2);
-constexpr size_t kWsProjEnd = kWsRope64 + (size_t)kMaxT * (kDI / 2) * sizeof(float2);
+constexpr size_t kWsProjEnd = kWsKiStage + (size_t)kMaxT * kDI * sizeof(float);
 
 hipError_t launch_proj_qkv(int kind, const void* x, const void* gamma, const void* w, int T,
                            float eps, float theta, int64_t pos0, void* qkv, void* q_att,
@@ -369,16 +368,10 @@ hipError_t launch_proj_qkv(int kind, const void* x, const void* gamma, const voi
   p.w = static_cast<const uint16_t*>(w);
   p.T = T;
   p.K = kHidden;
-  p.rpw = kind == 0 ? 8 : 4;                 // DSA: 298 workgroups, SWA: 320
+  p.rpw = kind == 0 ? 16 : 8;                // DSA: 149 workgroups, SWA: 160 (one per CU)
   uint8_t* w8 = static_cast<uint8_t*>(ws);
   p.kictr = reinterpret_cast<uint32_t*>(w8) + ctl::kDone;
   p.kistage = reinterpret_cast<float*>(w8 + kWsKiStage);
-  uint16_t* y = reinterpret_cast<uint16_t*>(w8 + kWsY);
-  float2* r128 = reinterpret_cast<float2*>(w8 + kWsRope128);
-  float2* r64 = reinterpret_cast<float2*>(w8 + kWsRope64);
-  p.y = y;
-  p.rope128 = r128;
-  p.rope64 = r64;
   p.gamma = static_cast<const uint16_t*>(gamma);
   p.eps = eps;
   p.theta = theta;
@@ -393,12 +386,11 @@ hipError_t launch_proj_qkv(int kind, const void* x, const void* gamma, const voi
   p.ring_cap = ring_cap;
   p.kidx = static_cast<uint8_t*>(kidx);
   p.kidx_scale = kidx_scale;
-  hipLaunchKernelGGL(norm_rope_kernel, dim3(T + 1), dim3(kProjThreads), 0, st, p.x, p.gamma, T, eps, theta,
-                     pos0, y, r128, r64);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
   const dim3 grid(proj_blocks(kind, p.rpw)), block(kProjThreads);
   // per-lane fragments: K / 8 waves / 4 lane groups / 8 = 16
+#ifdef DSA_TRACE
+  p.trace = dsa_trace_buffer() ? dsa_trace_buffer() + 512 * 16 : nullptr;   // rows 512.. of the buffer
+#endif
   hipLaunchKernelGGL((proj_kernel<0, 16>), grid, block, 0, st, p);
   return hipGetLastError();
 }

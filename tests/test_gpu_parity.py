@@ -327,7 +327,7 @@ def test_sparse_attention_fp8_values_all_codes(dsa):
 
 
 @pytest.mark.parametrize("pos0,T,window,cap", [(5000, 8, 128, 135), (3, 4, 128, 140), (1000, 1, 1, 8),
-                                               (70, 8, 128, 256)])
+                                               (70, 8, 128, 256), (5000, 8, 300, 320), (200, 3, 129, 140)])
 def test_swa_vs_oracle(dsa, pos0, T, window, cap):
     g = np.random.default_rng(pos0)
     Kr = synth.to_bf16_bits(g.standard_normal((cap, 128)).astype(np.float32))

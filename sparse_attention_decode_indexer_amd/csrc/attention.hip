@@ -40,6 +40,7 @@ struct AttnParams {
   const float* sink;      // [8] natural-log logits or nullptr
   void* out;
   int out_f32;
+  uint64_t* trace;        // profiling builds: [blocks][16] phase timestamps
   float* part;            // [T][nsplit][8][kPartStride]
   uint32_t* ctr;          // [T] counters, stride 64 words
   int nsplit;
@@ -76,9 +77,13 @@ DSA_DEV void store_out(const AttnParams& p, int t, int h, int d4, float (&o)[4],
   }
 }
 
-template <int KVDT, int MODE, int ROWS>
-__global__ void __launch_bounds__(kAttnThreads) attn_kernel(AttnParams p) {
-  static_assert(ROWS % 64 == 0 && ROWS <= kAttnThreads, "64-row blocks, one list entry per thread");
+// NT threads: the first 256 are (head = tid / 32, 4 dims); with NT = 1024 the P.V product
+// is split over 4 row groups whose partial sums are added in group order.
+template <int KVDT, int MODE, int ROWS, int NT>
+__global__ void __launch_bounds__(NT) attn_kernel(AttnParams p) {
+  static_assert(ROWS % 64 == 0 && ROWS <= NT && NT % kAttnThreads == 0, "64-row blocks, one list entry per thread");
+  constexpr int NW = NT / 64;                 // waves
+  constexpr int G = NT / kAttnThreads;        // P.V row groups
   using SH = AttnShared<KVDT, ROWS>;
   __shared__ SH sh;
   constexpr int RB = SH::RB;
@@ -87,6 +92,9 @@ __global__ void __launch_bounds__(kAttnThreads) attn_kernel(AttnParams p) {
   const int wave = tid >> 6;
   const int split = blockIdx.x;
   const int t = blockIdx.y;
+  uint64_t* trace = p.trace ? p.trace + (size_t)(t * gridDim.x) * 16 : nullptr;   // row = block index
+  (void)trace;
+  DSA_MARK(trace, 0);
   // ---- row list of this split
   if (tid < ROWS) {
     const int e = split * ROWS + tid;
@@ -108,15 +116,16 @@ __global__ void __launch_bounds__(kAttnThreads) attn_kernel(AttnParams p) {
     }
   }
   __syncthreads();
+  DSA_MARK(trace, 1);
   // ---- stage K and V rows (16-byte chunks, one row per RB/16 consecutive threads)
   {
     // every load is issued before any is consumed; invalid rows read row 0 and are zeroed
     constexpr int CPR = RB / 16;
-    constexpr int NCH = ROWS * CPR / kAttnThreads;
+    constexpr int NCH = ROWS * CPR / NT;
     uint4 kv[NCH], vv[NCH];
 #pragma unroll
     for (int u = 0; u < NCH; ++u) {
-      const int c = tid + u * kAttnThreads;
+      const int c = tid + u * NT;
       const int row = c / CPR, col = c % CPR;
       const int64_t r = sh.rows[row];
       const int64_t rr = r >= 0 ? r : 0;
@@ -125,7 +134,7 @@ __global__ void __launch_bounds__(kAttnThreads) attn_kernel(AttnParams p) {
     }
 #pragma unroll
     for (int u = 0; u < NCH; ++u) {
-      const int c = tid + u * kAttnThreads;
+      const int c = tid + u * NT;
       const int row = c / CPR, col = c % CPR;
       const bool ok = sh.rows[row] >= 0;
       *reinterpret_cast<uint4*>(&sh.kst[row * SH::KSTRIDE + col * 16]) = ok ? kv[u] : make_uint4(0u, 0u, 0u, 0u);
@@ -145,11 +154,14 @@ __global__ void __launch_bounds__(kAttnThreads) attn_kernel(AttnParams p) {
     }
   }
   __syncthreads();
-  // ---- S = K q^T: wave w owns rows 64b + 16w .. +15 of each 64-row block b
+  DSA_MARK(trace, 2);
+  // ---- S = K q^T: wave w owns the 16-row blocks w, w + NW, ...
 #pragma unroll
-  for (int rb = 0; rb < ROWS / 64; ++rb) {
+  for (int ib = 0; ib < (ROWS / 16 + NW - 1) / NW; ++ib) {
+    const int rb16 = wave + ib * NW;
+    if (rb16 >= ROWS / 16) break;
     f32x4_t acc = {};
-    const int row = rb * 64 + wave * 16 + (lane & 15);
+    const int row = rb16 * 16 + (lane & 15);
 #pragma unroll
     for (int kb = 0; kb < 4; ++kb) {
       Frag8 a;
@@ -170,7 +182,7 @@ __global__ void __launch_bounds__(kAttnThreads) attn_kernel(AttnParams p) {
     if (h < kHq) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const int rr = rb * 64 + wave * 16 + (lane >> 4) * 4 + i;
+        const int rr = rb16 * 16 + (lane >> 4) * 4 + i;
         float z = acc[i];
         if (KVDT == 1) z *= sh.kscl[rr];
         sh.s[h][rr] = (sh.rows[rr] >= 0) ? z * p.sm_log2 : -__builtin_inff();
@@ -178,12 +190,15 @@ __global__ void __launch_bounds__(kAttnThreads) attn_kernel(AttnParams p) {
     }
   }
   __syncthreads();
+  DSA_MARK(trace, 3);
   // ---- softmax of the split: thread (h = tid/32, j = tid%32) holds rows j, j+32, ...
   constexpr int RPT = ROWS / 32;
-  const int h = tid >> 5;
+  const int h = (tid >> 5) & (kHq - 1);
   const int jj = tid & 31;
-  float m, l;
-  {
+  const int grp = tid / kAttnThreads;         // P.V row group
+  const bool lead = grp == 0;
+  float m = -__builtin_inff(), l = 0.0f;
+  if (lead) {
     float z[RPT];
 #pragma unroll
     for (int i = 0; i < RPT; ++i) z[i] = sh.s[h][jj + 32 * i];
@@ -211,27 +226,53 @@ __global__ void __launch_bounds__(kAttnThreads) attn_kernel(AttnParams p) {
     }
   }
   __syncthreads();
+  DSA_MARK(trace, 4);
   // ---- acc[h][d4..d4+3] = sum_j p[h][j] * V[j][d4..d4+3]
   const int d4 = jj * 4;
   float acc[4] = {0.0f, 0.0f, 0.0f, 0.0f};
-  for (int j = 0; j < ROWS; ++j) {
-    const float pj = sh.s[h][j];
-    float v[4];
-    if constexpr (KVDT == 0) {
-      const uint2 raw = *reinterpret_cast<const uint2*>(&sh.vst[j * RB + d4 * 2]);
-      v[0] = __uint_as_float(raw.x << 16);
-      v[1] = __uint_as_float(raw.x & 0xffff0000u);
-      v[2] = __uint_as_float(raw.y << 16);
-      v[3] = __uint_as_float(raw.y & 0xffff0000u);
-    } else {
-      const uint32_t raw = *reinterpret_cast<const uint32_t*>(&sh.vst[j * RB + d4]);
-      auto lo = __builtin_amdgcn_cvt_pk_f32_fp8((int)raw, false);
-      auto hi = __builtin_amdgcn_cvt_pk_f32_fp8((int)raw, true);
-      v[0] = lo[0]; v[1] = lo[1]; v[2] = hi[0]; v[3] = hi[1];
+  // rows in groups of 8: the group's LDS reads are issued together
+  constexpr int PVU = 8;
+  constexpr int RG = ROWS / G;                // rows per group
+  for (int j0 = grp * RG; j0 < (grp + 1) * RG; j0 += PVU) {
+    float pj[PVU];
+    float v[PVU][4];
+#pragma unroll
+    for (int u = 0; u < PVU; ++u) {
+      const int j = j0 + u;
+      pj[u] = sh.s[h][j];
+      if constexpr (KVDT == 0) {
+        const uint2 raw = *reinterpret_cast<const uint2*>(&sh.vst[j * RB + d4 * 2]);
+        v[u][0] = __uint_as_float(raw.x << 16);
+        v[u][1] = __uint_as_float(raw.x & 0xffff0000u);
+        v[u][2] = __uint_as_float(raw.y << 16);
+        v[u][3] = __uint_as_float(raw.y & 0xffff0000u);
+      } else {
+        const uint32_t raw = *reinterpret_cast<const uint32_t*>(&sh.vst[j * RB + d4]);
+        auto lo = __builtin_amdgcn_cvt_pk_f32_fp8((int)raw, false);
+        auto hi = __builtin_amdgcn_cvt_pk_f32_fp8((int)raw, true);
+        v[u][0] = lo[0]; v[u][1] = lo[1]; v[u][2] = hi[0]; v[u][3] = hi[1];
+      }
     }
 #pragma unroll
-    for (int i = 0; i < 4; ++i) acc[i] = fmaf(pj, v[i], acc[i]);
+    for (int u = 0; u < PVU; ++u) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) acc[i] = fmaf(pj[u], v[u][i], acc[i]);
+    }
   }
+  if constexpr (G > 1) {
+    // group partials through LDS (the K staging area is free now), added in group order
+    float* pv = reinterpret_cast<float*>(sh.kst);                     // [G][kHq][kD]
+    *reinterpret_cast<float4*>(&pv[(grp * kHq + h) * kD + d4]) = make_float4(acc[0], acc[1], acc[2], acc[3]);
+    __syncthreads();
+    if (lead) {
+#pragma unroll
+      for (int g = 1; g < G; ++g) {
+        const float4 q4 = *reinterpret_cast<const float4*>(&pv[(g * kHq + h) * kD + d4]);
+        acc[0] += q4.x; acc[1] += q4.y; acc[2] += q4.z; acc[3] += q4.w;
+      }
+    }
+  }
+  DSA_MARK(trace, 5);
   float sink2 = -__builtin_inff();
   if (p.sink) sink2 = p.sink[h] * 1.4426950408889634f;
   if (p.nsplit == 1) {
@@ -248,24 +289,29 @@ __global__ void __launch_bounds__(kAttnThreads) attn_kernel(AttnParams p) {
       }
       if (sink2 != -__builtin_inff()) den += exp2f(sink2 - M);
     }
-    store_out(p, t, h, d4, o, den);
+    if (lead) store_out(p, t, h, d4, o, den);
+    DSA_MARK(trace, 6);
     return;
   }
   // ---- publish the split's partial
   float* part = p.part + (((size_t)t * p.nsplit + split) * kHq + h) * kPartStride;
-  if (jj == 0)
-    ast64(reinterpret_cast<uint64_t*>(part), (uint64_t)__float_as_uint(m) | ((uint64_t)__float_as_uint(l) << 32));
-  ast64(reinterpret_cast<uint64_t*>(part + 4 + d4),
-        (uint64_t)__float_as_uint(acc[0]) | ((uint64_t)__float_as_uint(acc[1]) << 32));
-  ast64(reinterpret_cast<uint64_t*>(part + 6 + d4),
-        (uint64_t)__float_as_uint(acc[2]) | ((uint64_t)__float_as_uint(acc[3]) << 32));
+  if (lead) {
+    if (jj == 0)
+      ast64(reinterpret_cast<uint64_t*>(part), (uint64_t)__float_as_uint(m) | ((uint64_t)__float_as_uint(l) << 32));
+    ast64(reinterpret_cast<uint64_t*>(part + 4 + d4),
+          (uint64_t)__float_as_uint(acc[0]) | ((uint64_t)__float_as_uint(acc[1]) << 32));
+    ast64(reinterpret_cast<uint64_t*>(part + 6 + d4),
+          (uint64_t)__float_as_uint(acc[2]) | ((uint64_t)__float_as_uint(acc[3]) << 32));
+  }
   vm_wait_all();
   __syncthreads();
   if (tid == 0) sh.last = (aadd(p.ctr + 64 * t, 1u) == (uint32_t)p.nsplit - 1u) ? 1u : 0u;
   __syncthreads();
+  DSA_MARK(trace, 6);
   if (!sh.last) return;
+  DSA_MARK(trace, 7);
   // ---- merge of all splits of token t, in split order.  Split statistics first (one
-  // coherent load per thread), then each thread's accumulators with 16 loads in flight.
+  // coherent load per thread), then each thread's accumulators, 16 loads in flight.
   const float* pt = p.part + (size_t)t * p.nsplit * kHq * kPartStride;
   if (tid < p.nsplit * kHq) {
     const uint64_t ml = ald64(reinterpret_cast<const uint64_t*>(pt + (size_t)tid * kPartStride));
@@ -305,7 +351,8 @@ __global__ void __launch_bounds__(kAttnThreads) attn_kernel(AttnParams p) {
     }
     if (sink2 != -__builtin_inff()) den += exp2f(sink2 - M);
   }
-  store_out(p, t, h, d4, o, den);
+  if (lead) store_out(p, t, h, d4, o, den);
+  DSA_MARK(trace, 8);
   if (tid == 0) ast(p.ctr + 64 * t, 0u);
 }
 
@@ -346,12 +393,15 @@ hipError_t launch_attention(int mode, int kvdt, const void* q, const void* kc, c
   uint8_t* w8 = static_cast<uint8_t*>(ws);
   p.ctr = reinterpret_cast<uint32_t*>(w8) + ctl::kDone;
   p.part = reinterpret_cast<float*>(w8 + ctl::kBytes);
-  const dim3 grid(p.nsplit, T), block(kAttnThreads);
+#ifdef DSA_TRACE
+  p.trace = dsa_trace_buffer() ? dsa_trace_buffer() + 768 * 16 : nullptr;   // rows 768.. of the buffer
+#endif
+  const dim3 grid(p.nsplit, T);
   if (mode == 0) {
-    if (kvdt == 0) hipLaunchKernelGGL((attn_kernel<0, 0, kSplitRows>), grid, block, 0, st, p);
-    else hipLaunchKernelGGL((attn_kernel<1, 0, kSplitRows>), grid, block, 0, st, p);
+    if (kvdt == 0) hipLaunchKernelGGL((attn_kernel<0, 0, kSplitRows, kAttnThreads>), grid, dim3(kAttnThreads), 0, st, p);
+    else hipLaunchKernelGGL((attn_kernel<1, 0, kSplitRows, kAttnThreads>), grid, dim3(kAttnThreads), 0, st, p);
   } else {
-    hipLaunchKernelGGL((attn_kernel<0, 1, kSwaRows>), grid, block, 0, st, p);
+    hipLaunchKernelGGL((attn_kernel<0, 1, kSwaRows, 4 * kAttnThreads>), grid, dim3(4 * kAttnThreads), 0, st, p);
   }
   return hipGetLastError();
 }

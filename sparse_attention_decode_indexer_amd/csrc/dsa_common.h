@@ -41,6 +41,14 @@ DSA_DEV uint16_t f32_to_bf16(float f) {
 
 DSA_DEV float round_bf16(float f) { return bf16_to_f32(f32_to_bf16(f)); }
 
+// two fp32 -> (lo, hi) bf16 pair in one word, each rounded to nearest even
+DSA_DEV uint32_t pack_bf16x2(float lo, float hi) {
+  typedef float f32x2v __attribute__((ext_vector_type(2)));
+  typedef __bf16 bf16x2v __attribute__((ext_vector_type(2)));
+  const bf16x2v b = __builtin_convertvector(f32x2v{lo, hi}, bf16x2v);
+  return __builtin_bit_cast(uint32_t, b);
+}
+
 // OCP e4m3fn code -> fp32, exact (integer construction of the IEEE bits)
 DSA_DEV float e4m3_to_f32(uint32_t c) {
   uint32_t s = (c & 0x80u) << 24;

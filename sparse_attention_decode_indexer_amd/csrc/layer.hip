@@ -14,7 +14,8 @@
 // M = T <= 8 tokens makes these weight-streaming products.  One workgroup owns RPW rows
 // of W (RPW = 4, 8 or 16, chosen so the launch covers the chip) over the full K; its
 // eight waves split K.  A v_mfma_f32_16x16x32_bf16 tile takes the rows on the M side
-// (rows >= RPW are zero) and the tokens on the N side (padded to 16).  Each lane streams
+// (rows >= RPW repeat row 0 and are not read) and the tokens on the N side (padded to
+// 16).  Each lane streams
 // its k chunks of one weight row straight into registers; the normalised activations
 // sit in LDS.  The eight partial tiles are summed in wave order.
 #include "dsa_common.h"
@@ -83,7 +84,6 @@ struct ProjParams {
   const uint16_t* x;        // [T][4096] bf16 (QKV: layer input; OUT: residual input)
   const uint16_t* w;        // [N][K] bf16
   int T;
-  int K;                    // reduction length (4096 QKV, 1024 OUT)
   int rpw;                  // weight rows per workgroup
   // QKV
   const uint16_t* gamma;
@@ -127,8 +127,9 @@ __global__ void __launch_bounds__(kProjThreads) proj_kernel(ProjParams p) {
   const int lane = tid & 63;
   const int wave = tid >> 6;
   const int b = blockIdx.x;
-  const int K = p.K;
-  const int Kw = K / kProjWaves;             // per wave (= NSTEP * 32)
+  constexpr int K = MODE == 0 ? kHidden : kHq * kD;    // reduction length (compile time: no divisions)
+  constexpr int Kw = K / kProjWaves;                     // per wave (= NSTEP * 32)
+  static_assert(Kw == NSTEP * 32, "each wave covers its k range in NSTEP steps of 32");
   const int kw0 = wave * Kw;
   const int T = p.T;
   const int rpw = p.rpw;
@@ -164,17 +165,30 @@ __global__ void __launch_bounds__(kProjThreads) proj_kernel(ProjParams p) {
   }
   uint4 gv = make_uint4(0u, 0u, 0u, 0u);
   if (MODE == 0) gv = reinterpret_cast<const uint4*>(p.gamma)[tid];   // gamma[8 tid .. 8 tid + 8)
-  // only the lanes of real rows load weights (the MFMA's unused rows stay zero)
+  // Every lane loads (unconditional loads keep the wait counts exact): lanes beyond the
+  // real rows repeat row 0's addresses, which the memory pipeline merges, and the MFMA
+  // rows they feed are never read.
   Frag8 wf[NSTEP];
-  if (lrow < rpw) {
+  {
     const uint4* wp = reinterpret_cast<const uint4*>(p.w + (size_t)wrow * K + kw0) + (lane >> 4);
 #pragma unroll
     for (int i = 0; i < NSTEP; ++i) wf[i].u = wp[4 * i];
-  } else {
-#pragma unroll
-    for (int i = 0; i < NSTEP; ++i) wf[i].u = make_uint4(0u, 0u, 0u, 0u);
   }
   DSA_MARK(trace, 1);
+  // rotary cos/sin of this block's pairs at the block's positions (first: it needs no
+  // loaded data, so it runs while the loads are in flight): angle
+  // (pos0 + t) * theta^(-2i/d) formed in fp64, cos/sin rounded to fp32
+  if (MODE == 0 && bi.rot_d && tid < 8 * kMaxT) {
+    const int t = tid >> 3, r = tid & 7;
+    if (t < T && r < rpw / 2) {
+      const int i = bi.i0 + r;
+      const double inv = pow((double)p.theta, -2.0 * (double)i / (double)bi.rot_d);
+      const double ang = (double)(p.pos0 + t) * inv;
+      sh.rc[t][r] = (float)cos(ang);
+      sh.rs[t][r] = (float)sin(ang);
+    }
+  }
+  DSA_MARK(trace, 5);
   if (MODE == 0) {
     // Input RMSNorm while the weights stream in: thread tid holds elements
     // [8 tid, 8 tid + 8) of every token.  Per token: squares summed in element order per
@@ -196,6 +210,7 @@ __global__ void __launch_bounds__(kProjThreads) proj_kernel(ProjParams p) {
       scr[t * kProjThreads + tid] = a2;
     }
     __syncthreads();
+    DSA_MARK(trace, 6);
     {
       const float4 q0 = *reinterpret_cast<const float4*>(&scr[wave * kProjThreads + lane * 8]);
       const float4 q1 = *reinterpret_cast<const float4*>(&scr[wave * kProjThreads + lane * 8 + 4]);
@@ -205,6 +220,7 @@ __global__ void __launch_bounds__(kProjThreads) proj_kernel(ProjParams p) {
       if (lane == 0) sh.rnorm[wave] = 1.0f / sqrtf(a / (float)kHidden + p.eps);
     }
     __syncthreads();
+    DSA_MARK(trace, 7);
     const uint32_t g4[4] = {gv.x, gv.y, gv.z, gv.w};
 #pragma unroll
     for (int t = 0; t < kMaxT; ++t) {
@@ -215,7 +231,7 @@ __global__ void __launch_bounds__(kProjThreads) proj_kernel(ProjParams p) {
       for (int q = 0; q < 4; ++q) {
         const float y0 = (__uint_as_float(x4[q] << 16) * r) * __uint_as_float(g4[q] << 16);
         const float y1 = (__uint_as_float(x4[q] & 0xffff0000u) * r) * __uint_as_float(g4[q] & 0xffff0000u);
-        o4[q] = (uint32_t)f32_to_bf16(y0) | ((uint32_t)f32_to_bf16(y1) << 16);
+        o4[q] = pack_bf16x2(y0, y1);
       }
       *reinterpret_cast<uint4*>(&sh.xs[t][8 * tid]) = t < T ? make_uint4(o4[0], o4[1], o4[2], o4[3])
                                                             : make_uint4(0u, 0u, 0u, 0u);
@@ -231,18 +247,6 @@ __global__ void __launch_bounds__(kProjThreads) proj_kernel(ProjParams p) {
         const int t = c / (K / 8), kk = (c % (K / 8)) * 8;
         *reinterpret_cast<uint4*>(&sh.xs[t][kk]) = t < T ? v[u] : make_uint4(0u, 0u, 0u, 0u);
       }
-    }
-  }
-  // rotary cos/sin of this block's pairs at the block's positions: angle
-  // (pos0 + t) * theta^(-2i/d) formed in fp64, cos/sin rounded to fp32
-  if (MODE == 0 && bi.rot_d && tid < 8 * kMaxT) {
-    const int t = tid >> 3, r = tid & 7;
-    if (t < T && r < rpw / 2) {
-      const int i = bi.i0 + r;
-      const double inv = pow((double)p.theta, -2.0 * (double)i / (double)bi.rot_d);
-      const double ang = (double)(p.pos0 + t) * inv;
-      sh.rc[t][r] = (float)cos(ang);
-      sh.rs[t][r] = (float)sin(ang);
     }
   }
   __syncthreads();
@@ -367,7 +371,6 @@ hipError_t launch_proj_qkv(int kind, const void* x, const void* gamma, const voi
   p.x = static_cast<const uint16_t*>(x);
   p.w = static_cast<const uint16_t*>(w);
   p.T = T;
-  p.K = kHidden;
   p.rpw = kind == 0 ? 16 : 8;                // DSA: 149 workgroups, SWA: 160 (one per CU)
   uint8_t* w8 = static_cast<uint8_t*>(ws);
   p.kictr = reinterpret_cast<uint32_t*>(w8) + ctl::kDone;
@@ -404,7 +407,6 @@ hipError_t launch_proj_out(const void* o, const void* w_o, const void* x, void* 
   p.o = static_cast<const uint16_t*>(o);
   p.xout = static_cast<uint16_t*>(xout);
   p.T = T;
-  p.K = kHq * kD;
   p.rpw = 16;
   const dim3 grid(kHidden / 16), block(kProjThreads);
   // 1024 / 8 waves / 4 lane groups / 8 = 4

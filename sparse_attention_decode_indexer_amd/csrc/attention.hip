@@ -43,6 +43,8 @@ struct AttnParams {
   uint64_t* trace;        // profiling builds: [blocks][16] phase timestamps
   float* part;            // [T][nsplit][8][kPartStride]
   uint32_t* ctr;          // [T] counters, stride 64 words
+  uint32_t* ctlw;         // control words of the workspace
+  int dist;               // 1: every split merges a slice (all workgroups co-resident)
   int nsplit;
 };
 
@@ -92,6 +94,8 @@ __global__ void __launch_bounds__(NT) attn_kernel(AttnParams p) {
   const int wave = tid >> 6;
   const int split = blockIdx.x;
   const int t = blockIdx.y;
+  // launch counter of token t (tags of the split flags); read before any flag is written
+  const uint32_t epoch = p.dist ? ald(p.ctlw + ctl::kEpochT + 16 * t) : 0u;
   uint64_t* trace = p.trace ? p.trace + (size_t)(t * gridDim.x) * 16 : nullptr;   // row = block index
   (void)trace;
   DSA_MARK(trace, 0);
@@ -305,6 +309,78 @@ __global__ void __launch_bounds__(NT) attn_kernel(AttnParams p) {
   }
   vm_wait_all();
   __syncthreads();
+  if (p.dist) {
+    // Every split of token t is resident: publish a tagged flag, wait for all of the
+    // token's flags, then merge output slices split, split + nsplit, ... (32 outputs =
+    // head slice >> 2, dims 32 (slice & 3) ..) in split order -- the same operations, in
+    // the same order, as the single-merger path below.
+    const uint32_t tag = epoch + 1u;
+    if (tid == 0) ast(p.ctlw + ctl::kFlags + 32 * t + split, tag);
+    if (wave == 0) {
+      const int ns = p.nsplit;
+      const uint32_t* fl = p.ctlw + ctl::kFlags + 32 * t;
+      const uint64_t t0 = __builtin_amdgcn_s_memrealtime();
+      while (true) {
+        const uint32_t v = ald(fl + (lane < ns ? lane : ns - 1));
+        if (__ballot(v != tag) == 0ull) break;
+        __builtin_amdgcn_s_sleep(1);
+        if (__builtin_amdgcn_s_memrealtime() - t0 > kSpinLimit) {
+          if (lane == 0) ast(p.ctlw + ctl::kError, 1u);
+          break;
+        }
+      }
+      // every split of token t has read the counter: advance it
+      if (split == 0 && lane == 0) ast(p.ctlw + ctl::kEpochT + 16 * t, next_epoch(epoch));
+      DSA_MARK(trace, 7);
+      const float* pt = p.part + (size_t)t * ns * kHq * kPartStride;
+      const int jl = lane & 31;
+      for (int slice = split; slice < 32; slice += ns) {
+        const int hh = slice >> 2, d0 = (slice & 3) * 32;
+        // split statistics: lane j holds split j's (m, l) of head hh
+        const int jc = jl < ns ? jl : ns - 1;
+        const uint64_t ml = ald64(reinterpret_cast<const uint64_t*>(pt + ((size_t)jc * kHq + hh) * kPartStride));
+        // accumulators: lane i (< 32) holds dim d0 + i of every split
+        float a[32];
+#pragma unroll
+        for (int j = 0; j < 32; ++j) {
+          const int js = j < ns ? j : ns - 1;
+          a[j] = aldf(pt + ((size_t)js * kHq + hh) * kPartStride + 4 + d0 + jl);
+        }
+        const float mj = jl < ns ? __uint_as_float((uint32_t)ml) : -__builtin_inff();
+        float M = mj;
+#pragma unroll
+        for (int d = 16; d >= 1; d >>= 1) M = fmaxf(M, __shfl_xor(M, d, 64));
+        float s2 = -__builtin_inff();
+        if (p.sink) s2 = p.sink[hh] * 1.4426950408889634f;
+        M = fmaxf(M, s2);
+        float den = 0.0f;
+        float o[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+        if (M != -__builtin_inff()) {
+          const float lj = __uint_as_float((uint32_t)(ml >> 32));
+          const float scj = exp2f(mj - M);       // lane j: split j's rescale factor
+#pragma unroll
+          for (int j = 0; j < 32; ++j) {
+            if (j >= ns) break;
+            const float ms = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(mj), j));
+            if (ms == -__builtin_inff()) continue;
+            const float sc = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(scj), j));
+            const float ls = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(lj), j));
+            den = fmaf(ls, sc, den);
+            o[0] = fmaf(a[j], sc, o[0]);
+          }
+          if (s2 != -__builtin_inff()) den += exp2f(s2 - M);
+        }
+        if (lane < 32) {
+          const float r = den > 0.0f ? o[0] / den : 0.0f;
+          const size_t ob = ((size_t)t * kHq + hh) * kD + d0 + lane;
+          if (p.out_f32) static_cast<float*>(p.out)[ob] = r;
+          else static_cast<uint16_t*>(p.out)[ob] = f32_to_bf16(r);
+        }
+      }
+      DSA_MARK(trace, 8);
+    }
+    return;
+  }
   if (tid == 0) sh.last = (aadd(p.ctr + 64 * t, 1u) == (uint32_t)p.nsplit - 1u) ? 1u : 0u;
   __syncthreads();
   DSA_MARK(trace, 6);
@@ -371,7 +447,8 @@ int attn_splits(int mode, int list_len) {
 hipError_t launch_attention(int mode, int kvdt, const void* q, const void* kc, const void* vc,
                             const float* ks, const float* vs, const int32_t* idx, int k, int T,
                             int64_t L, int64_t ring_cap, int64_t pos0, int window, float sm_scale,
-                            const float* sink, void* out, int out_f32, void* ws, hipStream_t st) {
+                            const float* sink, void* out, int out_f32, void* ws, int num_cu,
+                            hipStream_t st) {
   AttnParams p{};
   p.q = static_cast<const uint16_t*>(q);
   p.kc = static_cast<const uint8_t*>(kc);
@@ -392,12 +469,19 @@ hipError_t launch_attention(int mode, int kvdt, const void* q, const void* kc, c
   p.nsplit = attn_splits(mode, mode == 0 ? k : window);
   uint8_t* w8 = static_cast<uint8_t*>(ws);
   p.ctr = reinterpret_cast<uint32_t*>(w8) + ctl::kDone;
+  p.ctlw = reinterpret_cast<uint32_t*>(w8);
   p.part = reinterpret_cast<float*>(w8 + ctl::kBytes);
 #ifdef DSA_TRACE
   p.trace = dsa_trace_buffer() ? dsa_trace_buffer() + 768 * 16 : nullptr;   // rows 768.. of the buffer
 #endif
   const dim3 grid(p.nsplit, T);
   if (mode == 0) {
+    // split merge spread over the splits when every workgroup of the launch is resident
+    int per_cu = 0;
+    void* fn = kvdt == 0 ? (void*)attn_kernel<0, 0, kSplitRows, kAttnThreads>
+                         : (void*)attn_kernel<1, 0, kSplitRows, kAttnThreads>;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, fn, kAttnThreads, 0) != hipSuccess) per_cu = 0;
+    p.dist = (int64_t)per_cu * num_cu >= (int64_t)p.nsplit * T ? 1 : 0;
     if (kvdt == 0) hipLaunchKernelGGL((attn_kernel<0, 0, kSplitRows, kAttnThreads>), grid, dim3(kAttnThreads), 0, st, p);
     else hipLaunchKernelGGL((attn_kernel<1, 0, kSplitRows, kAttnThreads>), grid, dim3(kAttnThreads), 0, st, p);
   } else {

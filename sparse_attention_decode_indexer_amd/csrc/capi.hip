@@ -195,7 +195,8 @@ dsa_status_t dsa_sparse_attn(const void* q, const void* k_cache, const void* v_c
       (sink && !aligned16(sink)))
     return DSA_ERR_ALIGN;
   hipError_t e = dsa::launch_attention(0, fp8, q, k_cache, v_cache, k_scale, v_scale, idx, k, T, L, 0, 0, 0,
-                                       sm_scale, sink, out, out_dtype == DSA_FP32, ws, (hipStream_t)stream);
+                                       sm_scale, sink, out, out_dtype == DSA_FP32, ws, device_cus(),
+                                       (hipStream_t)stream);
   return e == hipSuccess ? DSA_OK : hip_fail(e, "dsa_sparse_attn");
 }
 
@@ -213,7 +214,7 @@ dsa_status_t swa_attn(const void* q, const void* k_ring, const void* v_ring, int
     return DSA_ERR_ALIGN;
   hipError_t e = dsa::launch_attention(1, 0, q, k_ring, v_ring, nullptr, nullptr, nullptr, 0, T, 0, ring_cap,
                                        pos0, window, sm_scale, sink, out, out_dtype == DSA_FP32, ws,
-                                       (hipStream_t)stream);
+                                       device_cus(), (hipStream_t)stream);
   return e == hipSuccess ? DSA_OK : hip_fail(e, "swa_attn");
 }
 
@@ -263,11 +264,11 @@ dsa_status_t dsa_layer_step(const dsa_layer_config_t* cfg, const dsa_layer_weigh
                            cfg->top_k, idx, nullptr, w8 + lw.sel, ncu, st);
     if (e != hipSuccess) return hip_fail(e, "dsa_layer_step: index/top-k");
     e = dsa::launch_attention(0, 0, q_att, cache->k, cache->v, nullptr, nullptr, idx, cfg->top_k, T, L, 0, 0,
-                              0, cfg->sm_scale, cfg->sink, attn_out, 0, w8 + lw.attn, st);
+                              0, cfg->sm_scale, cfg->sink, attn_out, 0, w8 + lw.attn, ncu, st);
   } else {
     e = dsa::launch_attention(1, 0, q_att, cache->k, cache->v, nullptr, nullptr, nullptr, 0, T, 0,
                               cache->capacity, pos0, cfg->window, cfg->sm_scale, cfg->sink, attn_out, 0,
-                              w8 + lw.attn, st);
+                              w8 + lw.attn, ncu, st);
   }
   if (e != hipSuccess) return hip_fail(e, "dsa_layer_step: attention");
   e = dsa::launch_proj_out(attn_out, w->w_o, x_in, x_out, T, w8 + lw.proj, st);

@@ -208,6 +208,8 @@ namespace ctl {
 constexpr int kError = 640;      // sticky error word (1 = a wait timed out)
 constexpr int kEpoch = 768;      // launch counter (tags of the tagged slots)
 constexpr int kDone = 1024;      // [8] per-token completion counters, stride 64
+constexpr int kEpochT = 1536;    // [8] per-token launch counters, stride 16
+constexpr int kFlags = 2048;     // [8][32] per-(token, split) tagged completion flags
 constexpr int kWords = 3072;
 constexpr size_t kBytes = 16384;
 }  // namespace ctl

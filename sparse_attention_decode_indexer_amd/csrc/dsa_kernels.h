@@ -33,7 +33,8 @@ int attn_splits(int mode, int list_len);   // mode 0: index list, 1: sliding win
 hipError_t launch_attention(int mode, int kvdt, const void* q, const void* kc, const void* vc,
                             const float* ks, const float* vs, const int32_t* idx, int k, int T,
                             int64_t L, int64_t ring_cap, int64_t pos0, int window, float sm_scale,
-                            const float* sink, void* out, int out_f32, void* ws, hipStream_t st);
+                            const float* sink, void* out, int out_f32, void* ws, int num_cu,
+                            hipStream_t st);
 
 size_t proj_workspace_bytes();
 hipError_t launch_proj_qkv(int kind, const void* x, const void* gamma, const void* w, int T,

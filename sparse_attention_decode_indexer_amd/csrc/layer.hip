@@ -18,6 +18,8 @@
 // 16).  Each lane streams
 // its k chunks of one weight row straight into registers; the normalised activations
 // sit in LDS.  The eight partial tiles are summed in wave order.
+#include <cmath>
+
 #include "dsa_common.h"
 #include "dsa_kernels.h"
 
@@ -106,6 +108,9 @@ struct ProjParams {
   const uint16_t* o;        // [T][1024] bf16 attention output
   uint16_t* xout;           // [T][4096]
   uint64_t* trace;          // profiling builds: [blocks][16] phase timestamps
+  // rotary inverse frequencies theta^(-2i/d) in fp64, formed on the host: [0, 64) for
+  // width-128 heads, [64, 96) for width-64 indexer heads
+  double inv_freq[kD / 2 + kDI / 2];
 };
 
 constexpr int kXsStride = kHidden + 8;      // padded LDS row: rows fall in different banks
@@ -182,10 +187,12 @@ __global__ void __launch_bounds__(kProjThreads) proj_kernel(ProjParams p) {
     const int t = tid >> 3, r = tid & 7;
     if (t < T && r < rpw / 2) {
       const int i = bi.i0 + r;
-      const double inv = pow((double)p.theta, -2.0 * (double)i / (double)bi.rot_d);
+      const double inv = bi.rot_d == kD ? p.inv_freq[i] : p.inv_freq[kD / 2 + i];
       const double ang = (double)(p.pos0 + t) * inv;
-      sh.rc[t][r] = (float)cos(ang);
-      sh.rs[t][r] = (float)sin(ang);
+      double sv, cv;
+      sincos(ang, &sv, &cv);
+      sh.rc[t][r] = (float)cv;
+      sh.rs[t][r] = (float)sv;
     }
   }
   DSA_MARK(trace, 5);
@@ -378,6 +385,8 @@ hipError_t launch_proj_qkv(int kind, const void* x, const void* gamma, const voi
   p.gamma = static_cast<const uint16_t*>(gamma);
   p.eps = eps;
   p.theta = theta;
+  for (int i = 0; i < kD / 2; ++i) p.inv_freq[i] = std::pow((double)theta, -2.0 * (double)i / (double)kD);
+  for (int i = 0; i < kDI / 2; ++i) p.inv_freq[kD / 2 + i] = std::pow((double)theta, -2.0 * (double)i / (double)kDI);
   p.pos0 = pos0;
   p.qkv = static_cast<uint16_t*>(qkv);
   p.nproj = kind == 0 ? kNProjDSA : kNProjSWA;

@@ -360,13 +360,13 @@ __global__ void __launch_bounds__(NT) attn_kernel(AttnParams p) {
           const float scj = exp2f(mj - M);       // lane j: split j's rescale factor
 #pragma unroll
           for (int j = 0; j < 32; ++j) {
-            if (j >= ns) break;
             const float ms = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(mj), j));
-            if (ms == -__builtin_inff()) continue;
-            const float sc = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(scj), j));
-            const float ls = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(lj), j));
-            den = fmaf(ls, sc, den);
-            o[0] = fmaf(a[j], sc, o[0]);
+            if ((j < ns) & (ms != -__builtin_inff())) {     // splits in order; empty ones skipped
+              const float sc = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(scj), j));
+              const float ls = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(lj), j));
+              den = fmaf(ls, sc, den);
+              o[0] = fmaf(a[j], sc, o[0]);
+            }
           }
           if (s2 != -__builtin_inff()) den += exp2f(s2 - M);
         }

@@ -40,6 +40,8 @@ def parse():
     ap.add_argument("--T", type=int, default=8)
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
+    ap.add_argument("--eager", action="store_true",
+                    help="skip the HIP-graph replay timing (reported beside the direct-launch step)")
     ap.add_argument("--only", choices=["module", "index_topk", "copy"], default="module",
                     help="index_topk / copy: run only that kernel (for counter passes)")
     return ap.parse_args()
@@ -123,7 +125,8 @@ def main():
 
     ev_dsa = []
 
-    def step(i, record=False):
+    def step(i, record=False, st=None):
+        st = stream if st is None else st
         per = structs[i % len(structs)]
         xin = x0
         for li, (kind, w, c) in enumerate(per):
@@ -131,14 +134,14 @@ def main():
                 if record:
                     e0 = torch.cuda.Event(enable_timing=True)
                     e1 = torch.cuda.Event(enable_timing=True)
-                    e0.record(stream)
+                    e0.record(st)
                 dsa.dsa_layer_step(cfg_dsa, w, c, xin, xs[li], T, pos0, idx_out=idx, qkv_out=qkv, ws=ws_dsa,
-                                   stream=stream)
+                                   stream=st)
                 if record:
-                    e1.record(stream)
+                    e1.record(st)
                     ev_dsa.append((e0, e1))
             else:
-                dsa.dsa_layer_step(cfg_swa, w, c, xin, xs[li], T, pos0, ws=ws_swa, stream=stream)
+                dsa.dsa_layer_step(cfg_swa, w, c, xin, xs[li], T, pos0, ws=ws_swa, stream=st)
             xin = xs[li]
 
     # ------------------------------------------------------------------ dominant-kernel inputs
@@ -181,6 +184,8 @@ def main():
         return
 
     # ------------------------------------------------------------------ timed module steps
+    # Direct launches: the step time (value) and the DSA layer-step time (events around
+    # its call).
     for i in range(args.warmup):
         step(i)
     torch.cuda.synchronize()
@@ -193,10 +198,35 @@ def main():
     e_end.record(stream)
     torch.cuda.synchronize()
     t_host = time.perf_counter() - t_host
-    ms_total = e_start.elapsed_time(e_end)
-    ms_step = ms_total / args.steps
+    ms_eager = e_start.elapsed_time(e_end) / args.steps
     dsa_us = [a.elapsed_time(b) * 1e3 for a, b in ev_dsa]
-    log(f"[bench] {args.steps} module steps: {ms_step * 1e3:.1f} us/step (host {t_host / args.steps * 1e6:.1f} us)")
+    log(f"[bench] {args.steps} module steps, direct launches: {ms_eager * 1e3:.1f} us/step "
+        f"(host {t_host / args.steps * 1e6:.1f} us)")
+    ms_step = ms_eager
+    ms_graph = None
+    if not args.eager:
+        # For reference: one HIP graph per input set holding a whole module step (19
+        # kernels), replayed as a serving loop would, one host launch per step.
+        graphs = []
+        cap = torch.cuda.Stream()
+        cap.wait_stream(stream)
+        for r in range(len(structs)):
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g, stream=cap):
+                step(r, st=torch.cuda.current_stream())
+            graphs.append(g)
+        stream.wait_stream(cap)
+        torch.cuda.synchronize()
+        for i in range(args.warmup):
+            graphs[i % len(graphs)].replay()
+        torch.cuda.synchronize()
+        e_start.record(stream)
+        for i in range(args.steps):
+            graphs[(args.warmup + i) % len(graphs)].replay()
+        e_end.record(stream)
+        torch.cuda.synchronize()
+        ms_graph = e_start.elapsed_time(e_end) / args.steps
+        log(f"[bench] {args.steps} module steps, graph replay: {ms_graph * 1e3:.1f} us/step")
 
     # ------------------------------------------------------------------ dominant kernel, live events
     sel_us = []
@@ -246,6 +276,7 @@ def main():
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": round(ms_step, 5),
+        "ms_per_step_graph": None if ms_graph is None else round(ms_graph, 5),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,

@@ -35,12 +35,11 @@
 namespace dsa {
 
 constexpr int kTile = 32;          // keys per MFMA column tile
-constexpr int kSelThreads = 512;   // 8 waves: wave pairs (w, w+4) share key tiles
+constexpr int kSelThreads = 512;   // 8 waves; wave w scores key tiles w, w + 8, ... for all tokens
 constexpr int kSelWaves = kSelThreads / 64;
-constexpr int kPairs = kSelWaves / 2;
 constexpr int kMaxChunk = 4096;    // keys per workgroup held in LDS
 constexpr int kTauMaxM = 32;
-constexpr int kPrefetch = 4;       // key tiles in flight per wave
+constexpr int kPrefetch = 2;       // key tiles in flight per wave
 constexpr int kMaxWG = 1024;
 
 // ----------------------------------------------------------------------------- tile math
@@ -161,6 +160,59 @@ DSA_DEV void load_qlin_frags(const uint16_t* ql, int rt0, Frag8 (&qf)[4]) {
   for (int j = 0; j < 4; ++j) {
     const uint4 v = *reinterpret_cast<const uint4*>(ql + (pc * kMaxT + tcl) * kDI + half * 32 + 8 * j);
     qf[j].u = ok ? v : make_uint4(0u, 0u, 0u, 0u);
+  }
+}
+
+// Query block staged in LDS: qs [kMaxT][kHI][kDI] bf16 and wsh [kMaxT][kHI] fp32, rows of
+// tokens >= T zero.  The loaders below read it with the same lane mapping and produce
+// the same values as load_q_frags / load_w / build_qlin.
+template <int RTW>
+DSA_DEV void load_q_frags_lds(const uint16_t* qs, Frag8 (&qa)[RTW][4]) {
+  const int l = threadIdx.x & 63;
+  const int half = l >> 5;
+  const int row = l & 31;
+#pragma unroll
+  for (int r = 0; r < RTW; ++r) {
+    const int tt = 2 * r + (row >> 4);
+    const int hh = row & 15;
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      qa[r][j].u = *reinterpret_cast<const uint4*>(qs + (tt * kHI + hh) * kDI + half * 32 + 8 * j);
+  }
+}
+
+template <int RTW>
+DSA_DEV void load_w_lds(const float* wsh, float (&wv)[RTW][16]) {
+  const int half = (threadIdx.x & 63) >> 5;
+#pragma unroll
+  for (int r = 0; r < RTW; ++r) {
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {              // elements 4g .. 4g+3: four consecutive heads
+      const int tt = 2 * r + (g >> 1);
+      const int hh = 8 * (g & 1) + 4 * half;
+      const float4 v = *reinterpret_cast<const float4*>(wsh + tt * kHI + hh);
+      wv[r][4 * g + 0] = 0.5f * v.x;
+      wv[r][4 * g + 1] = 0.5f * v.y;
+      wv[r][4 * g + 2] = 0.5f * v.z;
+      wv[r][4 * g + 3] = 0.5f * v.w;
+    }
+  }
+}
+
+template <int NT>
+DSA_DEV void build_qlin_lds(const uint16_t* qs, const float* wsh, uint16_t* ql) {
+  for (int i = threadIdx.x; i < kMaxT * kDI; i += NT) {
+    const int t = i / kDI, d = i % kDI;
+    float acc = 0.0f;
+#pragma unroll
+    for (int h = 0; h < kHI; ++h) acc = fmaf(0.5f * wsh[t * kHI + h], bf16_to_f32(qs[(t * kHI + h) * kDI + d]), acc);
+    const uint16_t hi = f32_to_bf16(acc);
+    const float r1 = acc - bf16_to_f32(hi);
+    const uint16_t mid = f32_to_bf16(r1);
+    const uint16_t lo = f32_to_bf16(r1 - bf16_to_f32(mid));
+    ql[(0 * kMaxT + t) * kDI + d] = hi;
+    ql[(1 * kMaxT + t) * kDI + d] = mid;
+    ql[(2 * kMaxT + t) * kDI + d] = lo;
   }
 }
 
@@ -758,7 +810,7 @@ DSA_DEV void resolve_token(const SelParams& p, int t, SelShared& sh, uint32_t ep
 
 template <int SRC, int KDT, int RTW>
 __global__ void __launch_bounds__(kSelThreads, 1) select_kernel(SelParams p) {
-  static_assert(RTW == 1 || RTW == 2, "a wave holds one or two row tiles");
+  static_assert(RTW >= 1 && RTW <= 4, "a wave holds one to four row tiles");
   __shared__ SelShared sh;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -779,22 +831,37 @@ __global__ void __launch_bounds__(kSelThreads, 1) select_kernel(SelParams p) {
 #pragma unroll
   for (int r = 0; r < RTW; ++r) gmax[r] = -__builtin_inff();
   if constexpr (SRC == 0) {
-    // waves w and w+4 take the same key tiles and different row tiles
-    const int pair = wave & (kPairs - 1);
-    const int rt0 = (wave >= kPairs) ? RTW : 0;
-    const bool active = 2 * rt0 < T;
+    // wave w takes key tiles w, w + 8, ... and scores them for every row tile
+    // (bf16 key tiles take twice the registers: one in flight when four row tiles are held)
+    constexpr int PF = (KDT == 0 && RTW >= 3) ? 1 : kPrefetch;
     const int ntiles = (nkeys + kTile - 1) / kTile;
-    const int nmine = ntiles > pair ? (ntiles - pair + kPairs - 1) / kPairs : 0;   // tiles pair, pair+kPairs, ...
+    const int nmine = ntiles > wave ? (ntiles - wave + kSelWaves - 1) / kSelWaves : 0;
     const int jlast = nmine > 0 ? nmine - 1 : 0;
     // Loads are unconditional (tile index clamped to the wave's last tile, which is then
-    // already cached; rows past L are clamped inside) so the compiler keeps kPrefetch
+    // already cached; rows past L are clamped inside) so the compiler keeps PF
     // tiles in flight without draining the memory counter at branch merges.
-    auto tile_of = [&](int j) { return c0 + (int64_t)(pair + (j < jlast ? j : jlast) * kPairs) * kTile; };
-    // the first key tiles and the chunk's row scales go out before anything else, so
-    // their latency overlaps the query set-up below
-    KeyTile<KDT> buf[kPrefetch];
+    auto tile_of = [&](int j) { return c0 + (int64_t)(wave + (j < jlast ? j : jlast) * kSelWaves) * kTile; };
+    // The block's queries and head weights are staged in LDS (the score area is free
+    // until the scan starts); their loads go out first, then the first key tiles and the
+    // chunk's row scales, whose latency overlaps the query set-up below.
+    uint16_t* qs = reinterpret_cast<uint16_t*>(&sh.sc[0][0]);        // [kMaxT][kHI][kDI]
+    float* wsh = &sh.sc[1][0];                                        // [kMaxT][kHI]
+    constexpr int QROW = kHI * kDI / 8;                               // uint4 per token
+    constexpr int QPER = kMaxT * QROW / kSelThreads;
+    static_assert(kMaxT * QROW % kSelThreads == 0 && kMaxT * kHI / 4 <= kSelThreads, "staging split");
+    uint4 qv[QPER];
 #pragma unroll
-    for (int i = 0; i < kPrefetch; ++i) load_key_tile<KDT, false>(p.k_idx, p.k_scale, p.L, tile_of(i), buf[i]);
+    for (int u = 0; u < QPER; ++u) {
+      const int i = tid + u * kSelThreads;
+      const int tq = i / QROW;
+      qv[u] = reinterpret_cast<const uint4*>(p.q_idx)[(tq < T ? tq : T - 1) * QROW + i % QROW];
+    }
+    float4 w4 = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+    const int tw = tid >> 2;
+    if (tid < kMaxT * kHI / 4) w4 = reinterpret_cast<const float4*>(p.w_idx)[(tw < T ? tw : T - 1) * 4 + (tid & 3)];
+    KeyTile<KDT> buf[PF];
+#pragma unroll
+    for (int i = 0; i < PF; ++i) load_key_tile<KDT, false>(p.k_idx, p.k_scale, p.L, tile_of(i), buf[i]);
     constexpr int PERS = kMaxChunk / kSelThreads;
     float sv[PERS];
     if constexpr (KDT == 1) {
@@ -804,63 +871,58 @@ __global__ void __launch_bounds__(kSelThreads, 1) select_kernel(SelParams p) {
         sv[q] = p.k_scale[c0 + (i < nkeys ? i : (nkeys > 0 ? nkeys - 1 : 0))];
       }
     }
+#pragma unroll
+    for (int u = 0; u < QPER; ++u) {
+      const int i = tid + u * kSelThreads;
+      reinterpret_cast<uint4*>(qs)[i] = (i / QROW < T) ? qv[u] : make_uint4(0u, 0u, 0u, 0u);
+    }
+    if (tid < kMaxT * kHI / 4)
+      reinterpret_cast<float4*>(wsh)[tid] = tw < T ? w4 : make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+    __syncthreads();
     Frag8 qa[RTW][4];
     float wv[RTW][16];
-    load_q_frags<RTW>(p.q_idx, T, rt0, qa);
-    load_w<RTW>(p.w_idx, T, rt0, wv);
-    build_qlin<kSelThreads>(p.q_idx, p.w_idx, T, sh.ql);
+    load_q_frags_lds<RTW>(qs, qa);
+    load_w_lds<RTW>(wsh, wv);
+    build_qlin_lds<kSelThreads>(qs, wsh, sh.ql);
     if constexpr (KDT == 1) {
 #pragma unroll
       for (int q = 0; q < PERS; ++q) sh.kscale[tid + q * kSelThreads] = sv[q];
     }
     __syncthreads();
     Frag8 qf[4];
-    load_qlin_frags<RTW>(sh.ql, rt0, qf);
+    load_qlin_frags<RTW>(sh.ql, 0, qf);
     DSA_MARK(p.trace, 1);
     DSA_MARK_CLK(p.trace, 14);
-    if (active && nmine > 0) {
-      // Software pipeline: the last row tile's epilogue of tile j-1 runs on the vector
-      // units while the matrix cores work on tile j, and each earlier row tile's
-      // epilogue runs under the next row tile's MFMAs.  Scores of clamped repeats go to
-      // a dump slot (selected by address, so no branch splits the schedule).
-      f32x16_t accp = {};
-      float linp = -__builtin_inff(), scp = 1.0f;      // the first "pending" row scores -inf
-      float* dstp = &sh.dump[lane];
-      for (int base = 0; base < nmine; base += kPrefetch) {
+    if (nmine > 0) {
+      // Row tile r's epilogue runs on the vector units while the matrix cores work on row
+      // tile r + 1.  Scores of clamped repeats go to a dump slot (selected by address, so
+      // no branch splits the schedule).
+      for (int base = 0; base < nmine; base += PF) {
 #pragma unroll
-        for (int i = 0; i < kPrefetch; ++i) {
+        for (int i = 0; i < PF; ++i) {
           const int j = base + i;
           const int jc = j < nmine ? j : nmine - 1;      // the tile actually loaded (clamped)
-          const int sl = (pair + jc * kPairs) * kTile + (lane & 31);
+          const int sl = (wave + jc * kSelWaves) * kTile + (lane & 31);
           const float scale = (KDT == 1) ? sh.kscale[sl & (kMaxChunk - 1)] : 1.0f;
           const bool keep = j < nmine;
           Frag8 kb[4];
           keys_to_bf16<KDT>(buf[i], kb);
-          load_key_tile<KDT, false>(p.k_idx, p.k_scale, p.L, tile_of(j + kPrefetch), buf[i]);
+          load_key_tile<KDT, false>(p.k_idx, p.k_scale, p.L, tile_of(j + PF), buf[i]);
           const f32x16_t lacc = mma_k64(qf, kb);
-          {
-            const float o = row_score<KDT>(accp, wv[RTW - 1], linp, scp);
-            gmax[RTW - 1] = fmaxf(gmax[RTW - 1], o);
-            *dstp = o;
-          }
           f32x16_t acc = mma_k64(qa[0], kb);
-          if constexpr (RTW == 2) {
-            const f32x16_t acc1 = mma_k64(qa[1], kb);
-            const float o = row_score<KDT>(acc, wv[0], lin_part<0>(lacc), scale);
-            gmax[0] = fmaxf(gmax[0], o);
-            float* d = keep ? &sh.sc[2 * rt0 + half][sl] : &sh.dump[lane];
-            *d = o;
-            acc = acc1;
+          float* row = keep ? &sh.sc[half][sl] : &sh.dump[lane];
+          const int rstride = keep ? 2 * kMaxChunk : 0;  // floats between row tiles' rows
+#pragma unroll
+          for (int r = 0; r < RTW; ++r) {
+            f32x16_t nxt = {};
+            if (r + 1 < RTW) nxt = mma_k64(qa[r + 1 < RTW ? r + 1 : r], kb);
+            const float o = row_score<KDT>(acc, wv[r], (lacc[4 * r] + lacc[4 * r + 1]) + lacc[4 * r + 2], scale);
+            gmax[r] = fmaxf(gmax[r], o);
+            row[r * rstride] = o;
+            acc = nxt;
           }
-          accp = acc;
-          linp = lin_part<RTW - 1>(lacc);
-          scp = scale;
-          dstp = keep ? &sh.sc[2 * (rt0 + RTW - 1) + half][sl] : &sh.dump[lane];
         }
       }
-      const float o = row_score<KDT>(accp, wv[RTW - 1], linp, scp);
-      gmax[RTW - 1] = fmaxf(gmax[RTW - 1], o);
-      *dstp = o;
     }
   } else {
     constexpr int PER = kMaxChunk / kSelThreads;
@@ -885,24 +947,25 @@ __global__ void __launch_bounds__(kSelThreads, 1) select_kernel(SelParams p) {
   // ---------------- tau bound.  Any split of the chunk's (visible) scores into at least
   // m non-empty groups gives one: the m-th largest group maximum is <= the m-th largest
   // score.  Computed scores use 64 groups per token: the keys at one position mod 32
-  // whose tile index mod 4 is in {p, p+2} (p = 0, 1); loaded scores use 64 groups of
+  // in the tiles of one index parity; loaded scores use 64 groups of
   // stride 64.  Only workgroups whose chunk lies entirely before pos0 publish, so every
   // score of the chunk is visible to every token.
   if (p.m > 0 && wg < p.n_part) {
     if constexpr (SRC == 0) {
-      // group (token, pair, key lane) maxima -> LDS (the row-scale area is free now);
-      // wave t then merges pairs (2q, 2q+1) per lane: 64 groups of the token
-      float* gm = sh.kscale;                                        // [kMaxT][128]
-      const int pair = wave & (kPairs - 1);
-      const int rt0 = (wave >= kPairs) ? RTW : 0;
+      // group (token, wave, key lane) maxima -> LDS (the row-scale area is free now);
+      // wave t then merges, per lane, the waves of one parity: 64 groups of the token
+      constexpr int GPT = kSelWaves * 32;                           // group maxima per token
+      float* gm = sh.kscale;                                        // [kMaxT][GPT]
 #pragma unroll
       for (int r = 0; r < RTW; ++r) {
-        const int tt = 2 * (rt0 + r) + half;
-        if (tt < T) gm[tt * 128 + pair * 32 + (lane & 31)] = gmax[r];
+        const int tt = 2 * r + half;
+        if (tt < T) gm[tt * GPT + wave * 32 + (lane & 31)] = gmax[r];
       }
       __syncthreads();
       for (int t = wave; t < T; t += kSelWaves) {
-        const uint32_t g = max(order_key_fast(gm[t * 128 + lane]), order_key_fast(gm[t * 128 + 64 + lane]));
+        uint32_t g = 0u;
+#pragma unroll
+        for (int i = 0; i < GPT / 64; ++i) g = max(g, order_key_fast(gm[t * GPT + 64 * i + lane]));
         const uint32_t tw = mth_largest_lanes(g, p.m);
         if (lane == 0) ast64(p.tauv + (size_t)t * kMaxWG + wg, ((uint64_t)tag << 32) | tw);
       }
@@ -1062,12 +1125,18 @@ hipError_t launch_select(int src, const void* q_idx, const float* w_idx, const v
   p.tauv = reinterpret_cast<uint64_t*>(w8 + ctl::kBytes + (size_t)kMaxT * kMaxWG * 8);
   p.cand = reinterpret_cast<uint64_t*>(w8 + ctl::kBytes + (size_t)kMaxT * kMaxWG * 16);
   void* args[] = {&p};
-  // row tiles per wave: the two waves of a pair split ceil(T/2) row tiles
-  const int rtw = row_tiles(T) <= 2 ? 1 : 2;
+  // every wave scores all ceil(T/2) row tiles of its key tiles
+  const int rt = row_tiles(T);
   void* fn = nullptr;
-  if (src == 1) fn = (void*)select_kernel<1, 0, 1>;
-  else if (kdt == 0) fn = rtw == 1 ? (void*)select_kernel<0, 0, 1> : (void*)select_kernel<0, 0, 2>;
-  else fn = rtw == 1 ? (void*)select_kernel<0, 1, 1> : (void*)select_kernel<0, 1, 2>;
+  if (src == 1) {
+    fn = (void*)select_kernel<1, 0, 1>;
+  } else if (kdt == 0) {
+    fn = rt == 1 ? (void*)select_kernel<0, 0, 1> : rt == 2 ? (void*)select_kernel<0, 0, 2>
+       : rt == 3 ? (void*)select_kernel<0, 0, 3> : (void*)select_kernel<0, 0, 4>;
+  } else {
+    fn = rt == 1 ? (void*)select_kernel<0, 1, 1> : rt == 2 ? (void*)select_kernel<0, 1, 2>
+       : rt == 3 ? (void*)select_kernel<0, 1, 3> : (void*)select_kernel<0, 1, 4>;
+  }
   // every workgroup must be resident at once (one per CU by the LDS footprint)
   int per_cu = 0;
   hipError_t e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, fn, kSelThreads, 0);

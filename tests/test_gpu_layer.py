@@ -153,3 +153,56 @@ def test_layer_step_with_sink_matches_oracle_attention(dsa):
     ref = O.project(attn, O.decode_bf16(lay.w_o)) + O.decode_bf16(x)
     gx = O.decode_bf16(g["x_out"])
     assert np.all(np.abs(gx - ref) <= 2e-2 * np.maximum(1.0, np.abs(ref)))
+
+
+@pytest.mark.parametrize("kind,L,T", [("dsa", 40000, 8), ("swa", 3000, 8), ("dsa", 777, 3)])
+def test_layer_step_graph_replays_match_direct_launch(dsa, kind, L, T):
+    """The layer step captured in a HIP graph: every replay, with the program's own eager
+    work and synchronisations between replays, reproduces the direct launch bit for bit."""
+    top_k = 2048 if L > 2048 else 64
+    lay = synth.layer_inputs(kind, 0, L, T, seed=17)
+    x_bits = synth.module_x(17, T)
+    pos0 = L - T
+    ref = _run_layer(dsa, kind, lay, x_bits, T, pos0, top_k=top_k)
+
+    n_proj = synth.N_PROJ_DSA if kind == "dsa" else synth.N_PROJ_SWA
+    cfg = dsa.layer_config(dsa.LAYER_DSA if kind == "dsa" else dsa.LAYER_SWA, top_k=top_k, window=128)
+    g_gamma, g_w, g_wo = up(lay.gamma), up(lay.w_qkvi), up(lay.w_o)
+    kc, vc = up(lay.k), up(lay.v)
+    ki = up(lay.k_idx) if kind == "dsa" else None
+    ks = up(lay.k_idx_scale) if kind == "dsa" else None
+    cache = dsa.LayerCache(kc.data_ptr(), vc.data_ptr(), ki.data_ptr() if ki is not None else None,
+                           ks.data_ptr() if ks is not None else None, lay.capacity)
+    w = dsa.LayerWeights(g_gamma.data_ptr(), g_w.data_ptr(), g_wo.data_ptr())
+    x = up(x_bits)
+    xo = torch.zeros_like(x)
+    qkv = torch.zeros((T, n_proj), dtype=torch.int16, device=DEV)
+    idx = torch.full((T, top_k), -7, dtype=torch.int32, device=DEV) if kind == "dsa" else None
+    ws = dsa.workspace(dsa.WS_LAYER_DSA if kind == "dsa" else dsa.WS_LAYER_SWA, T, L,
+                       top_k if kind == "dsa" else 128)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.graph(g, stream=side):
+        dsa.dsa_layer_step(cfg, w, cache, x, xo, T, pos0, idx_out=idx, qkv_out=qkv, ws=ws,
+                           stream=torch.cuda.current_stream())
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    for rep in range(3):
+        # eager work between replays: clear the outputs and run an unrelated reduction
+        xo.zero_()
+        qkv.zero_()
+        if idx is not None:
+            idx.fill_(-7)
+        _ = (x.float() * 1.5).sum().item()
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        got = {"x_out": bf16_bits(xo), "qkv": bf16_bits(qkv), "k": bf16_bits(kc), "v": bf16_bits(vc)}
+        if kind == "dsa":
+            got["idx"] = down(idx)
+            got["k_idx"] = down(ki)
+            got["k_idx_scale"] = down(ks)
+        for key in ref:
+            assert np.array_equal(got[key], ref[key]), (rep, key)

@@ -11,9 +11,9 @@
 // One workgroup = one (token, split of 64 list entries).  It stages the split's K and V
 // rows in LDS with 16-byte coalesced loads, computes S = K q^T on the matrix cores,
 // runs the softmax of the split in fp32 (base-2 exponentials of log2e-scaled logits),
-// accumulates P V, and writes (m, l, acc) to the workspace.  The last workgroup of a
-// token (atomic counter) merges the splits in split order, so the result does not
-// depend on which workgroup merges or on timing.
+// accumulates P V, and writes (m, l, acc) to the workspace.  A second, small kernel
+// merges each token's splits in split order (the kernel boundary makes the partials
+// visible), so the result does not depend on timing.
 #include "dsa_common.h"
 #include "dsa_kernels.h"
 
@@ -42,9 +42,6 @@ struct AttnParams {
   int out_f32;
   uint64_t* trace;        // profiling builds: [blocks][16] phase timestamps
   float* part;            // [T][nsplit][8][kPartStride]
-  uint32_t* ctr;          // [T] counters, stride 64 words
-  uint32_t* ctlw;         // control words of the workspace
-  int dist;               // 1: every split merges a slice (all workgroups co-resident)
   int nsplit;
 };
 
@@ -58,9 +55,6 @@ struct AttnShared {
   float kscl[ROWS];
   float vscl[ROWS];
   float s[kHq][ROWS];
-  float ms[kHq * 32];     // split maxima / sums of the merging workgroup
-  float ls[kHq * 32];
-  uint32_t last;
 };
 
 // out[t][h][d4 .. d4+3] = o / den (0 for an empty list), fp32 or bf16
@@ -94,8 +88,6 @@ __global__ void __launch_bounds__(NT) attn_kernel(AttnParams p) {
   const int wave = tid >> 6;
   const int split = blockIdx.x;
   const int t = blockIdx.y;
-  // launch counter of token t (tags of the split flags); read before any flag is written
-  const uint32_t epoch = p.dist ? ald(p.ctlw + ctl::kEpochT + 16 * t) : 0u;
   uint64_t* trace = p.trace ? p.trace + (size_t)(t * gridDim.x) * 16 : nullptr;   // row = block index
   (void)trace;
   DSA_MARK(trace, 0);
@@ -297,143 +289,66 @@ __global__ void __launch_bounds__(NT) attn_kernel(AttnParams p) {
     DSA_MARK(trace, 6);
     return;
   }
-  // ---- publish the split's partial
-  float* part = p.part + (((size_t)t * p.nsplit + split) * kHq + h) * kPartStride;
+  // ---- the split's partial (merged by attn_merge_kernel after this launch)
   if (lead) {
-    if (jj == 0)
-      ast64(reinterpret_cast<uint64_t*>(part), (uint64_t)__float_as_uint(m) | ((uint64_t)__float_as_uint(l) << 32));
-    ast64(reinterpret_cast<uint64_t*>(part + 4 + d4),
-          (uint64_t)__float_as_uint(acc[0]) | ((uint64_t)__float_as_uint(acc[1]) << 32));
-    ast64(reinterpret_cast<uint64_t*>(part + 6 + d4),
-          (uint64_t)__float_as_uint(acc[2]) | ((uint64_t)__float_as_uint(acc[3]) << 32));
+    float* part = p.part + (((size_t)t * p.nsplit + split) * kHq + h) * kPartStride;
+    if (jj == 0) *reinterpret_cast<float2*>(part) = make_float2(m, l);
+    *reinterpret_cast<float4*>(part + 4 + d4) = make_float4(acc[0], acc[1], acc[2], acc[3]);
   }
-  vm_wait_all();
-  __syncthreads();
-  if (p.dist) {
-    // Every split of token t is resident: publish a tagged flag, wait for all of the
-    // token's flags, then merge output slices split, split + nsplit, ... (32 outputs =
-    // head slice >> 2, dims 32 (slice & 3) ..) in split order -- the same operations, in
-    // the same order, as the single-merger path below.
-    const uint32_t tag = epoch + 1u;
-    if (tid == 0) ast(p.ctlw + ctl::kFlags + 32 * t + split, tag);
-    if (wave == 0) {
-      const int ns = p.nsplit;
-      const uint32_t* fl = p.ctlw + ctl::kFlags + 32 * t;
-      const uint64_t t0 = __builtin_amdgcn_s_memrealtime();
-      while (true) {
-        const uint32_t v = ald(fl + (lane < ns ? lane : ns - 1));
-        if (__ballot(v != tag) == 0ull) break;
-        __builtin_amdgcn_s_sleep(1);
-        if (__builtin_amdgcn_s_memrealtime() - t0 > kSpinLimit) {
-          if (lane == 0) ast(p.ctlw + ctl::kError, 1u);
-          break;
-        }
-      }
-      // every split of token t has read the counter: advance it
-      if (split == 0 && lane == 0) ast(p.ctlw + ctl::kEpochT + 16 * t, next_epoch(epoch));
-      DSA_MARK(trace, 7);
-      const float* pt = p.part + (size_t)t * ns * kHq * kPartStride;
-      const int jl = lane & 31;
-      for (int slice = split; slice < 32; slice += ns) {
-        const int hh = slice >> 2, d0 = (slice & 3) * 32;
-        // split statistics: lane j holds split j's (m, l) of head hh
-        const int jc = jl < ns ? jl : ns - 1;
-        const uint64_t ml = ald64(reinterpret_cast<const uint64_t*>(pt + ((size_t)jc * kHq + hh) * kPartStride));
-        // accumulators: lane i (< 32) holds dim d0 + i of every split
-        float a[32];
-#pragma unroll
-        for (int j = 0; j < 32; ++j) {
-          const int js = j < ns ? j : ns - 1;
-          a[j] = aldf(pt + ((size_t)js * kHq + hh) * kPartStride + 4 + d0 + jl);
-        }
-        const float mj = jl < ns ? __uint_as_float((uint32_t)ml) : -__builtin_inff();
-        float M = mj;
-#pragma unroll
-        for (int d = 16; d >= 1; d >>= 1) M = fmaxf(M, __shfl_xor(M, d, 64));
-        float s2 = -__builtin_inff();
-        if (p.sink) s2 = p.sink[hh] * 1.4426950408889634f;
-        M = fmaxf(M, s2);
-        float den = 0.0f;
-        float o[4] = {0.0f, 0.0f, 0.0f, 0.0f};
-        if (M != -__builtin_inff()) {
-          const float lj = __uint_as_float((uint32_t)(ml >> 32));
-          const float scj = exp2f(mj - M);       // lane j: split j's rescale factor
-#pragma unroll
-          for (int j = 0; j < 32; ++j) {
-            const float ms = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(mj), j));
-            if ((j < ns) & (ms != -__builtin_inff())) {     // splits in order; empty ones skipped
-              const float sc = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(scj), j));
-              const float ls = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(lj), j));
-              den = fmaf(ls, sc, den);
-              o[0] = fmaf(a[j], sc, o[0]);
-            }
-          }
-          if (s2 != -__builtin_inff()) den += exp2f(s2 - M);
-        }
-        if (lane < 32) {
-          const float r = den > 0.0f ? o[0] / den : 0.0f;
-          const size_t ob = ((size_t)t * kHq + hh) * kD + d0 + lane;
-          if (p.out_f32) static_cast<float*>(p.out)[ob] = r;
-          else static_cast<uint16_t*>(p.out)[ob] = f32_to_bf16(r);
-        }
-      }
-      DSA_MARK(trace, 8);
-    }
-    return;
-  }
-  if (tid == 0) sh.last = (aadd(p.ctr + 64 * t, 1u) == (uint32_t)p.nsplit - 1u) ? 1u : 0u;
-  __syncthreads();
   DSA_MARK(trace, 6);
-  if (!sh.last) return;
-  DSA_MARK(trace, 7);
-  // ---- merge of all splits of token t, in split order.  Split statistics first (one
-  // coherent load per thread), then each thread's accumulators, 16 loads in flight.
-  const float* pt = p.part + (size_t)t * p.nsplit * kHq * kPartStride;
-  if (tid < p.nsplit * kHq) {
-    const uint64_t ml = ald64(reinterpret_cast<const uint64_t*>(pt + (size_t)tid * kPartStride));
-    sh.ms[tid] = __uint_as_float((uint32_t)ml);
-    sh.ls[tid] = __uint_as_float((uint32_t)(ml >> 32));
+}
+
+// Merge of token t's splits for one output slice (head slice >> 2, dims 32 (slice & 3)
+// ..+31), one wave: lane j holds split j's (m, l); lane i < 32 holds dim i of every split.
+// Splits are combined in split order; empty splits (m = -inf) are skipped.
+__global__ void __launch_bounds__(64) attn_merge_kernel(AttnParams p) {
+  const int lane = threadIdx.x;
+  const int slice = blockIdx.x;
+  const int t = blockIdx.y;
+  const int ns = p.nsplit;
+  const int hh = slice >> 2, d0 = (slice & 3) * 32;
+  const int jl = lane & 31;
+  const float* pt = p.part + (size_t)t * ns * kHq * kPartStride;
+  const int jc = jl < ns ? jl : ns - 1;
+  const float2 ml = *reinterpret_cast<const float2*>(pt + ((size_t)jc * kHq + hh) * kPartStride);
+  float a[32];
+#pragma unroll
+  for (int j = 0; j < 32; ++j) {
+    const int js = j < ns ? j : ns - 1;
+    a[j] = pt[((size_t)js * kHq + hh) * kPartStride + 4 + d0 + jl];
   }
-  __syncthreads();
-  float M = -__builtin_inff();
-  for (int s = 0; s < p.nsplit; ++s) M = fmaxf(M, sh.ms[s * kHq + h]);
-  M = fmaxf(M, sink2);
-  float den = 0.0f;
-  float o[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+  const float mj = jl < ns ? ml.x : -__builtin_inff();
+  float M = mj;
+#pragma unroll
+  for (int d = 16; d >= 1; d >>= 1) M = fmaxf(M, __shfl_xor(M, d, 64));
+  float s2 = -__builtin_inff();
+  if (p.sink) s2 = p.sink[hh] * 1.4426950408889634f;
+  M = fmaxf(M, s2);
+  float den = 0.0f, o = 0.0f;
   if (M != -__builtin_inff()) {
-    constexpr int U = 8;
-    for (int s0 = 0; s0 < p.nsplit; s0 += U) {
-      uint64_t va[U], vb[U];
+    const float scj = exp2f(mj - M);       // lane j: split j's rescale factor
 #pragma unroll
-      for (int u = 0; u < U; ++u) {
-        const int sc = s0 + u < p.nsplit ? s0 + u : p.nsplit - 1;   // clamped: unconditional loads
-        const uint64_t* ps = reinterpret_cast<const uint64_t*>(pt + ((size_t)sc * kHq + h) * kPartStride + 4 + d4);
-        va[u] = ald64(ps);
-        vb[u] = ald64(ps + 1);
-      }
-#pragma unroll
-      for (int u = 0; u < U; ++u) {
-        const int s = s0 + u;
-        if (s >= p.nsplit) break;
-        const float ms = sh.ms[s * kHq + h];
-        if (ms == -__builtin_inff()) continue;
-        const float sc = exp2f(ms - M);
-        den = fmaf(sh.ls[s * kHq + h], sc, den);
-        o[0] = fmaf(__uint_as_float((uint32_t)va[u]), sc, o[0]);
-        o[1] = fmaf(__uint_as_float((uint32_t)(va[u] >> 32)), sc, o[1]);
-        o[2] = fmaf(__uint_as_float((uint32_t)vb[u]), sc, o[2]);
-        o[3] = fmaf(__uint_as_float((uint32_t)(vb[u] >> 32)), sc, o[3]);
+    for (int j = 0; j < 32; ++j) {
+      const float ms = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(mj), j));
+      if ((j < ns) & (ms != -__builtin_inff())) {     // splits in order; empty ones skipped
+        const float sc = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(scj), j));
+        const float ls = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(ml.y), j));
+        den = fmaf(ls, sc, den);
+        o = fmaf(a[j], sc, o);
       }
     }
-    if (sink2 != -__builtin_inff()) den += exp2f(sink2 - M);
+    if (s2 != -__builtin_inff()) den += exp2f(s2 - M);
   }
-  if (lead) store_out(p, t, h, d4, o, den);
-  DSA_MARK(trace, 8);
-  if (tid == 0) ast(p.ctr + 64 * t, 0u);
+  if (lane < 32) {
+    const float r = den > 0.0f ? o / den : 0.0f;
+    const size_t ob = ((size_t)t * kHq + hh) * kD + d0 + lane;
+    if (p.out_f32) static_cast<float*>(p.out)[ob] = r;
+    else static_cast<uint16_t*>(p.out)[ob] = f32_to_bf16(r);
+  }
 }
 
 size_t attn_workspace_bytes(int T, int nsplit) {
-  return ctl::kBytes + (size_t)T * nsplit * kHq * kPartStride * sizeof(float);
+  return (size_t)T * nsplit * kHq * kPartStride * sizeof(float);
 }
 
 // DSA lists (k up to 2048) split in 64-row pieces (enough workgroups to fill the chip);
@@ -467,25 +382,23 @@ hipError_t launch_attention(int mode, int kvdt, const void* q, const void* kc, c
   p.out = out;
   p.out_f32 = out_f32;
   p.nsplit = attn_splits(mode, mode == 0 ? k : window);
-  uint8_t* w8 = static_cast<uint8_t*>(ws);
-  p.ctr = reinterpret_cast<uint32_t*>(w8) + ctl::kDone;
-  p.ctlw = reinterpret_cast<uint32_t*>(w8);
-  p.part = reinterpret_cast<float*>(w8 + ctl::kBytes);
+  p.part = static_cast<float*>(ws);
 #ifdef DSA_TRACE
   p.trace = dsa_trace_buffer() ? dsa_trace_buffer() + 768 * 16 : nullptr;   // rows 768.. of the buffer
 #endif
+  (void)num_cu;
   const dim3 grid(p.nsplit, T);
   if (mode == 0) {
-    // split merge spread over the splits when every workgroup of the launch is resident
-    int per_cu = 0;
-    void* fn = kvdt == 0 ? (void*)attn_kernel<0, 0, kSplitRows, kAttnThreads>
-                         : (void*)attn_kernel<1, 0, kSplitRows, kAttnThreads>;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, fn, kAttnThreads, 0) != hipSuccess) per_cu = 0;
-    p.dist = (int64_t)per_cu * num_cu >= (int64_t)p.nsplit * T ? 1 : 0;
     if (kvdt == 0) hipLaunchKernelGGL((attn_kernel<0, 0, kSplitRows, kAttnThreads>), grid, dim3(kAttnThreads), 0, st, p);
     else hipLaunchKernelGGL((attn_kernel<1, 0, kSplitRows, kAttnThreads>), grid, dim3(kAttnThreads), 0, st, p);
   } else {
     hipLaunchKernelGGL((attn_kernel<0, 1, kSwaRows, 4 * kAttnThreads>), grid, dim3(4 * kAttnThreads), 0, st, p);
+  }
+  if (p.nsplit > 1) {
+#ifdef DSA_TRACE
+    p.trace = nullptr;
+#endif
+    hipLaunchKernelGGL(attn_merge_kernel, dim3(32, T), dim3(64), 0, st, p);
   }
   return hipGetLastError();
 }

@@ -13,11 +13,11 @@
 //
 // M = T <= 8 tokens makes these weight-streaming products.  One workgroup owns RPW rows
 // of W (RPW = 4, 8 or 16, chosen so the launch covers the chip) over the full K; its
-// eight waves split K.  A v_mfma_f32_16x16x32_bf16 tile takes the rows on the M side
-// (rows >= RPW repeat row 0 and are not read) and the tokens on the N side (padded to
+// sixteen waves split K.  A v_mfma_f32_16x16x32_bf16 tile takes the rows on the M side
+// (rows >= RPW are never read) and the tokens on the N side (padded to
 // 16).  Each lane streams
 // its k chunks of one weight row straight into registers; the normalised activations
-// sit in LDS.  The eight partial tiles are summed in wave order.
+// sit in LDS.  The sixteen partial tiles are summed in wave order.
 #include <cmath>
 
 #include "dsa_common.h"
@@ -25,8 +25,9 @@
 
 namespace dsa {
 
-constexpr int kProjThreads = 512;
+constexpr int kProjThreads = 1024;   // 16 waves: 4 per SIMD hide the load latency
 constexpr int kProjWaves = kProjThreads / 64;
+constexpr int kRowThreads = kHidden / 8;  // threads holding one token's 4096 inputs (8 each)
 
 // Row block b of the fused projection for `rpw` rows per block.  Rotated segments are
 // cut into blocks of rpw/2 rotary pairs (i, i + d/2) so RoPE is local to the block.
@@ -125,7 +126,10 @@ struct ProjShared {
   uint32_t last;
 };
 
-template <int MODE, int NSTEP>
+// R8: eight weight rows per workgroup.  The MFMA still has 16 rows, so lanes 8..15 of
+// each 16-lane group load the odd k steps of rows 0..7 (every load lane distinct) and a
+// row rotate by 8 hands those steps to lanes 0..7; MFMA rows 8..15 are never read.
+template <int MODE, int NSTEP, bool R8>
 __global__ void __launch_bounds__(kProjThreads) proj_kernel(ProjParams p) {
   __shared__ ProjShared sh;
   const int tid = threadIdx.x;
@@ -143,7 +147,7 @@ __global__ void __launch_bounds__(kProjThreads) proj_kernel(ProjParams p) {
   int wrow;
   if (MODE == 0) {
     bi = block_info(b, rpw);
-    wrow = block_row(bi, lrow < rpw ? lrow : 0, rpw);
+    wrow = block_row(bi, R8 ? (lrow & 7) : (lrow < rpw ? lrow : 0), rpw);
     if (bi.seg == 5 && wrow >= p.nproj) wrow = p.nproj - 1;   // partial last w_I block
   } else {
     wrow = b * rpw + (lrow < rpw ? lrow : 0);
@@ -169,58 +173,76 @@ __global__ void __launch_bounds__(kProjThreads) proj_kernel(ProjParams p) {
     v[u] = *reinterpret_cast<const uint4*>(src + (size_t)tc * K + kk);
   }
   uint4 gv = make_uint4(0u, 0u, 0u, 0u);
-  if (MODE == 0) gv = reinterpret_cast<const uint4*>(p.gamma)[tid];   // gamma[8 tid .. 8 tid + 8)
+  if (MODE == 0) gv = reinterpret_cast<const uint4*>(p.gamma)[tid % kRowThreads];   // gamma[8 j .. 8 j + 8)
   // Every lane loads (unconditional loads keep the wait counts exact): lanes beyond the
   // real rows repeat row 0's addresses, which the memory pipeline merges, and the MFMA
   // rows they feed are never read.
-  Frag8 wf[NSTEP];
+  constexpr int NW = R8 ? NSTEP / 2 : NSTEP;
+  static_assert(!R8 || NSTEP % 2 == 0, "R8 pairs the k steps");
+  Frag8 wf[NW];
   {
-    const uint4* wp = reinterpret_cast<const uint4*>(p.w + (size_t)wrow * K + kw0) + (lane >> 4);
+    const uint4* wp = reinterpret_cast<const uint4*>(p.w + (size_t)wrow * K + kw0) + (lane >> 4) +
+                      (R8 ? 4 * (lrow >> 3) : 0);
 #pragma unroll
-    for (int i = 0; i < NSTEP; ++i) wf[i].u = wp[4 * i];
+    for (int i = 0; i < NW; ++i) wf[i].u = wp[(R8 ? 8 : 4) * i];
   }
   DSA_MARK(trace, 1);
   // rotary cos/sin of this block's pairs at the block's positions (first: it needs no
   // loaded data, so it runs while the loads are in flight): angle
-  // (pos0 + t) * theta^(-2i/d) formed in fp64, cos/sin rounded to fp32
+  // (pos0 + t) * theta^(-2i/d) formed in fp64, cos/sin rounded to fp32.  The eight
+  // inverse frequencies of the block are wave-uniform kernel arguments: scalar loads,
+  // so no wait on the vector memory counter (which would also wait for the weights).
   if (MODE == 0 && bi.rot_d && tid < 8 * kMaxT) {
     const int t = tid >> 3, r = tid & 7;
+    const int fbase = (bi.rot_d == kD ? 0 : kD / 2) + bi.i0;
+    constexpr int NF = kD / 2 + kDI / 2;
+    double inv = 0.0;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const double f = p.inv_freq[fbase + j < NF ? fbase + j : NF - 1];
+      inv = r == j ? f : inv;
+    }
     if (t < T && r < rpw / 2) {
-      const int i = bi.i0 + r;
-      const double inv = bi.rot_d == kD ? p.inv_freq[i] : p.inv_freq[kD / 2 + i];
       const double ang = (double)(p.pos0 + t) * inv;
+      // Reduce by the nearest multiple of 2 pi first so sincos sees |x| <= pi (angles
+      // reach ~1e6 rad at 1M context): 2 pi is split into fl(2 pi) and 2 pi - fl(2 pi),
+      // each product removed by one fused multiply-add; the residual error (< 3e-16 rad)
+      // is far below the fp32 rounding of cos and sin.
+      const double kq = rint(ang * 0x1.45f306dc9c883p-3);                     // 1 / (2 pi)
+      const double red = fma(-kq, 0x1.1a62633145c07p-52, fma(-kq, 0x1.921fb54442d18p+2, ang));
       double sv, cv;
-      sincos(ang, &sv, &cv);
+      sincos(red, &sv, &cv);
       sh.rc[t][r] = (float)cv;
       sh.rs[t][r] = (float)sv;
     }
   }
   DSA_MARK(trace, 5);
   if (MODE == 0) {
-    // Input RMSNorm while the weights stream in: thread tid holds elements
-    // [8 tid, 8 tid + 8) of every token.  Per token: squares summed in element order per
-    // thread; thread partials go through LDS (the activation area, not yet in use) and
-    // wave t adds token t's: lane j takes threads 8j .. 8j+7 in order, then an xor
-    // butterfly over the wave.  y = bf16(x * (1 / sqrt(mean + eps)) * gamma).
-    static_assert(kProjWaves == kMaxT, "one wave per token for the norm reduction");
-    float* scr = reinterpret_cast<float*>(&sh.xs[0][0]);          // [kMaxT][kProjThreads]
+    // Input RMSNorm while the weights stream in: thread tid holds elements [8 j, 8 j + 8),
+    // j = tid mod 512, of tokens 2u + tid / 512 (u = 0..3).  Per token: squares summed in
+    // element pairs per thread; thread partials go through LDS (the activation area, not
+    // yet in use) and wave t adds token t's: lane i takes threads 8i .. 8i+7 in order,
+    // then an xor butterfly over the wave.  y = bf16(x * (1 / sqrt(mean + eps)) * gamma).
+    static_assert(MODE != 0 || (kProjWaves >= kMaxT && NCH * kProjThreads == kMaxT * kRowThreads), "norm layout");
+    float* scr = reinterpret_cast<float*>(&sh.xs[0][0]);          // [kMaxT][kRowThreads]
+    const int j8 = tid % kRowThreads;
 #pragma unroll
-    for (int t = 0; t < kMaxT; ++t) {
-      const uint32_t x4[4] = {v[t].x, v[t].y, v[t].z, v[t].w};
+    for (int u = 0; u < NCH; ++u) {
+      const int t = (tid + u * kProjThreads) / kRowThreads;
+      const uint32_t x4[4] = {v[u].x, v[u].y, v[u].z, v[u].w};
       float a2 = 0.0f;
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
-        const float a = __uint_as_float(x4[q] << 16), bb = __uint_as_float(x4[q] & 0xffff0000u);
-        a2 = fmaf(a, a, a2);
-        a2 = fmaf(bb, bb, a2);
+        const bf16x2_t xv = __builtin_bit_cast(bf16x2_t, x4[q]);
+        a2 = __builtin_amdgcn_fdot2_f32_bf16(xv, xv, a2, false);     // exact squares, fp32 sum
       }
-      scr[t * kProjThreads + tid] = a2;
+      scr[t * kRowThreads + j8] = a2;
     }
     __syncthreads();
     DSA_MARK(trace, 6);
-    {
-      const float4 q0 = *reinterpret_cast<const float4*>(&scr[wave * kProjThreads + lane * 8]);
-      const float4 q1 = *reinterpret_cast<const float4*>(&scr[wave * kProjThreads + lane * 8 + 4]);
+    if (wave < kMaxT) {
+      const float4 q0 = *reinterpret_cast<const float4*>(&scr[wave * kRowThreads + lane * 8]);
+      const float4 q1 = *reinterpret_cast<const float4*>(&scr[wave * kRowThreads + lane * 8 + 4]);
       float a = ((((((q0.x + q0.y) + q0.z) + q0.w) + q1.x) + q1.y) + q1.z) + q1.w;
 #pragma unroll
       for (int d = 32; d >= 1; d >>= 1) a += __shfl_xor(a, d, 64);
@@ -228,11 +250,14 @@ __global__ void __launch_bounds__(kProjThreads) proj_kernel(ProjParams p) {
     }
     __syncthreads();
     DSA_MARK(trace, 7);
+    // Rows of tokens >= T hold a copy of token T-1 (clamped loads): their products land
+    // in MFMA columns that are never read.
     const uint32_t g4[4] = {gv.x, gv.y, gv.z, gv.w};
 #pragma unroll
-    for (int t = 0; t < kMaxT; ++t) {
+    for (int u = 0; u < NCH; ++u) {
+      const int t = (tid + u * kProjThreads) / kRowThreads;
       const float r = sh.rnorm[t];
-      const uint32_t x4[4] = {v[t].x, v[t].y, v[t].z, v[t].w};
+      const uint32_t x4[4] = {v[u].x, v[u].y, v[u].z, v[u].w};
       uint32_t o4[4];
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
@@ -240,9 +265,7 @@ __global__ void __launch_bounds__(kProjThreads) proj_kernel(ProjParams p) {
         const float y1 = (__uint_as_float(x4[q] & 0xffff0000u) * r) * __uint_as_float(g4[q] & 0xffff0000u);
         o4[q] = pack_bf16x2(y0, y1);
       }
-      *reinterpret_cast<uint4*>(&sh.xs[t][8 * tid]) = t < T ? make_uint4(o4[0], o4[1], o4[2], o4[3])
-                                                            : make_uint4(0u, 0u, 0u, 0u);
-      __builtin_amdgcn_sched_barrier(0);   // one token at a time: keeps register use low
+      *reinterpret_cast<uint4*>(&sh.xs[t][8 * j8]) = make_uint4(o4[0], o4[1], o4[2], o4[3]);
     }
   }
   // 2) activations into LDS (QKV: already stored, normalised)
@@ -267,7 +290,19 @@ __global__ void __launch_bounds__(kProjThreads) proj_kernel(ProjParams p) {
       Frag8 bfr;
       bfr.u = *reinterpret_cast<const uint4*>(&sh.xs[tok & 7][kw0 + (4 * i + (lane >> 4)) * 8]);
       if (tok >= kMaxT) bfr.u = make_uint4(0u, 0u, 0u, 0u);
-      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wf[i].v, bfr.v, acc, 0, 0, 0);
+      Frag8 a;
+      if constexpr (R8) {
+        a = wf[i >> 1];
+        if (i & 1) {          // odd step: take lane (l + 8) mod 16 of the 16-lane row
+          a.u.x = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)a.u.x, 0x128, 0xf, 0xf, true);
+          a.u.y = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)a.u.y, 0x128, 0xf, 0xf, true);
+          a.u.z = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)a.u.z, 0x128, 0xf, 0xf, true);
+          a.u.w = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)a.u.w, 0x128, 0xf, 0xf, true);
+        }
+      } else {
+        a = wf[i];
+      }
+      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a.v, bfr.v, acc, 0, 0, 0);
     }
   }
   // D[row][tok]: lane holds tok = lane & 15, rows 4*(lane>>4) + i
@@ -403,7 +438,9 @@ hipError_t launch_proj_qkv(int kind, const void* x, const void* gamma, const voi
 #ifdef DSA_TRACE
   p.trace = dsa_trace_buffer() ? dsa_trace_buffer() + 512 * 16 : nullptr;   // rows 512.. of the buffer
 #endif
-  hipLaunchKernelGGL((proj_kernel<0, 16>), grid, block, 0, st, p);
+  constexpr int nstep = kHidden / kProjWaves / 32;
+  if (p.rpw == 8) hipLaunchKernelGGL((proj_kernel<0, nstep, true>), grid, block, 0, st, p);
+  else hipLaunchKernelGGL((proj_kernel<0, nstep, false>), grid, block, 0, st, p);
   return hipGetLastError();
 }
 
@@ -419,7 +456,8 @@ hipError_t launch_proj_out(const void* o, const void* w_o, const void* x, void* 
   p.rpw = 16;
   const dim3 grid(kHidden / 16), block(kProjThreads);
   // 1024 / 8 waves / 4 lane groups / 8 = 4
-  hipLaunchKernelGGL((proj_kernel<1, 4>), grid, block, 0, st, p);
+  constexpr int nstep = kHq * kD / kProjWaves / 32;
+  hipLaunchKernelGGL((proj_kernel<1, nstep, false>), grid, block, 0, st, p);
   return hipGetLastError();
 }
 

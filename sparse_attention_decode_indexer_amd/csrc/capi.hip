@@ -266,6 +266,12 @@ dsa_status_t dsa_layer_step(const dsa_layer_config_t* cfg, const dsa_layer_weigh
     e = dsa::launch_attention(0, 0, q_att, cache->k, cache->v, nullptr, nullptr, idx, cfg->top_k, T, L, 0, 0,
                               0, cfg->sm_scale, cfg->sink, attn_out, 0, w8 + lw.attn, ncu, st);
   } else {
+    if (dsa::swa_out_fits(T, cfg->window)) {
+      // the window is small enough for every output-projection workgroup to recompute it
+      e = dsa::launch_swa_out(q_att, cache->k, cache->v, cache->capacity, pos0, T, cfg->window, cfg->sm_scale,
+                              cfg->sink, w->w_o, x_in, x_out, st);
+      return e == hipSuccess ? DSA_OK : hip_fail(e, "dsa_layer_step: window attention + output projection");
+    }
     e = dsa::launch_attention(1, 0, q_att, cache->k, cache->v, nullptr, nullptr, nullptr, 0, T, 0,
                               cache->capacity, pos0, cfg->window, cfg->sm_scale, cfg->sink, attn_out, 0,
                               w8 + lw.attn, ncu, st);

@@ -45,6 +45,12 @@ hipError_t launch_proj_qkv(int kind, const void* x, const void* gamma, const voi
 hipError_t launch_proj_out(const void* o, const void* w_o, const void* x, void* xout, int T,
                            void* ws, hipStream_t st);
 
+// sliding-window attention fused with the output projection (window + T - 1 <= 160 rows)
+bool swa_out_fits(int T, int window);
+hipError_t launch_swa_out(const void* q, const void* kring, const void* vring, int64_t ring_cap,
+                          int64_t pos0, int T, int window, float sm_scale, const float* sink,
+                          const void* w_o, const void* x, void* xout, hipStream_t st);
+
 hipError_t launch_zero(void* p, size_t bytes, hipStream_t st);
 
 #ifdef DSA_TRACE

@@ -37,10 +37,13 @@
  *     DSA_ERR_HIP (dsa_last_error() gives the message).  Faults inside a kernel surface
  *     at the caller's next synchronisation.
  *   - Workspaces: a workspace must be zero-filled before its first use (allocate it with
- *     zeros or call dsa_workspace_init).  Every call that completes leaves the
- *     workspace's control words as it found them, so one workspace serves any number
- *     of stream-ordered calls.  Two calls that may run at the same time need distinct
- *     workspaces.
+ *     zeros or call dsa_workspace_init).  Its control words then carry state from call
+ *     to call: the selection keeps a launch counter there (its slots are tagged with the
+ *     counter, so no call has to clear them), and every call that completes leaves the
+ *     words valid for the next one, so one workspace serves any number of
+ *     stream-ordered calls, including replays of a captured graph.  Two calls that may
+ *     run at the same time need distinct workspaces; a workspace must not be copied or
+ *     re-zeroed while calls that use it are in flight.
  */
 #ifndef DSA_H_
 #define DSA_H_

@@ -229,6 +229,13 @@ dsa_status_t dsa_workspace_init(void* ws, size_t ws_bytes, void* stream);
  * (4096 positions per compute unit: 1,048,576 on a 256-CU MI355X). */
 int64_t dsa_max_context(void);
 
+/* Measurement helper, not a step of the method: reads `bytes` (a multiple of 16, src
+ * 16-byte aligned) of device memory as a plain stream, one workgroup per compute unit,
+ * and writes an xor fold of it to sink[0 .. min(CUs, 1024)) (caller-owned, at least 1024
+ * uint32 words on device).  Its duration gives the measured HBM read ceiling that the
+ * kernels' achieved bandwidth is compared with.  Asynchronous on `stream`. */
+dsa_status_t dsa_stream_read(const void* src, size_t bytes, uint32_t* sink, void* stream);
+
 const char* dsa_status_string(dsa_status_t s);
 
 /* Message of the last DSA_ERR_HIP / DSA_ERR_LAUNCH on this host thread ("" if none). */

@@ -16,7 +16,7 @@ LIB_PATH = os.path.join(_HERE, "libdsa.so")
 
 if not os.path.exists(LIB_PATH):
     raise ImportError(
-        f"{LIB_PATH} is missing: build it with `python -m sparse_attention_decode_indexer_amd.build` "
+        f"{LIB_PATH} is missing: build it with `python sparse_attention_decode_indexer_amd/build.py` "
         "(or __graft_entry__.build()); there is no fallback implementation.")
 
 _lib = C.CDLL(LIB_PATH)
@@ -30,7 +30,7 @@ STATUS = {0: "DSA_OK", 1: "DSA_ERR_NULL", 2: "DSA_ERR_SHAPE", 3: "DSA_ERR_DTYPE"
 
 EXPORTS = ("dsa_indexer_scores", "dsa_topk", "dsa_index_topk", "dsa_sparse_attn", "swa_attn",
            "dsa_layer_step", "dsa_workspace_bytes", "dsa_workspace_init", "dsa_max_context",
-           "dsa_status_string", "dsa_last_error")
+           "dsa_status_string", "dsa_last_error", "dsa_stream_read")
 
 
 class DSAError(RuntimeError):
@@ -66,6 +66,7 @@ _sig = {
     "dsa_layer_step": [C.POINTER(LayerConfig), C.POINTER(LayerWeights), C.POINTER(LayerCache),
                        _P, _P, _I, _L, _P, _P, _P, _S, _P],
     "dsa_workspace_init": [_P, _S, _P],
+    "dsa_stream_read": [_P, _S, _P, _P],
 }
 for _name, _args in _sig.items():
     getattr(_lib, _name).argtypes = _args
@@ -165,6 +166,11 @@ def dsa_workspace_bytes(kind, T, L, k):
 def dsa_workspace_init(ws, ws_bytes=None, stream=None):
     st = _lib.dsa_workspace_init(_ptr(ws), _nbytes(ws) if ws_bytes is None else ws_bytes, _stream(stream))
     return _check("dsa_workspace_init", st, True)
+
+
+def dsa_stream_read(src, nbytes, sink, stream=None, raise_on_error=True):
+    st = _lib.dsa_stream_read(_ptr(src), nbytes, _ptr(sink), _stream(stream))
+    return _check("dsa_stream_read", st, raise_on_error)
 
 
 def dsa_max_context():

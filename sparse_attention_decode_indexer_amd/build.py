@@ -3,7 +3,7 @@ import os
 import subprocess
 
 HERE = os.path.dirname(os.path.abspath(__file__))
-SOURCES = ["capi.hip", "index_topk.hip", "attention.hip", "layer.hip", "swa_out.hip"]
+SOURCES = ["capi.hip", "index_topk.hip", "attention.hip", "layer.hip", "swa_out.hip", "stream_read.hip"]
 LIB = os.path.join(HERE, "libdsa.so")
 
 HIPCC_FLAGS = [

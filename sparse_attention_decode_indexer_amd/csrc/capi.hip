@@ -90,6 +90,15 @@ const char* dsa_last_error(void) { return g_err; }
 
 int64_t dsa_max_context(void) { return dsa::select_max_context(device_cus()); }
 
+dsa_status_t dsa_stream_read(const void* src, size_t bytes, uint32_t* sink, void* stream) {
+  if (!src || !sink) return DSA_ERR_NULL;
+  if (!aligned16(src) || (bytes & 15u)) return DSA_ERR_ALIGN;
+  if (bytes == 0) return DSA_ERR_SHAPE;
+  const int nb = device_cus() < 1024 ? device_cus() : 1024;
+  hipError_t e = dsa::launch_stream_read(src, bytes, sink, nb, (hipStream_t)stream);
+  return e == hipSuccess ? DSA_OK : hip_fail(e, "dsa_stream_read");
+}
+
 size_t dsa_workspace_bytes(int kind, int T, int64_t L, int k) {
   if (T < 1 || T > dsa::kMaxT || L < 1) return 0;
   const int ncu = device_cus();

@@ -53,6 +53,10 @@ hipError_t launch_swa_out(const void* q, const void* kring, const void* vring, i
 
 hipError_t launch_zero(void* p, size_t bytes, hipStream_t st);
 
+// streaming read of `bytes` (a multiple of 16) by `nblocks` workgroups; one word per
+// workgroup into sink
+hipError_t launch_stream_read(const void* src, size_t bytes, uint32_t* sink, int nblocks, hipStream_t st);
+
 #ifdef DSA_TRACE
 uint64_t* dsa_trace_buffer();   // profiling builds: phase-timestamp buffer (or null)
 #endif

@@ -352,3 +352,17 @@ def test_attention_run_to_run_bitwise(dsa):
     for _ in range(3):
         b = _run_sparse(dsa, inp, idx.astype(np.int32), k, "f32")
         assert np.array_equal(a, b)
+
+
+@pytest.mark.parametrize("nbytes", [16, 4096 + 48, (1 << 20) + 16 * 777, 64 << 20])
+def test_stream_read_folds_every_word(dsa, nbytes):
+    """The bandwidth helper reads every 16-byte word exactly once: the xor of the
+    per-workgroup folds equals the host's xor of all 32-bit words."""
+    g = np.random.default_rng(nbytes)
+    words = g.integers(0, 2 ** 32, size=nbytes // 4, dtype=np.uint64).astype(np.uint32)
+    src = up(words.view(np.int32))
+    sink = torch.zeros(1024, dtype=torch.int32, device=DEV)
+    dsa.dsa_stream_read(src, nbytes, sink)
+    torch.cuda.synchronize()
+    fold = np.bitwise_xor.reduce(down(sink).view(np.uint32))
+    assert fold == np.bitwise_xor.reduce(words)

@@ -310,6 +310,35 @@ def project(y, W):
     return np.asarray(y, np.float64) @ np.asarray(W, np.float64).T
 
 
+# W8A8 projections (§How it was built: W8A8 kernels; §Get NaiveRT: W8A8 checkpoint).
+# The pages fix no granularity; the reading here is one fp32 scale per weight row and
+# one per token of the projection input, formed from the token's largest magnitude.
+
+
+def quantize_tokens_w8a8(rows):
+    """Per-token e4m3 quantisation of a projection input (fp64 rows holding bf16 values):
+    amax = max |y|; scale = fp32(amax / 448); inv = fp32(448 / amax) (both 1 when
+    amax = 0); code = e4m3(fp32(y * inv)), nearest even, saturating.
+    Returns (codes uint8 [T][K], scale fp32 [T]); y ~ decode(code) * scale."""
+    rows = np.asarray(rows, np.float64)
+    amax = np.max(np.abs(rows), axis=-1)
+    nz = amax > 0
+    safe = np.where(nz, amax, 1.0)
+    scale = np.where(nz, f32(safe / 448.0), 1.0)
+    inv = np.where(nz, f32(448.0 / safe), 1.0)
+    return encode_e4m3(f32(rows * inv[:, None])), scale.astype(np.float32)
+
+
+def project_w8a8(y, w_codes, w_scale):
+    """W8A8 product: y [T][K] (bf16 values) quantised per token, W as e4m3 codes [N][K]
+    with row scales [N].  Returns fp64 [T][N] = s_y[t] * s_w[n] * sum_k a[t,k] * b[n,k]
+    with a, b the decoded codes.  Every product of two e4m3 values is exact in fp64 and
+    all of them lie within 2^48 of each other, so the fp64 sum is exact in any order."""
+    codes, s_y = quantize_tokens_w8a8(y)
+    acc = decode_e4m3(codes) @ decode_e4m3(w_codes).T
+    return acc * np.asarray(s_y, np.float64)[:, None] * np.asarray(w_scale, np.float64)[None, :]
+
+
 # column layout of the fused projection output (per layer)
 def proj_layout(kind: str, H_q=8, D=128, H_I=16, D_I=64):
     lay = {"q": (0, H_q * D), "k": (H_q * D, D), "v": (H_q * D + D, D)}
@@ -323,7 +352,8 @@ def proj_layout(kind: str, H_q=8, D=128, H_I=16, D_I=64):
 
 def layer_step(kind: str, x_bits, gamma_bits, w_qkvi_bits, w_o_bits, cache: dict,
                pos0: int, *, eps=1e-6, theta=1e6, top_k=2048, window=128,
-               H_q=8, D=128, H_I=16, D_I=64, sm_scale=None, teacher=None):
+               H_q=8, D=128, H_I=16, D_I=64, sm_scale=None, teacher=None,
+               w_qkvi_scale=None, w_o_scale=None):
     """One layer step with the rounding points of the bf16 path.
 
     kind "dsa": RMSNorm -> projection (Q|K|V|q_I|k_I|w_I) -> RoPE on Q, K, q_I, k_I
@@ -340,6 +370,10 @@ def layer_step(kind: str, x_bits, gamma_bits, w_qkvi_bits, w_o_bits, cache: dict
     checked on identical inputs: keys "qkv" (post-RoPE projection, bf16 bits
     [T][N]), "idx" ([T][top_k]), "attn" (bf16 bits [T][H_q*D]).
 
+    W8A8: with ``w_qkvi_scale`` and ``w_o_scale`` given, ``w_qkvi_bits`` and
+    ``w_o_bits`` are e4m3 codes with those row scales and both projections are
+    ``project_w8a8`` of their bf16 inputs (the normalised rows, the attention output).
+
     Returns a dict of every stage's result.
     """
     if sm_scale is None:
@@ -352,7 +386,13 @@ def layer_step(kind: str, x_bits, gamma_bits, w_qkvi_bits, w_o_bits, cache: dict
     y = bf16_round_trip(rmsnorm(x, decode_bf16(gamma_bits), eps))
     res["normed"] = y
     # 2. projection -> bf16
-    p = bf16_round_trip(project(y, decode_bf16(w_qkvi_bits)))
+    w8a8 = w_qkvi_scale is not None
+    if w8a8 != (w_o_scale is not None):
+        raise ValueError("W8A8 needs both weight scales")
+    if w8a8:
+        p = bf16_round_trip(project_w8a8(y, w_qkvi_bits, w_qkvi_scale))
+    else:
+        p = bf16_round_trip(project(y, decode_bf16(w_qkvi_bits)))
     lay = proj_layout(kind, H_q, D, H_I, D_I)
     # 3. RoPE on Q, K (and q_I, k_I for DSA) -> bf16
     def seg(name):
@@ -412,7 +452,10 @@ def layer_step(kind: str, x_bits, gamma_bits, w_qkvi_bits, w_o_bits, cache: dict
     res["attn"] = attn
     if teacher is not None and "attn" in teacher:
         attn = decode_bf16(teacher["attn"])
-    out = project(attn, decode_bf16(w_o_bits)) + x
+    if w8a8:
+        out = project_w8a8(attn, w_o_bits, w_o_scale) + x
+    else:
+        out = project(attn, decode_bf16(w_o_bits)) + x
     res["x_out"] = bf16_round_trip(out)
     res["x_out_f64"] = out
     return res

@@ -230,6 +230,43 @@ def layer_inputs(kind: str, layer: int, L: int, T: int, seed: int = 0,
                        capacity=ring_cap)
 
 
+def w8a8_weights(lay: LayerInputs):
+    """The layer's bf16 weights stored as W8A8 weights: e4m3 codes with one fp32 scale
+    per output row (rowmax / 448, the same storage cast as the prefilled caches).
+    Returns (w_qkvi codes, w_qkvi scales, w_o codes, w_o scales)."""
+    def rows(bits):
+        return torch.from_numpy(bits.view(np.int16)).view(torch.bfloat16).float().numpy()
+    wq, sq = to_e4m3_rows(rows(lay.w_qkvi))
+    wo, so = to_e4m3_rows(rows(lay.w_o))
+    return wq, sq, wo, so
+
+
+# groups of 16 integers whose squares sum to 16 (zeros padded), for exact_norm_x
+_NORM_GROUPS = ((1,) * 16, (2, 2, 2, 2), (4,), (3, 2, 1, 1, 1), (2, 2, 2, 1, 1, 1, 1))
+
+
+def exact_norm_x(seed: int, T: int, groups=None, scale_exp=(-2, -1, 0, 1, 2)) -> np.ndarray:
+    """Residual rows [T][HIDDEN] bf16 bits whose mean square is an exact power of 4:
+    each row is 256 blocks of 16 drawn from small-integer groups with squares summing
+    to 16 (random order and signs), times a per-row power of two.  Every row holds at
+    least one block with the row's largest magnitude (4).  With eps = 0 the RMS factor
+    is an exact power of two, so normalised values are identical in any precision."""
+    groups = _NORM_GROUPS if groups is None else groups
+    g = rng_for(seed, "x")
+    out = np.zeros((T, HIDDEN), np.float32)
+    for t in range(T):
+        row = []
+        picks = g.integers(0, len(groups), size=HIDDEN // 16)
+        picks[g.integers(0, HIDDEN // 16)] = [i for i, gr in enumerate(groups) if gr[0] == 4][0]
+        for pk in picks:
+            blk = np.zeros(16, np.float32)
+            vals = np.array(groups[pk], np.float32)
+            blk[: len(vals)] = vals * np.where(g.integers(0, 2, size=len(vals)) == 1, -1.0, 1.0)
+            row.append(blk[g.permutation(16)])
+        out[t] = np.concatenate(row) * np.float32(2.0 ** int(g.choice(scale_exp)))
+    return to_bf16_bits(out)
+
+
 def module_x(seed: int, T: int) -> np.ndarray:
     """Residual-stream input [T][HIDDEN] bf16 bits ~N(0,1)."""
     return to_bf16_bits(normal(seed, "x", (T, HIDDEN)))

@@ -395,3 +395,123 @@ def test_layer_step_swa_small_context_is_dense():
     K = O.decode_bf16(cache["k"][:L]); V = O.decode_bf16(cache["v"][:L])
     dense = _sdpa_causal(q, K, V, L - T, 1 / math.sqrt(128)).reshape(T, 1024)
     np.testing.assert_array_equal(r["attn"], O.bf16_round_trip(dense))
+
+
+# ----------------------------------------------------------------------------- W8A8
+
+def _grid_rows(g, T, K, j):
+    """Rows of e4m3 values times 2^j[t]; each row's largest magnitude is 448 * 2^j[t]."""
+    codes = (g.integers(0, 127, size=(T, K)) | (g.integers(0, 2, size=(T, K)) << 7)).astype(np.uint8)
+    codes[:, 0] = 126                                     # +448
+    return O.decode_e4m3(codes) * np.exp2(np.asarray(j, np.float64))[:, None]
+
+
+def test_w8a8_quantiser_is_lossless_on_scaled_e4m3_rows():
+    g = np.random.default_rng(21)
+    j = np.array([-3, 0, 2, -7])
+    rows = _grid_rows(g, 4, 96, j)
+    codes, s = O.quantize_tokens_w8a8(rows)
+    np.testing.assert_array_equal(s, np.exp2(j).astype(np.float32))       # amax / 448 = 2^j exactly
+    np.testing.assert_array_equal(O.decode_e4m3(codes) * s[:, None].astype(np.float64), rows)
+
+
+def test_w8a8_quantiser_zero_rows_scaling_and_bounds():
+    g = np.random.default_rng(22)
+    rows = O.bf16_round_trip(g.standard_normal((32, 256)) * 2.5)
+    rows[3] = 0.0
+    codes, s = O.quantize_tokens_w8a8(rows)
+    assert s[3] == 1.0 and np.all(codes[3] & 0x7F == 0)
+    # a power-of-two rescaling of a row changes only its scale
+    c4, s4 = O.quantize_tokens_w8a8(rows * 4.0)
+    np.testing.assert_array_equal(c4, codes)
+    nz = np.arange(32) != 3                                 # (the zero row keeps scale 1)
+    np.testing.assert_array_equal(s4[nz], s[nz] * np.float32(4.0))
+    # each row's largest magnitude lands on +-448
+    assert np.all(np.max(np.abs(O.decode_e4m3(codes[nz])), axis=1) == 448.0)
+    # error bound: half an e4m3 ulp (2^-4 relative; 2^-10 * scale in the subnormal range)
+    # plus the fp32 roundings of the product and of the scale
+    deq = O.decode_e4m3(codes) * s[:, None].astype(np.float64)
+    bound = (2.0 ** -4 + 2.0 ** -22) * np.abs(rows) + 2.0 ** -10 * s[:, None]
+    assert np.all(np.abs(deq - rows) <= bound)
+
+
+def test_w8a8_quantiser_vs_torch_fp32_ops_and_cast():
+    """The same steps done by the library in fp32: 448 / amax, y * inv, cast to e4m3fn."""
+    g = np.random.default_rng(23)
+    rows = O.bf16_round_trip(g.standard_normal((48, 512)) * np.exp2(g.integers(-6, 6, size=(48, 1))))
+    codes, s = O.quantize_tokens_w8a8(rows)
+    t = torch.from_numpy(rows.astype(np.float32))
+    amax = t.abs().amax(dim=1)
+    inv = torch.tensor(448.0, dtype=torch.float32) / amax
+    ref = (t * inv[:, None]).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    np.testing.assert_array_equal(codes, ref)
+    np.testing.assert_array_equal(s, (amax / torch.tensor(448.0, dtype=torch.float32)).numpy())
+
+
+def test_w8a8_projection_lossless_rows_equal_dequantised_product():
+    """Rows the quantiser represents exactly: the W8A8 product is the plain product with
+    the dequantised weights (non-square shapes and distinct per-token / per-row scales
+    catch a transposed operand or a swapped scale)."""
+    g = np.random.default_rng(24)
+    T, K, N = 3, 64, 5
+    y = _grid_rows(g, T, K, [1, -2, 0])
+    wc = (g.integers(0, 127, size=(N, K)) | (g.integers(0, 2, size=(N, K)) << 7)).astype(np.uint8)
+    ws = (g.uniform(0.5, 2.0, size=N) * 1e-3).astype(np.float32)
+    got = O.project_w8a8(y, wc, ws)
+    wdeq = O.decode_e4m3(wc) * ws[:, None].astype(np.float64)
+    ref = O.project(y, wdeq)
+    mag = O.project(np.abs(y), np.abs(wdeq))
+    assert np.all(np.abs(got - ref) <= 1e-14 * mag)
+    # one nonzero weight per row selects one scaled input column
+    wc1 = np.zeros((N, K), np.uint8)
+    cols = g.permutation(K)[:N]
+    wc1[np.arange(N), cols] = 0x38                        # 1.0
+    got1 = O.project_w8a8(y, wc1, ws)
+    np.testing.assert_array_equal(got1, y[:, cols] * ws[None, :].astype(np.float64))
+
+
+def test_w8a8_projection_error_bound_on_general_rows():
+    g = np.random.default_rng(25)
+    T, K, N = 4, 1024, 7
+    y = O.bf16_round_trip(g.standard_normal((T, K)))
+    wc, ws = synth.to_e4m3_rows(g.standard_normal((N, K)).astype(np.float32) * 0.02)
+    _, s = O.quantize_tokens_w8a8(y)
+    wdeq = O.decode_e4m3(wc) * ws[:, None].astype(np.float64)
+    err = np.abs(O.project_w8a8(y, wc, ws) - O.project(y, wdeq))
+    bound = O.project((2.0 ** -4 + 2.0 ** -22) * np.abs(y) + 2.0 ** -10 * s[:, None].astype(np.float64),
+                      np.abs(wdeq))
+    assert np.all(err <= bound)
+    assert np.max(err) > 0                                  # the quantiser does act here
+
+
+def test_layer_step_w8a8_equals_bf16_step_when_lossless():
+    """gamma = 112 and exact-norm inputs make every normalised value 0, +-112, +-224 or
+    +-448 with 448 in every row (scale 1, lossless codes), and power-of-two weight row
+    scales make the dequantised weights exact bf16 values: the W8A8 step then equals the
+    bf16 step on those weights exactly up to the output projection, whose input (the
+    attention output) is quantised with the bounded error of the quantiser."""
+    T, L = 3, 300
+    g = np.random.default_rng(26)
+    lay, cache_a = _small_dsa_layer(4, L, T)
+    cache_b = {k: v.copy() for k, v in cache_a.items()}
+    x = synth.exact_norm_x(5, T, groups=((1,) * 16, (2, 2, 2, 2), (4,)))
+    gamma = synth.to_bf16_bits(np.full(4096, 112.0, np.float32))
+    wq = (g.integers(0, 127, size=lay.w_qkvi.shape) | (g.integers(0, 2, size=lay.w_qkvi.shape) << 7)).astype(np.uint8)
+    wo = (g.integers(0, 127, size=lay.w_o.shape) | (g.integers(0, 2, size=lay.w_o.shape) << 7)).astype(np.uint8)
+    sq = np.exp2(g.integers(-16, -12, size=wq.shape[0])).astype(np.float32)
+    so = np.exp2(g.integers(-16, -12, size=wo.shape[0])).astype(np.float32)
+    wq_bf = synth.to_bf16_bits((O.decode_e4m3(wq) * sq[:, None]).astype(np.float32))
+    wo_bf = synth.to_bf16_bits((O.decode_e4m3(wo) * so[:, None]).astype(np.float32))
+    assert np.array_equal(O.decode_bf16(wq_bf), O.decode_e4m3(wq) * sq[:, None])   # exact bf16 values
+    a = O.layer_step("dsa", x, gamma, wq, wo, cache_a, L - T, eps=0.0, top_k=64,
+                     w_qkvi_scale=sq, w_o_scale=so)
+    b = O.layer_step("dsa", x, gamma, wq_bf, wo_bf, cache_b, L - T, eps=0.0, top_k=64)
+    assert set(np.unique(np.abs(a["normed"]))) <= {0.0, 112.0, 224.0, 448.0}
+    for key in ("qkv", "idx", "attn"):
+        np.testing.assert_array_equal(a[key], b[key])
+    codes, s = O.quantize_tokens_w8a8(a["attn"])
+    wod = O.decode_bf16(wo_bf)
+    bound = O.project((2.0 ** -4 + 2.0 ** -22) * np.abs(a["attn"]) + 2.0 ** -10 * s[:, None].astype(np.float64),
+                      np.abs(wod))
+    assert np.all(np.abs(a["x_out_f64"] - b["x_out_f64"]) <= bound)
+    assert not np.array_equal(a["x_out_f64"], b["x_out_f64"])

@@ -42,6 +42,7 @@ def parse():
     ap.add_argument("--T", type=int, default=8)
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
+    ap.add_argument("--no-w8a8", action="store_true", help="skip the W8A8 module timing")
     ap.add_argument("--eager", action="store_true",
                     help="skip the HIP-graph replay timing (reported beside the direct-launch step)")
     ap.add_argument("--only", choices=["module", "index_topk", "copy"], default="module",
@@ -290,6 +291,64 @@ def main():
     ceiling = read_ceiling(torch, dev, stream, dsa)
     log(f"[bench] read ceiling: {ceiling}")
 
+    # ------------------------------------------------------------------ W8A8 module
+    # The same module with every projection weight stored as e4m3 codes + per-row fp32
+    # scales and the activations quantised per token on chip; caches and inputs are the
+    # bf16 run's (same rotated sets).
+    w8a8 = None
+    if not args.no_w8a8:
+        w8_host = [synth.w8a8_weights(lay) for lay in host_layers]
+        w8_sets = []
+        for r in range(len(dev_sets)):
+            per = []
+            for li, (wq, sq, wo, so) in enumerate(w8_host):
+                arrs = [up(a) for a in (wq, sq, wo, so)]
+                if r:
+                    arrs = [torch.roll(a, shifts=r * 7919, dims=0).contiguous() for a in arrs]
+                per.append(arrs)
+            w8_sets.append(per)
+        structs8 = []
+        for r, per in enumerate(structs):
+            row = []
+            for li, (kind, w, c) in enumerate(per):
+                wq, sq, wo, so = w8_sets[r][li]
+                w8 = dsa.LayerWeights(w.rms_gamma, wq.data_ptr(), wo.data_ptr(), dsa.FP8_E4M3, sq.data_ptr(),
+                                      so.data_ptr())
+                row.append((kind, w8, c))
+            structs8.append(row)
+
+        def step8(i):
+            per = structs8[i % len(structs8)]
+            xin = x0
+            for li, (kind, w, c) in enumerate(per):
+                if kind == "dsa":
+                    dsa.dsa_layer_step(cfg_dsa, w, c, xin, xs[li], T, pos0, idx_out=idx, qkv_out=qkv, ws=ws_dsa,
+                                       stream=stream)
+                else:
+                    dsa.dsa_layer_step(cfg_swa, w, c, xin, xs[li], T, pos0, ws=ws_swa, stream=stream)
+                xin = xs[li]
+
+        for i in range(args.warmup):
+            step8(i)
+        torch.cuda.synchronize()
+        e_start.record(stream)
+        for i in range(args.steps):
+            step8(args.warmup + i)
+        e_end.record(stream)
+        torch.cuda.synchronize()
+        ms8 = e_start.elapsed_time(e_end) / args.steps
+
+        def dsa_layer8(per):
+            kind, w, c = per[-1]
+            dsa.dsa_layer_step(cfg_dsa, w, c, xs[-2], xs[-1], T, pos0, idx_out=idx, qkv_out=qkv, ws=ws_dsa,
+                               stream=stream)
+        dsa8 = {"cold": stats(per_call(dsa_layer8, structs8, n_pc)),
+                "warm": stats(per_call(dsa_layer8, structs8[:1], n_pc))}
+        log(f"[bench] W8A8 module: {ms8 * 1e3:.1f} us/step; DSA layer cold median {dsa8['cold']['median']} us")
+        w8a8 = {"ms_per_step": round(ms8, 5), "tokens_per_s_module": round(T / (ms8 * 1e-3), 1),
+                "dsa_layer_step_us": dsa8}
+        del w8_sets
+
     # ------------------------------------------------------------------ algorithmic bytes
     idx_np = idx.cpu().numpy()
     union = np.unique(idx_np[idx_np >= 0]).size
@@ -305,6 +364,17 @@ def main():
     bytes_dsa = scan + gather + w_dsa + act + append_dsa + T * K * 4
     bytes_swa = w_swa + act + append_swa + ring
     bytes_step = bytes_dsa + 5 * bytes_swa
+    if w8a8 is not None:
+        # e4m3 weights + one fp32 scale per weight row
+        w8_dsa = synth.N_PROJ_DSA * (hidden + 4) + hidden * (1024 + 4) + hidden * 2
+        w8_swa = synth.N_PROJ_SWA * (hidden + 4) + hidden * (1024 + 4) + hidden * 2
+        b8_dsa = bytes_dsa - w_dsa + w8_dsa
+        b8_step = b8_dsa + 5 * (bytes_swa - w_swa + w8_swa)
+        med8 = w8a8["dsa_layer_step_us"]["cold"]["median"]
+        w8a8.update({"algorithmic_bytes_per_step": int(b8_step),
+                     "GBps": round(b8_step / (w8a8["ms_per_step"] * 1e-3) / 1e9, 1),
+                     "dsa_layer_step_GBps": round(b8_dsa / (med8 * 1e-6) / 1e9, 1),
+                     "dsa_layer_step_frac": round(b8_dsa / (med8 * 1e-6) / 1e9 / HBM_PEAK_GBPS, 4)})
     sel_bytes = scan + T * K * 4
     sel_avg = float(np.mean(sel_us))
     achieved = sel_bytes / (sel_avg * 1e-6) / 1e9
@@ -359,6 +429,7 @@ def main():
             "algorithmic_bytes": int(sel_bytes),
         },
         "cpu_baseline": cpu,
+        "w8a8": w8a8,
         "protocol": {"per_call_calls": n_pc, "warmup_calls": args.warmup, **dist,
                      "read_ceiling": ceiling, "scan_gather": scan_gather,
                      "module_step_GBps": round(value, 1)},

@@ -173,9 +173,17 @@ dsa_status_t swa_attn(const void* q, const void* k_ring, const void* v_ring, int
  * Rounding points: y, P, the rotated values and the attention output are rounded to
  * bf16; accumulation is fp32.
  *
- * Weights (bf16, out-features major):
- *   rms_gamma [hidden]; w_qkvi [N][hidden] with N = 2384 (DSA) or 1280 (SWA);
- *   w_o [hidden][1024].
+ * Weights (out-features major), w_dtype DSA_BF16:
+ *   rms_gamma [hidden] bf16; w_qkvi [N][hidden] bf16 with N = 2384 (DSA) or 1280 (SWA);
+ *   w_o [hidden][1024] bf16; w_qkvi_scale, w_o_scale NULL.
+ * W8A8 (w_dtype DSA_FP8_E4M3; §How it was built: W8A8 kernels were among those tuned;
+ * §Get NaiveRT: the released checkpoint is W8A8): w_qkvi and w_o hold OCP e4m3fn codes in the
+ * same layout, with one fp32 scale per weight row (w_qkvi_scale [N], w_o_scale [hidden]);
+ * rms_gamma stays bf16.  Each projection input row (the normalised y, and the bf16
+ * attention output before W_o) is quantised per token: amax = max |y|, scale =
+ * fp32(amax / 448) and codes e4m3(fp32(y * fp32(448 / amax))) rounded to nearest even
+ * (scale 1, codes 0 for an all-zero row); products of codes are accumulated in fp32 and
+ * multiplied by both scales.
  * Cache (DSA): k, v [capacity][128] bf16; k_idx [capacity][64] e4m3; k_idx_scale
  *   [capacity] fp32; pos0 + T <= capacity, pos0 + T <= dsa_max_context().
  * Cache (SWA): k, v rings [capacity][128] bf16 holding positions
@@ -202,6 +210,9 @@ typedef struct {
   const void* rms_gamma;
   const void* w_qkvi;
   const void* w_o;
+  int w_dtype;                /* DSA_BF16, or DSA_FP8_E4M3 for W8A8 */
+  const float* w_qkvi_scale;  /* [N] fp32 (W8A8 only, else NULL) */
+  const float* w_o_scale;     /* [hidden] fp32 (W8A8 only, else NULL) */
 } dsa_layer_weights_t;
 
 typedef struct {

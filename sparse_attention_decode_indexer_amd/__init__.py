@@ -48,7 +48,10 @@ class LayerConfig(C.Structure):
 
 
 class LayerWeights(C.Structure):
-    _fields_ = [("rms_gamma", C.c_void_p), ("w_qkvi", C.c_void_p), ("w_o", C.c_void_p)]
+    """rms_gamma, w_qkvi, w_o (+ w_dtype, w_qkvi_scale, w_o_scale for W8A8); unset
+    trailing fields are 0 / NULL, i.e. bf16 weights."""
+    _fields_ = [("rms_gamma", C.c_void_p), ("w_qkvi", C.c_void_p), ("w_o", C.c_void_p),
+                ("w_dtype", C.c_int), ("w_qkvi_scale", C.c_void_p), ("w_o_scale", C.c_void_p)]
 
 
 class LayerCache(C.Structure):

@@ -233,6 +233,11 @@ dsa_status_t dsa_layer_step(const dsa_layer_config_t* cfg, const dsa_layer_weigh
                             size_t ws_bytes, void* stream) {
   if (!cfg || !w || !cache || !x_in || !x_out) return DSA_ERR_NULL;
   if (!w->rms_gamma || !w->w_qkvi || !w->w_o || !cache->k || !cache->v) return DSA_ERR_NULL;
+  if (w->w_dtype != DSA_BF16 && w->w_dtype != DSA_FP8_E4M3) return DSA_ERR_DTYPE;
+  const bool w8a8 = w->w_dtype == DSA_FP8_E4M3;
+  if (w8a8 != (w->w_qkvi_scale != nullptr) || w8a8 != (w->w_o_scale != nullptr)) return DSA_ERR_DTYPE;
+  const float* wq_scale = w8a8 ? w->w_qkvi_scale : nullptr;
+  const float* wo_scale = w8a8 ? w->w_o_scale : nullptr;
   const bool dsa_kind = cfg->kind == DSA_LAYER_DSA;
   if (!dsa_kind && cfg->kind != DSA_LAYER_SWA) return DSA_ERR_SHAPE;
   if (dsa_kind && (!cache->k_idx || !cache->k_idx_scale)) return DSA_ERR_NULL;
@@ -262,7 +267,7 @@ dsa_status_t dsa_layer_step(const dsa_layer_config_t* cfg, const dsa_layer_weigh
   void* q_idx = w8 + lw.q_idx;
   float* w_idx = reinterpret_cast<float*>(w8 + lw.w_idx);
   void* attn_out = w8 + lw.attn_out;
-  hipError_t e = dsa::launch_proj_qkv(dsa_kind ? 0 : 1, x_in, w->rms_gamma, w->w_qkvi, T, cfg->rms_eps,
+  hipError_t e = dsa::launch_proj_qkv(dsa_kind ? 0 : 1, x_in, w->rms_gamma, w->w_qkvi, wq_scale, T, cfg->rms_eps,
                                       cfg->rope_theta, pos0, qkv_out, q_att, q_idx, w_idx, cache->k,
                                       cache->v, dsa_kind ? 0 : cache->capacity, cache->k_idx,
                                       cache->k_idx_scale, w8 + lw.proj, st);
@@ -278,7 +283,7 @@ dsa_status_t dsa_layer_step(const dsa_layer_config_t* cfg, const dsa_layer_weigh
     if (dsa::swa_out_fits(T, cfg->window)) {
       // the window is small enough for every output-projection workgroup to recompute it
       e = dsa::launch_swa_out(q_att, cache->k, cache->v, cache->capacity, pos0, T, cfg->window, cfg->sm_scale,
-                              cfg->sink, w->w_o, x_in, x_out, st);
+                              cfg->sink, w->w_o, wo_scale, x_in, x_out, st);
       return e == hipSuccess ? DSA_OK : hip_fail(e, "dsa_layer_step: window attention + output projection");
     }
     e = dsa::launch_attention(1, 0, q_att, cache->k, cache->v, nullptr, nullptr, nullptr, 0, T, 0,
@@ -286,7 +291,7 @@ dsa_status_t dsa_layer_step(const dsa_layer_config_t* cfg, const dsa_layer_weigh
                               w8 + lw.attn, ncu, st);
   }
   if (e != hipSuccess) return hip_fail(e, "dsa_layer_step: attention");
-  e = dsa::launch_proj_out(attn_out, w->w_o, x_in, x_out, T, w8 + lw.proj, st);
+  e = dsa::launch_proj_out(attn_out, w->w_o, wo_scale, x_in, x_out, T, w8 + lw.proj, st);
   if (e != hipSuccess) return hip_fail(e, "dsa_layer_step: output projection");
   return DSA_OK;
 }

@@ -92,6 +92,42 @@ DSA_DEV uint32_t f32_to_e4m3(float x) {
   return s | code;
 }
 
+// ------------------------------------------------------------------ W8A8 activations
+// Per-token e4m3 quantisation of bf16 activations: codes = e4m3(fp32(y * inv)) with
+// inv = fp32(448 / amax) (1 for an all-zero token), dequantisation scale fp32(amax / 448).
+
+// largest magnitude of eight bf16 held as four (lo, hi) pairs
+DSA_DEV float amax_bf16x8(const uint32_t y[4]) {
+  float m = 0.0f;
+#pragma unroll
+  for (int q = 0; q < 4; ++q)
+    m = fmaxf(m, fmaxf(fabsf(__uint_as_float(y[q] << 16)), fabsf(__uint_as_float(y[q] & 0xffff0000u))));
+  return m;
+}
+
+// eight bf16 (four pairs) times inv -> eight e4m3 codes, element i in byte i.  The
+// hardware conversion rounds to nearest even; |y * inv| <= fp32(448 (1 + 2^-24)) stays
+// below the overflow boundary 464, so every product lands on a finite code.
+DSA_DEV uint2 e4m3x8_scaled(const uint32_t y[4], float inv) {
+  int w[2];
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const uint32_t a = y[2 * h], b = y[2 * h + 1];
+    int r = __builtin_amdgcn_cvt_pk_fp8_f32(__uint_as_float(a << 16) * inv,
+                                            __uint_as_float(a & 0xffff0000u) * inv, 0, false);
+    r = __builtin_amdgcn_cvt_pk_fp8_f32(__uint_as_float(b << 16) * inv,
+                                        __uint_as_float(b & 0xffff0000u) * inv, r, true);
+    w[h] = r;
+  }
+  return make_uint2((uint32_t)w[0], (uint32_t)w[1]);
+}
+
+DSA_DEV float wave_max(float v) {
+#pragma unroll
+  for (int d = 32; d >= 1; d >>= 1) v = fmaxf(v, __shfl_xor(v, d, 64));
+  return v;
+}
+
 // ----------------------------------------------------------------------------- keys
 
 // Order-preserving map fp32 -> uint32 (larger score <=> larger key); -0 maps like +0.

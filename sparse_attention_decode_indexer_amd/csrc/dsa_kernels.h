@@ -37,19 +37,21 @@ hipError_t launch_attention(int mode, int kvdt, const void* q, const void* kc, c
                             hipStream_t st);
 
 size_t proj_workspace_bytes();
-hipError_t launch_proj_qkv(int kind, const void* x, const void* gamma, const void* w, int T,
-                           float eps, float theta, int64_t pos0, void* qkv, void* q_att,
-                           void* q_idx, float* w_idx, void* kcache, void* vcache,
-                           int64_t ring_cap, void* kidx, float* kidx_scale, void* ws,
+// wscale: per-row fp32 scales of e4m3 weights (W8A8), or nullptr for bf16 weights
+hipError_t launch_proj_qkv(int kind, const void* x, const void* gamma, const void* w,
+                           const float* wscale, int T, float eps, float theta, int64_t pos0,
+                           void* qkv, void* q_att, void* q_idx, float* w_idx, void* kcache,
+                           void* vcache, int64_t ring_cap, void* kidx, float* kidx_scale, void* ws,
                            hipStream_t st);
-hipError_t launch_proj_out(const void* o, const void* w_o, const void* x, void* xout, int T,
-                           void* ws, hipStream_t st);
+hipError_t launch_proj_out(const void* o, const void* w_o, const float* wscale, const void* x,
+                           void* xout, int T, void* ws, hipStream_t st);
 
 // sliding-window attention fused with the output projection (window + T - 1 <= 160 rows)
 bool swa_out_fits(int T, int window);
 hipError_t launch_swa_out(const void* q, const void* kring, const void* vring, int64_t ring_cap,
                           int64_t pos0, int T, int window, float sm_scale, const float* sink,
-                          const void* w_o, const void* x, void* xout, hipStream_t st);
+                          const void* w_o, const float* w_o_scale, const void* x, void* xout,
+                          hipStream_t st);
 
 hipError_t launch_zero(void* p, size_t bytes, hipStream_t st);
 

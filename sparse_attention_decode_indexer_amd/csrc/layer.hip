@@ -85,7 +85,8 @@ int proj_blocks(int kind, int rpw) {
 
 struct ProjParams {
   const uint16_t* x;        // [T][4096] bf16 (QKV: layer input; OUT: residual input)
-  const uint16_t* w;        // [N][K] bf16
+  const void* w;            // [N][K] bf16, or e4m3 codes (W8A8)
+  const float* wscale;      // [N] fp32 dequantisation scale of each weight row (W8A8)
   int T;
   int rpw;                  // weight rows per workgroup
   // QKV
@@ -117,7 +118,12 @@ struct ProjParams {
 constexpr int kXsStride = kHidden + 8;      // padded LDS row: rows fall in different banks
 
 struct ProjShared {
-  alignas(16) uint16_t xs[kMaxT][kXsStride];  // normalised activations (QKV) or attention output (OUT)
+  // normalised activations (QKV) or attention output (OUT): bf16, or for W8A8 their e4m3
+  // codes in rows of kXsStride bytes
+  alignas(16) uint16_t xs[kMaxT][kXsStride];
+  float amax[kMaxT][8];                        // W8A8: per-wave partial maxima of each token
+  float ascale[kMaxT];                         // W8A8: activation scale of each token
+  float wscale[16];                            // W8A8: scale of each of the block's weight rows
   float red[kProjWaves][16][16];
   float tile[16][16];
   float rc[kMaxT][8];
@@ -126,10 +132,15 @@ struct ProjShared {
   uint32_t last;
 };
 
+// Weights stream in 16-byte units: eight bf16 (one 16x16x32 bf16 step) or sixteen e4m3
+// codes (two 16x16x32 fp8 steps).  Unit j of lane group g covers unit 4 j + g of the
+// wave's k range, and the activation operand is read from the same unit.
 // R8: eight weight rows per workgroup.  The MFMA still has 16 rows, so lanes 8..15 of
-// each 16-lane group load the odd k steps of rows 0..7 (every load lane distinct) and a
-// row rotate by 8 hands those steps to lanes 0..7; MFMA rows 8..15 are never read.
-template <int MODE, int NSTEP, bool R8>
+// each 16-lane group load the odd units of rows 0..7 (every load lane distinct) and a
+// row rotate by 8 hands those units to lanes 0..7; MFMA rows 8..15 are never read.
+// F8 (W8A8): e4m3 weights with a per-row scale; the activations are quantised per token
+// to e4m3 on chip (see e4m3x8_scaled) and the fp32 products are scaled by both scales.
+template <int MODE, int NSTEP, bool R8, bool F8>
 __global__ void __launch_bounds__(kProjThreads) proj_kernel(ProjParams p) {
   __shared__ ProjShared sh;
   const int tid = threadIdx.x;
@@ -139,6 +150,10 @@ __global__ void __launch_bounds__(kProjThreads) proj_kernel(ProjParams p) {
   constexpr int K = MODE == 0 ? kHidden : kHq * kD;    // reduction length (compile time: no divisions)
   constexpr int Kw = K / kProjWaves;                     // per wave (= NSTEP * 32)
   static_assert(Kw == NSTEP * 32, "each wave covers its k range in NSTEP steps of 32");
+  constexpr int ESZ = F8 ? 1 : 2;                        // bytes per weight
+  constexpr int NU = NSTEP * ESZ / 2;                    // 16-byte units per lane group
+  constexpr int XQS = K + 16;                            // W8A8: LDS code row stride (bytes)
+  uint8_t* const xq = reinterpret_cast<uint8_t*>(&sh.xs[0][0]);
   const int kw0 = wave * Kw;
   const int T = p.T;
   const int rpw = p.rpw;
@@ -174,18 +189,34 @@ __global__ void __launch_bounds__(kProjThreads) proj_kernel(ProjParams p) {
   }
   uint4 gv = make_uint4(0u, 0u, 0u, 0u);
   if (MODE == 0) gv = reinterpret_cast<const uint4*>(p.gamma)[tid % kRowThreads];   // gamma[8 j .. 8 j + 8)
+  // W8A8: the scale of weight row (tid & 15) of the block, requested before the weights
+  // so that waiting for it does not wait for them
+  float wsv = 1.0f;
+  if constexpr (F8) {
+    const int lr = tid & 15;
+    int r;
+    if (MODE == 0) {
+      r = block_row(bi, lr < rpw ? lr : 0, rpw);
+      r = r < p.nproj ? r : p.nproj - 1;
+    } else {
+      r = b * rpw + (lr < rpw ? lr : 0);
+    }
+    wsv = p.wscale[r];
+  }
   // Every lane loads (unconditional loads keep the wait counts exact): lanes beyond the
   // real rows repeat row 0's addresses, which the memory pipeline merges, and the MFMA
   // rows they feed are never read.
-  constexpr int NW = R8 ? NSTEP / 2 : NSTEP;
-  static_assert(!R8 || NSTEP % 2 == 0, "R8 pairs the k steps");
+  constexpr int NW = R8 ? NU / 2 : NU;
+  static_assert(!R8 || NU % 2 == 0, "R8 pairs the units");
   Frag8 wf[NW];
   {
-    const uint4* wp = reinterpret_cast<const uint4*>(p.w + (size_t)wrow * K + kw0) + (lane >> 4) +
-                      (R8 ? 4 * (lrow >> 3) : 0);
+    const uint4* wp = reinterpret_cast<const uint4*>(static_cast<const uint8_t*>(p.w) +
+                                                     ((size_t)wrow * K + kw0) * ESZ) +
+                      (lane >> 4) + (R8 ? 4 * (lrow >> 3) : 0);
 #pragma unroll
     for (int i = 0; i < NW; ++i) wf[i].u = wp[(R8 ? 8 : 4) * i];
   }
+
   DSA_MARK(trace, 1);
   // rotary cos/sin of this block's pairs at the block's positions (first: it needs no
   // loaded data, so it runs while the loads are in flight): angle
@@ -265,11 +296,12 @@ __global__ void __launch_bounds__(kProjThreads) proj_kernel(ProjParams p) {
         const float y1 = (__uint_as_float(x4[q] & 0xffff0000u) * r) * __uint_as_float(g4[q] & 0xffff0000u);
         o4[q] = pack_bf16x2(y0, y1);
       }
-      *reinterpret_cast<uint4*>(&sh.xs[t][8 * j8]) = make_uint4(o4[0], o4[1], o4[2], o4[3]);
+      v[u] = make_uint4(o4[0], o4[1], o4[2], o4[3]);
+      if (!F8) *reinterpret_cast<uint4*>(&sh.xs[t][8 * j8]) = v[u];
     }
   }
-  // 2) activations into LDS (QKV: already stored, normalised)
-  if (MODE == 1) {
+  // 2) activations into LDS (QKV bf16: already stored, normalised)
+  if (MODE == 1 && !F8) {
 #pragma unroll
     for (int u = 0; u < NCH; ++u) {
       const int c = tid + u * kProjThreads;
@@ -279,6 +311,35 @@ __global__ void __launch_bounds__(kProjThreads) proj_kernel(ProjParams p) {
       }
     }
   }
+  if (F8) {
+    // W8A8: per-token quantisation of the activations held in v (the normalised input or
+    // the attention output; rows of tokens >= T hold copies of token T-1 and feed MFMA
+    // columns that are never read).  Chunk u of this thread belongs to token
+    // (wave + 16 u) / WPT; the WPT waves of a token publish their maxima, then every
+    // thread forms its token's scale and writes its eight codes.
+    constexpr int WPT = K / 8 / 64;                       // waves per token (8 QKV, 2 OUT)
+    static_assert(NCH * kProjThreads == kMaxT * K / 8 && WPT <= 8, "one chunk per (token, 8 elements)");
+#pragma unroll
+    for (int u = 0; u < NCH; ++u) {
+      const uint32_t y4[4] = {v[u].x, v[u].y, v[u].z, v[u].w};
+      const float m = wave_max(amax_bf16x8(y4));
+      if (lane == 0) sh.amax[(wave + 16 * u) / WPT][wave % WPT] = m;
+    }
+    if (tid < 16) sh.wscale[tid] = wsv;
+    __syncthreads();
+#pragma unroll
+    for (int u = 0; u < NCH; ++u) {
+      const int t = (wave + 16 * u) / WPT;
+      float am = sh.amax[t][0];
+#pragma unroll
+      for (int i = 1; i < WPT; ++i) am = fmaxf(am, sh.amax[t][i]);
+      const float inv = am > 0.0f ? 448.0f / am : 1.0f;
+      const uint32_t y4[4] = {v[u].x, v[u].y, v[u].z, v[u].w};
+      const int kk = ((tid + u * kProjThreads) % (K / 8)) * 8;
+      *reinterpret_cast<uint2*>(xq + t * XQS + kk) = e4m3x8_scaled(y4, inv);
+      if (((tid + u * kProjThreads) % (K / 8)) == 0) sh.ascale[t] = am > 0.0f ? am / 448.0f : 1.0f;
+    }
+  }
   __syncthreads();
   DSA_MARK(trace, 2);
   // 3) MFMA over this wave's k range
@@ -286,23 +347,33 @@ __global__ void __launch_bounds__(kProjThreads) proj_kernel(ProjParams p) {
   {
     const int tok = lane & 15;
 #pragma unroll
-    for (int i = 0; i < NSTEP; ++i) {
+    for (int j = 0; j < NU; ++j) {
+      const int unit = 4 * j + (lane >> 4);
       Frag8 bfr;
-      bfr.u = *reinterpret_cast<const uint4*>(&sh.xs[tok & 7][kw0 + (4 * i + (lane >> 4)) * 8]);
+      if (F8) bfr.u = *reinterpret_cast<const uint4*>(xq + (tok & 7) * XQS + kw0 + unit * 16);
+      else bfr.u = *reinterpret_cast<const uint4*>(&sh.xs[tok & 7][kw0 + unit * 8]);
       if (tok >= kMaxT) bfr.u = make_uint4(0u, 0u, 0u, 0u);
       Frag8 a;
       if constexpr (R8) {
-        a = wf[i >> 1];
-        if (i & 1) {          // odd step: take lane (l + 8) mod 16 of the 16-lane row
+        a = wf[j >> 1];
+        if (j & 1) {          // odd unit: take lane (l + 8) mod 16 of the 16-lane row
           a.u.x = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)a.u.x, 0x128, 0xf, 0xf, true);
           a.u.y = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)a.u.y, 0x128, 0xf, 0xf, true);
           a.u.z = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)a.u.z, 0x128, 0xf, 0xf, true);
           a.u.w = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)a.u.w, 0x128, 0xf, 0xf, true);
         }
       } else {
-        a = wf[i];
+        a = wf[j];
       }
-      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a.v, bfr.v, acc, 0, 0, 0);
+      if constexpr (F8) {
+        // two k steps of 32 codes: bytes 0..7 and 8..15 of the unit
+        const long a0 = (long)(((uint64_t)a.u.y << 32) | a.u.x), a1 = (long)(((uint64_t)a.u.w << 32) | a.u.z);
+        const long b0 = (long)(((uint64_t)bfr.u.y << 32) | bfr.u.x), b1 = (long)(((uint64_t)bfr.u.w << 32) | bfr.u.z);
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_fp8_fp8(a0, b0, acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_fp8_fp8(a1, b1, acc, 0, 0, 0);
+      } else {
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a.v, bfr.v, acc, 0, 0, 0);
+      }
     }
   }
   // D[row][tok]: lane holds tok = lane & 15, rows 4*(lane>>4) + i
@@ -314,6 +385,7 @@ __global__ void __launch_bounds__(kProjThreads) proj_kernel(ProjParams p) {
     float v = sh.red[0][r][c];
 #pragma unroll
     for (int w = 1; w < kProjWaves; ++w) v += sh.red[w][r][c];
+    if (F8) v *= sh.ascale[c & 7] * sh.wscale[r];     // W8A8: dequantise (columns >= T unused)
     sh.tile[r][c] = v;
   }
   __syncthreads();
@@ -404,14 +476,15 @@ __global__ void __launch_bounds__(kProjThreads) proj_kernel(ProjParams p) {
 constexpr size_t kWsKiStage = ctl::kBytes;
 constexpr size_t kWsProjEnd = kWsKiStage + (size_t)kMaxT * kDI * sizeof(float);
 
-hipError_t launch_proj_qkv(int kind, const void* x, const void* gamma, const void* w, int T,
-                           float eps, float theta, int64_t pos0, void* qkv, void* q_att,
-                           void* q_idx, float* w_idx, void* kcache, void* vcache,
-                           int64_t ring_cap, void* kidx, float* kidx_scale, void* ws,
+hipError_t launch_proj_qkv(int kind, const void* x, const void* gamma, const void* w,
+                           const float* wscale, int T, float eps, float theta, int64_t pos0,
+                           void* qkv, void* q_att, void* q_idx, float* w_idx, void* kcache,
+                           void* vcache, int64_t ring_cap, void* kidx, float* kidx_scale, void* ws,
                            hipStream_t st) {
   ProjParams p{};
   p.x = static_cast<const uint16_t*>(x);
-  p.w = static_cast<const uint16_t*>(w);
+  p.w = w;
+  p.wscale = wscale;
   p.T = T;
   p.rpw = kind == 0 ? 16 : 8;                // DSA: 149 workgroups, SWA: 160 (one per CU)
   uint8_t* w8 = static_cast<uint8_t*>(ws);
@@ -439,17 +512,23 @@ hipError_t launch_proj_qkv(int kind, const void* x, const void* gamma, const voi
   p.trace = dsa_trace_buffer() ? dsa_trace_buffer() + 512 * 16 : nullptr;   // rows 512.. of the buffer
 #endif
   constexpr int nstep = kHidden / kProjWaves / 32;
-  if (p.rpw == 8) hipLaunchKernelGGL((proj_kernel<0, nstep, true>), grid, block, 0, st, p);
-  else hipLaunchKernelGGL((proj_kernel<0, nstep, false>), grid, block, 0, st, p);
+  if (wscale) {
+    if (p.rpw == 8) hipLaunchKernelGGL((proj_kernel<0, nstep, true, true>), grid, block, 0, st, p);
+    else hipLaunchKernelGGL((proj_kernel<0, nstep, false, true>), grid, block, 0, st, p);
+  } else {
+    if (p.rpw == 8) hipLaunchKernelGGL((proj_kernel<0, nstep, true, false>), grid, block, 0, st, p);
+    else hipLaunchKernelGGL((proj_kernel<0, nstep, false, false>), grid, block, 0, st, p);
+  }
   return hipGetLastError();
 }
 
-hipError_t launch_proj_out(const void* o, const void* w_o, const void* x, void* xout, int T,
-                           void* ws, hipStream_t st) {
+hipError_t launch_proj_out(const void* o, const void* w_o, const float* wscale, const void* x,
+                           void* xout, int T, void* ws, hipStream_t st) {
   (void)ws;
   ProjParams p{};
   p.x = static_cast<const uint16_t*>(x);
-  p.w = static_cast<const uint16_t*>(w_o);
+  p.w = w_o;
+  p.wscale = wscale;
   p.o = static_cast<const uint16_t*>(o);
   p.xout = static_cast<uint16_t*>(xout);
   p.T = T;
@@ -457,7 +536,8 @@ hipError_t launch_proj_out(const void* o, const void* w_o, const void* x, void* 
   const dim3 grid(kHidden / 16), block(kProjThreads);
   // 1024 / 8 waves / 4 lane groups / 8 = 4
   constexpr int nstep = kHq * kD / kProjWaves / 32;
-  hipLaunchKernelGGL((proj_kernel<1, nstep, false>), grid, block, 0, st, p);
+  if (wscale) hipLaunchKernelGGL((proj_kernel<1, nstep, false, true>), grid, block, 0, st, p);
+  else hipLaunchKernelGGL((proj_kernel<1, nstep, false, false>), grid, block, 0, st, p);
   return hipGetLastError();
 }
 

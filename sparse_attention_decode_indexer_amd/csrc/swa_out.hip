@@ -46,7 +46,8 @@ struct SoParams {
   int window;
   float sm_log2;            // sm_scale * log2(e)
   const float* sink;        // [8] natural-log logits or nullptr
-  const uint16_t* w_o;      // [4096][1024] bf16
+  const void* w_o;          // [4096][1024] bf16, or e4m3 codes (W8A8)
+  const float* w_o_scale;   // [4096] fp32 row scales (W8A8) or nullptr
   const uint16_t* x;        // [T][4096] residual input
   uint16_t* xout;           // [T][4096]
   uint64_t* trace;          // profiling builds: [blocks][16] phase timestamps
@@ -60,6 +61,9 @@ struct SoShared {
   alignas(16) float s[kSoPairs][kSStride];
   float scale[kSoPairs];      // exp2(m - M) / denominator of each (token, head) row
   float tile[16][16];
+  float amax[kMaxT][2];       // W8A8: per-wave maxima of each token's attention output
+  float ascale[kMaxT];        // W8A8: activation scale of each token
+  float wscale[kOutRows];     // W8A8: scale of each of the workgroup's W_o rows
 };
 
 typedef short v4i16 __attribute__((ext_vector_type(4)));
@@ -96,6 +100,7 @@ DSA_DEV uint2 lds_tr16(const uint8_t* addr) {
 
 }  // namespace
 
+template <bool F8>
 __global__ void __launch_bounds__(kSoThreads) swa_out_kernel(SoParams p) {
   __shared__ SoShared sh;
   const int tid = threadIdx.x;
@@ -107,9 +112,14 @@ __global__ void __launch_bounds__(kSoThreads) swa_out_kernel(SoParams p) {
   constexpr int K = kHq * kD;                  // projection reduction length
   constexpr int Kw = K / kSoWaves;             // per wave
   constexpr int NSTEP = Kw / 32;
+  constexpr int NU = F8 ? NSTEP / 2 : NSTEP;   // 16-byte weight units per lane group
+  constexpr int ESZ = F8 ? 1 : 2;
+  constexpr int XQS = K + 16;                  // W8A8: LDS code row stride (bytes)
+  static_assert(NU >= 1, "at least one weight unit per lane");
   const int kw0 = wave * Kw;
   DSA_MARK(p.trace, 0);
-  Frag8 wf[NSTEP];                             // the workgroup's W_o rows (requested below)
+  Frag8 wf[NU];                                // the workgroup's W_o rows (requested below)
+  float wsv = 1.0f;
   // ---- 1) window rows: row u holds position pos0 - W + 1 + u, in ring slot
   //      (base + u) mod cap with base = (pos0 - W + 1) mod cap (cap >= W + T - 1 rows)
   const int U = W + T - 1;
@@ -140,9 +150,12 @@ __global__ void __launch_bounds__(kSoThreads) swa_out_kernel(SoParams p) {
         p.q + ((size_t)(tq < T ? tq : T - 1) * kHq + (pair & 7)) * kD + (tid & 15) * 8);
     // the workgroup's W_o rows (lane & 15 = row, lane >> 4 = k chunk) are requested after
     // the window (needed first); they stream in under the attention
-    const uint4* wp = reinterpret_cast<const uint4*>(p.w_o + (size_t)(b * kOutRows + (lane & 15)) * K + kw0) + (lane >> 4);
+    if constexpr (F8) wsv = p.w_o_scale[b * kOutRows + (tid & 15)];
+    const uint4* wp = reinterpret_cast<const uint4*>(static_cast<const uint8_t*>(p.w_o) +
+                                                     ((size_t)(b * kOutRows + (lane & 15)) * K + kw0) * ESZ) +
+                      (lane >> 4);
 #pragma unroll
-    for (int i = 0; i < NSTEP; ++i) wf[i].u = wp[4 * i];
+    for (int i = 0; i < NU; ++i) wf[i].u = wp[4 * i];
 #pragma unroll
     for (int u = 0; u < NCH; ++u) {
       const int c = tid + u * kSoThreads;
@@ -289,18 +302,45 @@ __global__ void __launch_bounds__(kSoThreads) swa_out_kernel(SoParams p) {
   }
   __syncthreads();
   DSA_MARK(p.trace, 5);
-  // ---- 5) output projection over this wave's k range, partial tiles summed in wave order
   const uint16_t* xs = reinterpret_cast<const uint16_t*>(sh.kq);
+  uint8_t* xq = sh.v;     // W8A8 codes [kMaxT][XQS] (V is no longer needed)
+  if constexpr (F8) {
+    // ---- 4b) per-token quantisation of the attention output: thread tid holds elements
+    //      8 (tid & 127) .. +7 of token tid >> 7 (two waves per token)
+    static_assert(kMaxT * K / 8 == kSoThreads && kMaxT * XQS <= kSoRows * kRowB, "one chunk per thread");
+    const int t = tid >> 7, kk = (tid & 127) * 8;
+    const uint4 y = *reinterpret_cast<const uint4*>(&xs[t * kXsStride + kk]);
+    const uint32_t y4[4] = {y.x, y.y, y.z, y.w};
+    const float m = wave_max(amax_bf16x8(y4));
+    if (lane == 0) sh.amax[t][wave & 1] = m;
+    if (tid < kOutRows) sh.wscale[tid] = wsv;
+    __syncthreads();
+    const float am = fmaxf(sh.amax[t][0], sh.amax[t][1]);
+    *reinterpret_cast<uint2*>(xq + t * XQS + kk) = e4m3x8_scaled(y4, am > 0.0f ? 448.0f / am : 1.0f);
+    if ((tid & 127) == 0) sh.ascale[t] = am > 0.0f ? am / 448.0f : 1.0f;
+    __syncthreads();
+  }
+  // ---- 5) output projection over this wave's k range, partial tiles summed in wave order
   float (*red)[16][16] = reinterpret_cast<float (*)[16][16]>(sh.kq + kMaxT * kXsStride * 2);
   {
     f32x4_t acc = {};
     const int tok = lane & 15;
 #pragma unroll
-    for (int i = 0; i < NSTEP; ++i) {
+    for (int j = 0; j < NU; ++j) {
+      const int unit = 4 * j + (lane >> 4);
       Frag8 bfr;
-      bfr.u = *reinterpret_cast<const uint4*>(&xs[(tok & 7) * kXsStride + kw0 + (4 * i + (lane >> 4)) * 8]);
+      if (F8) bfr.u = *reinterpret_cast<const uint4*>(xq + (tok & 7) * XQS + kw0 + unit * 16);
+      else bfr.u = *reinterpret_cast<const uint4*>(&xs[(tok & 7) * kXsStride + kw0 + unit * 8]);
       if (tok >= kMaxT) bfr.u = make_uint4(0u, 0u, 0u, 0u);
-      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wf[i].v, bfr.v, acc, 0, 0, 0);
+      if constexpr (F8) {
+        const Frag8 a = wf[j];
+        const long a0 = (long)(((uint64_t)a.u.y << 32) | a.u.x), a1 = (long)(((uint64_t)a.u.w << 32) | a.u.z);
+        const long b0 = (long)(((uint64_t)bfr.u.y << 32) | bfr.u.x), b1 = (long)(((uint64_t)bfr.u.w << 32) | bfr.u.z);
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_fp8_fp8(a0, b0, acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_fp8_fp8(a1, b1, acc, 0, 0, 0);
+      } else {
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wf[j].v, bfr.v, acc, 0, 0, 0);
+      }
     }
 #pragma unroll
     for (int i = 0; i < 4; ++i) red[wave][4 * (lane >> 4) + i][lane & 15] = acc[i];
@@ -311,6 +351,7 @@ __global__ void __launch_bounds__(kSoThreads) swa_out_kernel(SoParams p) {
     float v = red[0][r][c];
 #pragma unroll
     for (int w = 1; w < kSoWaves; ++w) v += red[w][r][c];
+    if (F8) v *= sh.ascale[c & 7] * sh.wscale[r];    // W8A8: dequantise (columns >= T unused)
     sh.tile[r][c] = v;
   }
   __syncthreads();
@@ -328,7 +369,8 @@ bool swa_out_fits(int T, int window) { return window >= 1 && window + T - 1 <= k
 
 hipError_t launch_swa_out(const void* q, const void* kring, const void* vring, int64_t ring_cap,
                           int64_t pos0, int T, int window, float sm_scale, const float* sink,
-                          const void* w_o, const void* x, void* xout, hipStream_t st) {
+                          const void* w_o, const float* w_o_scale, const void* x, void* xout,
+                          hipStream_t st) {
   SoParams p{};
   p.q = static_cast<const uint16_t*>(q);
   p.kc = static_cast<const uint8_t*>(kring);
@@ -339,13 +381,15 @@ hipError_t launch_swa_out(const void* q, const void* kring, const void* vring, i
   p.window = window;
   p.sm_log2 = sm_scale * 1.4426950408889634f;
   p.sink = sink;
-  p.w_o = static_cast<const uint16_t*>(w_o);
+  p.w_o = w_o;
+  p.w_o_scale = w_o_scale;
   p.x = static_cast<const uint16_t*>(x);
   p.xout = static_cast<uint16_t*>(xout);
 #ifdef DSA_TRACE
   p.trace = dsa_trace_buffer() ? dsa_trace_buffer() + 768 * 16 : nullptr;   // rows 768.. of the buffer
 #endif
-  hipLaunchKernelGGL(swa_out_kernel, dim3(kHidden / kOutRows), dim3(kSoThreads), 0, st, p);
+  if (w_o_scale) hipLaunchKernelGGL(swa_out_kernel<true>, dim3(kHidden / kOutRows), dim3(kSoThreads), 0, st, p);
+  else hipLaunchKernelGGL(swa_out_kernel<false>, dim3(kHidden / kOutRows), dim3(kSoThreads), 0, st, p);
   return hipGetLastError();
 }
 

@@ -43,7 +43,7 @@ HIDDEN = 4096
 _TID = {
     "q_idx": 1, "k_idx": 2, "w_idx": 3, "q": 4, "k": 5, "v": 6,
     "plant_set": 7, "plant_dir": 8, "x": 9, "w_qkvi": 10, "w_o": 11,
-    "ring_k": 12, "ring_v": 13, "sink": 14,
+    "ring_k": 12, "ring_v": 13, "sink": 14, "gamma": 15,
 }
 
 
@@ -265,6 +265,11 @@ def exact_norm_x(seed: int, T: int, groups=None, scale_exp=(-2, -1, 0, 1, 2)) ->
             row.append(blk[g.permutation(16)])
         out[t] = np.concatenate(row) * np.float32(2.0 ** int(g.choice(scale_exp)))
     return to_bf16_bits(out)
+
+
+def random_gamma(seed: int, std: float = 0.25) -> np.ndarray:
+    """RMSNorm gain [HIDDEN] bf16 bits ~N(1, std) (the module itself uses gamma = 1)."""
+    return to_bf16_bits(1.0 + normal(seed, "gamma", (HIDDEN,), std=std))
 
 
 def module_x(seed: int, T: int) -> np.ndarray:

@@ -122,10 +122,34 @@ DSA_DEV uint2 e4m3x8_scaled(const uint32_t y[4], float inv) {
   return make_uint2((uint32_t)w[0], (uint32_t)w[1]);
 }
 
+// lane exchange inside rows of 16 lanes (DPP): quad permutations and row rotations
+template <int CTRL>
+DSA_DEV float dppf(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xf, 0xf, true));
+}
+// max / sum over the 16 lanes of a row (quads first, then rotations by 4 and 8); every
+// lane ends with the row's maximum; the sum's association depends on the lane, so only
+// one fixed lane's sum is used
+DSA_DEV float row16_max(float v) {
+  v = fmaxf(v, dppf<0xB1>(v));      // quad_perm [1,0,3,2]
+  v = fmaxf(v, dppf<0x4E>(v));      // quad_perm [2,3,0,1]
+  v = fmaxf(v, dppf<0x124>(v));     // row_ror:4
+  return fmaxf(v, dppf<0x128>(v));  // row_ror:8
+}
+// maximum over a whole wave (rows of 16 first, then the four row maxima): wave-uniform
 DSA_DEV float wave_max(float v) {
-#pragma unroll
-  for (int d = 32; d >= 1; d >>= 1) v = fmaxf(v, __shfl_xor(v, d, 64));
-  return v;
+  v = row16_max(v);
+  const float a = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 0));
+  const float b = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 16));
+  const float c = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 32));
+  const float d = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 48));
+  return fmaxf(fmaxf(a, b), fmaxf(c, d));
+}
+DSA_DEV float row16_sum(float v) {
+  v += dppf<0xB1>(v);
+  v += dppf<0x4E>(v);
+  v += dppf<0x124>(v);
+  return v + dppf<0x128>(v);
 }
 
 // ----------------------------------------------------------------------------- keys

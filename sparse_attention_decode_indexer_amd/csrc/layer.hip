@@ -121,9 +121,9 @@ struct ProjShared {
   // normalised activations (QKV) or attention output (OUT): bf16, or for W8A8 their e4m3
   // codes in rows of kXsStride bytes
   alignas(16) uint16_t xs[kMaxT][kXsStride];
-  float amax[kMaxT][8];                        // W8A8: per-wave partial maxima of each token
+  alignas(16) float amax[kMaxT][32];           // W8A8: partial maxima of each token (16-lane rows)
   float ascale[kMaxT];                         // W8A8: activation scale of each token
-  float wscale[16];                            // W8A8: scale of each of the block's weight rows
+  float ainv[kMaxT];                           // W8A8: 448 / amax of each token (1 for amax = 0)
   float red[kProjWaves][16][16];
   float tile[16][16];
   float rc[kMaxT][8];
@@ -189,11 +189,11 @@ __global__ void __launch_bounds__(kProjThreads) proj_kernel(ProjParams p) {
   }
   uint4 gv = make_uint4(0u, 0u, 0u, 0u);
   if (MODE == 0) gv = reinterpret_cast<const uint4*>(p.gamma)[tid % kRowThreads];   // gamma[8 j .. 8 j + 8)
-  // W8A8: the scale of weight row (tid & 15) of the block, requested before the weights
-  // so that waiting for it does not wait for them
+  // W8A8: the scale of weight row (tid >> 4) & 15 of the block (the row this thread
+  // dequantises in the tile reduction), requested before the weights
   float wsv = 1.0f;
   if constexpr (F8) {
-    const int lr = tid & 15;
+    const int lr = (tid >> 4) & 15;
     int r;
     if (MODE == 0) {
       r = block_row(bi, lr < rpw ? lr : 0, rpw);
@@ -300,6 +300,18 @@ __global__ void __launch_bounds__(kProjThreads) proj_kernel(ProjParams p) {
       if (!F8) *reinterpret_cast<uint4*>(&sh.xs[t][8 * j8]) = v[u];
     }
   }
+  // W8A8: partial maxima of |activation| per token, one per 16-lane row (chunk u of this
+  // thread belongs to token (wave + 16 u) / WPT; WPT waves per token)
+  constexpr int WPT = K / 8 / 64;                         // 8 (QKV) or 2 (OUT)
+  if constexpr (F8) {
+    static_assert(NCH * kProjThreads == kMaxT * K / 8 && WPT <= 8, "one chunk per (token, 8 elements)");
+#pragma unroll
+    for (int u = 0; u < NCH; ++u) {
+      const uint32_t y4[4] = {v[u].x, v[u].y, v[u].z, v[u].w};
+      const float m = row16_max(amax_bf16x8(y4));
+      if ((lane & 15) == 0) sh.amax[(wave + 16 * u) / WPT][(wave % WPT) * 4 + (lane >> 4)] = m;
+    }
+  }
   // 2) activations into LDS (QKV bf16: already stored, normalised)
   if (MODE == 1 && !F8) {
 #pragma unroll
@@ -311,36 +323,29 @@ __global__ void __launch_bounds__(kProjThreads) proj_kernel(ProjParams p) {
       }
     }
   }
-  if (F8) {
+  __syncthreads();
+  if constexpr (F8) {
     // W8A8: per-token quantisation of the activations held in v (the normalised input or
     // the attention output; rows of tokens >= T hold copies of token T-1 and feed MFMA
-    // columns that are never read).  Chunk u of this thread belongs to token
-    // (wave + 16 u) / WPT; the WPT waves of a token publish their maxima, then every
-    // thread forms its token's scale and writes its eight codes.
-    constexpr int WPT = K / 8 / 64;                       // waves per token (8 QKV, 2 OUT)
-    static_assert(NCH * kProjThreads == kMaxT * K / 8 && WPT <= 8, "one chunk per (token, 8 elements)");
-#pragma unroll
-    for (int u = 0; u < NCH; ++u) {
-      const uint32_t y4[4] = {v[u].x, v[u].y, v[u].z, v[u].w};
-      const float m = wave_max(amax_bf16x8(y4));
-      if (lane == 0) sh.amax[(wave + 16 * u) / WPT][wave % WPT] = m;
+    // columns that are never read).  Wave t < 8 folds token t's 4 WPT partial maxima into
+    // its scale and reciprocal; then every thread writes the eight codes of each chunk.
+    if (wave < kMaxT) {
+      const float am = wave_max(lane < 4 * WPT ? sh.amax[wave][lane] : 0.0f);
+      if (lane == 0) {
+        sh.ainv[wave] = am > 0.0f ? 448.0f / am : 1.0f;
+        sh.ascale[wave] = am > 0.0f ? am / 448.0f : 1.0f;
+      }
     }
-    if (tid < 16) sh.wscale[tid] = wsv;
     __syncthreads();
 #pragma unroll
     for (int u = 0; u < NCH; ++u) {
       const int t = (wave + 16 * u) / WPT;
-      float am = sh.amax[t][0];
-#pragma unroll
-      for (int i = 1; i < WPT; ++i) am = fmaxf(am, sh.amax[t][i]);
-      const float inv = am > 0.0f ? 448.0f / am : 1.0f;
       const uint32_t y4[4] = {v[u].x, v[u].y, v[u].z, v[u].w};
       const int kk = ((tid + u * kProjThreads) % (K / 8)) * 8;
-      *reinterpret_cast<uint2*>(xq + t * XQS + kk) = e4m3x8_scaled(y4, inv);
-      if (((tid + u * kProjThreads) % (K / 8)) == 0) sh.ascale[t] = am > 0.0f ? am / 448.0f : 1.0f;
+      *reinterpret_cast<uint2*>(xq + t * XQS + kk) = e4m3x8_scaled(y4, sh.ainv[t]);
     }
+    __syncthreads();
   }
-  __syncthreads();
   DSA_MARK(trace, 2);
   // 3) MFMA over this wave's k range
   f32x4_t acc = {};
@@ -385,7 +390,7 @@ __global__ void __launch_bounds__(kProjThreads) proj_kernel(ProjParams p) {
     float v = sh.red[0][r][c];
 #pragma unroll
     for (int w = 1; w < kProjWaves; ++w) v += sh.red[w][r][c];
-    if (F8) v *= sh.ascale[c & 7] * sh.wscale[r];     // W8A8: dequantise (columns >= T unused)
+    if (F8) v *= sh.ascale[c & 7] * wsv;              // W8A8: dequantise (columns >= T unused)
     sh.tile[r][c] = v;
   }
   __syncthreads();

@@ -61,33 +61,12 @@ struct SoShared {
   alignas(16) float s[kSoPairs][kSStride];
   float scale[kSoPairs];      // exp2(m - M) / denominator of each (token, head) row
   float tile[16][16];
-  float amax[kMaxT][2];       // W8A8: per-wave maxima of each token's attention output
+  alignas(16) float amax[kMaxT][8];  // W8A8: partial maxima of each token's attention output
   float ascale[kMaxT];        // W8A8: activation scale of each token
-  float wscale[kOutRows];     // W8A8: scale of each of the workgroup's W_o rows
+  float ainv[kMaxT];          // W8A8: 448 / amax of each token (1 for amax = 0)
 };
 
 typedef short v4i16 __attribute__((ext_vector_type(4)));
-
-// lane exchange inside rows of 16 lanes (DPP): quad permutations and row rotations
-template <int CTRL>
-DSA_DEV float dppf(float v) {
-  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xf, 0xf, true));
-}
-// max / sum over the 16 lanes of a row (quads first, then rotations by 4 and 8); every
-// lane ends with the row's maximum; the sum's association depends on the lane, so only
-// one fixed lane's sum is used
-DSA_DEV float row16_max(float v) {
-  v = fmaxf(v, dppf<0xB1>(v));      // quad_perm [1,0,3,2]
-  v = fmaxf(v, dppf<0x4E>(v));      // quad_perm [2,3,0,1]
-  v = fmaxf(v, dppf<0x124>(v));     // row_ror:4
-  return fmaxf(v, dppf<0x128>(v));  // row_ror:8
-}
-DSA_DEV float row16_sum(float v) {
-  v += dppf<0xB1>(v);
-  v += dppf<0x4E>(v);
-  v += dppf<0x124>(v);
-  return v + dppf<0x128>(v);
-}
 
 // Four 16-bit values through the LDS transpose path: within each 16-lane group, lane q
 // supplies the 8 bytes at its address and receives element (q & 3) of the values
@@ -150,7 +129,8 @@ __global__ void __launch_bounds__(kSoThreads) swa_out_kernel(SoParams p) {
         p.q + ((size_t)(tq < T ? tq : T - 1) * kHq + (pair & 7)) * kD + (tid & 15) * 8);
     // the workgroup's W_o rows (lane & 15 = row, lane >> 4 = k chunk) are requested after
     // the window (needed first); they stream in under the attention
-    if constexpr (F8) wsv = p.w_o_scale[b * kOutRows + (tid & 15)];
+    // W8A8: scale of W_o row (tid >> 4) & 15, the row this thread dequantises in the reduction
+    if constexpr (F8) wsv = p.w_o_scale[b * kOutRows + ((tid >> 4) & 15)];
     const uint4* wp = reinterpret_cast<const uint4*>(static_cast<const uint8_t*>(p.w_o) +
                                                      ((size_t)(b * kOutRows + (lane & 15)) * K + kw0) * ESZ) +
                       (lane >> 4);
@@ -311,13 +291,18 @@ __global__ void __launch_bounds__(kSoThreads) swa_out_kernel(SoParams p) {
     const int t = tid >> 7, kk = (tid & 127) * 8;
     const uint4 y = *reinterpret_cast<const uint4*>(&xs[t * kXsStride + kk]);
     const uint32_t y4[4] = {y.x, y.y, y.z, y.w};
-    const float m = wave_max(amax_bf16x8(y4));
-    if (lane == 0) sh.amax[t][wave & 1] = m;
-    if (tid < kOutRows) sh.wscale[tid] = wsv;
+    const float m = row16_max(amax_bf16x8(y4));
+    if ((lane & 15) == 0) sh.amax[t][(wave & 1) * 4 + (lane >> 4)] = m;
     __syncthreads();
-    const float am = fmaxf(sh.amax[t][0], sh.amax[t][1]);
-    *reinterpret_cast<uint2*>(xq + t * XQS + kk) = e4m3x8_scaled(y4, am > 0.0f ? 448.0f / am : 1.0f);
-    if ((tid & 127) == 0) sh.ascale[t] = am > 0.0f ? am / 448.0f : 1.0f;
+    if (wave < kMaxT) {             // wave t folds token t's eight partial maxima
+      const float am = wave_max(lane < 8 ? sh.amax[wave][lane] : 0.0f);
+      if (lane == 0) {
+        sh.ainv[wave] = am > 0.0f ? 448.0f / am : 1.0f;
+        sh.ascale[wave] = am > 0.0f ? am / 448.0f : 1.0f;
+      }
+    }
+    __syncthreads();
+    *reinterpret_cast<uint2*>(xq + t * XQS + kk) = e4m3x8_scaled(y4, sh.ainv[t]);
     __syncthreads();
   }
   // ---- 5) output projection over this wave's k range, partial tiles summed in wave order
@@ -351,7 +336,7 @@ __global__ void __launch_bounds__(kSoThreads) swa_out_kernel(SoParams p) {
     float v = red[0][r][c];
 #pragma unroll
     for (int w = 1; w < kSoWaves; ++w) v += red[w][r][c];
-    if (F8) v *= sh.ascale[c & 7] * sh.wscale[r];    // W8A8: dequantise (columns >= T unused)
+    if (F8) v *= sh.ascale[c & 7] * wsv;             // W8A8: dequantise (columns >= T unused)
     sh.tile[r][c] = v;
   }
   __syncthreads();

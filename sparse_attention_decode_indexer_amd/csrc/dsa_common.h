@@ -268,8 +268,7 @@ namespace ctl {
 constexpr int kError = 640;      // sticky error word (1 = a wait timed out)
 constexpr int kEpoch = 768;      // launch counter (tags of the tagged slots)
 constexpr int kDone = 1024;      // [8] per-token completion counters, stride 64
-constexpr int kEpochT = 1536;    // [8] per-token launch counters, stride 16
-constexpr int kFlags = 2048;     // [8][32] per-(token, split) tagged completion flags
+constexpr int kTauG = 2048;      // [8] tagged slots (64-bit, stride 16 words): per-token tau
 constexpr int kWords = 3072;
 constexpr size_t kBytes = 16384;
 }  // namespace ctl
@@ -300,6 +299,22 @@ DSA_DEV uint32_t next_epoch(uint32_t e) { return (e + 1u) & 0x7fffffffu; }
 // Wave-wide wait for slots[0 .. n) (n >= 1, n <= 64 * N) to carry `tag`; returns the
 // minimum of their values.  A wait longer than kSpinLimit sets the sticky error word and
 // gives up, so a launch whose workgroups are not all resident ends instead of hanging.
+// Wait until one tagged slot carries `tag` and return its value (the wave polls one
+// address: one load per round).
+DSA_DEV uint32_t wait_tagged_one(const uint64_t* slot, uint32_t tag, uint32_t* ctl_words) {
+  uint64_t v = ald64(slot);
+  const uint64_t t0 = __builtin_amdgcn_s_memrealtime();
+  while ((uint32_t)(v >> 32) != tag) {
+    __builtin_amdgcn_s_sleep(1);
+    if (__builtin_amdgcn_s_memrealtime() - t0 > kSpinLimit) {
+      if ((threadIdx.x & 63) == 0) ast(ctl_words + ctl::kError, 1u);
+      break;
+    }
+    v = ald64(slot);
+  }
+  return (uint32_t)v;
+}
+
 template <int N>
 DSA_DEV uint32_t wait_tagged_min(const uint64_t* slots, int n, uint32_t tag, uint32_t* ctl_words) {
   const int lane = threadIdx.x & 63;

@@ -386,19 +386,17 @@ struct SelShared {
   uint32_t scan[32];
 };
 
-// m-th largest of the 64 values held by the lanes of one wave (1 <= m <= 64): each
-// lane counts the values ranked above its own (larger, or equal in a lower lane); the
-// lane of rank m-1 holds the answer.
+// m-th largest of the 64 values held by the lanes of one wave (1 <= m <= 64): the
+// largest x with at least m lanes holding a value >= x, built bit by bit from the top
+// (one compare and one ballot count per bit).
 DSA_DEV uint32_t mth_largest_lanes(uint32_t v, int m) {
-  const int lane = threadIdx.x & 63;
-  int rank = 0;
+  uint32_t r = 0u;
 #pragma unroll
-  for (int o = 0; o < 64; ++o) {
-    const uint32_t w = __builtin_amdgcn_readlane(v, o);
-    rank += (w > v) || (w == v && o < lane);
+  for (int b = 31; b >= 0; --b) {
+    const uint32_t c = r | (1u << b);
+    if (__builtin_popcountll(__ballot(v >= c)) >= m) r = c;
   }
-  const uint64_t bal = __ballot(rank == m - 1);
-  return __builtin_amdgcn_readlane(v, __builtin_ctzll(bal));
+  return r;
 }
 
 constexpr int kRegPer = 16;                                  // candidates per lane
@@ -988,14 +986,22 @@ __global__ void __launch_bounds__(kSelThreads, 1) select_kernel(SelParams p) {
   DSA_MARK(p.trace, 3);
   // ---------------- P2: wave t takes token t: tau = min of the published bounds, then
   // the chunk's visible scores >= tau go out in position order (one ballot per 64
-  // positions, running offset) and the wave publishes their count.
+  // positions, running offset) and the wave publishes their count.  Workgroup t alone
+  // gathers token t's bounds and republishes their minimum in one tagged slot, which
+  // every other workgroup polls (a single address instead of n_part slots per poller).
   if (wave < T) {
     const int t = wave;
     uint32_t tm = 0u;
-    if (p.m > 0) {                       // wait for every participating bound of token t
-      const uint64_t* slots = p.tauv + (size_t)t * kMaxWG;
-      tm = p.n_part <= 256 ? wait_tagged_min<4>(slots, p.n_part, tag, p.ctl)
-                           : wait_tagged_min<16>(slots, p.n_part, tag, p.ctl);
+    if (p.m > 0) {
+      uint64_t* tslot = reinterpret_cast<uint64_t*>(p.ctl + ctl::kTauG) + 8 * t;
+      if (wg == t) {                     // wait for every participating bound of token t
+        const uint64_t* slots = p.tauv + (size_t)t * kMaxWG;
+        tm = p.n_part <= 256 ? wait_tagged_min<4>(slots, p.n_part, tag, p.ctl)
+                             : wait_tagged_min<16>(slots, p.n_part, tag, p.ctl);
+        if (lane == 0) ast64(tslot, ((uint64_t)tag << 32) | tm);
+      } else {
+        tm = wait_tagged_one(tslot, tag, p.ctl);
+      }
     }
     DSA_MARK(p.trace, 5);
     // score >= tau as a float compare (equal keys <=> equal floats, -0 == +0)
@@ -1005,11 +1011,31 @@ __global__ void __launch_bounds__(kSelThreads, 1) select_kernel(SelParams p) {
     const int nseg = p.chunk / 64;                                        // a multiple of 8
     const int seg_vis = lim >= 0 ? ((lim >> 6) + 8) & ~7 : 0;            // segments up to lim, rounded to 8
     const int nloop = seg_vis < nseg ? seg_vis : nseg;
+    const int nfull = (lim + 1) >> 6;                                     // segments wholly visible
     uint64_t* dst = p.cand + ((size_t)t * p.nwg + wg) * p.chunk;
     const float* row = sh.sc[t];
     const uint64_t lt = (1ull << lane) - 1ull;
     uint32_t off = 0;
-    for (int s0 = 0; s0 < nloop; s0 += 8) {
+    int s0 = 0;
+    // batches of 8 wholly visible segments: one compare per segment decides
+    for (; s0 + 8 <= nfull; s0 += 8) {
+      float v[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) v[u] = row[(s0 + u) * 64 + lane];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const bool q = v[u] >= tauf;
+        const uint64_t m = __ballot(q);
+        if (m != 0ull) {                 // wave-uniform: most segments hold no candidate
+          if (q)
+            ast64(dst + off + (uint32_t)__builtin_popcountll(m & lt),
+                  ((uint64_t)(uint32_t)(c0 + (s0 + u) * 64 + lane) << 32) | order_key(v[u]));
+          off += (uint32_t)__builtin_popcountll(m);
+        }
+      }
+    }
+    // the rest, up to the last visible position
+    for (; s0 < nloop; s0 += 8) {
       float v[8];
 #pragma unroll
       for (int u = 0; u < 8; ++u) v[u] = row[(s0 + u) * 64 + lane];
@@ -1018,7 +1044,7 @@ __global__ void __launch_bounds__(kSelThreads, 1) select_kernel(SelParams p) {
         const int i = (s0 + u) * 64 + lane;
         const bool q = (i <= lim) & (v[u] >= tauf);
         const uint64_t m = __ballot(q);
-        if (m != 0ull) {                 // wave-uniform: most segments hold no candidate
+        if (m != 0ull) {
           if (q)
             ast64(dst + off + (uint32_t)__builtin_popcountll(m & lt),
                   ((uint64_t)(uint32_t)(c0 + i) << 32) | order_key(v[u]));

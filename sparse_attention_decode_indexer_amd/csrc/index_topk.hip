@@ -818,8 +818,10 @@ __global__ void __launch_bounds__(kSelThreads, 1) select_kernel(SelParams p) {
   const int64_t c0 = (int64_t)wg * p.chunk;
   const int T = p.T;
   DSA_MARK(p.trace, 0);
-  const uint32_t epoch = ald(p.ctl + ctl::kEpoch);
-  const uint32_t tag = epoch + 1u;                       // this launch's slot tag
+  // The launch counter (read with a device-scope load, slow to return) is requested after
+  // the prologue's loads, so that waiting for the queries and the first key tiles does
+  // not wait for it; it is first needed when the tau bound is published.
+  uint32_t epoch = 0u;
   // ---------------- P1: scores of this chunk into LDS
   int64_t nk64 = p.L - c0;
   nk64 = nk64 < 0 ? 0 : (nk64 > p.chunk ? p.chunk : nk64);
@@ -840,8 +842,8 @@ __global__ void __launch_bounds__(kSelThreads, 1) select_kernel(SelParams p) {
     // tiles in flight without draining the memory counter at branch merges.
     auto tile_of = [&](int j) { return c0 + (int64_t)(wave + (j < jlast ? j : jlast) * kSelWaves) * kTile; };
     // The block's queries and head weights are staged in LDS (the score area is free
-    // until the scan starts); their loads go out first, then the first key tiles and the
-    // chunk's row scales, whose latency overlaps the query set-up below.
+    // until the scan starts); their loads go out first, then the first key tiles (with
+    // their row scales), whose latency overlaps the query set-up below.
     uint16_t* qs = reinterpret_cast<uint16_t*>(&sh.sc[0][0]);        // [kMaxT][kHI][kDI]
     float* wsh = &sh.sc[1][0];                                        // [kMaxT][kHI]
     constexpr int QROW = kHI * kDI / 8;                               // uint4 per token
@@ -859,16 +861,7 @@ __global__ void __launch_bounds__(kSelThreads, 1) select_kernel(SelParams p) {
     if (tid < kMaxT * kHI / 4) w4 = reinterpret_cast<const float4*>(p.w_idx)[(tw < T ? tw : T - 1) * 4 + (tid & 3)];
     KeyTile<KDT> buf[PF];
 #pragma unroll
-    for (int i = 0; i < PF; ++i) load_key_tile<KDT, false>(p.k_idx, p.k_scale, p.L, tile_of(i), buf[i]);
-    constexpr int PERS = kMaxChunk / kSelThreads;
-    float sv[PERS];
-    if constexpr (KDT == 1) {
-#pragma unroll
-      for (int q = 0; q < PERS; ++q) {
-        const int i = tid + q * kSelThreads;
-        sv[q] = p.k_scale[c0 + (i < nkeys ? i : (nkeys > 0 ? nkeys - 1 : 0))];
-      }
-    }
+    for (int i = 0; i < PF; ++i) load_key_tile<KDT, true>(p.k_idx, p.k_scale, p.L, tile_of(i), buf[i]);
 #pragma unroll
     for (int u = 0; u < QPER; ++u) {
       const int i = tid + u * kSelThreads;
@@ -882,13 +875,10 @@ __global__ void __launch_bounds__(kSelThreads, 1) select_kernel(SelParams p) {
     load_q_frags_lds<RTW>(qs, qa);
     load_w_lds<RTW>(wsh, wv);
     build_qlin_lds<kSelThreads>(qs, wsh, sh.ql);
-    if constexpr (KDT == 1) {
-#pragma unroll
-      for (int q = 0; q < PERS; ++q) sh.kscale[tid + q * kSelThreads] = sv[q];
-    }
     __syncthreads();
     Frag8 qf[4];
     load_qlin_frags<RTW>(sh.ql, 0, qf);
+    epoch = ald(p.ctl + ctl::kEpoch);
     DSA_MARK(p.trace, 1);
     DSA_MARK_CLK(p.trace, 14);
     if (nmine > 0) {
@@ -901,11 +891,11 @@ __global__ void __launch_bounds__(kSelThreads, 1) select_kernel(SelParams p) {
           const int j = base + i;
           const int jc = j < nmine ? j : nmine - 1;      // the tile actually loaded (clamped)
           const int sl = (wave + jc * kSelWaves) * kTile + (lane & 31);
-          const float scale = (KDT == 1) ? sh.kscale[sl & (kMaxChunk - 1)] : 1.0f;
+          const float scale = buf[i].scale;
           const bool keep = j < nmine;
           Frag8 kb[4];
           keys_to_bf16<KDT>(buf[i], kb);
-          load_key_tile<KDT, false>(p.k_idx, p.k_scale, p.L, tile_of(j + PF), buf[i]);
+          load_key_tile<KDT, true>(p.k_idx, p.k_scale, p.L, tile_of(j + PF), buf[i]);
           const f32x16_t lacc = mma_k64(qf, kb);
           f32x16_t acc = mma_k64(qa[0], kb);
           float* row = keep ? &sh.sc[half][sl] : &sh.dump[lane];
@@ -923,6 +913,7 @@ __global__ void __launch_bounds__(kSelThreads, 1) select_kernel(SelParams p) {
       }
     }
   } else {
+    epoch = ald(p.ctl + ctl::kEpoch);
     constexpr int PER = kMaxChunk / kSelThreads;
     for (int t = 0; t < T; ++t) {
       const float* src = p.scores + (size_t)t * p.ld + c0;
@@ -939,6 +930,7 @@ __global__ void __launch_bounds__(kSelThreads, 1) select_kernel(SelParams p) {
       }
     }
   }
+  const uint32_t tag = epoch + 1u;                       // this launch's slot tag
   __syncthreads();
   DSA_MARK(p.trace, 2);
   if (wg >= T) DSA_MARK_CLK(p.trace, 13);     // core clock over P1 (profiling builds)

@@ -430,16 +430,22 @@ DSA_DEV void resolve_regs(const SelParams& p, int t, SelShared& sh, const uint64
     kstar = kmin;
     take_eq = 0xffffffffu;
   } else {
-    // MSB-first radix select on the bits where candidate keys differ
+    // MSB-first radix select on the bits where candidate keys differ: a first pass of 12
+    // bits (4096 bins), then, when the boundary bin holds at most 64 keys, one wave
+    // finds the cut among them directly; otherwise 11-bit passes continue
     const uint32_t diff = kmin ^ kmax;
     int hi = diff ? 32 - __builtin_clz(diff) : 0;
     uint32_t known = hi >= 32 ? 0u : (kmax & ~((1u << hi) - 1u));
     uint32_t need = kk;
+    uint32_t* binl = hist + 4096;                                     // [64] keys of a small bin
+    bool first = true;
     while (hi > 0) {
-      const int dbits = hi < 11 ? hi : 11;
+      const int maxd = first ? 12 : 11;
+      first = false;
+      const int dbits = hi < maxd ? hi : maxd;
       const int lo = hi - dbits;
       const uint32_t nb = 1u << dbits;
-      for (int b2 = tid; b2 < 2048; b2 += kSelThreads) hist[b2] = 0u;
+      for (int b2 = tid; b2 < 4096; b2 += kSelThreads) hist[b2] = 0u;
       __syncthreads();
       const uint32_t pmask = hi >= 32 ? 0u : ~((1u << hi) - 1u);
 #pragma unroll
@@ -449,7 +455,7 @@ DSA_DEV void resolve_regs(const SelParams& p, int t, SelShared& sh, const uint64
       }
       __syncthreads();
       // largest digit d with count(digit >= d) >= need
-      constexpr int PER = 2048 / kSelThreads;
+      constexpr int PER = 4096 / kSelThreads;
       const int rb = kSelThreads - 1 - tid;           // reversed thread order
       uint32_t loc = 0;
 #pragma unroll
@@ -485,6 +491,33 @@ DSA_DEV void resolve_regs(const SelParams& p, int t, SelShared& sh, const uint64
         known = block_min_u32<kSelThreads>(bmin, sh.scan);
         need = 0xffffffffu;      // every key equal to the cut is taken
         hi = 0;
+      } else if (hi > 0 && in_bin <= 64u) {
+        // small boundary bin: gather its keys (any order) and let wave 0 take the
+        // need-th largest; `need` then counts the keys equal to it that are taken
+        if (tid == 0) misc[2] = 0u;
+        __syncthreads();
+        const uint32_t pm = ~((1u << hi) - 1u);
+#pragma unroll
+        for (int i = 0; i < kRegPer; ++i) {
+          const uint32_t key = (uint32_t)e[i];
+          if (((uint32_t)i < nmine) & ((key & pm) == known)) binl[atomicAdd(&misc[2], 1u)] = key;
+        }
+        __syncthreads();
+        if (wave == 0) {
+          const bool mine = (uint32_t)lane < in_bin;
+          const uint32_t v = mine ? binl[lane] : 0u;
+          const uint32_t cut = mth_largest_lanes(v, (int)need);
+          const uint32_t gt = (uint32_t)__builtin_popcountll(__ballot(mine & (v > cut)));
+          if (lane == 0) {
+            misc[0] = cut;
+            misc[1] = need - gt;
+          }
+        }
+        __syncthreads();
+        known = misc[0];
+        need = misc[1];
+        hi = 0;
+        __syncthreads();
       }
     }
     kstar = known;
@@ -541,8 +574,8 @@ DSA_DEV void resolve_regs(const SelParams& p, int t, SelShared& sh, const uint64
 // K*, then the first `take_eq` (in position order) of the keys equal to K*.
 DSA_DEV void resolve_token(const SelParams& p, int t, SelShared& sh, uint32_t epoch) {
   uint32_t* pre = reinterpret_cast<uint32_t*>(&sh.sc[0][0]);         // [nwg + 1]
-  uint32_t* hist = pre + 1040;                                        // [2048]
-  uint32_t* misc = hist + 2048;                                       // small
+  uint32_t* hist = pre + 1040;                                        // [4096] + [64] bin list
+  uint32_t* misc = hist + 4096 + 64;                                  // small
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
@@ -604,7 +637,7 @@ DSA_DEV void resolve_token(const SelParams& p, int t, SelShared& sh, uint32_t ep
   // ..., lane = element, so each load instruction reads one contiguous run; 16 segments
   // are in flight per wave.
   uint64_t* lc = reinterpret_cast<uint64_t*>(misc + 16);              // 8-byte aligned
-  const uint32_t lds_cap = (uint32_t)((sizeof(sh.sc) - (1040 + 2048 + 16) * 4) / 8);
+  const uint32_t lds_cap = (uint32_t)((sizeof(sh.sc) - (1040 + 4096 + 64 + 16) * 4) / 8);
   const bool in_lds = nc > 0 && nc <= lds_cap;
   uint32_t kmin = 0xffffffffu, kmax = 0u;
   if (in_lds) {

@@ -150,7 +150,21 @@ TOPK_CASES = [
     ("mid-nc", 2, 12000, 2048, lambda g, T, L: g.standard_normal((T, L)).astype(np.float32)),
     ("sparse-big", 8, 262144, 2048,
      lambda g, T, L: np.where(g.random((T, L)) < 0.003, 100 + g.random((T, L)), g.random((T, L))).astype(np.float32)),
+    # ties at the cut inside a small boundary bin of the first radix digit (the bin's keys
+    # are resolved by one wave), taken whole or in part
+    ("cut-ties", 8, 70000, 2048, lambda g, T, L: _with_cut_ties(g, g.standard_normal((T, L)), 2048, 6)),
+    ("cut-ties-many", 4, 40000, 1000, lambda g, T, L: _with_cut_ties(g, g.random((T, L)), 1000, 40)),
 ]
+
+
+def _with_cut_ties(g, s, k, n):
+    """Copies of each row's k-th largest early score written at n random early positions."""
+    s = s.astype(np.float32)
+    T, L = s.shape
+    for t in range(T):
+        v = np.sort(s[t, : L - T])[-k]
+        s[t, g.choice(L - T, n, replace=False)] = v
+    return s
 
 
 @pytest.mark.parametrize("case", TOPK_CASES, ids=[c[0] for c in TOPK_CASES])

@@ -548,18 +548,31 @@ DSA_DEV void resolve_regs(const SelParams& p, int t, SelShared& sh, const uint64
   int32_t* out = p.idx + (size_t)t * p.k;
   const uint64_t lt = (1ull << lane) - 1ull;
   uint32_t er = eq_base, o = sel_base;
+  if (eb <= take_eq) {
+    // every key equal to the cut is taken (the usual case): selected <=> key >= cut
 #pragma unroll
-  for (int i = 0; i < kRegPer; ++i) {
-    const uint32_t key = (uint32_t)e[i];
-    const bool v = (uint32_t)i < nmine;
-    const bool eq = v & (key == kstar);
-    const uint64_t me = __ballot(eq);
-    const bool sel = v & ((key > kstar) | (eq & (er + (uint32_t)__builtin_popcountll(me & lt) < take_eq)));
-    const uint64_t ms = __ballot(sel);
-    const uint32_t oo = o + (uint32_t)__builtin_popcountll(ms & lt);
-    if (sel & (oo < kk)) out[oo] = (int32_t)(e[i] >> 32);
-    er += (uint32_t)__builtin_popcountll(me);
-    o += (uint32_t)__builtin_popcountll(ms);
+    for (int i = 0; i < kRegPer; ++i) {
+      const uint32_t key = (uint32_t)e[i];
+      const bool sel = ((uint32_t)i < nmine) & (key >= kstar);
+      const uint64_t ms = __ballot(sel);
+      const uint32_t oo = o + (uint32_t)__builtin_popcountll(ms & lt);
+      if (sel & (oo < kk)) out[oo] = (int32_t)(e[i] >> 32);
+      o += (uint32_t)__builtin_popcountll(ms);
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < kRegPer; ++i) {
+      const uint32_t key = (uint32_t)e[i];
+      const bool v = (uint32_t)i < nmine;
+      const bool eq = v & (key == kstar);
+      const uint64_t me = __ballot(eq);
+      const bool sel = v & ((key > kstar) | (eq & (er + (uint32_t)__builtin_popcountll(me & lt) < take_eq)));
+      const uint64_t ms = __ballot(sel);
+      const uint32_t oo = o + (uint32_t)__builtin_popcountll(ms & lt);
+      if (sel & (oo < kk)) out[oo] = (int32_t)(e[i] >> 32);
+      er += (uint32_t)__builtin_popcountll(me);
+      o += (uint32_t)__builtin_popcountll(ms);
+    }
   }
   DSA_MARK(p.trace, 12);
   for (int i = (int)kk + tid; i < p.k; i += kSelThreads) out[i] = -1;

@@ -226,3 +226,36 @@ def test_layer_step_graph_replays_match_direct_launch(dsa, kind, L, T):
             got["k_idx_scale"] = down(ks)
         for key in got:
             assert np.array_equal(got[key], ref[key]), (rep, key)
+
+
+@pytest.mark.parametrize("w8a8", [False, True])
+def test_dsa_layer_step_full_context(dsa, w8a8):
+    """The DSA layer step at the benchmark's size (L = 2^20, T = 8, top-2048): appended rows
+    bitwise, the selection within the score band of the fp64 scores of the GPU's own rotated
+    queries over the updated cache, and the output against the teacher-forced oracle."""
+    L, T, top_k = 1 << 20, 8, 2048
+    pos0 = L - T
+    lay = synth.layer_inputs("dsa", 5, L, T, seed=21)
+    x = synth.module_x(21, T)
+    w8 = synth.w8a8_weights(lay) if w8a8 else None
+    g = _run_layer(dsa, "dsa", lay, x, T, pos0, top_k=top_k, w8=w8)
+    kw = dict(top_k=top_k)
+    wq, wo = lay.w_qkvi, lay.w_o
+    if w8a8:
+        wq, wo = w8[0], w8[2]
+        kw.update(w_qkvi_scale=w8[1], w_o_scale=w8[3])
+    cache = {"k": lay.k.copy(), "v": lay.v.copy(), "k_idx": lay.k_idx.copy(), "k_idx_scale": lay.k_idx_scale.copy()}
+    tf = O.layer_step("dsa", x, lay.gamma, wq, wo, cache, pos0, teacher={"qkv": g["qkv"], "idx": g["idx"]}, **kw)
+    assert np.array_equal(g["k"][pos0:L], g["qkv"][:, 1024:1152])
+    assert np.array_equal(g["v"][pos0:L], g["qkv"][:, 1152:1280])
+    assert np.array_equal(g["k_idx"][pos0:L], cache["k_idx"][pos0:L])
+    assert np.array_equal(g["k_idx_scale"][pos0:L], cache["k_idx_scale"][pos0:L])
+    krows = O.dequant_rows(cache["k_idx"][:L], "fp8", cache["k_idx_scale"][:L])
+    qi = O.decode_bf16(g["qkv"][:, 1280:2304]).reshape(T, 16, 64)
+    wi = O.decode_bf16(g["qkv"][:, 2368:2384])
+    r, S = O.indexer_scores(qi, wi, krows, pos0, with_abs=True)
+    ridx, _ = O.topk_indices(r, pos0, top_k)
+    okb, nd = tie_band_ok(g["idx"], ridx, r, S, pos0, top_k)
+    assert okb, nd
+    gx = O.decode_bf16(g["x_out"])
+    assert np.all(np.abs(gx - tf["x_out"]) <= 2e-2 * np.maximum(1.0, np.abs(tf["x_out"])))

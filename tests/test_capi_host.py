@@ -94,3 +94,25 @@ def test_validation_errors_without_launch():
     cfg.hidden = 4096
     c.k_idx = None
     assert L() == E["DSA_ERR_NULL"]
+
+
+def test_w8a8_and_stream_read_validation_without_launch():
+    import sparse_attention_decode_indexer_amd as dsa
+    E = {v: k for k, v in dsa.STATUS.items()}
+    cfg = dsa.layer_config(dsa.LAYER_DSA)
+    c = dsa.LayerCache(FAKE, FAKE, FAKE, FAKE, 1000)
+
+    def L(w):
+        return dsa.dsa_layer_step(cfg, w, c, FAKE, FAKE + 0x1000, 8, 100, ws=FAKE, ws_bytes=1 << 40,
+                                  stream=0, raise_on_error=False)
+    assert L(dsa.LayerWeights(FAKE, FAKE, FAKE, 7, None, None)) == E["DSA_ERR_DTYPE"]
+    # e4m3 weights need both row-scale vectors; bf16 weights take none
+    assert L(dsa.LayerWeights(FAKE, FAKE, FAKE, dsa.FP8_E4M3, None, None)) == E["DSA_ERR_DTYPE"]
+    assert L(dsa.LayerWeights(FAKE, FAKE, FAKE, dsa.FP8_E4M3, FAKE, None)) == E["DSA_ERR_DTYPE"]
+    assert L(dsa.LayerWeights(FAKE, FAKE, FAKE, dsa.BF16, FAKE, FAKE)) == E["DSA_ERR_DTYPE"]
+    r = lambda *a: dsa.dsa_stream_read(*a, stream=0, raise_on_error=False)
+    assert r(None, 1024, FAKE) == E["DSA_ERR_NULL"]
+    assert r(FAKE, 1024, None) == E["DSA_ERR_NULL"]
+    assert r(MIS, 1024, FAKE) == E["DSA_ERR_ALIGN"]
+    assert r(FAKE, 1000, FAKE) == E["DSA_ERR_ALIGN"]
+    assert r(FAKE, 0, FAKE) == E["DSA_ERR_SHAPE"]

@@ -318,24 +318,27 @@ __global__ void __launch_bounds__(64) attn_merge_kernel(AttnParams p) {
     a[j] = pt[((size_t)js * kHq + hh) * kPartStride + 4 + d0 + jl];
   }
   const float mj = jl < ns ? ml.x : -__builtin_inff();
-  float M = mj;
-#pragma unroll
-  for (int d = 16; d >= 1; d >>= 1) M = fmaxf(M, __shfl_xor(M, d, 64));
+  const float mr = row16_max(mj);                          // rows of 16 lanes, then the two rows
+  float M = fmaxf(__int_as_float(__builtin_amdgcn_readlane(__float_as_int(mr), 0)),
+                  __int_as_float(__builtin_amdgcn_readlane(__float_as_int(mr), 16)));
   float s2 = -__builtin_inff();
   if (p.sink) s2 = p.sink[hh] * 1.4426950408889634f;
   M = fmaxf(M, s2);
+  // split j's rescale factor (0 for empty or missing splits, whose accumulators are 0) and
+  // denominator go through LDS, so every lane walks the splits in order without lane moves
+  __shared__ float wsc[32], lsc[32];
+  if (lane < 32) {
+    wsc[lane] = (M != -__builtin_inff() && mj != -__builtin_inff()) ? exp2f(mj - M) : 0.0f;
+    lsc[lane] = jl < ns ? ml.y : 0.0f;
+  }
+  __syncthreads();
   float den = 0.0f, o = 0.0f;
   if (M != -__builtin_inff()) {
-    const float scj = exp2f(mj - M);       // lane j: split j's rescale factor
 #pragma unroll
     for (int j = 0; j < 32; ++j) {
-      const float ms = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(mj), j));
-      if ((j < ns) & (ms != -__builtin_inff())) {     // splits in order; empty ones skipped
-        const float sc = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(scj), j));
-        const float ls = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(ml.y), j));
-        den = fmaf(ls, sc, den);
-        o = fmaf(a[j], sc, o);
-      }
+      const float sc = wsc[j];
+      den = fmaf(lsc[j], sc, den);
+      o = fmaf(a[j], sc, o);
     }
     if (s2 != -__builtin_inff()) den += exp2f(s2 - M);
   }

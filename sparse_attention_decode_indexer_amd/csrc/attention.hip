@@ -201,8 +201,13 @@ __global__ void __launch_bounds__(NT) attn_kernel(AttnParams p) {
     m = z[0];
 #pragma unroll
     for (int i = 1; i < RPT; ++i) m = fmaxf(m, z[i]);
-#pragma unroll
-    for (int d = 16; d >= 1; d >>= 1) m = fmaxf(m, __shfl_xor(m, d, 64));
+    // head h lives in one half-wave (rows 0-1 or 2-3 of 16 lanes): DPP row maxima, then
+    // one row-pair swap
+    m = row16_max(m);
+    {
+      const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(m), __float_as_uint(m), false, false);
+      m = fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+    }
     float pz[RPT];
 #pragma unroll
     for (int i = 0; i < RPT; ++i) pz[i] = 0.0f;
@@ -213,8 +218,16 @@ __global__ void __launch_bounds__(NT) attn_kernel(AttnParams p) {
     l = pz[0];
 #pragma unroll
     for (int i = 1; i < RPT; ++i) l += pz[i];
-#pragma unroll
-    for (int d = 16; d >= 1; d >>= 1) l += __shfl_xor(l, d, 64);
+    // half-wave sum: DPP row sums and a row-pair swap; the association differs by lane, so
+    // the half's first lane's total is broadcast to the half
+    l = row16_sum(l);
+    {
+      const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(l), __float_as_uint(l), false, false);
+      l = __uint_as_float(r[0]) + __uint_as_float(r[1]);
+      const float l0 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(l), 0));
+      const float l1 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(l), 32));
+      l = (lane & 32) ? l1 : l0;
+    }
 #pragma unroll
     for (int i = 0; i < RPT; ++i) {
       if (KVDT == 1) pz[i] *= sh.vscl[jj + 32 * i];

@@ -163,39 +163,48 @@ DSA_DEV uint32_t order_key(float f) {
 
 // ----------------------------------------------------------------------------- scans
 
-// Inclusive prefix sum across one wavefront (64 lanes).
+// DPP lane exchange of a 32-bit value: `old` where the source lane is outside the row or
+// the row is masked off (row shifts, row broadcasts)
+template <int CTRL, int ROWMASK = 0xf>
+DSA_DEV uint32_t dppu(uint32_t v) {
+  return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, CTRL, ROWMASK, 0xf, false);
+}
+
+// Inclusive prefix sum across one wavefront (64 lanes, all active): row shifts by 1, 2, 4
+// and 8 within rows of 16 lanes, then lane 15's total into rows 1 and 3 and lane 31's into
+// rows 2 and 3.
 DSA_DEV uint32_t wave_incl_scan(uint32_t v) {
-  const int lane = threadIdx.x & 63;
-#pragma unroll
-  for (int d = 1; d < 64; d <<= 1) {
-    uint32_t o = __shfl_up(v, d, 64);
-    if (lane >= d) v += o;
-  }
+  v += dppu<0x111>(v);           // row_shr:1
+  v += dppu<0x112>(v);           // row_shr:2
+  v += dppu<0x114>(v);           // row_shr:4
+  v += dppu<0x118>(v);           // row_shr:8
+  v += dppu<0x142, 0xa>(v);      // row_bcast:15
+  v += dppu<0x143, 0xc>(v);      // row_bcast:31
   return v;
 }
 
-DSA_DEV uint32_t wave_sum(uint32_t v) {
-#pragma unroll
-  for (int d = 32; d >= 1; d >>= 1) v += __shfl_xor(v, d, 64);
-  return v;
-}
-
+// max / min over the wave (all lanes active; every lane gets the result): rotations
+// within rows of 16, then the row-pair and half-wave swaps
 DSA_DEV uint32_t wave_max_u32(uint32_t v) {
-#pragma unroll
-  for (int d = 32; d >= 1; d >>= 1) v = max(v, (uint32_t)__shfl_xor(v, d, 64));
-  return v;
+  v = max(v, dppu<0xB1>(v));
+  v = max(v, dppu<0x4E>(v));
+  v = max(v, dppu<0x124>(v));
+  v = max(v, dppu<0x128>(v));
+  const auto r = __builtin_amdgcn_permlane16_swap(v, v, false, false);
+  v = max((uint32_t)r[0], (uint32_t)r[1]);
+  const auto q = __builtin_amdgcn_permlane32_swap(v, v, false, false);
+  return max((uint32_t)q[0], (uint32_t)q[1]);
 }
 
 DSA_DEV uint32_t wave_min_u32(uint32_t v) {
-#pragma unroll
-  for (int d = 32; d >= 1; d >>= 1) v = min(v, (uint32_t)__shfl_xor(v, d, 64));
-  return v;
-}
-
-DSA_DEV float wave_max_f32(float v) {
-#pragma unroll
-  for (int d = 32; d >= 1; d >>= 1) v = fmaxf(v, __shfl_xor(v, d, 64));
-  return v;
+  v = min(v, dppu<0xB1>(v));
+  v = min(v, dppu<0x4E>(v));
+  v = min(v, dppu<0x124>(v));
+  v = min(v, dppu<0x128>(v));
+  const auto r = __builtin_amdgcn_permlane16_swap(v, v, false, false);
+  v = min((uint32_t)r[0], (uint32_t)r[1]);
+  const auto q = __builtin_amdgcn_permlane32_swap(v, v, false, false);
+  return min((uint32_t)q[0], (uint32_t)q[1]);
 }
 
 // Exclusive prefix sum across the block; `scratch` holds >= nwaves+1 words of LDS.

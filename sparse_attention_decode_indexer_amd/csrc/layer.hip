@@ -275,8 +275,15 @@ __global__ void __launch_bounds__(kProjThreads) proj_kernel(ProjParams p) {
       const float4 q0 = *reinterpret_cast<const float4*>(&scr[wave * kRowThreads + lane * 8]);
       const float4 q1 = *reinterpret_cast<const float4*>(&scr[wave * kRowThreads + lane * 8 + 4]);
       float a = ((((((q0.x + q0.y) + q0.z) + q0.w) + q1.x) + q1.y) + q1.z) + q1.w;
-#pragma unroll
-      for (int d = 32; d >= 1; d >>= 1) a += __shfl_xor(a, d, 64);
+      // wave total in lane 0: DPP sums within rows of 16, then the row-pair and
+      // half-wave swaps (a fixed order)
+      a = row16_sum(a);
+      {
+        const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(a), __float_as_uint(a), false, false);
+        a = __uint_as_float(r[0]) + __uint_as_float(r[1]);
+        const auto h = __builtin_amdgcn_permlane32_swap(__float_as_uint(a), __float_as_uint(a), false, false);
+        a = __uint_as_float(h[0]) + __uint_as_float(h[1]);
+      }
       if (lane == 0) sh.rnorm[wave] = 1.0f / sqrtf(a / (float)kHidden + p.eps);
     }
     __syncthreads();
@@ -465,9 +472,7 @@ __global__ void __launch_bounds__(kProjThreads) proj_kernel(ProjParams p) {
   if (wave < T) {                 // wave t: lane = dim
     const int t = wave, d = lane;
     const float v = aldf(p.kistage + t * kDI + d);
-    float am = fabsf(v);
-#pragma unroll
-    for (int dd = 32; dd >= 1; dd >>= 1) am = fmaxf(am, __shfl_xor(am, dd, 64));
+    const float am = wave_max(fabsf(v));
     const float scale = am > 0.0f ? am / 448.0f : 1.0f;
     const uint32_t code = f32_to_e4m3(v / scale);
     const int64_t pos = p.pos0 + t;

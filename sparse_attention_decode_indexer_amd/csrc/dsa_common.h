@@ -243,6 +243,27 @@ DSA_DEV uint32_t block_max_u32(uint32_t v, uint32_t* scratch) {
   return r;
 }
 
+// minimum and maximum over the block in one exchange (scratch holds 2 * NT / 64 words)
+template <int NT>
+DSA_DEV void block_minmax_u32(uint32_t& mn, uint32_t& mx, uint32_t* scratch) {
+  constexpr int NW = NT / 64;
+  const uint32_t a = wave_min_u32(mn), b = wave_max_u32(mx);
+  if ((threadIdx.x & 63) == 0) {
+    scratch[threadIdx.x >> 6] = a;
+    scratch[NW + (threadIdx.x >> 6)] = b;
+  }
+  __syncthreads();
+  uint32_t r0 = scratch[0], r1 = scratch[NW];
+#pragma unroll
+  for (int i = 1; i < NW; ++i) {
+    r0 = min(r0, scratch[i]);
+    r1 = max(r1, scratch[NW + i]);
+  }
+  __syncthreads();
+  mn = r0;
+  mx = r1;
+}
+
 template <int NT>
 DSA_DEV uint32_t block_min_u32(uint32_t v, uint32_t* scratch) {
   constexpr int NW = NT / 64;

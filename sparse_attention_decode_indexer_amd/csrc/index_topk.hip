@@ -399,6 +399,18 @@ DSA_DEV uint32_t mth_largest_lanes(uint32_t v, int m) {
   return r;
 }
 
+// The same when every lane that counts holds a value whose bits from `hi` up equal
+// those of `known` (lower bits of `known` zero) and the other lanes hold 0, which no
+// candidate key equals: only the low `hi` bits are searched.
+DSA_DEV uint32_t mth_largest_lanes_below(uint32_t v, int m, uint32_t known, int hi) {
+  uint32_t r = known;
+  for (int b = hi - 1; b >= 0; --b) {
+    const uint32_t c = r | (1u << b);
+    if (__builtin_popcountll(__ballot(v >= c)) >= m) r = c;
+  }
+  return r;
+}
+
 constexpr int kRegPer = 16;                                  // candidates per lane
 constexpr uint32_t kRegCands = kSelThreads * kRegPer;        // register-resident limit
 
@@ -422,8 +434,7 @@ DSA_DEV void resolve_regs(const SelParams& p, int t, SelShared& sh, const uint64
     const uint32_t g = w0 + 64u * i + lane;
     e[i] = lc[g < nc ? g : nc - 1];
   }
-  kmin = block_min_u32<kSelThreads>(kmin, sh.scan);
-  kmax = block_max_u32<kSelThreads>(kmax, sh.scan);
+  block_minmax_u32<kSelThreads>(kmin, kmax, sh.scan);
   DSA_MARK(p.trace, 10);
   uint32_t kstar, take_eq;
   if (kk == nc) {
@@ -439,14 +450,18 @@ DSA_DEV void resolve_regs(const SelParams& p, int t, SelShared& sh, const uint64
     uint32_t need = kk;
     uint32_t* binl = hist + 4096;                                     // [64] keys of a small bin
     bool first = true;
+    bool first_pass_zeroed = true;
     while (hi > 0) {
       const int maxd = first ? 12 : 11;
       first = false;
       const int dbits = hi < maxd ? hi : maxd;
       const int lo = hi - dbits;
       const uint32_t nb = 1u << dbits;
-      for (int b2 = tid; b2 < 4096; b2 += kSelThreads) hist[b2] = 0u;
-      __syncthreads();
+      if (!first_pass_zeroed) {          // the first pass finds the histogram cleared
+        for (int b2 = tid; b2 < 4096; b2 += kSelThreads) hist[b2] = 0u;
+        __syncthreads();
+      }
+      first_pass_zeroed = false;
       const uint32_t pmask = hi >= 32 ? 0u : ~((1u << hi) - 1u);
 #pragma unroll
       for (int i = 0; i < kRegPer; ++i) {
@@ -506,7 +521,7 @@ DSA_DEV void resolve_regs(const SelParams& p, int t, SelShared& sh, const uint64
         if (wave == 0) {
           const bool mine = (uint32_t)lane < in_bin;
           const uint32_t v = mine ? binl[lane] : 0u;
-          const uint32_t cut = mth_largest_lanes(v, (int)need);
+          const uint32_t cut = mth_largest_lanes_below(v, (int)need, known, hi);
           const uint32_t gt = (uint32_t)__builtin_popcountll(__ballot(mine & (v > cut)));
           if (lane == 0) {
             misc[0] = cut;
@@ -646,44 +661,68 @@ DSA_DEV void resolve_token(const SelParams& p, int t, SelShared& sh, uint32_t ep
   uint32_t kk = (uint32_t)((int64_t)p.k < vis ? p.k : vis);
   if (kk > nc) kk = nc;   // cannot happen when the bound holds; keeps reads in range
   const uint64_t* base = p.cand + (size_t)t * nwg * p.chunk;
-  // Bring the candidates on chip when they fit: wave w copies source segments w, w+8,
-  // ..., lane = element, so each load instruction reads one contiguous run; 16 segments
-  // are in flight per wave.
+  // Bring the candidates on chip when they fit.  Wave w copies source segments w, w+8,
+  // ...; one load instruction covers two of them (lanes 0-31 and 32-63, element = lane &
+  // 31), since most segments hold fewer than 32 candidates.  Elements 32-63 follow in a
+  // second batch when one of the wave's segments is that long, longer runs in a loop.
   uint64_t* lc = reinterpret_cast<uint64_t*>(misc + 16);              // 8-byte aligned
   const uint32_t lds_cap = (uint32_t)((sizeof(sh.sc) - (1040 + 4096 + 64 + 16) * 4) / 8);
   const bool in_lds = nc > 0 && nc <= lds_cap;
   uint32_t kmin = 0xffffffffu, kmax = 0u;
   if (in_lds) {
-    constexpr int U = 16;
-    for (int s0 = wave; s0 < nwg; s0 += kSelWaves * U) {
-      uint64_t v[U];
-      uint32_t b0[U], n[U];
+    // the first radix pass finds its histogram cleared (separate from pre[] and lc[])
+    for (int b2 = tid; b2 < 4096; b2 += kSelThreads) hist[b2] = 0u;
+    constexpr int UP = 16;                                            // segment pairs per round
+    const int wv = __builtin_amdgcn_readfirstlane(wave);
+    const int hl = lane >> 5;
+    const uint32_t el = (uint32_t)lane & 31u;
+    for (int s0 = wv; s0 < nwg; s0 += kSelWaves * 2 * UP) {
+      uint32_t b0[UP], n[UP], so[UP];
 #pragma unroll
-      for (int u = 0; u < U; ++u) {
-        const int sgi = s0 + kSelWaves * u;
-        const int sc = sgi < nwg ? sgi : nwg - 1;
-        b0[u] = pre[sc];
-        n[u] = sgi < nwg ? pre[sc + 1] - b0[u] : 0u;
-        // slot 0 of every segment exists, so the clamped read stays in the workspace
-        v[u] = ald64(base + (size_t)sc * p.chunk + ((uint32_t)lane < n[u] ? (uint32_t)lane : 0u));
+      for (int u = 0; u < UP; ++u) {
+        const int sg = s0 + kSelWaves * (2 * u + hl);
+        const int sc = sg < nwg ? sg : nwg - 1;
+        const uint32_t x0 = pre[sc], x1 = pre[sc + 1];
+        b0[u] = x0;
+        n[u] = sg < nwg ? x1 - x0 : 0u;
+        so[u] = (uint32_t)sc * (uint32_t)p.chunk;                     // < kMaxWG * kMaxChunk
       }
+      uint64_t v[UP];
+      // slot 0 of every segment exists, so the clamped reads stay in the workspace
 #pragma unroll
-      for (int u = 0; u < U; ++u) {
-        if ((uint32_t)lane < n[u]) {
-          lc[b0[u] + lane] = v[u];
+      for (int u = 0; u < UP; ++u) v[u] = ald64(base + so[u] + (el < n[u] ? el : 0u));
+      bool lng = false;
+#pragma unroll
+      for (int u = 0; u < UP; ++u) {
+        if (el < n[u]) {
+          lc[b0[u] + el] = v[u];
           kmin = min(kmin, (uint32_t)v[u]);
           kmax = max(kmax, (uint32_t)v[u]);
         }
+        lng |= n[u] > 32u;
       }
+      if (__ballot(lng) != 0ull) {
 #pragma unroll
-      for (int u = 0; u < U; ++u) {
-        if (n[u] > 64u) {                // long segments (few): the rest, 64 at a time
-          const uint64_t* src = base + (size_t)(s0 + kSelWaves * u) * p.chunk;
-          for (uint32_t j = 64u + lane; j < n[u]; j += 64u) {
-            const uint64_t x = ald64(src + j);
-            lc[b0[u] + j] = x;
-            kmin = min(kmin, (uint32_t)x);
-            kmax = max(kmax, (uint32_t)x);
+        for (int u = 0; u < UP; ++u) v[u] = ald64(base + so[u] + (el + 32u < n[u] ? el + 32u : 0u));
+        bool vlong = false;
+#pragma unroll
+        for (int u = 0; u < UP; ++u) {
+          if (el + 32u < n[u]) {
+            lc[b0[u] + 32u + el] = v[u];
+            kmin = min(kmin, (uint32_t)v[u]);
+            kmax = max(kmax, (uint32_t)v[u]);
+          }
+          vlong |= n[u] > 64u;
+        }
+        if (__ballot(vlong) != 0ull) {
+#pragma unroll 1
+          for (int u = 0; u < UP; ++u) {
+            for (uint32_t j = 64u + el; j < n[u]; j += 32u) {
+              const uint64_t x = ald64(base + so[u] + j);
+              lc[b0[u] + j] = x;
+              kmin = min(kmin, (uint32_t)x);
+              kmax = max(kmax, (uint32_t)x);
+            }
           }
         }
       }
@@ -713,8 +752,7 @@ DSA_DEV void resolve_token(const SelParams& p, int t, SelShared& sh, uint32_t ep
       kmax = max(kmax, key);
     }
   }
-  kmin = block_min_u32<kSelThreads>(kmin, sh.scan);
-  kmax = block_max_u32<kSelThreads>(kmax, sh.scan);
+  block_minmax_u32<kSelThreads>(kmin, kmax, sh.scan);
   DSA_MARK(p.trace, 10);
   uint32_t kstar;
   uint32_t take_eq;

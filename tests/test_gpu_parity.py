@@ -154,7 +154,18 @@ TOPK_CASES = [
     # are resolved by one wave), taken whole or in part
     ("cut-ties", 8, 70000, 2048, lambda g, T, L: _with_cut_ties(g, g.standard_normal((T, L)), 2048, 6)),
     ("cut-ties-many", 4, 40000, 1000, lambda g, T, L: _with_cut_ties(g, g.random((T, L)), 1000, 40)),
+    # runs of high scores: some workgroups then hold 33-64 and hundreds of candidates
+    ("clustered", 4, 70000, 2048,
+     lambda g, T, L: _with_runs(g, g.standard_normal((T, L)), [(1000, 300), (20000, 30), (40100, 60)])),
 ]
+
+
+def _with_runs(g, s, runs):
+    """Scores 5 + U(0,1) over each (start, length) run of positions."""
+    s = s.astype(np.float32)
+    for a, n in runs:
+        s[:, a:a + n] = (5 + g.random((s.shape[0], n))).astype(np.float32)
+    return s
 
 
 def _with_cut_ties(g, s, k, n):

@@ -415,31 +415,33 @@ constexpr int kRegPer = 16;                                  // candidates per l
 constexpr uint32_t kRegCands = kSelThreads * kRegPer;        // register-resident limit
 
 // Register-resident tail of the selection for nc <= kRegCands candidates already in LDS
-// (position order): wave w holds elements [w*R, (w+1)*R) as 64-element blocks (lane =
-// element), so ballots give position-ordered ranks.  Radix passes histogram the
-// registers; the compaction counts (above, equal) per wave in one pass and writes in a
-// second.
+// (position order): wave w holds elements [w*R, (w+1)*R) as NB 64-element blocks (lane
+// = element), so ballots give position-ordered ranks.  Radix passes histogram the
+// registers; the compaction counts per wave in one pass and writes in a second.
+template <int NB>
 DSA_DEV void resolve_regs(const SelParams& p, int t, SelShared& sh, const uint64_t* lc,
                           uint32_t nc, uint32_t kk, uint32_t kmin, uint32_t kmax,
                           uint32_t* hist, uint32_t* misc) {
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
-  const uint32_t R = ((nc + kSelWaves - 1) / kSelWaves + 63) & ~63u;   // <= 64 * kRegPer
+  const uint32_t R = ((nc + kSelWaves - 1) / kSelWaves + 63) & ~63u;   // <= 64 * NB
   const uint32_t w0 = min(nc, (uint32_t)wave * R), w1 = min(nc, w0 + R);
   const uint32_t nmine = (w1 > w0 + lane) ? (w1 - w0 - lane + 63u) / 64u : 0u;
-  uint64_t e[kRegPer];
+  uint64_t e[NB];
 #pragma unroll
-  for (int i = 0; i < kRegPer; ++i) {
+  for (int i = 0; i < NB; ++i) {
     const uint32_t g = w0 + 64u * i + lane;
     e[i] = lc[g < nc ? g : nc - 1];
   }
   block_minmax_u32<kSelThreads>(kmin, kmax, sh.scan);
   DSA_MARK(p.trace, 10);
   uint32_t kstar, take_eq;
+  bool all_eq = false;                 // every key equal to the cut is taken (known early)
   if (kk == nc) {
     kstar = kmin;
     take_eq = 0xffffffffu;
+    all_eq = true;
   } else {
     // MSB-first radix select on the bits where candidate keys differ: a first pass of 12
     // bits (4096 bins), then, when the boundary bin holds at most 64 keys, one wave
@@ -464,8 +466,8 @@ DSA_DEV void resolve_regs(const SelParams& p, int t, SelShared& sh, const uint64
       first_pass_zeroed = false;
       const uint32_t pmask = hi >= 32 ? 0u : ~((1u << hi) - 1u);
 #pragma unroll
-      for (int i = 0; i < kRegPer; ++i) {
-        const uint32_t key = (uint32_t)e[i];
+      for (int i = 0; i < NB; ++i) {
+          const uint32_t key = (uint32_t)e[i];
         if (((uint32_t)i < nmine) & ((key & pmask) == known)) atomicAdd(&hist[(key >> lo) & (nb - 1u)], 1u);
       }
       __syncthreads();
@@ -494,17 +496,19 @@ DSA_DEV void resolve_regs(const SelParams& p, int t, SelShared& sh, const uint64
       hi = lo;
       const uint32_t in_bin = hist[d];
       __syncthreads();
+      if (hi == 0) all_eq = need == in_bin;   // the last digit fixed every bit
       if (need == in_bin && hi > 0) {
         // the whole boundary bin is taken: the cut is its smallest key
         const uint32_t pm = ~((1u << hi) - 1u);
         uint32_t bmin = 0xffffffffu;
 #pragma unroll
-        for (int i = 0; i < kRegPer; ++i) {
-          const uint32_t key = (uint32_t)e[i];
+        for (int i = 0; i < NB; ++i) {
+              const uint32_t key = (uint32_t)e[i];
           if (((uint32_t)i < nmine) & ((key & pm) == known)) bmin = min(bmin, key);
         }
         known = block_min_u32<kSelThreads>(bmin, sh.scan);
         need = 0xffffffffu;      // every key equal to the cut is taken
+        all_eq = true;
         hi = 0;
       } else if (hi > 0 && in_bin <= 64u) {
         // small boundary bin: gather its keys (any order) and let wave 0 take the
@@ -513,8 +517,8 @@ DSA_DEV void resolve_regs(const SelParams& p, int t, SelShared& sh, const uint64
         __syncthreads();
         const uint32_t pm = ~((1u << hi) - 1u);
 #pragma unroll
-        for (int i = 0; i < kRegPer; ++i) {
-          const uint32_t key = (uint32_t)e[i];
+        for (int i = 0; i < NB; ++i) {
+              const uint32_t key = (uint32_t)e[i];
           if (((uint32_t)i < nmine) & ((key & pm) == known)) binl[atomicAdd(&misc[2], 1u)] = key;
         }
         __syncthreads();
@@ -523,14 +527,17 @@ DSA_DEV void resolve_regs(const SelParams& p, int t, SelShared& sh, const uint64
           const uint32_t v = mine ? binl[lane] : 0u;
           const uint32_t cut = mth_largest_lanes_below(v, (int)need, known, hi);
           const uint32_t gt = (uint32_t)__builtin_popcountll(__ballot(mine & (v > cut)));
+          const uint32_t eq = (uint32_t)__builtin_popcountll(__ballot(mine & (v == cut)));
           if (lane == 0) {
             misc[0] = cut;
             misc[1] = need - gt;
+            misc[3] = eq == need - gt;   // the bin holds every key equal to the cut
           }
         }
         __syncthreads();
         known = misc[0];
         need = misc[1];
+        all_eq = misc[3] != 0u;
         hi = 0;
         __syncthreads();
       }
@@ -539,36 +546,51 @@ DSA_DEV void resolve_regs(const SelParams& p, int t, SelShared& sh, const uint64
     take_eq = need;
   }
   DSA_MARK(p.trace, 11);
-  // per-wave counts of keys above and equal to the cut
-  uint32_t cgt = 0, ceq = 0;
-#pragma unroll
-  for (int i = 0; i < kRegPer; ++i) {
-    const uint32_t key = (uint32_t)e[i];
-    const bool v = (uint32_t)i < nmine;
-    cgt += (uint32_t)__builtin_popcountll(__ballot(v & (key > kstar)));
-    ceq += (uint32_t)__builtin_popcountll(__ballot(v & (key == kstar)));
-  }
-  uint32_t* wq = sh.wcnt;           // [8] above counts, then [8] equal counts
-  if (lane == 0) { wq[wave] = cgt; wq[kSelWaves + wave] = ceq; }
-  __syncthreads();
-  uint32_t eq_base = 0, sel_base = 0, eb = 0;
-#pragma unroll
-  for (int j = 0; j < kSelWaves; ++j) {
-    const uint32_t gj = wq[j], ej = wq[kSelWaves + j];
-    const uint32_t rem = take_eq > eb ? take_eq - eb : 0u;
-    const uint32_t sj = gj + (ej < rem ? ej : rem);
-    if (j < wave) { eq_base += ej; sel_base += sj; }
-    eb += ej;
-  }
+  // Compaction in position order: per-wave counts give each wave's first output slot.
+  // When every key equal to the cut is taken (known from the radix step, or found from
+  // the counts) a key is selected iff it is >= the cut and one count per wave suffices;
+  // otherwise keys above and equal to the cut are counted apart and the first take_eq
+  // equal keys in position order are taken.
   int32_t* out = p.idx + (size_t)t * p.k;
   const uint64_t lt = (1ull << lane) - 1ull;
-  uint32_t er = eq_base, o = sel_base;
-  if (eb <= take_eq) {
-    // every key equal to the cut is taken (the usual case): selected <=> key >= cut
+  uint32_t* wq = sh.wcnt;           // [8] selected (or above) counts, then [8] equal counts
+  uint32_t o = 0, er = 0;
+  if (all_eq) {
+    uint32_t cs = 0;
 #pragma unroll
-    for (int i = 0; i < kRegPer; ++i) {
+    for (int i = 0; i < NB; ++i) {
+      cs += (uint32_t)__builtin_popcountll(__ballot(((uint32_t)i < nmine) & ((uint32_t)e[i] >= kstar)));
+    }
+    if (lane == 0) wq[wave] = cs;
+    __syncthreads();
+#pragma unroll
+    for (int j = 0; j < kSelWaves; ++j) o += j < wave ? wq[j] : 0u;
+  } else {
+    uint32_t cgt = 0, ceq = 0;
+#pragma unroll
+    for (int i = 0; i < NB; ++i) {
       const uint32_t key = (uint32_t)e[i];
-      const bool sel = ((uint32_t)i < nmine) & (key >= kstar);
+      const bool v = (uint32_t)i < nmine;
+      cgt += (uint32_t)__builtin_popcountll(__ballot(v & (key > kstar)));
+      ceq += (uint32_t)__builtin_popcountll(__ballot(v & (key == kstar)));
+    }
+    if (lane == 0) { wq[wave] = cgt; wq[kSelWaves + wave] = ceq; }
+    __syncthreads();
+    uint32_t eb = 0;
+#pragma unroll
+    for (int j = 0; j < kSelWaves; ++j) {
+      const uint32_t gj = wq[j], ej = wq[kSelWaves + j];
+      const uint32_t rem = take_eq > eb ? take_eq - eb : 0u;
+      const uint32_t sj = gj + (ej < rem ? ej : rem);
+      if (j < wave) { er += ej; o += sj; }
+      eb += ej;
+    }
+    all_eq = eb <= take_eq;
+  }
+  if (all_eq) {
+#pragma unroll
+    for (int i = 0; i < NB; ++i) {
+      const bool sel = ((uint32_t)i < nmine) & ((uint32_t)e[i] >= kstar);
       const uint64_t ms = __ballot(sel);
       const uint32_t oo = o + (uint32_t)__builtin_popcountll(ms & lt);
       if (sel & (oo < kk)) out[oo] = (int32_t)(e[i] >> 32);
@@ -576,7 +598,7 @@ DSA_DEV void resolve_regs(const SelParams& p, int t, SelShared& sh, const uint64
     }
   } else {
 #pragma unroll
-    for (int i = 0; i < kRegPer; ++i) {
+    for (int i = 0; i < NB; ++i) {
       const uint32_t key = (uint32_t)e[i];
       const bool v = (uint32_t)i < nmine;
       const bool eq = v & (key == kstar);
@@ -730,7 +752,11 @@ DSA_DEV void resolve_token(const SelParams& p, int t, SelShared& sh, uint32_t ep
     __syncthreads();
     DSA_MARK(p.trace, 9);
     if (nc <= kRegCands) {
-      resolve_regs(p, t, sh, lc, nc, kk, kmin, kmax, hist, misc);
+      // blocks of 64 candidates per wave: the register passes are unrolled to that many
+      const uint32_t nb = (((nc + kSelWaves - 1) / kSelWaves + 63) & ~63u) / 64u;
+      if (nb <= 8u) resolve_regs<8>(p, t, sh, lc, nc, kk, kmin, kmax, hist, misc);
+      else if (nb <= 12u) resolve_regs<12>(p, t, sh, lc, nc, kk, kmin, kmax, hist, misc);
+      else resolve_regs<kRegPer>(p, t, sh, lc, nc, kk, kmin, kmax, hist, misc);
       return;
     }
   }

@@ -189,6 +189,12 @@ __global__ void __launch_bounds__(kProjThreads) proj_kernel(ProjParams p) {
   }
   uint4 gv = make_uint4(0u, 0u, 0u, 0u);
   if (MODE == 0) gv = reinterpret_cast<const uint4*>(p.gamma)[tid % kRowThreads];   // gamma[8 j .. 8 j + 8)
+  // OUT: the residual element this thread adds at the end, requested ahead of the weights
+  uint16_t xres = 0;
+  if (MODE == 1) {
+    const int r = tid >> 4, t = tid & 15;
+    if (tid < 256 && r < rpw && t < T) xres = p.x[(size_t)t * kHidden + b * rpw + r];
+  }
   // W8A8: the scale of weight row (tid >> 4) & 15 of the block (the row this thread
   // dequantises in the tile reduction), requested before the weights
   float wsv = 1.0f;
@@ -408,8 +414,7 @@ __global__ void __launch_bounds__(kProjThreads) proj_kernel(ProjParams p) {
     const int r = tid >> 4, t = tid & 15;
     if (tid < 256 && r < rpw && t < T) {
       const size_t o = (size_t)t * kHidden + b * rpw + r;
-      const float xr = bf16_to_f32(p.x[o]);
-      p.xout[o] = f32_to_bf16(sh.tile[r][t] + xr);
+      p.xout[o] = f32_to_bf16(sh.tile[r][t] + bf16_to_f32(xres));
     }
     return;
   }

@@ -16,7 +16,8 @@
 //      base-2 exponentials, the sink in the denominator); P is written back as bf16
 //      hi + lo parts (P = hi + lo to ~2^-16 relative);
 //   4  O = P V on the matrix cores (both parts, fp32 accumulation; V read with LDS
-//      transpose loads), normalised and rounded to bf16 in LDS -- the attention output;
+//      transpose loads; eight waves), normalised and rounded to bf16 in LDS -- the
+//      attention output;
 //   5  the output projection of that block plus the residual, as the unfused kernel.
 // Every workgroup computes the same attention output bit for bit (same code, same
 // order), so the projection sees one consistent input.
@@ -99,6 +100,8 @@ __global__ void __launch_bounds__(kSoThreads) swa_out_kernel(SoParams p) {
   DSA_MARK(p.trace, 0);
   Frag8 wf[NU];                                // the workgroup's W_o rows (requested below)
   float wsv = 1.0f;
+  uint16_t xres = 0;                           // residual element of the final add
+  float sinkv = 0.0f;                          // sink logit of this thread's softmax row
   // ---- 1) window rows: row u holds position pos0 - W + 1 + u, in ring slot
   //      (base + u) mod cap with base = (pos0 - W + 1) mod cap (cap >= W + T - 1 rows)
   const int U = W + T - 1;
@@ -127,6 +130,13 @@ __global__ void __launch_bounds__(kSoThreads) swa_out_kernel(SoParams p) {
     const int pair = tid >> 4, tq = pair >> 3;
     const uint4 qv = *reinterpret_cast<const uint4*>(
         p.q + ((size_t)(tq < T ? tq : T - 1) * kHq + (pair & 7)) * kD + (tid & 15) * 8);
+    // the residual element this thread adds at the end and the sink logit of its softmax
+    // row are requested now, ahead of W_o, so that neither wait later holds up the other
+    {
+      const int r = tid >> 4, t = tid & 15;
+      if (tid < 256 && t < T) xres = p.x[(size_t)t * kHidden + b * kOutRows + r];
+      if (p.sink) sinkv = p.sink[(tid >> 4) & 7];
+    }
     // the workgroup's W_o rows (lane & 15 = row, lane >> 4 = k chunk) are requested after
     // the window (needed first); they stream in under the attention
     // W8A8: scale of W_o row (tid >> 4) & 15, the row this thread dequantises in the reduction
@@ -211,7 +221,7 @@ __global__ void __launch_bounds__(kSoThreads) swa_out_kernel(SoParams p) {
     }
     l = row16_sum(l);
     if (j == 0) {
-      const float sink2 = p.sink ? p.sink[pair & 7] * 1.4426950408889634f : -__builtin_inff();
+      const float sink2 = p.sink ? sinkv * 1.4426950408889634f : -__builtin_inff();
       const float M = fmaxf(m, sink2);
       float sc = 0.0f, den = 0.0f;
       if (M != -__builtin_inff()) {
@@ -226,12 +236,12 @@ __global__ void __launch_bounds__(kSoThreads) swa_out_kernel(SoParams p) {
   }
   __syncthreads();
   DSA_MARK(p.trace, 4);
-  // ---- 4) O = P V: wave w < 4 takes pairs 32 (w >> 1) .. +31 and dims 64 (w & 1) .. +63 as
-  //      2 x 2 tiles of 32 x 32 (tile rows: 16 pairs x {hi, lo} parts; row m -> pair
-  //      (m & 15), part m >> 4), K = 160 rows in 10 steps.  Fewer, larger tiles keep the
-  //      LDS operand traffic low.
-  if (wave < 4) {
-    const int pb = wave >> 1, db = wave & 1;
+  // ---- 4) O = P V: wave w < 8 takes pairs 32 (w >> 2) .. +31 and dims 32 (w & 3) .. +31 as
+  //      2 tiles of 32 x 32 (tile rows: 16 pairs x {hi, lo} parts; row m -> pair (m & 15),
+  //      part m >> 4), K = 160 rows in 10 steps.  Two waves per SIMD hide each other's
+  //      operand loads.
+  if (wave < 8) {
+    const int pb = wave >> 2, db = wave & 3;
     const int m = lane & 31;
     const int poff = ((m >> 4) * kSStride + 8 * (lane >> 5)) * 2;
     const uint8_t* pa0 = reinterpret_cast<const uint8_t*>(&sh.s[pb * 32 + (m & 15)][0]) + poff;
@@ -240,28 +250,24 @@ __global__ void __launch_bounds__(kSoThreads) swa_out_kernel(SoParams p) {
     // rows 8 (g >> 1) .. +7 of the step; lane q of the group points at row (q >> 2), dims
     // 4 (q & 3) .. +3 (then 4 rows further for the second half)
     const int g = lane >> 4, q = lane & 15;
-    const uint8_t* vb = sh.v + (8 * (g >> 1) + (q >> 2)) * kRowB + (64 * db + 16 * (g & 1) + 4 * (q & 3)) * 2;
-    f32x16_t acc[2][2] = {};
+    const uint8_t* vb = sh.v + (8 * (g >> 1) + (q >> 2)) * kRowB + (32 * db + 16 * (g & 1) + 4 * (q & 3)) * 2;
+    f32x16_t acc[2] = {};
 #pragma unroll
     for (int ks = 0; ks < kSoRows / 16; ++ks) {
-      Frag8 a[2], bv[2];
+      Frag8 a[2], bv;
       a[0].u = *reinterpret_cast<const uint4*>(pa0 + ks * 32);
       a[1].u = *reinterpret_cast<const uint4*>(pa1 + ks * 32);
-#pragma unroll
-      for (int nt = 0; nt < 2; ++nt) {
-        const uint2 lo4 = lds_tr16(vb + nt * 64 + (16 * ks) * kRowB);
-        const uint2 hi4 = lds_tr16(vb + nt * 64 + (16 * ks + 4) * kRowB);
-        bv[nt].u = make_uint4(lo4.x, lo4.y, hi4.x, hi4.y);
-      }
+      const uint2 lo4 = lds_tr16(vb + (16 * ks) * kRowB);
+      const uint2 hi4 = lds_tr16(vb + (16 * ks + 4) * kRowB);
+      bv.u = make_uint4(lo4.x, lo4.y, hi4.x, hi4.y);
 #pragma unroll
       for (int mt = 0; mt < 2; ++mt)
-#pragma unroll
-        for (int nt = 0; nt < 2; ++nt)
-          acc[mt][nt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[mt].v, bv[nt].v, acc[mt][nt], 0, 0, 0);
+        acc[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[mt].v, bv.v, acc[mt], 0, 0, 0);
     }
     // lane l, element e < 8: pair +8 (e >> 2) + 4 (l >> 5) + (e & 3) of the tile (hi part),
     // the same pair's lo part in element e + 8; dim +(l & 31)
     uint16_t* xs = reinterpret_cast<uint16_t*>(sh.kq);
+    const int dim = 32 * db + (lane & 31);
 #pragma unroll
     for (int mt = 0; mt < 2; ++mt) {
       const int pbase = pb * 32 + mt * 16 + 4 * (lane >> 5);
@@ -269,14 +275,9 @@ __global__ void __launch_bounds__(kSoThreads) swa_out_kernel(SoParams p) {
       const float4 s1 = *reinterpret_cast<const float4*>(&sh.scale[pbase + 8]);
       const float scl[8] = {s0.x, s0.y, s0.z, s0.w, s1.x, s1.y, s1.z, s1.w};
 #pragma unroll
-      for (int nt = 0; nt < 2; ++nt) {
-        const int dim = 64 * db + 32 * nt + (lane & 31);
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const int pair = pbase + 8 * (e >> 2) + (e & 3);
-          xs[(pair >> 3) * kXsStride + (pair & 7) * kD + dim] =
-              f32_to_bf16((acc[mt][nt][e] + acc[mt][nt][e + 8]) * scl[e]);
-        }
+      for (int e = 0; e < 8; ++e) {
+        const int pair = pbase + 8 * (e >> 2) + (e & 3);
+        xs[(pair >> 3) * kXsStride + (pair & 7) * kD + dim] = f32_to_bf16((acc[mt][e] + acc[mt][e + 8]) * scl[e]);
       }
     }
   }
@@ -345,7 +346,7 @@ __global__ void __launch_bounds__(kSoThreads) swa_out_kernel(SoParams p) {
     const int r = tid >> 4, t = tid & 15;
     if (tid < 256 && t < T) {
       const size_t o = (size_t)t * kHidden + b * kOutRows + r;
-      p.xout[o] = f32_to_bf16(sh.tile[r][t] + bf16_to_f32(p.x[o]));
+      p.xout[o] = f32_to_bf16(sh.tile[r][t] + bf16_to_f32(xres));
     }
   }
 }

@@ -146,6 +146,24 @@ def test_swa_layer_step_stages(dsa, pos0, T, window):
     assert np.all(np.abs(gx - tf["x_out"]) <= 2.0 ** -7 * np.maximum(np.abs(tf["x_out"]), 1 / 16))
 
 
+def test_swa_layer_step_with_sink_matches_oracle_attention(dsa):
+    """Sink logits through the fused window attention: the oracle's window attention with
+    the sink on the GPU's rotated q/k/v, rounded to bf16, projected, plus the residual."""
+    pos0, T, window, cap = 3000, 8, 128, 256
+    L = pos0 + T
+    lay = synth.layer_inputs("swa", 1, L, T, seed=17, ring_cap=cap)
+    x = synth.module_x(17, T)
+    sink = synth.sink_logits(17, std=2.0)
+    g = _run_layer(dsa, "swa", lay, x, T, pos0, window=window, sink=up(sink))
+    q = O.decode_bf16(g["qkv"][:, :1024]).reshape(T, 8, 128)
+    attn = O.swa_attention(q, O.decode_bf16(g["k"]), O.decode_bf16(g["v"]), cap, pos0, window,
+                           1 / math.sqrt(128), sink.astype(np.float64))
+    attn = O.bf16_round_trip(attn.reshape(T, 1024))
+    ref = O.bf16_round_trip(O.project(attn, O.decode_bf16(lay.w_o)) + O.decode_bf16(x))
+    gx = O.decode_bf16(g["x_out"])
+    assert np.all(np.abs(gx - ref) <= 2.0 ** -7 * np.maximum(np.abs(ref), 1 / 16))
+
+
 def test_layer_step_run_to_run_bitwise(dsa):
     L, T = 20000, 8
     lay = synth.layer_inputs("dsa", 0, L, T, seed=11)

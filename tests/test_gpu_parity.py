@@ -203,7 +203,8 @@ def test_topk_full_context(dsa):
 # ----------------------------------------------------------------------------- fused scan + top-k
 
 @pytest.mark.parametrize("name,L,T,seed", [("tiny", None, None, 0), ("verify64k", 65536, 8, 0),
-                                           ("verify256k_fp8", 40000, 8, 1), ("verify1m", 100000, 7, 2)])
+                                           ("verify256k_fp8", 40000, 8, 1), ("verify1m", 100000, 7, 2),
+                                           ("verify1m", None, None, 3)])
 def test_index_topk_matches_materialised_path_and_oracle(dsa, name, L, T, seed):
     inp = synth.dsa_config(name, seed=seed, L=L, T=T)
     T, L, k = inp.T, inp.L, inp.top_k

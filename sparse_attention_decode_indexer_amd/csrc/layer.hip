@@ -209,6 +209,10 @@ __global__ void __launch_bounds__(kProjThreads) proj_kernel(ProjParams p) {
     }
     wsv = p.wscale[r];
   }
+  // Every wave's activation requests go out before any wave's weight requests (an
+  // execution barrier only: nothing waits for data), so the CU's return path serves the
+  // block the norm needs first.
+  __builtin_amdgcn_s_barrier();
   // Every lane loads (unconditional loads keep the wait counts exact): lanes beyond the
   // real rows repeat row 0's addresses, which the memory pipeline merges, and the MFMA
   // rows they feed are never read.

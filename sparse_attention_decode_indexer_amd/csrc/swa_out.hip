@@ -141,6 +141,9 @@ __global__ void __launch_bounds__(kSoThreads) swa_out_kernel(SoParams p) {
     // the window (needed first); they stream in under the attention
     // W8A8: scale of W_o row (tid >> 4) & 15, the row this thread dequantises in the reduction
     if constexpr (F8) wsv = p.w_o_scale[b * kOutRows + ((tid >> 4) & 15)];
+    // every wave's window requests go out before any wave's W_o requests (an execution
+    // barrier only), so the CU's memory path returns the window first
+    __builtin_amdgcn_s_barrier();
     const uint4* wp = reinterpret_cast<const uint4*>(static_cast<const uint8_t*>(p.w_o) +
                                                      ((size_t)(b * kOutRows + (lane & 15)) * K + kw0) * ESZ) +
                       (lane >> 4);

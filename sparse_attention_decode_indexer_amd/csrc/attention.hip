@@ -405,8 +405,9 @@ hipError_t launch_attention(int mode, int kvdt, const void* q, const void* kc, c
   (void)num_cu;
   const dim3 grid(p.nsplit, T);
   if (mode == 0) {
-    if (kvdt == 0) hipLaunchKernelGGL((attn_kernel<0, 0, kSplitRows, kAttnThreads>), grid, dim3(kAttnThreads), 0, st, p);
-    else hipLaunchKernelGGL((attn_kernel<1, 0, kSplitRows, kAttnThreads>), grid, dim3(kAttnThreads), 0, st, p);
+    // two P.V row groups (512 threads): each thread's P.V loop is half as long
+    if (kvdt == 0) hipLaunchKernelGGL((attn_kernel<0, 0, kSplitRows, 2 * kAttnThreads>), grid, dim3(2 * kAttnThreads), 0, st, p);
+    else hipLaunchKernelGGL((attn_kernel<1, 0, kSplitRows, 2 * kAttnThreads>), grid, dim3(2 * kAttnThreads), 0, st, p);
   } else {
     hipLaunchKernelGGL((attn_kernel<0, 1, kSwaRows, 4 * kAttnThreads>), grid, dim3(4 * kAttnThreads), 0, st, p);
   }

@@ -179,6 +179,7 @@ __global__ void __launch_bounds__(kProjThreads) proj_kernel(ProjParams p) {
   constexpr int NCH = kMaxT * (MODE == 0 ? kHidden : kHq * kD) / 8 / kProjThreads;   // uint4 chunks per thread
   const int chunks = kMaxT * K / 8;
   uint4 v[NCH];
+  float amx[NCH];                              // W8A8, QKV: running max |y| of each chunk
 #pragma unroll
   for (int u = 0; u < NCH; ++u) {
     const int c = tid + u * kProjThreads;
@@ -307,11 +308,13 @@ __global__ void __launch_bounds__(kProjThreads) proj_kernel(ProjParams p) {
       const float r = sh.rnorm[t];
       const uint32_t x4[4] = {v[u].x, v[u].y, v[u].z, v[u].w};
       uint32_t o4[4];
+      amx[u] = 0.0f;
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
         const float y0 = (__uint_as_float(x4[q] << 16) * r) * __uint_as_float(g4[q] << 16);
         const float y1 = (__uint_as_float(x4[q] & 0xffff0000u) * r) * __uint_as_float(g4[q] & 0xffff0000u);
         o4[q] = pack_bf16x2(y0, y1);
+        if (F8) amx[u] = fmaxf(amx[u], fmaxf(fabsf(y0), fabsf(y1)));
       }
       v[u] = make_uint4(o4[0], o4[1], o4[2], o4[3]);
       if (!F8) *reinterpret_cast<uint4*>(&sh.xs[t][8 * j8]) = v[u];
@@ -325,7 +328,9 @@ __global__ void __launch_bounds__(kProjThreads) proj_kernel(ProjParams p) {
 #pragma unroll
     for (int u = 0; u < NCH; ++u) {
       const uint32_t y4[4] = {v[u].x, v[u].y, v[u].z, v[u].w};
-      const float m = row16_max(amax_bf16x8(y4));
+      // QKV: the chunk's fp32 max |y| rounded once equals the max of its rounded values
+      // (round to nearest even is monotone and symmetric)
+      const float m = row16_max(MODE == 0 ? round_bf16(amx[u]) : amax_bf16x8(y4));
       if ((lane & 15) == 0) sh.amax[(wave + 16 * u) / WPT][(wave % WPT) * 4 + (lane >> 4)] = m;
     }
   }

@@ -471,22 +471,20 @@ DSA_DEV void resolve_regs(const SelParams& p, int t, SelShared& sh, const uint64
     uint32_t need = kk;
     uint32_t* binl = hist + 4096;                                     // [64] keys of a small bin
     bool first = true;
-    bool first_pass_zeroed = true;
     while (hi > 0) {
       const int maxd = first ? 12 : 11;
-      first = false;
       const int dbits = hi < maxd ? hi : maxd;
       const int lo = hi - dbits;
       const uint32_t nb = 1u << dbits;
-      if (!first_pass_zeroed) {          // the first pass finds the histogram cleared
+      if (!first) {                      // the first pass finds the histogram cleared
         for (int b2 = tid; b2 < 4096; b2 += kSelThreads) hist[b2] = 0u;
         __syncthreads();
       }
-      first_pass_zeroed = false;
+      first = false;
       const uint32_t pmask = hi >= 32 ? 0u : ~((1u << hi) - 1u);
 #pragma unroll
       for (int i = 0; i < NB; ++i) {
-          const uint32_t key = (uint32_t)e[i];
+        const uint32_t key = (uint32_t)e[i];
         if (((uint32_t)i < nmine) & ((key & pmask) == known)) atomicAdd(&hist[(key >> lo) & (nb - 1u)], 1u);
       }
       __syncthreads();
@@ -522,7 +520,7 @@ DSA_DEV void resolve_regs(const SelParams& p, int t, SelShared& sh, const uint64
         uint32_t bmin = 0xffffffffu;
 #pragma unroll
         for (int i = 0; i < NB; ++i) {
-              const uint32_t key = (uint32_t)e[i];
+          const uint32_t key = (uint32_t)e[i];
           if (((uint32_t)i < nmine) & ((key & pm) == known)) bmin = min(bmin, key);
         }
         known = block_min_u32<kSelThreads>(bmin, sh.scan);
@@ -537,7 +535,7 @@ DSA_DEV void resolve_regs(const SelParams& p, int t, SelShared& sh, const uint64
         const uint32_t pm = ~((1u << hi) - 1u);
 #pragma unroll
         for (int i = 0; i < NB; ++i) {
-              const uint32_t key = (uint32_t)e[i];
+          const uint32_t key = (uint32_t)e[i];
           if (((uint32_t)i < nmine) & ((key & pm) == known)) binl[atomicAdd(&misc[2], 1u)] = key;
         }
         __syncthreads();

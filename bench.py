@@ -57,8 +57,8 @@ def log(*a):
 def main():
     args = parse()
     if args.gpus != 1:
-        print(json.dumps({"error": "this build runs on exactly one GPU; --gpus must be 1 "
-                                   "(multi-GPU sharding is described in DESIGN.md, not built)"}))
+        print(json.dumps({"error": "the decode step runs on exactly one GPU; --gpus must be 1 "
+                                   "(no multi-GPU sharding is implemented)"}))
         sys.exit(2)
     import numpy as np
     import torch

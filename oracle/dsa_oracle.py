@@ -27,10 +27,14 @@ steps: ``numpy.matmul`` (dot products), ``numpy.lexsort`` (the sort that *is*
 the top-k definition), ``numpy.exp``/``cos``/``sin``.
 
 Parity status: every function here is pinned by ``tests/test_oracle_pins.py``
-(closed forms, brute force, library routines, invariants).  The composed
-layer step is pinned only as the composition of pinned stages plus special
-cases with closed forms; beyond that its end-to-end parity is unpinned (the
-pages print no worked example).
+(closed forms, brute force, library routines, invariants), including the band
+magnitude S of ``indexer_scores`` (hand-derived example, sign invariance, equality
+with the score on non-negative inputs).  Within the composed layer step the DSA
+indexer leg is pinned on its own: q_I and k_I rotated by absolute position (a shift
+of the block multiplies every pair by the shift's rotation), w_I not rotated, the
+block's own keys read back quantised, and the block's scores invariant under a shift
+within the quantiser bound.  Beyond the pinned stages and special cases with closed
+forms, the end-to-end layer step is unpinned (the pages print no worked example).
 """
 from __future__ import annotations
 

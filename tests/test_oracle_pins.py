@@ -116,6 +116,174 @@ def test_indexer_causal_mask_and_fp8_scale():
     np.testing.assert_allclose(s[vis], (unscaled * scale[None, :])[vis], rtol=1e-12)
 
 
+def test_indexer_magnitude_hand_example():
+    """The band magnitude S[t,s] = sum_h |w| sum_d |q k|, worked out by hand in the fixture."""
+    g = json.load(open(os.path.join(GOLD, "indexer_topk_tiny.json")))
+    s, S = O.indexer_scores(np.array(g["q"], float), np.array(g["w"], float),
+                            np.array(g["k"], float), g["pos0"], with_abs=True)
+    assert np.array_equal(S, np.array(g["magnitude"]))
+    assert np.array_equal(s, np.array(g["scores"]))
+
+
+def test_indexer_magnitude_invariants():
+    """S ignores every sign (q, k, w, per head or per element), equals the score when every
+    input is non-negative (relu and |.| are then the identity), bounds |I|, scales with |w|,
+    and is 0 beyond the causal limit."""
+    g = np.random.default_rng(31)
+    T, H, D, L = 3, 16, 64, 50
+    q = g.standard_normal((T, H, D))
+    k = g.standard_normal((L, D))
+    w = g.standard_normal((T, H))
+    pos0 = L - T
+    s, S = O.indexer_scores(q, w, k, pos0, with_abs=True)
+    flips = np.where(g.random((T, H, D)) < 0.5, -1.0, 1.0)
+    kflips = np.where(g.random((L, D)) < 0.5, -1.0, 1.0)
+    for q2, k2, w2 in ((-q, k, w), (q * flips, k, w), (q, -k, w), (q, k * kflips, w), (q, k, -w),
+                       (q * flips, k * kflips, -w)):
+        _, S2 = O.indexer_scores(q2, w2, k2, pos0, with_abs=True)
+        np.testing.assert_allclose(S2, S, rtol=1e-13, atol=0)
+    vis = np.isfinite(s)
+    assert np.all(np.abs(s[vis]) <= S[vis] * (1 + 1e-13))
+    assert np.all(S[~vis] == 0)
+    sp, Sp = O.indexer_scores(np.abs(q), np.abs(w), np.abs(k), pos0, with_abs=True)
+    np.testing.assert_allclose(sp[vis], Sp[vis], rtol=1e-13)
+    _, S3 = O.indexer_scores(q, 3.0 * w, k, pos0, with_abs=True)
+    np.testing.assert_allclose(S3, 3.0 * S, rtol=1e-13)
+    # per-head weights: S is linear in |w| head by head
+    e = np.zeros((T, H)); e[:, 5] = 1.0
+    _, S5 = O.indexer_scores(q, e, k, pos0, with_abs=True)
+    ref5 = np.abs(q[:, 5, :]) @ np.abs(k).T
+    np.testing.assert_allclose(S5[vis], ref5[vis], rtol=1e-13)
+
+
+# ----------------------------------------------------------------------------- the indexer leg of the layer step
+
+_LEG_T, _LEG_A, _LEG_SHIFT = 4, 3, 65539
+
+
+def _zero_prefix_dsa(pos0, T, seed=41):
+    """A DSA layer whose cache rows before pos0 are zero (indexer codes 0, scale 1)."""
+    L = pos0 + T
+    lay = synth.layer_inputs("dsa", 0, 64, T, seed=seed)          # weights only (they do not depend on L)
+    cache = {"k": np.zeros((L, 128), np.uint16), "v": np.zeros((L, 128), np.uint16),
+             "k_idx": np.zeros((L, 64), np.uint8), "k_idx_scale": np.ones(L, np.float32)}
+    return lay, cache
+
+
+@pytest.fixture(scope="module")
+def indexer_leg():
+    """The same block (inputs and weights) stepped at pos0 = A and at pos0 = A + shift over
+    all-zero prefix caches."""
+    T = _LEG_T
+    x = synth.module_x(41, T)
+    out = {}
+    for pos0 in (_LEG_A, _LEG_A + _LEG_SHIFT):
+        lay, cache = _zero_prefix_dsa(pos0, T)
+        r = O.layer_step("dsa", x, lay.gamma, lay.w_qkvi, lay.w_o, cache, pos0, top_k=64)
+        out[pos0] = (r, cache)
+    return out
+
+
+def _pairs(seg, d):
+    """[T][n] -> complex [T][n/d][d/2]: rotate-half pairs (i, i + d/2) as a + ib."""
+    b = seg.reshape(seg.shape[0], -1, d)
+    return b[..., : d // 2] + 1j * b[..., d // 2:]
+
+
+def test_layer_step_rotates_indexer_queries_and_keys_by_position(indexer_leg):
+    """Rotate-half RoPE by absolute position on q_I and k_I (and Q, K): moving the block by
+    `shift` positions multiplies every pair by exp(i * shift * theta^(-2j/d)) (within the
+    bf16 roundings of both results); the indexer head weights w_I are not rotated (bit-equal
+    at both positions); V is not rotated.  Fails if q_I or k_I is left unrotated, rotated by
+    the in-block offset only, or if w_I is rotated."""
+    A, B = _LEG_A, _LEG_A + _LEG_SHIFT
+    ra, rb = indexer_leg[A][0], indexer_leg[B][0]
+    lay = O.proj_layout("dsa")
+    for name, d in (("q_idx", 64), ("k_idx", 64), ("q", 128), ("k", 128)):
+        o, n = lay[name]
+        za, zb = _pairs(ra["qkv"][:, o:o + n], d), _pairs(rb["qkv"][:, o:o + n], d)
+        j = np.arange(d // 2)
+        rot = np.exp(1j * _LEG_SHIFT * 1e6 ** (-2.0 * j / d))
+        err = np.abs(zb - za * rot)
+        tol = 2.0 ** -7 * (np.abs(za) + np.abs(zb)) + 1e-30
+        assert np.all(err <= tol), name
+        # the rotation does act: a pair keeps its place only if it is (near) zero
+        moved = np.abs(zb - za) > 4 * tol
+        assert moved.mean() > 0.9, name
+    for name in ("w_idx", "v"):
+        o, n = lay[name]
+        assert np.array_equal(ra["qkv"][:, o:o + n], rb["qkv"][:, o:o + n]), name
+
+
+def test_layer_step_rotation_is_identity_at_position_zero():
+    """Token 0 of a block at pos0 = 0 sits at position 0, where RoPE is the identity: its
+    rotated q_I / k_I / Q / K equal the bf16 projection of the normalised row."""
+    T = 2
+    lay, cache = _zero_prefix_dsa(0, T)
+    x = synth.module_x(43, T)
+    r = O.layer_step("dsa", x, lay.gamma, lay.w_qkvi, lay.w_o, cache, 0, top_k=64)
+    pre = O.bf16_round_trip(O.project(r["normed"], O.decode_bf16(lay.w_qkvi)))
+    assert np.array_equal(r["qkv"][0], pre[0])
+    assert not np.array_equal(r["qkv"][1], pre[1])      # token 1 is at position 1
+
+
+def test_layer_step_indexer_reads_back_quantised_rows(indexer_leg):
+    """The indexer of the layer step scores the cache as stored: the block's own k_I rows
+    quantised to e4m3 (codes and scales equal the row quantiser of the rotated k_I), the
+    rotated q_I and the unrotated w_I; an all-zero prefix scores exactly 0."""
+    lay = O.proj_layout("dsa")
+    for pos0, (r, cache) in indexer_leg.items():
+        T = _LEG_T
+        L = pos0 + T
+        o, n = lay["k_idx"]
+        codes, sc = O.quantize_rows_e4m3(r["qkv"][:, o:o + n])
+        assert np.array_equal(cache["k_idx"][pos0:L], codes)
+        assert np.array_equal(cache["k_idx_scale"][pos0:L], sc)
+        o, n = lay["q_idx"]
+        qi = r["qkv"][:, o:o + n].reshape(T, 16, 64)
+        o, n = lay["w_idx"]
+        wi = r["qkv"][:, o:o + n]
+        kt = O.decode_e4m3(codes) * sc.astype(np.float64)[:, None]
+        d = np.einsum("thd,sd->ths", qi, kt)
+        ref = np.einsum("th,ths->ts", wi, np.maximum(d, 0.0))
+        mag = np.einsum("th,ths->ts", np.abs(wi), np.einsum("thd,sd->ths", np.abs(qi), np.abs(kt)))
+        for t in range(T):
+            assert np.all(r["scores"][t, :pos0] == 0.0)
+            got = r["scores"][t, pos0:pos0 + t + 1]
+            assert np.all(np.abs(got - ref[t, : t + 1]) <= 1e-13 * mag[t, : t + 1])
+            assert np.all(np.isneginf(r["scores"][t, pos0 + t + 1:]))
+
+
+def test_layer_step_block_scores_shift_invariant_within_quantiser_bound(indexer_leg):
+    """q_I(p) . k_I(p') depends only on p' - p, so the block's own indexer scores at pos0 = A
+    and at A + shift agree within the rounding of each side: bf16 rotated rows (half an ulp,
+    2^-8 relative), e4m3 keys (2^-4 relative, 2^-10 of the row scale below the normal
+    range) and fp32 cos/sin (2^-22 of the pair norm, with slack)."""
+    lay = O.proj_layout("dsa")
+    T = _LEG_T
+    scores, bounds = [], []
+    for pos0, (r, cache) in indexer_leg.items():
+        o, n = lay["q_idx"]
+        q = r["qkv"][:, o:o + n].reshape(T, 16, 64)
+        o, n = lay["k_idx"]
+        k = r["qkv"][:, o:o + n]
+        o, n = lay["w_idx"]
+        w = r["qkv"][:, o:o + n]
+        s = cache["k_idx_scale"][pos0:pos0 + T].astype(np.float64)
+        nq = np.abs(_pairs(q.reshape(T, -1), 64)).reshape(T, 16, 32)
+        nq = np.concatenate([nq, nq], axis=-1)
+        nk = np.abs(_pairs(k, 64)).reshape(T, 32)
+        nk = np.concatenate([nk, nk], axis=-1)
+        ek = (2.0 ** -4 + 2.0 ** -7) * np.abs(k) + 2.0 ** -10 * s[:, None] + 2.0 ** -20 * nk
+        eq = 2.0 ** -7 * np.abs(q) + 2.0 ** -20 * nq
+        e = (np.einsum("thd,sd->ths", np.abs(q), ek) + np.einsum("thd,sd->ths", eq, np.abs(k) + ek))
+        bounds.append(np.einsum("th,ths->ts", np.abs(w), e))
+        scores.append(r["scores"][:, pos0:pos0 + T])
+    for t in range(T):
+        a, b = scores[0][t, : t + 1], scores[1][t, : t + 1]
+        assert np.all(np.abs(a - b) <= bounds[0][t, : t + 1] + bounds[1][t, : t + 1])
+
+
 # ----------------------------------------------------------------------------- top-k
 
 def _brute_topk(scores, pos0, k):

@@ -43,10 +43,12 @@ def parse():
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
     ap.add_argument("--no-w8a8", action="store_true", help="skip the W8A8 module timing")
+    ap.add_argument("--no-configs", action="store_true",
+                    help="skip the standalone timings (and oracle stage times) of the smaller configs")
     ap.add_argument("--eager", action="store_true",
                     help="skip the HIP-graph replay timing (reported beside the direct-launch step)")
-    ap.add_argument("--only", choices=["module", "index_topk", "copy"], default="module",
-                    help="index_topk / copy: run only that kernel (for counter passes)")
+    ap.add_argument("--only", choices=["module", "index_topk", "sparse_attn", "copy"], default="module",
+                    help="index_topk / sparse_attn / copy: run only that call (for counter passes)")
     return ap.parse_args()
 
 
@@ -185,6 +187,20 @@ def main():
         torch.cuda.synchronize()
         print(json.dumps({"index_topk_launches": args.steps}))
         return
+    if args.only == "sparse_attn":
+        # the DSA layer's own selection (idx) and rotated queries over its cache
+        ws_a = dsa.workspace(dsa.WS_SPARSE_ATTN, T, L, K)
+        q_a = qkv[:, 0:1024].contiguous()
+        o_a = torch.zeros((T, 1024), dtype=torch.int16, device=dev)
+        for i in range(args.warmup + args.steps):
+            dsa.dsa_sparse_attn(q_a, d_dsa["k"], d_dsa["v"], None, None, dsa.BF16, idx, K, T, L, 1.0 / math.sqrt(128),
+                                None, o_a, dsa.BF16, ws_a, stream=stream)
+        torch.cuda.synchronize()
+        idx_np = idx.cpu().numpy()
+        union = int(np.unique(idx_np[idx_np >= 0]).size)
+        print(json.dumps({"sparse_attn_launches": args.steps, "union_rows": union,
+                          "gather_bytes": union * 2 * 128 * 2}))
+        return
 
     # ------------------------------------------------------------------ timed module steps
     # Direct launches: the step time (value) and the DSA layer-step time (events around
@@ -290,6 +306,9 @@ def main():
         f"{k} {v['cold']['median']}/{v['warm']['median']}" for k, v in dist.items()))
     ceiling = read_ceiling(torch, dev, stream, dsa)
     log(f"[bench] read ceiling: {ceiling}")
+    configs = None
+    if not args.no_configs:
+        configs = config_timings(args, dsa, torch, np, synth, dev, stream)
 
     # ------------------------------------------------------------------ W8A8 module
     # The same module with every projection weight stored as e4m3 codes + per-row fp32
@@ -391,7 +410,7 @@ def main():
     # ------------------------------------------------------------------ oracle CPU baseline
     cpu = None
     if not args.no_cpu:
-        cpu = cpu_baseline(host_layers, x_host, L, T, bytes_step)
+        cpu = cpu_baseline(host_layers, x_host, L, T, bytes_step, with_configs=not args.no_configs)
 
     out = {
         "metric": "DSA layer-step µs + HBM GB/s (% roofline) at 1M ctx, 8-token verify, 1 GPU",
@@ -430,11 +449,98 @@ def main():
         },
         "cpu_baseline": cpu,
         "w8a8": w8a8,
+        "configs": configs,
         "protocol": {"per_call_calls": n_pc, "warmup_calls": args.warmup, **dist,
                      "read_ceiling": ceiling, "scan_gather": scan_gather,
                      "module_step_GBps": round(value, 1)},
     }
     print(json.dumps(out))
+
+
+CONFIGS = (
+    # (synth workload, label): the smaller configs of the workload list at their stated sizes
+    ("tiny", "config0: L=4096, T=1, integer-valued bf16 indexer keys, bf16 K/V"),
+    ("verify64k", "config1: L=65536, T=8, bf16 indexer keys ~N(0,1/64), bf16 K/V"),
+    ("verify256k_fp8", "config2: L=262144, T=8, e4m3 indexer keys and e4m3 K/V with row scales"),
+    ("verify1m", "config3: L=1048576, T=8, e4m3 indexer keys with 1% planted rows, bf16 K/V"),
+)
+
+
+def config_timings(args, dsa, torch, np, synth, dev, stream):
+    """Standalone DSA path per config (fused index + top-k, then sparse attention): per-call
+    p10 / median / p90 in us, cold (consecutive calls cycle over rotated input copies whose
+    total exceeds the last-level cache) and warm (one copy), tokens/s = T / median step, and
+    the algorithmic bytes (key scan + union of gathered K/V rows) over the cold median."""
+    import math
+    out = {}
+    sm = 1.0 / math.sqrt(128)
+    for name, label in CONFIGS:
+        inp = synth.dsa_config(name, seed=args.seed)
+        T, Lc, K = inp.T, inp.L, inp.top_k
+        fp8k = inp.k_idx_dtype == "fp8"
+        fp8v = inp.kv_dtype == "fp8"
+        key_row = 64 + 4 if fp8k else 128
+        kv_row = (128 + 4) * 2 if fp8v else 256 * 2
+        set_bytes = Lc * (key_row + kv_row)
+        R = int(max(1, min(8, math.ceil(600e6 / set_bytes))))
+
+        def up(a):
+            a = np.ascontiguousarray(a)
+            if a.dtype == np.uint16:
+                a = a.view(np.int16)
+            return torch.from_numpy(a).to(dev)
+        base = {n: (None if getattr(inp, n) is None else up(getattr(inp, n)))
+                for n in ("q_idx", "w_idx", "k_idx", "k_idx_scale", "q", "k", "v", "k_scale", "v_scale")}
+        sets = [base]
+        for r in range(1, R):
+            sets.append({n: (t if t is None or n in ("q_idx", "w_idx", "q") else
+                             torch.roll(t, shifts=r * 7919, dims=0).contiguous()) for n, t in base.items()})
+        idx = torch.full((T, K), -1, dtype=torch.int32, device=dev)
+        o = torch.zeros((T, 1024), dtype=torch.int16, device=dev)
+        ws_s = dsa.workspace(dsa.WS_INDEX_TOPK, T, Lc, K)
+        ws_a = dsa.workspace(dsa.WS_SPARSE_ATTN, T, Lc, K)
+
+        def select(d):
+            dsa.dsa_index_topk(d["q_idx"], d["w_idx"], d["k_idx"], d["k_idx_scale"],
+                               dsa.FP8_E4M3 if fp8k else dsa.BF16, T, Lc, inp.pos0, K, idx, None, ws_s, stream=stream)
+
+        def attend(d):
+            dsa.dsa_sparse_attn(d["q"], d["k"], d["v"], d["k_scale"], d["v_scale"], dsa.FP8_E4M3 if fp8v else dsa.BF16,
+                                idx, K, T, Lc, sm, None, o, dsa.BF16, ws_a, stream=stream)
+
+        def both(d):
+            select(d)
+            attend(d)
+
+        def per_call(fn, ss, n):
+            for i in range(max(3, args.warmup)):
+                fn(ss[i % len(ss)])
+            evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n)]
+            for i, (a, b) in enumerate(evs):
+                a.record(stream)
+                fn(ss[i % len(ss)])
+                b.record(stream)
+            torch.cuda.synchronize()
+            return [a.elapsed_time(b) * 1e3 for a, b in evs]
+        n = max(args.steps, 10)
+        res = {"label": label, "L": Lc, "T": T, "rotate_sets": R,
+               "step_us": {"cold": stats(per_call(both, sets, n)), "warm": stats(per_call(both, sets[:1], n))},
+               "index_topk_us": {"cold": stats(per_call(select, sets, n))},
+               "sparse_attn_us": {"cold": stats(per_call(attend, sets, n))}}
+        select(sets[0])
+        torch.cuda.synchronize()
+        ii = idx.cpu().numpy()
+        union = int(np.unique(ii[ii >= 0]).size)
+        alg = Lc * key_row + union * kv_row
+        med = res["step_us"]["cold"]["median"]
+        res.update({"tokens_per_s": round(T / (med * 1e-6), 1), "algorithmic_bytes": int(alg),
+                    "GBps": round(alg / (med * 1e-6) / 1e9, 1),
+                    "frac_of_peak": round(alg / (med * 1e-6) / 1e9 / HBM_PEAK_GBPS, 4)})
+        log(f"[bench] {name}: step cold median {med} us, {res['tokens_per_s']} tok/s, {res['GBps']} GB/s")
+        out[name] = res
+        del sets, base
+        torch.cuda.synchronize()
+    return out
 
 
 def stats(v):
@@ -446,20 +552,30 @@ def stats(v):
 
 
 def read_ceiling(torch, dev, stream, dsa):
-    """Measured HBM read ceiling: dsa_stream_read (a plain streaming read, one workgroup
-    per CU, 64 KiB in flight per CU) over 1 GiB, and over 64 MiB per call rotated across
-    8 buffers (the key scan's size, cold in the 256 MB last-level cache); median of 20
-    calls, one event pair per call."""
+    """Measured HBM read ceiling: the streaming-read helper of libdsa_read_ceiling.so (a
+    plain streaming read, one workgroup per CU, 64 KiB in flight per CU; not part of the
+    library) over 1 GiB, and over 64 MiB per call rotated across 8 buffers (the key scan's
+    size, cold in the 256 MB last-level cache); median of 20 calls, one event pair per call."""
+    import ctypes as C
+    lib = C.CDLL(os.path.join(os.path.dirname(dsa.LIB_PATH), "libdsa_read_ceiling.so"))
+    fn = lib.dsa_read_ceiling_stream
+    fn.argtypes = [C.c_void_p, C.c_size_t, C.c_void_p, C.c_void_p]
+    fn.restype = C.c_int
     sink = torch.zeros(1024, dtype=torch.int32, device=dev)
+
+    def call(b, nb):
+        rc = fn(b.data_ptr(), nb, sink.data_ptr(), stream.cuda_stream)
+        if rc != 0:
+            raise RuntimeError(f"dsa_read_ceiling_stream failed ({rc})")
 
     def run(bufs, n=20):
         nb = bufs[0].numel()
         for b in bufs[:2]:
-            dsa.dsa_stream_read(b, nb, sink, stream=stream)
+            call(b, nb)
         evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n)]
         for i, (a, e) in enumerate(evs):
             a.record(stream)
-            dsa.dsa_stream_read(bufs[i % len(bufs)], nb, sink, stream=stream)
+            call(bufs[i % len(bufs)], nb)
             e.record(stream)
         torch.cuda.synchronize()
         t = sorted(a.elapsed_time(e) * 1e-3 for a, e in evs)
@@ -471,7 +587,7 @@ def read_ceiling(torch, dev, stream, dsa):
     g_small = run(small)
     del small
     torch.cuda.synchronize()
-    return {"kernel": "dsa_stream_read (one event pair per call, median of 20)",
+    return {"kernel": "dsa_read_ceiling_stream (one event pair per call, median of 20)",
             "GBps_1GiB": round(g_big, 1), "GBps_64MiB_rotated_x8": round(g_small, 1)}
 
 
@@ -511,8 +627,9 @@ def measured_traffic(L, T):
         return None
 
 
-def cpu_baseline(host_layers, x_host, L, T, bytes_step):
-    """The oracle (fp64 numpy, unmodified) on one full module step of the same workload."""
+def cpu_baseline(host_layers, x_host, L, T, bytes_step, with_configs=True):
+    """The oracle (fp64 numpy, unmodified) on one full module step of the same workload,
+    plus (with_configs) its indexer / top-k / attention stage times on each smaller config."""
     import numpy as np
     from oracle import dsa_oracle as O
     try:
@@ -541,9 +658,33 @@ def cpu_baseline(host_layers, x_host, L, T, bytes_step):
     stages["dsa_layer"] = round(layer_s["dsa"][0], 3)
     stages["swa_layer_mean"] = round(sum(layer_s["swa"]) / len(layer_s["swa"]), 3)
     log(f"[bench] oracle DSA stages (s): {stages}")
+    per_config = None
+    if with_configs:
+        import synth
+        per_config = {}
+        for name, _ in CONFIGS:
+            inp = synth.dsa_config(name, seed=0)
+            t0 = time.perf_counter()
+            krows = O.dequant_rows(inp.k_idx, inp.k_idx_dtype, inp.k_idx_scale)
+            sc = O.indexer_scores(O.decode_bf16(inp.q_idx), inp.w_idx, krows, inp.pos0)
+            t1 = time.perf_counter()
+            ix, _ = O.topk_indices(sc, inp.pos0, inp.top_k)
+            t2 = time.perf_counter()
+            if inp.kv_dtype == "bf16":
+                Kr = lambda j, a=inp.k: O.decode_bf16(a[j])
+                Vr = lambda j, a=inp.v: O.decode_bf16(a[j])
+            else:
+                Kr = lambda j, a=inp.k, s=inp.k_scale: O.dequant_rows(a[j], "fp8", s[j])
+                Vr = lambda j, a=inp.v, s=inp.v_scale: O.dequant_rows(a[j], "fp8", s[j])
+            O.sparse_attention(O.decode_bf16(inp.q), Kr, Vr, ix, 1.0 / math.sqrt(128), L=inp.L)
+            t3 = time.perf_counter()
+            per_config[name] = {"indexer": round(t1 - t0, 3), "topk": round(t2 - t1, 3),
+                                "attention": round(t3 - t2, 3), "tokens_per_s": round(inp.T / (t3 - t0), 2)}
+            log(f"[bench] oracle {name} stages (s): {per_config[name]}")
     return {"value": round(bytes_step / dt / 1e9, 4), "unit": "GB/s", "cores": int(cores), "kind": "oracle",
             "sample": f"one full module step (5 SWA + 1 DSA layers, L={L}, T={T}), fp64 numpy oracle",
-            "seconds": round(dt, 2), "cpu_model": cpu_model(), "stage_seconds": stages}
+            "seconds": round(dt, 2), "cpu_model": cpu_model(), "stage_seconds": stages,
+            "config_stage_seconds": per_config}
 
 
 def oracle_stages(O, r, cache, L, T, K=2048):

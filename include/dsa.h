@@ -36,14 +36,27 @@
  *     error nothing is written and nothing is launched.  A failing HIP launch returns
  *     DSA_ERR_HIP (dsa_last_error() gives the message).  Faults inside a kernel surface
  *     at the caller's next synchronisation.
- *   - Workspaces: a workspace must be zero-filled before its first use (allocate it with
- *     zeros or call dsa_workspace_init).  Its control words then carry state from call
- *     to call: the selection keeps a launch counter there (its slots are tagged with the
- *     counter, so no call has to clear them), and every call that completes leaves the
- *     words valid for the next one, so one workspace serves any number of
- *     stream-ordered calls, including replays of a captured graph.  Two calls that may
- *     run at the same time need distinct workspaces; a workspace must not be copied or
- *     re-zeroed while calls that use it are in flight.
+ *   - Workspaces: every workspace starts with a 16 KiB control block and must be
+ *     zero-filled before its first use (allocate it with zeros or call
+ *     dsa_workspace_init).  Its control words then carry state from call to call: the
+ *     selection keeps a launch counter there (its slots are tagged with the counter, so
+ *     no call has to clear them), and every call that completes leaves the words valid
+ *     for the next one, so one workspace serves any number of stream-ordered calls,
+ *     including replays of a captured graph.  Two calls that may run at the same time
+ *     need distinct workspaces; a workspace must not be copied or re-zeroed while calls
+ *     that use it are in flight.
+ *   - Co-residency: the selection (dsa_topk, dsa_index_topk, the DSA layer step) runs
+ *     one launch whose workgroups hand data to each other, so all of them must be
+ *     resident at once.  The call checks on the host that the device can hold them and
+ *     returns DSA_ERR_LAUNCH otherwise, before anything is launched.  Kernels of other
+ *     streams or processes that occupy compute units at the same time can still keep a
+ *     workgroup from starting; every wait inside the launch is bounded (0.2 s), and a
+ *     wait that gives up sets a sticky error word in the workspace and writes an empty
+ *     selection (indices -1, count 0) for the tokens it concerns.  dsa_workspace_status
+ *     reports it; while the word is set, later selection calls on that workspace write
+ *     empty selections and nothing else, until dsa_workspace_init clears it.
+ *     (Test hook: the environment variable DSA_RESIDENT_LIMIT=n makes the host check
+ *     assume at most n resident workgroups.)
  */
 #ifndef DSA_H_
 #define DSA_H_
@@ -153,12 +166,14 @@ dsa_status_t dsa_sparse_attn(const void* q, const void* k_cache, const void* v_c
  * Token t at p = pos0 + t attends positions [max(0, p - window + 1), p], read from a
  * ring buffer where position p lives in slot p % ring_cap; the ring must hold all of
  * them, so ring_cap >= window + T - 1.  Same softmax and sink rule as dsa_sparse_attn.
- * q [T][8][128] bf16; k_ring, v_ring [ring_cap][128] bf16; 1 <= window <= 2048.
- * out [T][8][128] bf16 or fp32.  ws: DSA_WS_SWA_ATTN.
+ * q [T][8][128] bf16; k_ring, v_ring [ring_cap][128] bf16 (kv_dtype DSA_BF16, scales
+ * NULL) or e4m3 codes with k_scale, v_scale [ring_cap] fp32 row scales (DSA_FP8_E4M3);
+ * 1 <= window <= 2048.  out [T][8][128] bf16 or fp32.  ws: DSA_WS_SWA_ATTN.
  */
-dsa_status_t swa_attn(const void* q, const void* k_ring, const void* v_ring, int64_t ring_cap,
-                      int T, int64_t pos0, int window, float sm_scale, const float* sink,
-                      void* out, int out_dtype, void* ws, size_t ws_bytes, void* stream);
+dsa_status_t swa_attn(const void* q, const void* k_ring, const void* v_ring, const float* k_scale,
+                      const float* v_scale, int kv_dtype, int64_t ring_cap, int T, int64_t pos0,
+                      int window, float sm_scale, const float* sink, void* out, int out_dtype,
+                      void* ws, size_t ws_bytes, void* stream);
 
 /* ---------------------------------------------------------------------------------
  * One layer step (§A DSA layer: from 29 kernels to one; §Optimizing inside the kernel).
@@ -236,16 +251,15 @@ size_t dsa_workspace_bytes(int kind, int T, int64_t L, int k);
 /* Zero-fills a workspace on `stream` with a kernel (no hipMemset). */
 dsa_status_t dsa_workspace_init(void* ws, size_t ws_bytes, void* stream);
 
+/* Synchronises `stream`, then reads the workspace's sticky error word: DSA_OK, or
+ * DSA_ERR_LAUNCH if a launch on the workspace gave up waiting for workgroups that were
+ * not resident (its outputs are then not valid; dsa_last_error() says so).  The word
+ * stays set until dsa_workspace_init.  Blocking; not for use under graph capture. */
+dsa_status_t dsa_workspace_status(const void* ws, size_t ws_bytes, void* stream);
+
 /* Largest context length L the top-k calls accept on the current device
  * (4096 positions per compute unit: 1,048,576 on a 256-CU MI355X). */
 int64_t dsa_max_context(void);
-
-/* Measurement helper, not a step of the method: reads `bytes` (a multiple of 16, src
- * 16-byte aligned) of device memory as a plain stream, one workgroup per compute unit,
- * and writes an xor fold of it to sink[0 .. min(CUs, 1024)) (caller-owned, at least 1024
- * uint32 words on device).  Its duration gives the measured HBM read ceiling that the
- * kernels' achieved bandwidth is compared with.  Asynchronous on `stream`. */
-dsa_status_t dsa_stream_read(const void* src, size_t bytes, uint32_t* sink, void* stream);
 
 const char* dsa_status_string(dsa_status_t s);
 

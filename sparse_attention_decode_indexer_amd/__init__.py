@@ -29,8 +29,8 @@ STATUS = {0: "DSA_OK", 1: "DSA_ERR_NULL", 2: "DSA_ERR_SHAPE", 3: "DSA_ERR_DTYPE"
           5: "DSA_ERR_WORKSPACE", 6: "DSA_ERR_LAUNCH", 7: "DSA_ERR_HIP"}
 
 EXPORTS = ("dsa_indexer_scores", "dsa_topk", "dsa_index_topk", "dsa_sparse_attn", "swa_attn",
-           "dsa_layer_step", "dsa_workspace_bytes", "dsa_workspace_init", "dsa_max_context",
-           "dsa_status_string", "dsa_last_error", "dsa_stream_read")
+           "dsa_layer_step", "dsa_workspace_bytes", "dsa_workspace_init", "dsa_workspace_status",
+           "dsa_max_context", "dsa_status_string", "dsa_last_error")
 
 
 class DSAError(RuntimeError):
@@ -65,11 +65,11 @@ _sig = {
     "dsa_topk": [_P, _I, _L, _L, _L, _I, _P, _P, _P, _S, _P],
     "dsa_index_topk": [_P, _P, _P, _P, _I, _I, _L, _L, _I, _P, _P, _P, _S, _P],
     "dsa_sparse_attn": [_P, _P, _P, _P, _P, _I, _P, _I, _I, _L, _F, _P, _P, _I, _P, _S, _P],
-    "swa_attn": [_P, _P, _P, _L, _I, _L, _I, _F, _P, _P, _I, _P, _S, _P],
+    "swa_attn": [_P, _P, _P, _P, _P, _I, _L, _I, _L, _I, _F, _P, _P, _I, _P, _S, _P],
     "dsa_layer_step": [C.POINTER(LayerConfig), C.POINTER(LayerWeights), C.POINTER(LayerCache),
                        _P, _P, _I, _L, _P, _P, _P, _S, _P],
     "dsa_workspace_init": [_P, _S, _P],
-    "dsa_stream_read": [_P, _S, _P, _P],
+    "dsa_workspace_status": [_P, _S, _P],
 }
 for _name, _args in _sig.items():
     getattr(_lib, _name).argtypes = _args
@@ -145,10 +145,10 @@ def dsa_sparse_attn(q, k_cache, v_cache, k_scale, v_scale, kv_dtype, idx, k, T, 
     return _check("dsa_sparse_attn", st, raise_on_error)
 
 
-def swa_attn(q, k_ring, v_ring, ring_cap, T, pos0, window, sm_scale, sink, out, out_dtype, ws,
-             ws_bytes=None, stream=None, raise_on_error=True):
-    st = _lib.swa_attn(_ptr(q), _ptr(k_ring), _ptr(v_ring), ring_cap, T, pos0, window, sm_scale,
-                       _ptr(sink), _ptr(out), out_dtype, _ptr(ws),
+def swa_attn(q, k_ring, v_ring, k_scale, v_scale, kv_dtype, ring_cap, T, pos0, window, sm_scale, sink,
+             out, out_dtype, ws, ws_bytes=None, stream=None, raise_on_error=True):
+    st = _lib.swa_attn(_ptr(q), _ptr(k_ring), _ptr(v_ring), _ptr(k_scale), _ptr(v_scale), kv_dtype, ring_cap,
+                       T, pos0, window, sm_scale, _ptr(sink), _ptr(out), out_dtype, _ptr(ws),
                        _nbytes(ws) if ws_bytes is None else ws_bytes, _stream(stream))
     return _check("swa_attn", st, raise_on_error)
 
@@ -171,9 +171,10 @@ def dsa_workspace_init(ws, ws_bytes=None, stream=None):
     return _check("dsa_workspace_init", st, True)
 
 
-def dsa_stream_read(src, nbytes, sink, stream=None, raise_on_error=True):
-    st = _lib.dsa_stream_read(_ptr(src), nbytes, _ptr(sink), _stream(stream))
-    return _check("dsa_stream_read", st, raise_on_error)
+def dsa_workspace_status(ws, ws_bytes=None, stream=None, raise_on_error=True):
+    """Blocking: synchronises the stream and reports the workspace's sticky error word."""
+    st = _lib.dsa_workspace_status(_ptr(ws), _nbytes(ws) if ws_bytes is None else ws_bytes, _stream(stream))
+    return _check("dsa_workspace_status", st, raise_on_error)
 
 
 def dsa_max_context():

@@ -409,7 +409,8 @@ hipError_t launch_attention(int mode, int kvdt, const void* q, const void* kc, c
     if (kvdt == 0) hipLaunchKernelGGL((attn_kernel<0, 0, kSplitRows, 2 * kAttnThreads>), grid, dim3(2 * kAttnThreads), 0, st, p);
     else hipLaunchKernelGGL((attn_kernel<1, 0, kSplitRows, 2 * kAttnThreads>), grid, dim3(2 * kAttnThreads), 0, st, p);
   } else {
-    hipLaunchKernelGGL((attn_kernel<0, 1, kSwaRows, 4 * kAttnThreads>), grid, dim3(4 * kAttnThreads), 0, st, p);
+    if (kvdt == 0) hipLaunchKernelGGL((attn_kernel<0, 1, kSwaRows, 4 * kAttnThreads>), grid, dim3(4 * kAttnThreads), 0, st, p);
+    else hipLaunchKernelGGL((attn_kernel<1, 1, kSwaRows, 4 * kAttnThreads>), grid, dim3(4 * kAttnThreads), 0, st, p);
   }
   if (p.nsplit > 1) {
 #ifdef DSA_TRACE

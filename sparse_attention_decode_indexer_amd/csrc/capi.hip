@@ -46,7 +46,9 @@ __global__ void zero_kernel(uint4* p, size_t n16) {
     p[i] = make_uint4(0u, 0u, 0u, 0u);
 }
 
-// ---- layer-step workspace layout
+// ---- layer-step workspace layout.  Every workspace starts with the control block
+// (dsa::ctl); in a layer workspace the projection's counter and the selection's launch
+// counter, error word and tau slots share it.
 struct LayerWs {
   size_t proj, q_att, q_idx, w_idx, attn_out, idx, attn, sel, total;
 };
@@ -54,7 +56,7 @@ struct LayerWs {
 LayerWs layer_ws(int kind, int T, int64_t L, int k, int window, int ncu) {
   LayerWs w{};
   size_t o = 0;
-  w.proj = o; o = align_up(o + dsa::proj_workspace_bytes());
+  w.proj = o; o = align_up(o + dsa::proj_workspace_bytes());     // control block + k_I staging
   w.q_att = o; o = align_up(o + (size_t)dsa::kMaxT * dsa::kHq * dsa::kD * 2);
   w.q_idx = o; o = align_up(o + (size_t)dsa::kMaxT * dsa::kHI * dsa::kDI * 2);
   w.w_idx = o; o = align_up(o + (size_t)dsa::kMaxT * dsa::kHI * 4);
@@ -63,7 +65,7 @@ LayerWs layer_ws(int kind, int T, int64_t L, int k, int window, int ncu) {
   w.idx = o; o = align_up(o + (kind == DSA_LAYER_DSA ? (size_t)dsa::kMaxT * k * 4 : 0));
   w.attn = o; o = align_up(o + dsa::attn_workspace_bytes(dsa::kMaxT, dsa::attn_splits(kind == DSA_LAYER_DSA ? 0 : 1, list)));
   w.sel = o;
-  if (kind == DSA_LAYER_DSA) o = align_up(o + dsa::select_workspace_bytes(T, L, k, ncu));
+  if (kind == DSA_LAYER_DSA) o = align_up(o + dsa::select_data_bytes(T, L, k, ncu));
   w.total = o;
   return w;
 }
@@ -90,15 +92,6 @@ const char* dsa_last_error(void) { return g_err; }
 
 int64_t dsa_max_context(void) { return dsa::select_max_context(device_cus()); }
 
-dsa_status_t dsa_stream_read(const void* src, size_t bytes, uint32_t* sink, void* stream) {
-  if (!src || !sink) return DSA_ERR_NULL;
-  if (!aligned16(src) || (bytes & 15u)) return DSA_ERR_ALIGN;
-  if (bytes == 0) return DSA_ERR_SHAPE;
-  const int nb = device_cus() < 1024 ? device_cus() : 1024;
-  hipError_t e = dsa::launch_stream_read(src, bytes, sink, nb, (hipStream_t)stream);
-  return e == hipSuccess ? DSA_OK : hip_fail(e, "dsa_stream_read");
-}
-
 size_t dsa_workspace_bytes(int kind, int T, int64_t L, int k) {
   if (T < 1 || T > dsa::kMaxT || L < 1) return 0;
   const int ncu = device_cus();
@@ -107,15 +100,33 @@ size_t dsa_workspace_bytes(int kind, int T, int64_t L, int k) {
     case DSA_WS_INDEX_TOPK:
       return dsa::select_workspace_bytes(T, L, k, ncu);
     case DSA_WS_SPARSE_ATTN:
-      return dsa::attn_workspace_bytes(T, dsa::attn_splits(0, k));
+      return dsa::ctl::kBytes + dsa::attn_workspace_bytes(T, dsa::attn_splits(0, k));
     case DSA_WS_SWA_ATTN:
-      return dsa::attn_workspace_bytes(T, dsa::attn_splits(1, k));
+      return dsa::ctl::kBytes + dsa::attn_workspace_bytes(T, dsa::attn_splits(1, k));
     case DSA_WS_LAYER_DSA:
       return layer_ws(DSA_LAYER_DSA, T, L, k, 0, ncu).total;
     case DSA_WS_LAYER_SWA:
       return layer_ws(DSA_LAYER_SWA, T, L, 0, k, ncu).total;
   }
   return 0;
+}
+
+dsa_status_t dsa_workspace_status(const void* ws, size_t ws_bytes, void* stream) {
+  if (!ws) return DSA_ERR_NULL;
+  if (!aligned16(ws)) return DSA_ERR_ALIGN;
+  if (ws_bytes < dsa::ctl::kBytes) return DSA_ERR_WORKSPACE;
+  hipError_t e = hipStreamSynchronize((hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "dsa_workspace_status: stream synchronize");
+  uint32_t word = 0;
+  e = hipMemcpy(&word, static_cast<const uint32_t*>(ws) + dsa::ctl::kError, sizeof(word), hipMemcpyDeviceToHost);
+  if (e != hipSuccess) return hip_fail(e, "dsa_workspace_status: read of the error word");
+  if (word != 0) {
+    snprintf(g_err, sizeof(g_err),
+             "a launch on this workspace gave up waiting for workgroups that were not resident; "
+             "its outputs are not valid and the workspace must be cleared (dsa_workspace_init)");
+    return DSA_ERR_LAUNCH;
+  }
+  return DSA_OK;
 }
 
 dsa_status_t dsa_workspace_init(void* ws, size_t ws_bytes, void* stream) {
@@ -166,7 +177,8 @@ dsa_status_t dsa_topk(const float* scores, int T, int64_t L, int64_t ld, int64_t
   size_t need = 0;
   if (dsa_status_t s = check_topk_common(T, L, pos0, k, idx, ws, ws_bytes, &need)) return s;
   hipError_t e = dsa::launch_select(1, nullptr, nullptr, nullptr, nullptr, 0, scores, ld, T, L, pos0,
-                                    k, idx, count, ws, device_cus(), (hipStream_t)stream);
+                                    k, idx, count, ws, static_cast<uint8_t*>(ws) + dsa::ctl::kBytes,
+                                    device_cus(), (hipStream_t)stream);
   return e == hipSuccess ? DSA_OK : hip_fail(e, "dsa_topk");
 }
 
@@ -183,7 +195,8 @@ dsa_status_t dsa_index_topk(const void* q_idx, const float* w_idx, const void* k
   size_t need = 0;
   if (dsa_status_t s = check_topk_common(T, L, pos0, k, idx, ws, ws_bytes, &need)) return s;
   hipError_t e = dsa::launch_select(0, q_idx, w_idx, k_idx, k_idx_scale, k_dtype == DSA_FP8_E4M3, nullptr,
-                                    0, T, L, pos0, k, idx, count, ws, device_cus(), (hipStream_t)stream);
+                                    0, T, L, pos0, k, idx, count, ws, static_cast<uint8_t*>(ws) + dsa::ctl::kBytes,
+                                    device_cus(), (hipStream_t)stream);
   return e == hipSuccess ? DSA_OK : hip_fail(e, "dsa_index_topk");
 }
 
@@ -198,32 +211,38 @@ dsa_status_t dsa_sparse_attn(const void* q, const void* k_cache, const void* v_c
   if (fp8 != (k_scale != nullptr) || fp8 != (v_scale != nullptr)) return DSA_ERR_DTYPE;
   if (out_dtype != DSA_BF16 && out_dtype != DSA_FP32) return DSA_ERR_DTYPE;
   if (T < 1 || T > dsa::kMaxT || k < 1 || k > dsa::kMaxTopK || L < 1 || L > kMaxL) return DSA_ERR_SHAPE;
-  const size_t need = dsa::attn_workspace_bytes(T, dsa::attn_splits(0, k));
+  const size_t need = dsa::ctl::kBytes + dsa::attn_workspace_bytes(T, dsa::attn_splits(0, k));
   if (!ws || ws_bytes < need) return DSA_ERR_WORKSPACE;
   if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) || !aligned16(out) || !aligned16(ws) ||
       (sink && !aligned16(sink)))
     return DSA_ERR_ALIGN;
   hipError_t e = dsa::launch_attention(0, fp8, q, k_cache, v_cache, k_scale, v_scale, idx, k, T, L, 0, 0, 0,
-                                       sm_scale, sink, out, out_dtype == DSA_FP32, ws, device_cus(),
+                                       sm_scale, sink, out, out_dtype == DSA_FP32,
+                                       static_cast<uint8_t*>(ws) + dsa::ctl::kBytes, device_cus(),
                                        (hipStream_t)stream);
   return e == hipSuccess ? DSA_OK : hip_fail(e, "dsa_sparse_attn");
 }
 
-dsa_status_t swa_attn(const void* q, const void* k_ring, const void* v_ring, int64_t ring_cap,
-                      int T, int64_t pos0, int window, float sm_scale, const float* sink,
-                      void* out, int out_dtype, void* ws, size_t ws_bytes, void* stream) {
+dsa_status_t swa_attn(const void* q, const void* k_ring, const void* v_ring, const float* k_scale,
+                      const float* v_scale, int kv_dtype, int64_t ring_cap, int T, int64_t pos0,
+                      int window, float sm_scale, const float* sink, void* out, int out_dtype,
+                      void* ws, size_t ws_bytes, void* stream) {
   if (!q || !k_ring || !v_ring || !out) return DSA_ERR_NULL;
+  if (kv_dtype != DSA_BF16 && kv_dtype != DSA_FP8_E4M3) return DSA_ERR_DTYPE;
+  const bool fp8 = kv_dtype == DSA_FP8_E4M3;
+  if (fp8 != (k_scale != nullptr) || fp8 != (v_scale != nullptr)) return DSA_ERR_DTYPE;
   if (out_dtype != DSA_BF16 && out_dtype != DSA_FP32) return DSA_ERR_DTYPE;
   if (T < 1 || T > dsa::kMaxT || window < 1 || window > dsa::kMaxTopK || pos0 < 0) return DSA_ERR_SHAPE;
   if (ring_cap < (int64_t)window + T - 1 || ring_cap > kMaxL) return DSA_ERR_SHAPE;
-  const size_t need = dsa::attn_workspace_bytes(T, dsa::attn_splits(1, window));
+  const size_t need = dsa::ctl::kBytes + dsa::attn_workspace_bytes(T, dsa::attn_splits(1, window));
   if (!ws || ws_bytes < need) return DSA_ERR_WORKSPACE;
   if (!aligned16(q) || !aligned16(k_ring) || !aligned16(v_ring) || !aligned16(out) || !aligned16(ws) ||
       (sink && !aligned16(sink)))
     return DSA_ERR_ALIGN;
-  hipError_t e = dsa::launch_attention(1, 0, q, k_ring, v_ring, nullptr, nullptr, nullptr, 0, T, 0, ring_cap,
-                                       pos0, window, sm_scale, sink, out, out_dtype == DSA_FP32, ws,
-                                       device_cus(), (hipStream_t)stream);
+  hipError_t e = dsa::launch_attention(1, fp8, q, k_ring, v_ring, k_scale, v_scale, nullptr, 0, T, 0, ring_cap,
+                                       pos0, window, sm_scale, sink, out, out_dtype == DSA_FP32,
+                                       static_cast<uint8_t*>(ws) + dsa::ctl::kBytes, device_cus(),
+                                       (hipStream_t)stream);
   return e == hipSuccess ? DSA_OK : hip_fail(e, "swa_attn");
 }
 
@@ -261,6 +280,11 @@ dsa_status_t dsa_layer_step(const dsa_layer_config_t* cfg, const dsa_layer_weigh
       (qkv_out && !aligned16(qkv_out)) || (idx_out && !aligned16(idx_out)) ||
       (cache->k_idx && !aligned16(cache->k_idx)) || (cfg->sink && !aligned16(cfg->sink)))
     return DSA_ERR_ALIGN;
+  if (dsa_kind) {
+    // nothing is launched (and no cache row written) unless the selection can run
+    hipError_t e0 = dsa::select_check_resident(0, 1, T, L, pos0, cfg->top_k, ncu);
+    if (e0 != hipSuccess) return hip_fail(e0, "dsa_layer_step: index/top-k workgroups cannot all be resident");
+  }
   hipStream_t st = (hipStream_t)stream;
   uint8_t* w8 = static_cast<uint8_t*>(ws);
   void* q_att = w8 + lw.q_att;
@@ -275,7 +299,7 @@ dsa_status_t dsa_layer_step(const dsa_layer_config_t* cfg, const dsa_layer_weigh
   if (dsa_kind) {
     int32_t* idx = idx_out ? idx_out : reinterpret_cast<int32_t*>(w8 + lw.idx);
     e = dsa::launch_select(0, q_idx, w_idx, cache->k_idx, cache->k_idx_scale, 1, nullptr, 0, T, L, pos0,
-                           cfg->top_k, idx, nullptr, w8 + lw.sel, ncu, st);
+                           cfg->top_k, idx, nullptr, w8, w8 + lw.sel, ncu, st);
     if (e != hipSuccess) return hip_fail(e, "dsa_layer_step: index/top-k");
     e = dsa::launch_attention(0, 0, q_att, cache->k, cache->v, nullptr, nullptr, idx, cfg->top_k, T, L, 0, 0,
                               0, cfg->sm_scale, cfg->sink, attn_out, 0, w8 + lw.attn, ncu, st);

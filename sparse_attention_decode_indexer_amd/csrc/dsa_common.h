@@ -293,10 +293,12 @@ DSA_DEV uint32_t aadd(uint32_t* p, uint32_t v) { return __hip_atomic_fetch_add(p
 DSA_DEV uint32_t amax(uint32_t* p, uint32_t v) { return __hip_atomic_fetch_max(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT); }
 DSA_DEV void vm_wait_all() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
-// Control words of a workspace (uint32 index; every counter on its own 256-byte line).
+// Control block at the start of every workspace (uint32 index; every polled word on its
+// own 256-byte line).  The launch counter and the sticky error word share one 8-byte
+// word so a launch reads both with one load.
 namespace ctl {
-constexpr int kError = 640;      // sticky error word (1 = a wait timed out)
 constexpr int kEpoch = 768;      // launch counter (tags of the tagged slots)
+constexpr int kError = 769;      // sticky error word (1 = a wait inside a launch gave up)
 constexpr int kDone = 1024;      // [8] per-token completion counters, stride 64
 constexpr int kTauG = 2048;      // [8] tagged slots (64-bit, stride 16 words): per-token tau
 constexpr int kWords = 3072;

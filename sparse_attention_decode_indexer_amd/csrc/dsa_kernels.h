@@ -4,28 +4,26 @@
 #include <stddef.h>
 #include <stdint.h>
 
+#include "select_geometry.h"
+
 namespace dsa {
 
-struct SelGeometry {
-  int chunk;    // keys per workgroup
-  int nwg;      // workgroups
-  int n_part;   // workgroups publishing a tau bound
-  int m;        // tau rank (0: no bound)
-  bool fits;    // chunk fits LDS and nwg fits the count arrays
-};
 
 hipError_t launch_indexer_scores(const void* q_idx, const float* w_idx, const void* k_idx,
                                  const float* k_scale, int kdt, int T, int64_t L, int64_t pos0,
                                  float* scores, int64_t ld, hipStream_t st);
 
-SelGeometry select_geometry(int T, int64_t L, int64_t pos0, int k, int num_cu);
-size_t select_workspace_bytes(int T, int64_t L, int k, int num_cu);
-int64_t select_max_context(int num_cu);
-// src 0: scan k_idx (fused); src 1: read scores
+size_t select_workspace_bytes(int T, int64_t L, int k, int num_cu);   // control block + data
+size_t select_data_bytes(int T, int64_t L, int k, int num_cu);
+// hipErrorCooperativeLaunchTooLarge when the selection's workgroups cannot all be resident
+hipError_t select_check_resident(int src, int kdt, int T, int64_t L, int64_t pos0, int k, int num_cu);
+hipError_t resident_capacity(const void* fn, int threads, int num_cu, int64_t* cap);
+// src 0: scan k_idx (fused); src 1: read scores.  ctl: the workspace's control block;
+// data: select_data_bytes of slots and candidate lists
 hipError_t launch_select(int src, const void* q_idx, const float* w_idx, const void* k_idx,
                          const float* k_scale, int kdt, const float* scores, int64_t ld, int T,
-                         int64_t L, int64_t pos0, int k, int32_t* idx, int32_t* count, void* ws,
-                         int num_cu, hipStream_t st);
+                         int64_t L, int64_t pos0, int k, int32_t* idx, int32_t* count, void* ctl,
+                         void* data, int num_cu, hipStream_t st);
 
 size_t attn_workspace_bytes(int T, int nsplit);
 int attn_splits(int mode, int list_len);   // mode 0: index list, 1: sliding window
@@ -54,10 +52,6 @@ hipError_t launch_swa_out(const void* q, const void* kring, const void* vring, i
                           hipStream_t st);
 
 hipError_t launch_zero(void* p, size_t bytes, hipStream_t st);
-
-// streaming read of `bytes` (a multiple of 16) by `nblocks` workgroups; one word per
-// workgroup into sink
-hipError_t launch_stream_read(const void* src, size_t bytes, uint32_t* sink, int nblocks, hipStream_t st);
 
 #ifdef DSA_TRACE
 uint64_t* dsa_trace_buffer();   // profiling builds: phase-timestamp buffer (or null)

@@ -29,18 +29,16 @@
 // m * n_part >= k, the candidates always contain the k best; the result is exact and
 // independent of tau.  All cross-workgroup arithmetic is integer, so the result is
 // bitwise reproducible.
+#include <stdlib.h>
+
 #include "dsa_common.h"
 #include "dsa_kernels.h"
 
 namespace dsa {
 
 constexpr int kTile = 32;          // keys per MFMA column tile
-constexpr int kSelThreads = 512;   // 8 waves; wave w scores key tiles w, w + 8, ... for all tokens
 constexpr int kSelWaves = kSelThreads / 64;
-constexpr int kMaxChunk = 4096;    // keys per workgroup held in LDS
-constexpr int kTauMaxM = 32;
 constexpr int kPrefetch = 2;       // key tiles in flight per wave
-constexpr int kMaxWG = 1024;
 
 // ----------------------------------------------------------------------------- tile math
 
@@ -653,6 +651,7 @@ DSA_DEV void resolve_token(const SelParams& p, int t, SelShared& sh, uint32_t ep
   constexpr int kCntPer = kMaxWG / kSelThreads;
   const uint32_t tag = epoch + 1u;
   uint32_t cw[kCntPer];
+  bool gave_up = false;
   {
     uint64_t v[kCntPer];
 #pragma unroll
@@ -669,6 +668,7 @@ DSA_DEV void resolve_token(const SelParams& p, int t, SelShared& sh, uint32_t ep
         if (__builtin_amdgcn_s_memrealtime() - t0 > kSpinLimit) {
           ast(p.ctl + ctl::kError, 1u);
           v[j] = 0;
+          gave_up = true;
           break;
         }
         v[j] = ald64(cnt_t + (w < nwg ? w : nwg - 1));
@@ -676,7 +676,15 @@ DSA_DEV void resolve_token(const SelParams& p, int t, SelShared& sh, uint32_t ep
       cw[j] = (w < nwg) ? (uint32_t)v[j] : 0u;
     }
   }
-  __syncthreads();
+  if (__syncthreads_or(gave_up)) {
+    // not every workgroup published (they were not all resident): this token's selection
+    // is empty, the error word is set, and the launch counter stays as it is -- a
+    // workgroup that has not run yet reads it later and tags with this launch
+    int32_t* out = p.idx + (size_t)t * p.k;
+    for (int i = tid; i < p.k; i += kSelThreads) out[i] = -1;
+    if (tid == 0 && p.count) p.count[t] = 0;
+    return;
+  }
   DSA_MARK(p.trace, 8);
   // every workgroup has published, so every workgroup has read the launch counter
   if (t == 0 && tid == 0) ast(p.ctl + ctl::kEpoch, next_epoch(epoch));
@@ -945,10 +953,11 @@ __global__ void __launch_bounds__(kSelThreads, 1) select_kernel(SelParams p) {
   const int64_t c0 = (int64_t)wg * p.chunk;
   const int T = p.T;
   DSA_MARK(p.trace, 0);
-  // The launch counter (read with a device-scope load, slow to return) is requested after
-  // the prologue's loads, so that waiting for the queries and the first key tiles does
-  // not wait for it; it is first needed when the tau bound is published.
-  uint32_t epoch = 0u;
+  // The launch counter and the error word (read with one device-scope load, slow to
+  // return) are requested after the prologue's loads, so that waiting for the queries and
+  // the first key tiles does not wait for them; they are first needed when the tau bound
+  // is published.
+  uint64_t ctlw = 0u;
   // ---------------- P1: scores of this chunk into LDS
   int64_t nk64 = p.L - c0;
   nk64 = nk64 < 0 ? 0 : (nk64 > p.chunk ? p.chunk : nk64);
@@ -1005,7 +1014,7 @@ __global__ void __launch_bounds__(kSelThreads, 1) select_kernel(SelParams p) {
     __syncthreads();
     Frag8 qf[4];
     load_qlin_frags<RTW>(sh.ql, 0, qf);
-    epoch = ald(p.ctl + ctl::kEpoch);
+    ctlw = ald64(reinterpret_cast<const uint64_t*>(p.ctl + ctl::kEpoch));
     DSA_MARK(p.trace, 1);
     DSA_MARK_CLK(p.trace, 14);
     if (nmine > 0) {
@@ -1040,15 +1049,16 @@ __global__ void __launch_bounds__(kSelThreads, 1) select_kernel(SelParams p) {
       }
     }
   } else {
-    epoch = ald(p.ctl + ctl::kEpoch);
+    ctlw = ald64(reinterpret_cast<const uint64_t*>(p.ctl + ctl::kEpoch));
     constexpr int PER = kMaxChunk / kSelThreads;
-    for (int t = 0; t < T; ++t) {
+    // a workgroup past the last key (nwg = T > ceil(L / chunk)) reads no scores
+    for (int t = 0; t < (nkeys > 0 ? T : 0); ++t) {
       const float* src = p.scores + (size_t)t * p.ld + c0;
       float v[PER];
 #pragma unroll
       for (int q = 0; q < PER; ++q) {
         const int i = tid + q * kSelThreads;
-        v[q] = src[i < nkeys ? i : (nkeys > 0 ? nkeys - 1 : 0)];
+        v[q] = src[i < nkeys ? i : nkeys - 1];
       }
 #pragma unroll
       for (int q = 0; q < PER; ++q) {
@@ -1057,9 +1067,21 @@ __global__ void __launch_bounds__(kSelThreads, 1) select_kernel(SelParams p) {
       }
     }
   }
+  const uint32_t epoch = (uint32_t)ctlw;
   const uint32_t tag = epoch + 1u;                       // this launch's slot tag
   __syncthreads();
   DSA_MARK(p.trace, 2);
+  // A workspace whose error word is set (an earlier launch on it gave up waiting) is not
+  // trusted: the launch publishes nothing and writes an empty selection, until the
+  // workspace is cleared again.
+  if ((ctlw >> 32) != 0u) {
+    if (wg < T) {
+      int32_t* out = p.idx + (size_t)wg * p.k;
+      for (int i = tid; i < p.k; i += kSelThreads) out[i] = -1;
+      if (tid == 0 && p.count) p.count[wg] = 0;
+    }
+    return;
+  }
   if (wg >= T) DSA_MARK_CLK(p.trace, 13);     // core clock over P1 (profiling builds)
   // ---------------- tau bound.  Any split of the chunk's (visible) scores into at least
   // m non-empty groups gives one: the m-th largest group maximum is <= the m-th largest
@@ -1206,32 +1228,17 @@ hipError_t launch_indexer_scores(const void* q_idx, const float* w_idx, const vo
   return hipGetLastError();
 }
 
-SelGeometry select_geometry(int T, int64_t L, int64_t pos0, int k, int num_cu) {
-  SelGeometry g{};
-  int64_t per = (L + num_cu - 1) / num_cu;
-  int64_t chunk = ((per + kSelThreads - 1) / kSelThreads) * kSelThreads;
-  if (chunk < kSelThreads) chunk = kSelThreads;
-  g.chunk = (int)chunk;
-  int64_t nwg = (L + chunk - 1) / chunk;
-  if (nwg < T) nwg = T;
-  g.nwg = (int)nwg;
-  g.fits = chunk <= kMaxChunk && nwg <= kMaxWG;
-  g.n_part = (int)(pos0 / chunk);
-  const int64_t kmax = (int64_t)k < L ? k : L;
-  g.m = 0;
-  if (g.n_part >= 1) {
-    const int64_t m = (kmax + g.n_part - 1) / g.n_part;
-    if (m >= 1 && m <= kTauMaxM) g.m = (int)m;
-  }
-  return g;
+// data part of a selection workspace (after the control block): count and tau slots, then
+// the candidate lists
+size_t select_data_bytes(int T, int64_t L, int k, int num_cu) {
+  static_assert(kSelMaxT == kMaxT, "one verify-block limit");
+  return (size_t)kMaxT * kMaxWG * (8 + 8) + (size_t)select_candidate_slots(T, L, k, num_cu) * sizeof(uint64_t);
 }
 
 size_t select_workspace_bytes(int T, int64_t L, int k, int num_cu) {
-  SelGeometry g = select_geometry(T, L, L - T, k, num_cu);
-  return ctl::kBytes + (size_t)kMaxT * kMaxWG * (8 + 8) + (size_t)kMaxT * g.nwg * g.chunk * sizeof(uint64_t);
+  return ctl::kBytes + select_data_bytes(T, L, k, num_cu);
 }
 
-int64_t select_max_context(int num_cu) { return (int64_t)num_cu * kMaxChunk; }
 
 #ifdef DSA_TRACE
 static uint64_t* g_trace = nullptr;
@@ -1239,10 +1246,45 @@ extern "C" void dsa_trace_set(void* buf) { g_trace = static_cast<uint64_t*>(buf)
 uint64_t* dsa_trace_buffer() { return g_trace; }
 #endif
 
+static void* select_fn(int src, int kdt, int T) {
+  // every wave scores all ceil(T/2) row tiles of its key tiles
+  const int rt = row_tiles(T);
+  if (src == 1) return (void*)select_kernel<1, 0, 1>;
+  if (kdt == 0)
+    return rt == 1 ? (void*)select_kernel<0, 0, 1> : rt == 2 ? (void*)select_kernel<0, 0, 2>
+         : rt == 3 ? (void*)select_kernel<0, 0, 3> : (void*)select_kernel<0, 0, 4>;
+  return rt == 1 ? (void*)select_kernel<0, 1, 1> : rt == 2 ? (void*)select_kernel<0, 1, 2>
+       : rt == 3 ? (void*)select_kernel<0, 1, 3> : (void*)select_kernel<0, 1, 4>;
+}
+
+// Workgroups `fn` can hold resident at once on the device (blocks per CU x CUs).  Test
+// hook: the environment variable DSA_RESIDENT_LIMIT, when set to a positive number, caps
+// the result, standing in for CUs held by other work.
+hipError_t resident_capacity(const void* fn, int threads, int num_cu, int64_t* cap) {
+  int per_cu = 0;
+  hipError_t e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, fn, threads, 0);
+  if (e != hipSuccess) return e;
+  int64_t c = (int64_t)per_cu * num_cu;
+  if (const char* lim = getenv("DSA_RESIDENT_LIMIT")) {
+    const long v = strtol(lim, nullptr, 10);
+    if (v > 0 && v < c) c = v;
+  }
+  *cap = c;
+  return hipSuccess;
+}
+
+hipError_t select_check_resident(int src, int kdt, int T, int64_t L, int64_t pos0, int k, int num_cu) {
+  const SelGeometry g = select_geometry(T, L, pos0, k, num_cu);
+  int64_t cap = 0;
+  hipError_t e = resident_capacity(select_fn(src, kdt, T), kSelThreads, num_cu, &cap);
+  if (e != hipSuccess) return e;
+  return cap < g.nwg ? hipErrorCooperativeLaunchTooLarge : hipSuccess;
+}
+
 hipError_t launch_select(int src, const void* q_idx, const float* w_idx, const void* k_idx,
                          const float* k_scale, int kdt, const float* scores, int64_t ld, int T,
-                         int64_t L, int64_t pos0, int k, int32_t* idx, int32_t* count, void* ws,
-                         int num_cu, hipStream_t st) {
+                         int64_t L, int64_t pos0, int k, int32_t* idx, int32_t* count, void* ctlp,
+                         void* data, int num_cu, hipStream_t st) {
   SelGeometry g = select_geometry(T, L, pos0, k, num_cu);
   SelParams p{};
   p.q_idx = static_cast<const uint16_t*>(q_idx);
@@ -1264,29 +1306,18 @@ hipError_t launch_select(int src, const void* q_idx, const float* w_idx, const v
 #ifdef DSA_TRACE
   p.trace = g_trace;
 #endif
-  uint8_t* w8 = static_cast<uint8_t*>(ws);
-  p.ctl = reinterpret_cast<uint32_t*>(w8);
-  p.cnt = reinterpret_cast<uint64_t*>(w8 + ctl::kBytes);
-  p.tauv = reinterpret_cast<uint64_t*>(w8 + ctl::kBytes + (size_t)kMaxT * kMaxWG * 8);
-  p.cand = reinterpret_cast<uint64_t*>(w8 + ctl::kBytes + (size_t)kMaxT * kMaxWG * 16);
+  uint8_t* w8 = static_cast<uint8_t*>(data);
+  p.ctl = static_cast<uint32_t*>(ctlp);
+  p.cnt = reinterpret_cast<uint64_t*>(w8);
+  p.tauv = reinterpret_cast<uint64_t*>(w8 + (size_t)kMaxT * kMaxWG * 8);
+  p.cand = reinterpret_cast<uint64_t*>(w8 + (size_t)kMaxT * kMaxWG * 16);
   void* args[] = {&p};
-  // every wave scores all ceil(T/2) row tiles of its key tiles
-  const int rt = row_tiles(T);
-  void* fn = nullptr;
-  if (src == 1) {
-    fn = (void*)select_kernel<1, 0, 1>;
-  } else if (kdt == 0) {
-    fn = rt == 1 ? (void*)select_kernel<0, 0, 1> : rt == 2 ? (void*)select_kernel<0, 0, 2>
-       : rt == 3 ? (void*)select_kernel<0, 0, 3> : (void*)select_kernel<0, 0, 4>;
-  } else {
-    fn = rt == 1 ? (void*)select_kernel<0, 1, 1> : rt == 2 ? (void*)select_kernel<0, 1, 2>
-       : rt == 3 ? (void*)select_kernel<0, 1, 3> : (void*)select_kernel<0, 1, 4>;
-  }
+  void* fn = select_fn(src, kdt, T);
   // every workgroup must be resident at once (one per CU by the LDS footprint)
-  int per_cu = 0;
-  hipError_t e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, fn, kSelThreads, 0);
+  int64_t cap = 0;
+  hipError_t e = resident_capacity(fn, kSelThreads, num_cu, &cap);
   if (e != hipSuccess) return e;
-  if ((int64_t)per_cu * num_cu < g.nwg) return hipErrorCooperativeLaunchTooLarge;
+  if (cap < g.nwg) return hipErrorCooperativeLaunchTooLarge;
   return hipLaunchKernel(fn, dim3(g.nwg), dim3(kSelThreads), args, 0, st);
 }
 

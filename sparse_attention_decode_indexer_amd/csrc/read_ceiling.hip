@@ -1,12 +1,15 @@
+// Measurement helper, built as its own library (libdsa_read_ceiling.so) and used by the
+// benchmark only; it is no step of the method and not part of libdsa.so.
+//
 // Streaming read of a device buffer: the measured HBM read ceiling that the kernels'
 // achieved bandwidth is compared with.  One 1024-thread workgroup per compute unit
 // reads a contiguous slice with four 16-byte loads in flight per thread (64 KiB per
 // CU), folds the words with xor and writes one word per workgroup, so the write
 // traffic is negligible and the loads cannot be elided.
-#include "dsa_common.h"
-#include "dsa_kernels.h"
+#include <hip/hip_runtime.h>
+#include <stdint.h>
 
-namespace dsa {
+namespace {
 
 constexpr int kSrThreads = 1024;
 constexpr int kSrUnroll = 4;
@@ -41,12 +44,21 @@ __global__ void __launch_bounds__(kSrThreads) stream_read_kernel(const uint4* __
   }
 }
 
-hipError_t launch_stream_read(const void* src, size_t bytes, uint32_t* sink, int nblocks, hipStream_t st) {
+}  // namespace
+
+// Reads `bytes` (a multiple of 16, src 16-byte aligned) as a plain stream with one
+// workgroup per compute unit (at most 1024) and writes an xor fold of it to
+// sink[0 .. workgroups) (caller-owned, at least 1024 uint32 words on the device).
+// Returns 0, or -1 for bad arguments, or the HIP error code of the launch.
+extern "C" int dsa_read_ceiling_stream(const void* src, size_t bytes, uint32_t* sink, void* stream) {
+  if (!src || !sink || (reinterpret_cast<uintptr_t>(src) & 15u) || (bytes & 15u) || bytes == 0) return -1;
+  int dev = 0, ncu = 256;
+  if (hipGetDevice(&dev) != hipSuccess || hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+    return (int)hipGetLastError();
+  const int nblocks = ncu < 1024 ? ncu : 1024;
   const size_t n16 = bytes / 16;
   const size_t per = (n16 + nblocks - 1) / nblocks;
-  hipLaunchKernelGGL(stream_read_kernel, dim3(nblocks), dim3(kSrThreads), 0, st,
+  hipLaunchKernelGGL(stream_read_kernel, dim3(nblocks), dim3(kSrThreads), 0, (hipStream_t)stream,
                      static_cast<const uint4*>(src), n16, per, sink);
-  return hipGetLastError();
+  return (int)hipGetLastError();
 }
-
-}  // namespace dsa

@@ -1,0 +1,57 @@
+// Launch geometry of the fused indexer scan + top-k selection (plain C++, no device code,
+// so host-side checks can compile it on their own).
+//
+// The keys [0, L) are cut into chunks of `chunk` keys, one workgroup per chunk and at
+// least one workgroup per token (the resolver of token t is workgroup t).  Workgroups
+// whose chunk lies wholly before pos0 hold only keys visible to every token; each of
+// them publishes a lower bound of its m-th largest score with m * n_part >= min(k, L),
+// so at least k scores lie at or above the smallest published bound.
+#pragma once
+#include <stdint.h>
+
+namespace dsa {
+
+constexpr int kSelThreads = 512;   // 8 waves; wave w scores key tiles w, w + 8, ... for all tokens
+constexpr int kMaxChunk = 4096;    // keys per workgroup held in LDS
+constexpr int kTauMaxM = 32;       // largest tau rank a workgroup searches (one per lane pair)
+constexpr int kMaxWG = 1024;       // slots per token in the count and tau arrays
+constexpr int kSelMaxT = 8;        // tokens of a verify block
+
+struct SelGeometry {
+  int chunk;    // keys per workgroup (a multiple of kSelThreads)
+  int nwg;      // workgroups
+  int n_part;   // workgroups [0, n_part) publish a tau bound
+  int m;        // tau rank (0: no bound)
+  bool fits;    // chunk fits LDS and nwg fits the count arrays
+};
+
+inline SelGeometry select_geometry(int T, int64_t L, int64_t pos0, int k, int num_cu) {
+  SelGeometry g{};
+  const int64_t per = (L + num_cu - 1) / num_cu;
+  int64_t chunk = ((per + kSelThreads - 1) / kSelThreads) * kSelThreads;
+  if (chunk < kSelThreads) chunk = kSelThreads;
+  g.chunk = (int)chunk;
+  int64_t nwg = (L + chunk - 1) / chunk;
+  if (nwg < T) nwg = T;
+  g.nwg = (int)nwg;
+  g.fits = chunk <= kMaxChunk && nwg <= kMaxWG;
+  g.n_part = (int)(pos0 / chunk);
+  const int64_t kmax = (int64_t)k < L ? k : L;
+  g.m = 0;
+  if (g.n_part >= 1) {
+    const int64_t m = (kmax + g.n_part - 1) / g.n_part;
+    if (m >= 1 && m <= kTauMaxM) g.m = (int)m;
+  }
+  return g;
+}
+
+inline int64_t select_max_context(int num_cu) { return (int64_t)num_cu * kMaxChunk; }
+
+// candidate slots of a selection workspace sized for (T, L): one chunk per (token,
+// workgroup) for the largest block, so any pos0 and T <= kSelMaxT fit
+inline int64_t select_candidate_slots(int T, int64_t L, int k, int num_cu) {
+  const SelGeometry g = select_geometry(T, L, L - T, k, num_cu);
+  return (int64_t)kSelMaxT * g.nwg * g.chunk;
+}
+
+}  // namespace dsa

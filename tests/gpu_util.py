@@ -50,3 +50,14 @@ def tie_band_ok(idx_gpu, idx_ref, scores_ref, mag_ref, pos0, k, rel=2.0 ** -16):
             if abs(s[p] - theta) > band:
                 return False, ndiff
     return True, ndiff
+
+
+def check_oproj(gx, tf_x, attn, wo_deq, x, allowance=0.0):
+    """x_out = bf16(x + attn . W_o^T) against the oracle's fp64 value on the same attention
+    output: one bf16 ulp of the result, the fp32 accumulation bound 2^-16 * sum |terms|
+    (1024 products and the residual), and any code-flip allowance."""
+    from oracle import dsa_oracle as O
+    S = O.project(np.abs(attn), np.abs(wo_deq)) + np.abs(x)
+    tol = 2.0 ** -7 * np.abs(tf_x) + 2.0 ** -16 * S + allowance
+    bad = np.abs(gx - tf_x) > tol
+    assert not bad.any(), f"{bad.sum()} output values beyond tolerance, worst {np.max(np.abs(gx - tf_x) - tol)}"

@@ -78,8 +78,15 @@ def test_validation_errors_without_launch():
     assert a(FAKE, FAKE, FAKE, None, None, dsa.BF16, FAKE, 16, 1, 100, 0.1, None, FAKE, dsa.FP32,
              FAKE, 8) == E["DSA_ERR_WORKSPACE"]
     s = lambda *x: dsa.swa_attn(*x, stream=0, raise_on_error=False)
-    assert s(FAKE, FAKE, FAKE, 130, 8, 500, 128, 0.1, None, FAKE, dsa.FP32, FAKE, 1 << 30) == E["DSA_ERR_SHAPE"]
-    assert s(FAKE, FAKE, FAKE, 135, 8, 500, 128, 0.1, None, FAKE, dsa.FP32, None, 1 << 30) == E["DSA_ERR_WORKSPACE"]
+    assert s(FAKE, FAKE, FAKE, None, None, dsa.BF16, 130, 8, 500, 128, 0.1, None, FAKE, dsa.FP32, FAKE,
+             1 << 30) == E["DSA_ERR_SHAPE"]
+    assert s(FAKE, FAKE, FAKE, None, None, dsa.BF16, 135, 8, 500, 128, 0.1, None, FAKE, dsa.FP32, None,
+             1 << 30) == E["DSA_ERR_WORKSPACE"]
+    # e4m3 rings need both row-scale vectors, bf16 rings none
+    assert s(FAKE, FAKE, FAKE, None, FAKE, dsa.FP8_E4M3, 135, 8, 500, 128, 0.1, None, FAKE, dsa.FP32, FAKE,
+             1 << 30) == E["DSA_ERR_DTYPE"]
+    assert s(FAKE, FAKE, FAKE, FAKE, FAKE, dsa.BF16, 135, 8, 500, 128, 0.1, None, FAKE, dsa.FP32, FAKE,
+             1 << 30) == E["DSA_ERR_DTYPE"]
     cfg = dsa.layer_config(dsa.LAYER_DSA)
     w = dsa.LayerWeights(FAKE, FAKE, FAKE)
     c = dsa.LayerCache(FAKE, FAKE, FAKE, FAKE, 1000)
@@ -96,7 +103,7 @@ def test_validation_errors_without_launch():
     assert L() == E["DSA_ERR_NULL"]
 
 
-def test_w8a8_and_stream_read_validation_without_launch():
+def test_w8a8_validation_without_launch():
     import sparse_attention_decode_indexer_amd as dsa
     E = {v: k for k, v in dsa.STATUS.items()}
     cfg = dsa.layer_config(dsa.LAYER_DSA)
@@ -110,9 +117,37 @@ def test_w8a8_and_stream_read_validation_without_launch():
     assert L(dsa.LayerWeights(FAKE, FAKE, FAKE, dsa.FP8_E4M3, None, None)) == E["DSA_ERR_DTYPE"]
     assert L(dsa.LayerWeights(FAKE, FAKE, FAKE, dsa.FP8_E4M3, FAKE, None)) == E["DSA_ERR_DTYPE"]
     assert L(dsa.LayerWeights(FAKE, FAKE, FAKE, dsa.BF16, FAKE, FAKE)) == E["DSA_ERR_DTYPE"]
-    r = lambda *a: dsa.dsa_stream_read(*a, stream=0, raise_on_error=False)
-    assert r(None, 1024, FAKE) == E["DSA_ERR_NULL"]
-    assert r(FAKE, 1024, None) == E["DSA_ERR_NULL"]
-    assert r(MIS, 1024, FAKE) == E["DSA_ERR_ALIGN"]
-    assert r(FAKE, 1000, FAKE) == E["DSA_ERR_ALIGN"]
-    assert r(FAKE, 0, FAKE) == E["DSA_ERR_SHAPE"]
+
+
+def test_workspace_status_validation_without_device_access():
+    """The status call checks its arguments before it synchronises or reads anything."""
+    import sparse_attention_decode_indexer_amd as dsa
+    E = {v: k for k, v in dsa.STATUS.items()}
+    st = lambda *a: dsa.dsa_workspace_status(*a, stream=0, raise_on_error=False)
+    assert st(None, 1 << 20) == E["DSA_ERR_NULL"]
+    assert st(MIS, 1 << 20) == E["DSA_ERR_ALIGN"]
+    assert st(FAKE, 16383) == E["DSA_ERR_WORKSPACE"]        # smaller than the control block
+
+
+def test_every_workspace_holds_the_control_block():
+    import sparse_attention_decode_indexer_amd as dsa
+    for kind, k in ((dsa.WS_TOPK, 64), (dsa.WS_INDEX_TOPK, 64), (dsa.WS_SPARSE_ATTN, 64),
+                    (dsa.WS_SWA_ATTN, 128), (dsa.WS_LAYER_DSA, 64), (dsa.WS_LAYER_SWA, 128)):
+        assert dsa.dsa_workspace_bytes(kind, 1, 4096, k) >= 16384, kind
+
+
+def test_read_ceiling_helper_is_outside_the_library_and_validates():
+    """The benchmark's streaming-read helper lives in its own library: libdsa.so does not
+    export it, and it rejects bad arguments without launching."""
+    import sparse_attention_decode_indexer_amd as dsa
+    lib = C.CDLL(dsa.LIB_PATH)
+    assert not hasattr(lib, "dsa_stream_read") and not hasattr(lib, "dsa_read_ceiling_stream")
+    rc = C.CDLL(os.path.join(os.path.dirname(dsa.LIB_PATH), "libdsa_read_ceiling.so"))
+    f = rc.dsa_read_ceiling_stream
+    f.argtypes = [C.c_void_p, C.c_size_t, C.c_void_p, C.c_void_p]
+    f.restype = C.c_int
+    assert f(None, 1024, FAKE, None) == -1
+    assert f(FAKE, 1024, None, None) == -1
+    assert f(MIS, 1024, FAKE, None) == -1
+    assert f(FAKE, 1000, FAKE, None) == -1
+    assert f(FAKE, 0, FAKE, None) == -1

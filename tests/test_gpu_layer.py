@@ -6,7 +6,11 @@ Stage checks are teacher-forced: the oracle consumes the GPU's own rotated proje
 * cache append: K/V rows equal the exported rotated rows bit for bit; the e4m3 indexer
   rows and scales equal the oracle's quantisation of the exported k_I bit for bit;
 * selection: within the 2^-16 * S rounding band of the fp64 indexer scores;
-* layer output: |gpu - ref| <= 2e-2 * max(1, |ref|) (bf16 storage of large values).
+* DSA layer output: the standalone sparse attention on the step's own rotated queries,
+  cache and indices reproduces the layer's attention output bit for bit; the oracle's
+  output projection of it must match to one bf16 ulp plus the fp32 accumulation bound
+  2^-16 * sum |terms| (and the free-running oracle to 2e-2 * max(1, |ref|));
+* SWA layer output: two bf16 ulps of the teacher-forced oracle.
 """
 import math
 
@@ -16,7 +20,7 @@ import torch
 
 import synth
 from oracle import dsa_oracle as O
-from tests.gpu_util import DEV, up, down, bf16_bits, tie_band_ok
+from tests.gpu_util import DEV, up, down, bf16_bits, tie_band_ok, check_oproj
 
 pytestmark = pytest.mark.gpu
 
@@ -82,6 +86,38 @@ def _run_layer(dsa, kind, lay, x_bits, T, pos0, top_k=2048, window=128, sink=Non
     return out
 
 
+def _gpu_attention(dsa, g, T, L, top_k, sink=None):
+    """The layer's attention output as the standalone call computes it on the step's own
+    rotated queries, cache and indices (bf16 bits [T][1024])."""
+    d = g["dev"]
+    att = torch.zeros((T, 1024), dtype=torch.int16, device=DEV)
+    ws = dsa.workspace(dsa.WS_SPARSE_ATTN, T, L, top_k)
+    dsa.dsa_sparse_attn(d["qkv"][:, :1024].contiguous(), d["k"], d["v"], None, None, dsa.BF16, d["idx"], top_k, T,
+                        L, 1 / math.sqrt(128), sink, att, dsa.BF16, ws)
+    torch.cuda.synchronize()
+    return bf16_bits(att)
+
+
+def _check_dsa_output(dsa, g, lay, x, T, pos0, top_k, sink=None, w8=None):
+    """Tight check of the DSA layer's output: teacher-forced oracle fed the GPU's rotated
+    projection, indices and attention output; one bf16 ulp + 2^-16 * sum |terms|."""
+    L = pos0 + T
+    att = _gpu_attention(dsa, g, T, L, top_k, sink)
+    cache = {"k": lay.k.copy(), "v": lay.v.copy(), "k_idx": lay.k_idx.copy(), "k_idx_scale": lay.k_idx_scale.copy()}
+    kw = dict(top_k=top_k)
+    wq, wo = lay.w_qkvi, lay.w_o
+    if w8 is not None:
+        wq, wo = w8[0], w8[2]
+        kw.update(w_qkvi_scale=w8[1], w_o_scale=w8[3])
+        wo_deq = O.decode_e4m3(w8[2]) * np.asarray(w8[3], np.float64)[:, None]
+    else:
+        wo_deq = O.decode_bf16(lay.w_o)
+    tf = O.layer_step("dsa", x, lay.gamma, wq, wo, cache, pos0, teacher={"qkv": g["qkv"], "idx": g["idx"], "attn": att},
+                      **kw)
+    check_oproj(O.decode_bf16(g["x_out"]), tf["x_out_f64"], O.decode_bf16(att), wo_deq, O.decode_bf16(x))
+    return tf
+
+
 @pytest.mark.parametrize("L,T,top_k", [(3000, 8, 2048), (40000, 8, 2048), (777, 3, 64)])
 def test_dsa_layer_step_stages(dsa, L, T, top_k):
     pos0 = L - T
@@ -113,7 +149,9 @@ def test_dsa_layer_step_stages(dsa, L, T, top_k):
     ridx, _ = O.topk_indices(r, pos0, top_k)
     okb, nd = tie_band_ok(g["idx"], ridx, r, S, pos0, top_k)
     assert okb, nd
-    # layer output (teacher-forced and free-running)
+    # layer output: tight against the teacher-forced oracle on the GPU's attention output,
+    # loose against the free-running oracle (whose selection may differ inside the band)
+    _check_dsa_output(dsa, g, lay, x, T, pos0, top_k)
     gx = O.decode_bf16(g["x_out"])
     for ref in (tf["x_out"], free["x_out"]):
         assert np.all(np.abs(gx - ref) <= 2e-2 * np.maximum(1.0, np.abs(ref)))
@@ -122,7 +160,7 @@ def test_dsa_layer_step_stages(dsa, L, T, top_k):
 # windows up to 153 run attention inside the output projection (W + T - 1 <= 160 rows);
 # 200 takes the separate attention launch
 @pytest.mark.parametrize("pos0,T,window", [(5000, 8, 128), (100, 8, 128), (0, 1, 128), (3, 5, 128),
-                                           (5000, 8, 153), (5000, 8, 200), (20, 8, 200)])
+                                           (5000, 8, 153), (5000, 8, 200), (20, 8, 200), ((1 << 20) - 8, 8, 128)])
 def test_swa_layer_step_stages(dsa, pos0, T, window):
     cap = 256
     L = pos0 + T
@@ -191,6 +229,13 @@ def test_layer_step_with_sink_matches_oracle_attention(dsa):
     ref = O.project(attn, O.decode_bf16(lay.w_o)) + O.decode_bf16(x)
     gx = O.decode_bf16(g["x_out"])
     assert np.all(np.abs(gx - ref) <= 2e-2 * np.maximum(1.0, np.abs(ref)))
+    # the GPU's own attention output with the sink (the standalone call on the step's
+    # inputs): the oracle's attention with the sink within the attention tolerance, and
+    # the output projection of it within one ulp + the accumulation bound
+    att = _gpu_attention(dsa, g, T, L, 2048, sink)
+    assert np.max(np.abs(O.decode_bf16(att) - attn)) <= 2e-2
+    ref_t = O.project(O.decode_bf16(att), O.decode_bf16(lay.w_o)) + O.decode_bf16(x)
+    check_oproj(gx, ref_t, O.decode_bf16(att), O.decode_bf16(lay.w_o), O.decode_bf16(x))
 
 
 @pytest.mark.parametrize("kind,L,T", [("dsa", 40000, 8), ("swa", 3000, 8), ("dsa", 777, 3)])
@@ -248,9 +293,11 @@ def test_layer_step_graph_replays_match_direct_launch(dsa, kind, L, T):
 
 @pytest.mark.parametrize("w8a8", [False, True])
 def test_dsa_layer_step_full_context(dsa, w8a8):
-    """The DSA layer step at the benchmark's size (L = 2^20, T = 8, top-2048): appended rows
+    """The DSA layer step at the benchmark's size (L = 2^20, T = 8, top-2048): the projection
+    and RoPE at positions 2^20 - 8 .. 2^20 - 1 against the free-running oracle, appended rows
     bitwise, the selection within the score band of the fp64 scores of the GPU's own rotated
-    queries over the updated cache, and the output against the teacher-forced oracle."""
+    queries over the updated cache, and the output against the teacher-forced oracle fed the
+    GPU's own attention output (one ulp + the accumulation bound)."""
     L, T, top_k = 1 << 20, 8, 2048
     pos0 = L - T
     lay = synth.layer_inputs("dsa", 5, L, T, seed=21)
@@ -264,6 +311,13 @@ def test_dsa_layer_step_full_context(dsa, w8a8):
         kw.update(w_qkvi_scale=w8[1], w_o_scale=w8[3])
     cache = {"k": lay.k.copy(), "v": lay.v.copy(), "k_idx": lay.k_idx.copy(), "k_idx_scale": lay.k_idx_scale.copy()}
     tf = O.layer_step("dsa", x, lay.gamma, wq, wo, cache, pos0, teacher={"qkv": g["qkv"], "idx": g["idx"]}, **kw)
+    # tf["qkv"] is the oracle's own (free-running) projection + RoPE at these positions
+    if w8a8:
+        from tests.test_gpu_w8a8 import _proj_ok
+        _proj_ok(O.decode_bf16(g["qkv"]), tf["qkv"], tf["normed"], w8[0], w8[1], "dsa")
+    else:
+        okq = _within_ulp(O.decode_bf16(g["qkv"]), tf["qkv"])
+        assert okq.all(), f"{(~okq).sum()} projection values beyond tolerance at 1M positions"
     assert np.array_equal(g["k"][pos0:L], g["qkv"][:, 1024:1152])
     assert np.array_equal(g["v"][pos0:L], g["qkv"][:, 1152:1280])
     assert np.array_equal(g["k_idx"][pos0:L], cache["k_idx"][pos0:L])
@@ -277,3 +331,4 @@ def test_dsa_layer_step_full_context(dsa, w8a8):
     assert okb, nd
     gx = O.decode_bf16(g["x_out"])
     assert np.all(np.abs(gx - tf["x_out"]) <= 2e-2 * np.maximum(1.0, np.abs(tf["x_out"])))
+    _check_dsa_output(dsa, g, lay, x, T, pos0, top_k, w8=w8)

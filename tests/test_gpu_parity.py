@@ -109,13 +109,12 @@ def test_indexer_full_context_sampled(dsa):
     cols = np.unique(np.concatenate([rng.choice(inp.L, 4000, replace=False),
                                      np.arange(inp.L - 64, inp.L), inp.planted[:500]]))
     krows = O.dequant_rows(inp.k_idx[cols], "fp8", inp.k_idx_scale[cols])
-    q = O.decode_bf16(inp.q_idx)
+    # the oracle over the sampled rows only, every row visible to every token; the causal
+    # limit is then applied by the rows' own positions
+    r, S = O.indexer_scores(O.decode_bf16(inp.q_idx), inp.w_idx, krows, len(cols) - 1, with_abs=True)
     for t in range(inp.T):
-        d = q[t] @ krows.T
-        r = inp.w_idx[t].astype(np.float64) @ np.maximum(d, 0)
-        S = np.abs(inp.w_idx[t].astype(np.float64)) @ (np.abs(q[t]) @ np.abs(krows).T)
         vis = cols <= inp.pos0 + t
-        assert np.all(np.abs(g[t, cols[vis]] - r[vis]) <= 2.0 ** -16 * S[vis] + 1e-30)
+        assert np.all(np.abs(g[t, cols[vis]] - r[t, vis]) <= 2.0 ** -16 * S[t, vis] + 1e-30)
         assert np.all(np.isneginf(g[t, cols[~vis]]))
 
 
@@ -202,11 +201,16 @@ def test_topk_full_context(dsa):
 
 # ----------------------------------------------------------------------------- fused scan + top-k
 
-@pytest.mark.parametrize("name,L,T,seed", [("tiny", None, None, 0), ("verify64k", 65536, 8, 0),
-                                           ("verify256k_fp8", 40000, 8, 1), ("verify1m", 100000, 7, 2),
-                                           ("verify1m", None, None, 3)])
-def test_index_topk_matches_materialised_path_and_oracle(dsa, name, L, T, seed):
-    inp = synth.dsa_config(name, seed=seed, L=L, T=T)
+@pytest.mark.parametrize("name,L,T,seed,tie", [("tiny", None, None, 0, False), ("tiny", None, None, 0, True),
+                                               ("tiny", None, 8, 1, True), ("verify64k", 65536, 8, 0, False),
+                                               ("verify256k_fp8", 40000, 8, 1, False),
+                                               ("verify256k_fp8", None, None, 0, False),
+                                               ("verify1m", 100000, 7, 2, False), ("verify1m", None, None, 3, False)])
+def test_index_topk_matches_materialised_path_and_oracle(dsa, name, L, T, seed, tie):
+    """Fused scan + top-k equals top-k of the GPU's own materialised scores bit for bit, and
+    the oracle's selection within the rounding band; on the integer configs (plain and
+    tie-stress, where most keys tie at the cut) it equals the oracle's bit for bit."""
+    inp = synth.dsa_config(name, seed=seed, L=L, T=T, tie_stress=tie)
     T, L, k = inp.T, inp.L, inp.top_k
     idx = torch.full((T, k), -7, dtype=torch.int32, device=DEV)
     cnt = torch.zeros(T, dtype=torch.int32, device=DEV)
@@ -308,6 +312,24 @@ def test_sparse_attention_vs_oracle(dsa, name, L, out_dtype, with_sink):
     _check_attn(got, ref, out_dtype)
 
 
+def test_sparse_attention_fp8_cache_full_256k(dsa):
+    """The 256K verify config at its stated size: e4m3 indexer keys and e4m3 K/V with row
+    scales; attention over the fused selection's own indices against the oracle."""
+    inp = synth.dsa_config("verify256k_fp8", seed=0)
+    T, L, k = inp.T, inp.L, inp.top_k
+    idx = torch.full((T, k), -7, dtype=torch.int32, device=DEV)
+    ws = dsa.workspace(dsa.WS_INDEX_TOPK, T, L, k)
+    dsa.dsa_index_topk(up(inp.q_idx), up(inp.w_idx), up(inp.k_idx), up(inp.k_idx_scale), dsa.FP8_E4M3, T, L,
+                       inp.pos0, k, idx, None, ws)
+    torch.cuda.synchronize()
+    gi = down(idx)
+    assert np.all((gi >= 0).sum(axis=1) == k)
+    K, V = _attn_inputs(inp)
+    ref = O.sparse_attention(O.decode_bf16(inp.q), K, V, gi, SM)
+    for out_dtype in ("f32", "bf16"):
+        _check_attn(_run_sparse(dsa, inp, gi, k, out_dtype), ref, out_dtype)
+
+
 def test_sparse_attention_ragged_lists(dsa):
     """Skipped entries (-1, >= L), duplicates, a short list, an empty token row."""
     inp = synth.dsa_config("verify64k", seed=4, L=2000, T=4)
@@ -352,20 +374,30 @@ def test_sparse_attention_fp8_values_all_codes(dsa):
             assert np.array_equal(got[t, h].astype(np.float64), want[t])
 
 
-@pytest.mark.parametrize("pos0,T,window,cap", [(5000, 8, 128, 135), (3, 4, 128, 140), (1000, 1, 1, 8),
-                                               (70, 8, 128, 256), (5000, 8, 300, 320), (200, 3, 129, 140)])
-def test_swa_vs_oracle(dsa, pos0, T, window, cap):
+@pytest.mark.parametrize("pos0,T,window,cap,kv", [(5000, 8, 128, 135, "bf16"), (3, 4, 128, 140, "bf16"),
+                                                  (1000, 1, 1, 8, "bf16"), (70, 8, 128, 256, "bf16"),
+                                                  (5000, 8, 300, 320, "bf16"), (200, 3, 129, 140, "bf16"),
+                                                  (5000, 8, 128, 135, "fp8"), (1048568, 8, 128, 256, "fp8"),
+                                                  (40, 5, 300, 320, "fp8")])
+def test_swa_vs_oracle(dsa, pos0, T, window, cap, kv):
     g = np.random.default_rng(pos0)
-    Kr = synth.to_bf16_bits(g.standard_normal((cap, 128)).astype(np.float32))
-    Vr = synth.to_bf16_bits(g.standard_normal((cap, 128)).astype(np.float32))
+    Kf = g.standard_normal((cap, 128)).astype(np.float32)
+    Vf = g.standard_normal((cap, 128)).astype(np.float32)
+    if kv == "bf16":
+        Kr, Vr, ks, vs = synth.to_bf16_bits(Kf), synth.to_bf16_bits(Vf), None, None
+        K64, V64 = O.decode_bf16(Kr), O.decode_bf16(Vr)
+    else:
+        (Kr, ks), (Vr, vs) = synth.to_e4m3_rows(Kf), synth.to_e4m3_rows(Vf)
+        K64, V64 = O.dequant_rows(Kr, "fp8", ks), O.dequant_rows(Vr, "fp8", vs)
     q = synth.to_bf16_bits(g.standard_normal((T, 8, 128)).astype(np.float32))
     for sink in (None, synth.sink_logits(5)):
         out = torch.full((T, 8, 128), float("nan"), dtype=torch.float32, device=DEV)
         ws = dsa.workspace(dsa.WS_SWA_ATTN, T, pos0 + T, window)
-        dsa.swa_attn(up(q), up(Kr), up(Vr), cap, T, pos0, window, SM, None if sink is None else up(sink), out,
-                     dsa.FP32, ws)
+        dsa.swa_attn(up(q), up(Kr), up(Vr), None if ks is None else up(ks), None if vs is None else up(vs),
+                     dsa.BF16 if kv == "bf16" else dsa.FP8_E4M3, cap, T, pos0, window, SM,
+                     None if sink is None else up(sink), out, dsa.FP32, ws)
         torch.cuda.synchronize()
-        ref = O.swa_attention(O.decode_bf16(q), O.decode_bf16(Kr), O.decode_bf16(Vr), cap, pos0, window, SM, sink)
+        ref = O.swa_attention(O.decode_bf16(q), K64, V64, cap, pos0, window, SM, sink)
         _check_attn(down(out).astype(np.float64), ref, "f32")
 
 
@@ -381,14 +413,90 @@ def test_attention_run_to_run_bitwise(dsa):
 
 
 @pytest.mark.parametrize("nbytes", [16, 4096 + 48, (1 << 20) + 16 * 777, 64 << 20])
-def test_stream_read_folds_every_word(dsa, nbytes):
-    """The bandwidth helper reads every 16-byte word exactly once: the xor of the
-    per-workgroup folds equals the host's xor of all 32-bit words."""
+def test_read_ceiling_stream_folds_every_word(dsa, nbytes):
+    """The benchmark's bandwidth helper (its own library) reads every 16-byte word exactly
+    once: the xor of the per-workgroup folds equals the host's xor of all 32-bit words."""
+    import ctypes as C
+    import os
+    lib = C.CDLL(os.path.join(os.path.dirname(dsa.LIB_PATH), "libdsa_read_ceiling.so"))
+    fn = lib.dsa_read_ceiling_stream
+    fn.argtypes = [C.c_void_p, C.c_size_t, C.c_void_p, C.c_void_p]
+    fn.restype = C.c_int
     g = np.random.default_rng(nbytes)
     words = g.integers(0, 2 ** 32, size=nbytes // 4, dtype=np.uint64).astype(np.uint32)
     src = up(words.view(np.int32))
     sink = torch.zeros(1024, dtype=torch.int32, device=DEV)
-    dsa.dsa_stream_read(src, nbytes, sink)
+    assert fn(src.data_ptr(), nbytes, sink.data_ptr(), torch.cuda.current_stream().cuda_stream) == 0
     torch.cuda.synchronize()
     fold = np.bitwise_xor.reduce(down(sink).view(np.uint32))
     assert fold == np.bitwise_xor.reduce(words)
+
+
+# ----------------------------------------------------------------------------- failure reporting
+
+def test_workspace_status_reports_a_set_error_word_and_poisons_the_workspace(dsa):
+    """The error word is set from the host (standing in for a launch that gave up): the
+    status call reports DSA_ERR_LAUNCH, selection calls on the workspace write empty
+    selections, and after dsa_workspace_init the workspace selects correctly again."""
+    inp = synth.dsa_config("tiny", seed=0)
+    T, L, k = inp.T, inp.L, inp.top_k
+    ws = dsa.workspace(dsa.WS_INDEX_TOPK, T, L, k)
+    assert dsa.dsa_workspace_status(ws) == 0
+    ws.view(torch.int32)[769] = 1                      # the sticky error word
+    E = {v: kk for kk, v in dsa.STATUS.items()}
+    assert dsa.dsa_workspace_status(ws, raise_on_error=False) == E["DSA_ERR_LAUNCH"]
+    assert "not valid" in dsa.dsa_last_error()
+    idx = torch.full((T, k), -7, dtype=torch.int32, device=DEV)
+    cnt = torch.full((T,), -7, dtype=torch.int32, device=DEV)
+    args = (up(inp.q_idx), up(inp.w_idx), up(inp.k_idx), None, dsa.BF16, T, L, inp.pos0, k, idx, cnt, ws)
+    dsa.dsa_index_topk(*args)
+    torch.cuda.synchronize()
+    assert np.all(down(idx) == -1) and np.all(down(cnt) == 0)
+    assert dsa.dsa_workspace_status(ws, raise_on_error=False) == E["DSA_ERR_LAUNCH"]
+    dsa.dsa_workspace_init(ws)
+    assert dsa.dsa_workspace_status(ws) == 0
+    dsa.dsa_index_topk(*args)
+    torch.cuda.synchronize()
+    s_ref = O.indexer_scores(O.decode_bf16(inp.q_idx), inp.w_idx, O.decode_bf16(inp.k_idx), inp.pos0)
+    ridx, rcnt = O.topk_indices(s_ref, inp.pos0, k)
+    assert np.array_equal(down(idx), ridx) and np.array_equal(down(cnt), rcnt)
+    assert dsa.dsa_workspace_status(ws) == 0
+
+
+def test_resident_limit_hook_refuses_before_launching(dsa, monkeypatch):
+    """With fewer resident workgroups than the selection needs, the selection calls and the
+    DSA layer step return DSA_ERR_LAUNCH before writing anything (outputs and cache rows
+    keep their values)."""
+    E = {v: kk for kk, v in dsa.STATUS.items()}
+    inp = synth.dsa_config("verify1m", seed=1, L=200000, T=8)
+    T, L, k = inp.T, inp.L, inp.top_k
+    ws = dsa.workspace(dsa.WS_INDEX_TOPK, T, L, k)
+    idx = torch.full((T, k), -7, dtype=torch.int32, device=DEV)
+    monkeypatch.setenv("DSA_RESIDENT_LIMIT", "3")
+    st = dsa.dsa_index_topk(up(inp.q_idx), up(inp.w_idx), up(inp.k_idx), up(inp.k_idx_scale), dsa.FP8_E4M3, T, L,
+                            inp.pos0, k, idx, None, ws, raise_on_error=False)
+    assert st == E["DSA_ERR_LAUNCH"]
+    sc = up(np.zeros((T, L), np.float32))
+    st = dsa.dsa_topk(sc, T, L, L, inp.pos0, k, idx, None, dsa.workspace(dsa.WS_TOPK, T, L, k),
+                      raise_on_error=False)
+    assert st == E["DSA_ERR_LAUNCH"]
+    torch.cuda.synchronize()
+    assert np.all(down(idx) == -7)
+    lay = synth.layer_inputs("dsa", 0, 20000, T, seed=3)
+    kc, vc, ki, ks = up(lay.k), up(lay.v), up(lay.k_idx), up(lay.k_idx_scale)
+    cache = dsa.LayerCache(kc.data_ptr(), vc.data_ptr(), ki.data_ptr(), ks.data_ptr(), lay.capacity)
+    g_gamma, g_w, g_wo = up(lay.gamma), up(lay.w_qkvi), up(lay.w_o)
+    w = dsa.LayerWeights(g_gamma.data_ptr(), g_w.data_ptr(), g_wo.data_ptr())
+    x = up(synth.module_x(3, T))
+    xo = torch.zeros_like(x)
+    wsl = dsa.workspace(dsa.WS_LAYER_DSA, T, 20000, k)
+    st = dsa.dsa_layer_step(dsa.layer_config(dsa.LAYER_DSA), w, cache, x, xo, T, 20000 - T, ws=wsl,
+                            raise_on_error=False)
+    assert st == E["DSA_ERR_LAUNCH"]
+    torch.cuda.synchronize()
+    assert np.array_equal(bf16_bits(kc), lay.k) and np.array_equal(down(ki), lay.k_idx)
+    assert np.all(down(xo) == 0)
+    monkeypatch.delenv("DSA_RESIDENT_LIMIT")
+    dsa.dsa_layer_step(dsa.layer_config(dsa.LAYER_DSA), w, cache, x, xo, T, 20000 - T, ws=wsl)
+    torch.cuda.synchronize()
+    assert not np.array_equal(bf16_bits(kc), lay.k)

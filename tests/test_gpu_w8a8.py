@@ -23,7 +23,7 @@ import torch
 
 import synth
 from oracle import dsa_oracle as O
-from tests.gpu_util import DEV, up, down, bf16_bits, tie_band_ok
+from tests.gpu_util import DEV, up, down, bf16_bits, tie_band_ok, check_oproj
 from tests.test_gpu_layer import _run_layer, _within_ulp
 
 pytestmark = pytest.mark.gpu
@@ -57,13 +57,7 @@ def _proj_ok(gq, rq, y, w_codes, w_scale, kind):
                              f"oracle {rq[t, c]!r} sum|terms| {S[t, c]!r}")
 
 
-def _check_oproj(gx, tf_x, attn, wo_deq, x, allowance=0.0):
-    """x_out = bf16(x + o-proj): one bf16 ulp of the result, the fp32 accumulation
-    bound 2^-16 * sum |terms|, and any code-flip allowance."""
-    S = O.project(np.abs(attn), np.abs(wo_deq)) + np.abs(x)
-    tol = 2.0 ** -7 * np.abs(tf_x) + 2.0 ** -16 * S + allowance
-    bad = np.abs(gx - tf_x) > tol
-    assert not bad.any(), f"{bad.sum()} output values beyond tolerance, worst {np.max(np.abs(gx - tf_x) - tol)}"
+_check_oproj = check_oproj
 
 
 @pytest.mark.parametrize("L,T,top_k", [(3000, 8, 2048), (40000, 8, 2048), (777, 3, 64)])
@@ -144,8 +138,8 @@ def test_w8a8_swa_layer_step(dsa, pos0, T, window):
         d = g["dev"]
         att = torch.zeros((T, 1024), dtype=torch.int16, device=DEV)
         ws = dsa.workspace(dsa.WS_SWA_ATTN, T, L, window)
-        dsa.swa_attn(d["qkv"][:, :1024].contiguous(), d["k"], d["v"], cap, T, pos0, window, SM, None, att,
-                     dsa.BF16, ws)
+        dsa.swa_attn(d["qkv"][:, :1024].contiguous(), d["k"], d["v"], None, None, dsa.BF16, cap, T, pos0, window,
+                     SM, None, att, dsa.BF16, ws)
         torch.cuda.synchronize()
         att_bits = bf16_bits(att)
         tf = O.layer_step("swa", x, gamma, w8[0], w8[2], c1, pos0, teacher={"qkv": g["qkv"], "attn": att_bits}, **kw)

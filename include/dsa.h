@@ -160,6 +160,21 @@ dsa_status_t dsa_sparse_attn(const void* q, const void* k_cache, const void* v_c
                              size_t ws_bytes, void* stream);
 
 /*
+ * dsa_sparse_attn without a workspace, for callers that cannot allocate device memory
+ * (code under HIP graph capture, tight serving loops, harnesses that forbid hipMalloc).
+ * Same arguments, result and kernels as dsa_sparse_attn, minus ws / ws_bytes: the split
+ * partials live in a library-owned device array of 1,081,344 bytes (the largest call,
+ * T = 8, k = 2048), one per GPU, held until the process ends; a call needing more returns
+ * DSA_ERR_WORKSPACE.  The call allocates nothing.  Every call on one GPU shares that
+ * GPU's array, so calls that may overlap on one GPU (different streams, or concurrent
+ * host threads) race and must not be issued; stream-ordered calls are safe.
+ */
+dsa_status_t dsa_sparse_attn_static(const void* q, const void* k_cache, const void* v_cache,
+                                    const float* k_scale, const float* v_scale, int kv_dtype,
+                                    const int32_t* idx, int k, int T, int64_t L, float sm_scale,
+                                    const float* sink, void* out, int out_dtype, void* stream);
+
+/*
  * Sliding-window attention (§Hybrid SWA-DSA Architecture: a 128-token window; §Model
  * Architecture: per-token cost independent of context length).
  *

@@ -28,7 +28,7 @@ LAYER_DSA, LAYER_SWA = 0, 1
 STATUS = {0: "DSA_OK", 1: "DSA_ERR_NULL", 2: "DSA_ERR_SHAPE", 3: "DSA_ERR_DTYPE", 4: "DSA_ERR_ALIGN",
           5: "DSA_ERR_WORKSPACE", 6: "DSA_ERR_LAUNCH", 7: "DSA_ERR_HIP"}
 
-EXPORTS = ("dsa_indexer_scores", "dsa_topk", "dsa_index_topk", "dsa_sparse_attn", "swa_attn",
+EXPORTS = ("dsa_indexer_scores", "dsa_topk", "dsa_index_topk", "dsa_sparse_attn", "dsa_sparse_attn_static", "swa_attn",
            "dsa_layer_step", "dsa_workspace_bytes", "dsa_workspace_init", "dsa_workspace_status",
            "dsa_max_context", "dsa_status_string", "dsa_last_error")
 
@@ -65,6 +65,7 @@ _sig = {
     "dsa_topk": [_P, _I, _L, _L, _L, _I, _P, _P, _P, _S, _P],
     "dsa_index_topk": [_P, _P, _P, _P, _I, _I, _L, _L, _I, _P, _P, _P, _S, _P],
     "dsa_sparse_attn": [_P, _P, _P, _P, _P, _I, _P, _I, _I, _L, _F, _P, _P, _I, _P, _S, _P],
+    "dsa_sparse_attn_static": [_P, _P, _P, _P, _P, _I, _P, _I, _I, _L, _F, _P, _P, _I, _P],
     "swa_attn": [_P, _P, _P, _P, _P, _I, _L, _I, _L, _I, _F, _P, _P, _I, _P, _S, _P],
     "dsa_layer_step": [C.POINTER(LayerConfig), C.POINTER(LayerWeights), C.POINTER(LayerCache),
                        _P, _P, _I, _L, _P, _P, _P, _S, _P],
@@ -143,6 +144,14 @@ def dsa_sparse_attn(q, k_cache, v_cache, k_scale, v_scale, kv_dtype, idx, k, T, 
                               kv_dtype, _ptr(idx), k, T, L, sm_scale, _ptr(sink), _ptr(out), out_dtype,
                               _ptr(ws), _nbytes(ws) if ws_bytes is None else ws_bytes, _stream(stream))
     return _check("dsa_sparse_attn", st, raise_on_error)
+
+
+def dsa_sparse_attn_static(q, k_cache, v_cache, k_scale, v_scale, kv_dtype, idx, k, T, L, sm_scale, sink,
+                           out, out_dtype, stream=None, raise_on_error=True):
+    st = _lib.dsa_sparse_attn_static(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(k_scale), _ptr(v_scale),
+                                     kv_dtype, _ptr(idx), k, T, L, sm_scale, _ptr(sink), _ptr(out), out_dtype,
+                                     _stream(stream))
+    return _check("dsa_sparse_attn_static", st, raise_on_error)
 
 
 def swa_attn(q, k_ring, v_ring, k_scale, v_scale, kv_dtype, ring_cap, T, pos0, window, sm_scale, sink,

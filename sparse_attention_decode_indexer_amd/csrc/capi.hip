@@ -5,6 +5,8 @@
 #include <stdio.h>
 #include <string.h>
 
+#include <mutex>
+
 #include "../../include/dsa.h"
 #include "dsa_common.h"
 #include "dsa_kernels.h"
@@ -68,6 +70,38 @@ LayerWs layer_ws(int kind, int T, int64_t L, int k, int window, int ncu) {
   if (kind == DSA_LAYER_DSA) o = align_up(o + dsa::select_data_bytes(T, L, k, ncu));
   w.total = o;
   return w;
+}
+
+// ---- scratch of the allocation-free attention entry point: the split partials of the
+// largest call (T = 8, k = 2048), one copy per GPU held until the process ends.  In host
+// code `scratch` names a host-side stand-in; its device address comes from
+// hipGetSymbolAddress, once per device, and only that address is handed to kernels.
+constexpr size_t kStaticScratchBytes = (size_t)dsa::kMaxT * 32 * dsa::kHq * 132 * sizeof(float);   // 1,081,344
+static __device__ __align__(256) uint8_t scratch[kStaticScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// Device address of this device's scratch (resolved on the first call on the device).
+dsa_status_t scratch_address(void** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e, "dsa_sparse_attn_static: hipGetDevice");
+  if (dev < 0 || dev >= kMaxDevices) {
+    snprintf(g_err, sizeof(g_err), "dsa_sparse_attn_static: device %d beyond the %d supported", dev, kMaxDevices);
+    return DSA_ERR_HIP;
+  }
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* ptr = nullptr;
+    e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !ptr) return hip_fail(e != hipSuccess ? e : hipErrorInvalidSymbol,
+                                                 "dsa_sparse_attn_static: hipGetSymbolAddress(scratch)");
+    g_scratch_ptr[dev] = ptr;
+  }
+  *out = g_scratch_ptr[dev];
+  return DSA_OK;
 }
 
 }  // namespace
@@ -221,6 +255,34 @@ dsa_status_t dsa_sparse_attn(const void* q, const void* k_cache, const void* v_c
                                        static_cast<uint8_t*>(ws) + dsa::ctl::kBytes, device_cus(),
                                        (hipStream_t)stream);
   return e == hipSuccess ? DSA_OK : hip_fail(e, "dsa_sparse_attn");
+}
+
+dsa_status_t dsa_sparse_attn_static(const void* q, const void* k_cache, const void* v_cache,
+                                    const float* k_scale, const float* v_scale, int kv_dtype,
+                                    const int32_t* idx, int k, int T, int64_t L, float sm_scale,
+                                    const float* sink, void* out, int out_dtype, void* stream) {
+  if (!q || !k_cache || !v_cache || !idx || !out) return DSA_ERR_NULL;
+  if (kv_dtype != DSA_BF16 && kv_dtype != DSA_FP8_E4M3) return DSA_ERR_DTYPE;
+  const bool fp8 = kv_dtype == DSA_FP8_E4M3;
+  if (fp8 != (k_scale != nullptr) || fp8 != (v_scale != nullptr)) return DSA_ERR_DTYPE;
+  if (out_dtype != DSA_BF16 && out_dtype != DSA_FP32) return DSA_ERR_DTYPE;
+  if (T < 1 || T > dsa::kMaxT || k < 1 || k > dsa::kMaxTopK || L < 1 || L > kMaxL) return DSA_ERR_SHAPE;
+  const size_t need = dsa::attn_workspace_bytes(T, dsa::attn_splits(0, k));
+  if (need > kStaticScratchBytes) {
+    snprintf(g_err, sizeof(g_err), "dsa_sparse_attn_static: %zu scratch bytes needed, %zu available", need,
+             kStaticScratchBytes);
+    return DSA_ERR_WORKSPACE;
+  }
+  if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) || !aligned16(out) || (sink && !aligned16(sink)))
+    return DSA_ERR_ALIGN;
+  void* ptr = nullptr;
+  if (dsa_status_t st = scratch_address(&ptr)) return st;
+  // every split writes its whole partial before the merge reads it, so nothing in the
+  // scratch has to start at zero
+  hipError_t e = dsa::launch_attention(0, fp8, q, k_cache, v_cache, k_scale, v_scale, idx, k, T, L, 0, 0, 0,
+                                       sm_scale, sink, out, out_dtype == DSA_FP32, ptr, device_cus(),
+                                       (hipStream_t)stream);
+  return e == hipSuccess ? DSA_OK : hip_fail(e, "dsa_sparse_attn_static");
 }
 
 dsa_status_t swa_attn(const void* q, const void* k_ring, const void* v_ring, const float* k_scale,

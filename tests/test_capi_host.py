@@ -151,3 +151,17 @@ def test_read_ceiling_helper_is_outside_the_library_and_validates():
     assert f(MIS, 1024, FAKE, None) == -1
     assert f(FAKE, 1000, FAKE, None) == -1
     assert f(FAKE, 0, FAKE, None) == -1
+
+
+def test_static_attention_validation_without_launch():
+    """The allocation-free attention call checks its arguments before it looks up its scratch
+    or launches anything."""
+    import sparse_attention_decode_indexer_amd as dsa
+    E = {v: k for k, v in dsa.STATUS.items()}
+    a = lambda *x: dsa.dsa_sparse_attn_static(*x, stream=0, raise_on_error=False)
+    assert a(None, FAKE, FAKE, None, None, dsa.BF16, FAKE, 16, 1, 100, 0.1, None, FAKE, dsa.FP32) == E["DSA_ERR_NULL"]
+    assert a(FAKE, FAKE, FAKE, None, None, dsa.FP8_E4M3, FAKE, 16, 1, 100, 0.1, None, FAKE,
+             dsa.FP32) == E["DSA_ERR_DTYPE"]
+    assert a(FAKE, FAKE, FAKE, None, None, dsa.BF16, FAKE, 2049, 1, 100, 0.1, None, FAKE, dsa.FP32) == E["DSA_ERR_SHAPE"]
+    assert a(FAKE, FAKE, FAKE, None, None, dsa.BF16, FAKE, 16, 9, 100, 0.1, None, FAKE, dsa.FP32) == E["DSA_ERR_SHAPE"]
+    assert a(MIS, FAKE, FAKE, None, None, dsa.BF16, FAKE, 16, 1, 100, 0.1, None, FAKE, dsa.FP32) == E["DSA_ERR_ALIGN"]

@@ -3,6 +3,7 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 #include <stdio.h>
+#include <stdlib.h>
 #include <string.h>
 
 #include <mutex>
@@ -342,9 +343,15 @@ dsa_status_t dsa_layer_step(const dsa_layer_config_t* cfg, const dsa_layer_weigh
       (qkv_out && !aligned16(qkv_out)) || (idx_out && !aligned16(idx_out)) ||
       (cache->k_idx && !aligned16(cache->k_idx)) || (cfg->sink && !aligned16(cfg->sink)))
     return DSA_ERR_ALIGN;
+  // The DSA layer runs as the projection plus one launch for everything after it; the
+  // environment variable DSA_LAYER_UNFUSED=1 selects the equivalent five-launch chain
+  // (selection, attention, split merge, output projection), for comparison.
+  const char* unf = getenv("DSA_LAYER_UNFUSED");
+  const bool fused = !(unf && unf[0] == '1');
   if (dsa_kind) {
     // nothing is launched (and no cache row written) unless the selection can run
-    hipError_t e0 = dsa::select_check_resident(0, 1, T, L, pos0, cfg->top_k, ncu);
+    hipError_t e0 = fused ? dsa::layer_tail_check_resident(T, L, pos0, cfg->top_k, w8a8, ncu)
+                          : dsa::select_check_resident(0, 1, T, L, pos0, cfg->top_k, ncu);
     if (e0 != hipSuccess) return hip_fail(e0, "dsa_layer_step: index/top-k workgroups cannot all be resident");
   }
   hipStream_t st = (hipStream_t)stream;
@@ -358,6 +365,13 @@ dsa_status_t dsa_layer_step(const dsa_layer_config_t* cfg, const dsa_layer_weigh
                                       cache->v, dsa_kind ? 0 : cache->capacity, cache->k_idx,
                                       cache->k_idx_scale, w8 + lw.proj, st);
   if (e != hipSuccess) return hip_fail(e, "dsa_layer_step: projection");
+  if (dsa_kind && fused) {
+    int32_t* idx = idx_out ? idx_out : reinterpret_cast<int32_t*>(w8 + lw.idx);
+    e = dsa::launch_dsa_layer_tail(q_idx, w_idx, cache->k_idx, cache->k_idx_scale, T, L, pos0, cfg->top_k, idx, w8,
+                                   w8 + lw.sel, q_att, cache->k, cache->v, cfg->sm_scale, cfg->sink, attn_out,
+                                   w8 + lw.attn, w->w_o, wo_scale, x_in, x_out, ncu, st);
+    return e == hipSuccess ? DSA_OK : hip_fail(e, "dsa_layer_step: selection + attention + output projection");
+  }
   if (dsa_kind) {
     int32_t* idx = idx_out ? idx_out : reinterpret_cast<int32_t*>(w8 + lw.idx);
     e = dsa::launch_select(0, q_idx, w_idx, cache->k_idx, cache->k_idx_scale, 1, nullptr, 0, T, L, pos0,

@@ -222,6 +222,10 @@ dsa_status_t swa_attn(const void* q, const void* k_ring, const void* v_ring, con
  * idx_out [T][top_k] int32 (DSA only, optional): the selected positions.
  * qkv_out [T][N] bf16 (optional): the projection after RoPE.
  * ws: DSA_WS_LAYER_DSA or DSA_WS_LAYER_SWA sized for (T, pos0 + T, top_k).
+ * A DSA layer runs as five stream-ordered launches (projection, index/top-k, attention,
+ * split merge, output projection); with the environment variable
+ * DSA_LAYER_PERSISTENT_TAIL=1 everything after the index/top-k runs as one persistent
+ * launch instead, with the same result bit for bit.
  * --------------------------------------------------------------------------------- */
 typedef enum { DSA_LAYER_DSA = 0, DSA_LAYER_SWA = 1 } dsa_layer_kind_t;
 

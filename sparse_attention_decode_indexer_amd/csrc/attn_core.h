@@ -36,7 +36,48 @@ struct AttnParams {
   uint64_t* trace;        // profiling builds: [blocks][16] phase timestamps
   float* part;            // [T][nsplit][8][kPartStride]
   int nsplit;
+  // persistent launches (COH): results handed between the launch's workgroups as 64-bit
+  // words (launch tag << 32 | 32-bit value), polled by the reader until the tag matches
+  uint64_t* tpart;        // [T][nsplit][8][kTagPart] split partials: m, l, acc[128]
+  uint64_t* tout;         // [T][512] the attention output, two bf16 per word
+  uint32_t* ctl;          // the workspace's control words (error word on a wait that gives up)
 };
+
+constexpr int kTagPart = 2 + kD;   // tagged words per (token, split, head): m, l, acc[128]
+
+// Word of dim d within a tagged partial: dims are stored (d % 4)-major, so the four
+// stores of a thread holding dims 4 j .. 4 j + 3 each cover 32 consecutive words.
+DSA_DEV int tag_dim_word(int d) { return 2 + (d & 3) * (kD / 4) + (d >> 2); }
+
+// N tagged words addr(0 .. N-1) loaded together, then the ones not yet carrying `tag`
+// reloaded until all do (bounded); the low halves into val.
+template <int N, typename F>
+DSA_DEV void poll_words(F addr, uint32_t tag, uint32_t (&val)[N], uint32_t* ctl_words) {
+  uint64_t v[N];
+#pragma unroll
+  for (int i = 0; i < N; ++i) v[i] = ald64(addr(i));
+  bool ok = true;
+#pragma unroll
+  for (int i = 0; i < N; ++i) ok = ok & ((uint32_t)(v[i] >> 32) == tag);
+  if (!ok) {
+    const uint64_t t0 = __builtin_amdgcn_s_memrealtime();
+    while (!ok) {
+      __builtin_amdgcn_s_sleep(1);
+      if (__builtin_amdgcn_s_memrealtime() - t0 > kSpinLimit) {
+        ast(ctl_words + ctl::kError, 1u);
+        break;
+      }
+#pragma unroll
+      for (int i = 0; i < N; ++i)
+        if ((uint32_t)(v[i] >> 32) != tag) v[i] = ald64(addr(i));
+      ok = true;
+#pragma unroll
+      for (int i = 0; i < N; ++i) ok = ok & ((uint32_t)(v[i] >> 32) == tag);
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < N; ++i) val[i] = (uint32_t)v[i];
+}
 
 template <int KVDT, int ROWS>
 struct AttnShared {
@@ -50,38 +91,38 @@ struct AttnShared {
   float s[kHq][ROWS];
 };
 
-// out[t][h][d4 .. d4+3] = o / den (0 for an empty list), fp32 or bf16; COH: agent-scope
-// atomic stores (64-bit words)
+// out[t][h][d4 .. d4+3] = o / den (0 for an empty list), fp32 or bf16; COH (bf16 only):
+// two tagged words of the fused launch's attention output
 template <bool COH>
-DSA_DEV void store_out(const AttnParams& p, int t, int h, int d4, float (&o)[4], float den) {
+DSA_DEV void store_out(const AttnParams& p, int t, int h, int d4, float (&o)[4], float den, uint32_t tag) {
 #pragma unroll
   for (int i = 0; i < 4; ++i) o[i] = den > 0.0f ? o[i] / den : 0.0f;
   const size_t ob = ((size_t)t * kHq + h) * kD + d4;
-  if (p.out_f32) {
+  if (COH) {
+    const uint32_t w0 = (uint32_t)f32_to_bf16(o[0]) | ((uint32_t)f32_to_bf16(o[1]) << 16);
+    const uint32_t w1 = (uint32_t)f32_to_bf16(o[2]) | ((uint32_t)f32_to_bf16(o[3]) << 16);
+    const uint64_t tg = (uint64_t)tag << 32;
+    ast64(p.tout + ob / 2, tg | w0);
+    ast64(p.tout + ob / 2 + 1, tg | w1);
+  } else if (p.out_f32) {
     float* of = static_cast<float*>(p.out) + ob;
-    if (COH) {
-      ast64(reinterpret_cast<uint64_t*>(of), ((uint64_t)__float_as_uint(o[1]) << 32) | __float_as_uint(o[0]));
-      ast64(reinterpret_cast<uint64_t*>(of) + 1, ((uint64_t)__float_as_uint(o[3]) << 32) | __float_as_uint(o[2]));
-    } else {
-      *reinterpret_cast<float4*>(of) = make_float4(o[0], o[1], o[2], o[3]);
-    }
+    *reinterpret_cast<float4*>(of) = make_float4(o[0], o[1], o[2], o[3]);
   } else {
     uint16_t* ob16 = static_cast<uint16_t*>(p.out) + ob;
     const uint32_t w0 = (uint32_t)f32_to_bf16(o[0]) | ((uint32_t)f32_to_bf16(o[1]) << 16);
     const uint32_t w1 = (uint32_t)f32_to_bf16(o[2]) | ((uint32_t)f32_to_bf16(o[3]) << 16);
-    if (COH) ast64(reinterpret_cast<uint64_t*>(ob16), ((uint64_t)w1 << 32) | w0);
-    else *reinterpret_cast<uint2*>(ob16) = make_uint2(w0, w1);
+    *reinterpret_cast<uint2*>(ob16) = make_uint2(w0, w1);
   }
 }
 
 // One (token, split) of the attention by a workgroup of NT threads: the first 256 are
 // (head = tid / 32, 4 dims); with NT = 512 or 1024 the P.V product is split over 2 or 4
-// row groups whose partial sums are added in group order.  COH: the index list is read
-// and the result (partial or final output) written with agent-scope atomic accesses, for
-// use inside a launch whose other workgroups produce the list and consume the result;
-// the arithmetic is the same either way.
+// row groups whose partial sums are added in group order.  COH: the result (partial or
+// final output) is written as tagged words, for a launch whose other workgroups consume
+// it; the arithmetic is the same either way.
 template <int KVDT, int MODE, int ROWS, int NT, bool COH>
-DSA_DEV void attn_split(const AttnParams& p, int t, int split, AttnShared<KVDT, ROWS>& sh, uint64_t* trace) {
+DSA_DEV void attn_split(const AttnParams& p, int t, int split, AttnShared<KVDT, ROWS>& sh, uint64_t* trace,
+                        uint32_t tag = 0u) {
   static_assert(ROWS % 64 == 0 && ROWS <= NT && NT % kAttnThreads == 0, "64-row blocks, one list entry per thread");
   constexpr int NW = NT / 64;                 // waves
   constexpr int G = NT / kAttnThreads;        // P.V row groups
@@ -98,8 +139,7 @@ DSA_DEV void attn_split(const AttnParams& p, int t, int split, AttnShared<KVDT, 
     int64_t r = -1;
     if (MODE == 0) {
       if (e < p.k) {
-        const int32_t v = COH ? (int32_t)ald(reinterpret_cast<const uint32_t*>(p.idx) + (size_t)t * p.k + e)
-                              : p.idx[(size_t)t * p.k + e];
+        const int32_t v = p.idx[(size_t)t * p.k + e];
         if (v >= 0 && (int64_t)v < p.L) r = v;
       }
     } else {
@@ -300,53 +340,28 @@ DSA_DEV void attn_split(const AttnParams& p, int t, int split, AttnShared<KVDT, 
       }
       if (sink2 != -__builtin_inff()) den += exp2f(sink2 - M);
     }
-    if (lead) store_out<COH>(p, t, h, d4, o, den);
+    if (lead) store_out<COH>(p, t, h, d4, o, den, tag);
     DSA_MARK(trace, 6);
     return;
   }
   // ---- the split's partial (merged by the split merge)
   if (lead) {
-    float* part = p.part + (((size_t)t * p.nsplit + split) * kHq + h) * kPartStride;
     if (COH) {
-      uint64_t* pw = reinterpret_cast<uint64_t*>(part);
-      if (jj == 0) ast64(pw, ((uint64_t)__float_as_uint(l) << 32) | __float_as_uint(m));
-      ast64(pw + 2 + d4 / 2, ((uint64_t)__float_as_uint(acc[1]) << 32) | __float_as_uint(acc[0]));
-      ast64(pw + 3 + d4 / 2, ((uint64_t)__float_as_uint(acc[3]) << 32) | __float_as_uint(acc[2]));
+      uint64_t* pw = p.tpart + (((size_t)t * p.nsplit + split) * kHq + h) * kTagPart;
+      const uint64_t tg = (uint64_t)tag << 32;
+      if (jj == 0) {
+        ast64(pw, tg | __float_as_uint(m));
+        ast64(pw + 1, tg | __float_as_uint(l));
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i) ast64(pw + tag_dim_word(d4 + i), tg | __float_as_uint(acc[i]));
     } else {
+      float* part = p.part + (((size_t)t * p.nsplit + split) * kHq + h) * kPartStride;
       if (jj == 0) *reinterpret_cast<float2*>(part) = make_float2(m, l);
       *reinterpret_cast<float4*>(part + 4 + d4) = make_float4(acc[0], acc[1], acc[2], acc[3]);
     }
   }
   DSA_MARK(trace, 6);
-}
-
-// Output element (head hh, dim d) of token t from its ns split partials (pt = the
-// token's [ns][8][kPartStride] block): splits combined in split order, empty splits
-// (m = -inf) skipped, the sink logit (log2 units, -inf for none) in the denominator.
-// COH: partials read with agent-scope atomic loads.  Same arithmetic, in the same order,
-// as attn_merge_kernel.
-template <bool COH>
-DSA_DEV float merge_element(const float* pt, int ns, int hh, int d, float s2) {
-  float M = -__builtin_inff();
-  for (int j = 0; j < ns; ++j) {
-    const float* q = pt + ((size_t)j * kHq + hh) * kPartStride;
-    M = fmaxf(M, COH ? aldf(q) : q[0]);
-  }
-  M = fmaxf(M, s2);
-  float den = 0.0f, o = 0.0f;
-  if (M != -__builtin_inff()) {
-    for (int j = 0; j < ns; ++j) {
-      const float* q = pt + ((size_t)j * kHq + hh) * kPartStride;
-      const float mj = COH ? aldf(q) : q[0];
-      const float lj = COH ? aldf(q + 1) : q[1];
-      const float aj = COH ? aldf(q + 4 + d) : q[4 + d];
-      const float sc = mj != -__builtin_inff() ? exp2f(mj - M) : 0.0f;
-      den = fmaf(lj, sc, den);
-      o = fmaf(aj, sc, o);
-    }
-    if (s2 != -__builtin_inff()) den += exp2f(s2 - M);
-  }
-  return den > 0.0f ? o / den : 0.0f;
 }
 
 }  // namespace dsa

@@ -53,7 +53,7 @@ __global__ void zero_kernel(uint4* p, size_t n16) {
 // (dsa::ctl); in a layer workspace the projection's counter and the selection's launch
 // counter, error word and tau slots share it.
 struct LayerWs {
-  size_t proj, q_att, q_idx, w_idx, attn_out, idx, attn, sel, total;
+  size_t proj, q_att, q_idx, w_idx, attn_out, idx, attn, tags, sel, total;
 };
 
 LayerWs layer_ws(int kind, int T, int64_t L, int k, int window, int ncu) {
@@ -67,6 +67,7 @@ LayerWs layer_ws(int kind, int T, int64_t L, int k, int window, int ncu) {
   const int list = kind == DSA_LAYER_DSA ? k : window;
   w.idx = o; o = align_up(o + (kind == DSA_LAYER_DSA ? (size_t)dsa::kMaxT * k * 4 : 0));
   w.attn = o; o = align_up(o + dsa::attn_workspace_bytes(dsa::kMaxT, dsa::attn_splits(kind == DSA_LAYER_DSA ? 0 : 1, list)));
+  w.tags = o; o = align_up(o + (kind == DSA_LAYER_DSA ? dsa::layer_tail_tag_bytes(k) : 0));
   w.sel = o;
   if (kind == DSA_LAYER_DSA) o = align_up(o + dsa::select_data_bytes(T, L, k, ncu));
   w.total = o;
@@ -343,16 +344,19 @@ dsa_status_t dsa_layer_step(const dsa_layer_config_t* cfg, const dsa_layer_weigh
       (qkv_out && !aligned16(qkv_out)) || (idx_out && !aligned16(idx_out)) ||
       (cache->k_idx && !aligned16(cache->k_idx)) || (cfg->sink && !aligned16(cfg->sink)))
     return DSA_ERR_ALIGN;
-  // The DSA layer runs as the projection plus one launch for everything after it; the
-  // environment variable DSA_LAYER_UNFUSED=1 selects the equivalent five-launch chain
-  // (selection, attention, split merge, output projection), for comparison.
-  const char* unf = getenv("DSA_LAYER_UNFUSED");
-  const bool fused = !(unf && unf[0] == '1');
+  // The DSA layer runs as projection, selection, then separate attention, split-merge and
+  // output-projection launches (five in all).  The environment variable
+  // DSA_LAYER_PERSISTENT_TAIL=1 selects one persistent launch for everything after the
+  // selection instead (three in all); it gives the same result bit for bit and measured
+  // about 1.8 us slower per DSA layer on MI355X, where a hand-off between workgroups
+  // through memory costs about as much as a launch boundary.
+  const char* pt = getenv("DSA_LAYER_PERSISTENT_TAIL");
+  const bool fused = pt && pt[0] == '1';
   if (dsa_kind) {
     // nothing is launched (and no cache row written) unless the selection can run
-    hipError_t e0 = fused ? dsa::layer_tail_check_resident(T, L, pos0, cfg->top_k, w8a8, ncu)
-                          : dsa::select_check_resident(0, 1, T, L, pos0, cfg->top_k, ncu);
-    if (e0 != hipSuccess) return hip_fail(e0, "dsa_layer_step: index/top-k workgroups cannot all be resident");
+    hipError_t e0 = dsa::select_check_resident(0, 1, T, L, pos0, cfg->top_k, ncu);
+    if (e0 == hipSuccess && fused) e0 = dsa::attn_oproj_check_resident(w8a8, ncu);
+    if (e0 != hipSuccess) return hip_fail(e0, "dsa_layer_step: workgroups cannot all be resident");
   }
   hipStream_t st = (hipStream_t)stream;
   uint8_t* w8 = static_cast<uint8_t*>(ws);
@@ -367,10 +371,12 @@ dsa_status_t dsa_layer_step(const dsa_layer_config_t* cfg, const dsa_layer_weigh
   if (e != hipSuccess) return hip_fail(e, "dsa_layer_step: projection");
   if (dsa_kind && fused) {
     int32_t* idx = idx_out ? idx_out : reinterpret_cast<int32_t*>(w8 + lw.idx);
-    e = dsa::launch_dsa_layer_tail(q_idx, w_idx, cache->k_idx, cache->k_idx_scale, T, L, pos0, cfg->top_k, idx, w8,
-                                   w8 + lw.sel, q_att, cache->k, cache->v, cfg->sm_scale, cfg->sink, attn_out,
-                                   w8 + lw.attn, w->w_o, wo_scale, x_in, x_out, ncu, st);
-    return e == hipSuccess ? DSA_OK : hip_fail(e, "dsa_layer_step: selection + attention + output projection");
+    e = dsa::launch_select(0, q_idx, w_idx, cache->k_idx, cache->k_idx_scale, 1, nullptr, 0, T, L, pos0,
+                           cfg->top_k, idx, nullptr, w8, w8 + lw.sel, ncu, st);
+    if (e != hipSuccess) return hip_fail(e, "dsa_layer_step: index/top-k");
+    e = dsa::launch_attn_oproj(idx, T, L, cfg->top_k, w8, q_att, cache->k, cache->v, cfg->sm_scale, cfg->sink,
+                               w8 + lw.tags, w->w_o, wo_scale, x_in, x_out, ncu, st);
+    return e == hipSuccess ? DSA_OK : hip_fail(e, "dsa_layer_step: attention + output projection");
   }
   if (dsa_kind) {
     int32_t* idx = idx_out ? idx_out : reinterpret_cast<int32_t*>(w8 + lw.idx);

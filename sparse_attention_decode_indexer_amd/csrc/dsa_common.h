@@ -300,10 +300,7 @@ namespace ctl {
 constexpr int kEpoch = 768;      // launch counter (tags of the tagged slots)
 constexpr int kError = 769;      // sticky error word (1 = a wait inside a launch gave up)
 constexpr int kDone = 1024;      // [8] per-token completion counters, stride 64
-constexpr int kAttnCnt = 1536;   // [8] per-token attention split counters, stride 64
 constexpr int kTauG = 2048;      // [8] tagged slots (64-bit, stride 16 words): per-token tau
-constexpr int kIdxG = 2304;      // [8] tagged slots (64-bit, stride 8 words): indices published
-constexpr int kOutG = 2432;      // [8] tagged slots (64-bit, stride 8 words): attention output published
 constexpr int kWords = 3072;
 constexpr size_t kBytes = 16384;
 }  // namespace ctl

@@ -25,16 +25,16 @@ hipError_t launch_select(int src, const void* q_idx, const float* w_idx, const v
                          int64_t L, int64_t pos0, int k, int32_t* idx, int32_t* count, void* ctl,
                          void* data, int num_cu, hipStream_t st);
 
-// The DSA layer after its projection as one launch (selection, attention, split merge,
-// output projection + residual): ctl = the workspace's control block, seldata =
-// select_data_bytes, o_buf [T][1024] bf16 and part (attn_workspace_bytes) scratch.
-// w_o_scale != nullptr selects W8A8 (e4m3 W_o).
-hipError_t launch_dsa_layer_tail(const void* q_idx, const float* w_idx, const void* k_idx, const float* k_scale,
-                                 int T, int64_t L, int64_t pos0, int k, int32_t* idx, void* ctl, void* seldata,
-                                 const void* q_att, const void* kcache, const void* vcache, float sm_scale,
-                                 const float* sink, void* o_buf, void* part, const void* w_o,
-                                 const float* w_o_scale, const void* x, void* xout, int num_cu, hipStream_t st);
-hipError_t layer_tail_check_resident(int T, int64_t L, int64_t pos0, int k, bool w8a8, int num_cu);
+// The DSA layer after its selection as one persistent launch of num_cu workgroups
+// (attention over idx, split merge, output projection + residual): ctl = the workspace's
+// control block (the selection's launch counter gives the tag), tags =
+// layer_tail_tag_bytes(k) of tagged hand-off words.  w_o_scale != nullptr selects W8A8.
+size_t layer_tail_tag_bytes(int k);
+hipError_t launch_attn_oproj(const int32_t* idx, int T, int64_t L, int k, void* ctl, const void* q_att,
+                             const void* kcache, const void* vcache, float sm_scale, const float* sink, void* tags,
+                             const void* w_o, const float* w_o_scale, const void* x, void* xout, int num_cu,
+                             hipStream_t st);
+hipError_t attn_oproj_check_resident(bool w8a8, int num_cu);
 
 size_t attn_workspace_bytes(int T, int nsplit);
 int attn_splits(int mode, int list_len);   // mode 0: index list, 1: sliding window

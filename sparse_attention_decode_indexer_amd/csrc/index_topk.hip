@@ -57,7 +57,7 @@ template <int SRC, int KDT, int RTW>
 __global__ void __launch_bounds__(kSelThreads, 1) select_kernel(SelParams p) {
   __shared__ SelShared sh;
   uint32_t epoch;
-  select_body<SRC, KDT, RTW, false>(p, sh, epoch);
+  select_body<SRC, KDT, RTW>(p, sh, epoch);
 }
 
 // ----------------------------------------------------------------------------- host launchers

@@ -1,37 +1,39 @@
-// The DSA layer after its projection, as one launch, for gfx950: indexer scan, exact
-// top-k, sparse attention over the selected rows, the fixed-order split merge and the
-// output projection with the residual.
+// The DSA layer after its selection, as one persistent launch, for gfx950: sparse
+// attention over the selected rows, the fixed-order split merge and the output projection
+// with the residual.
 //
 // Method: NaiveAI research page on Naive-N0.5-Flash (naive.ai/en/research).
-//   §A DSA layer: from 29 kernels to one: the layer's stages run inside one persistent
+//   §A DSA layer: from 29 kernels to one: the layer's stages run inside a persistent
 //     kernel instead of a chain of launches.
 //   §Optimizing inside the kernel: the selected K/V rows are staged on chip split by
 //     split; the output-projection weights are fetched before they are needed.
-//   §Model Architecture / §Hybrid SWA-DSA Architecture: indexer over the full history,
-//     top 2,048, GQA attention over the selected rows only, sink bias.
+//   §Model Architecture / §Hybrid SWA-DSA Architecture: GQA attention over the selected
+//     rows only, sink bias.
 //
-// One workgroup per chunk of keys, all resident (as the selection alone).  After the
-// selection (select_core.h), each workgroup carries on instead of ending:
-//   1  the resolver of token t publishes its indices (agent-scope stores, then a tagged
-//      slot) and runs split 0 of token t itself;
-//   2  every workgroup requests the W_o rows of its output-projection block (and the
-//      residual elements) into registers, long before it needs them;
-//   3  the other (token, split) attention items go round the remaining workgroups: each
-//      waits for its token's slot, stages its 64 rows and writes its partial (the code of
-//      the standalone attention, attn_core.h); the last split of a token to finish (a
-//      per-token counter) merges the token's splits in split order and publishes the
-//      token's attention output;
-//   4  every workgroup waits for all tokens' outputs and computes 16 output columns of
+// One workgroup per compute unit, all resident.  Each workgroup
+//   1  requests the W_o rows of its output-projection block (and the residual elements)
+//      into registers at once, so they stream in under the attention;
+//   2  takes (token, split) attention items in turn: stages the split's 64 selected rows
+//      and writes its partial (the code of the standalone attention, attn_core.h);
+//   3  takes (token, head) merges in turn: combines the token's split partials in split
+//      order (the standalone merge's arithmetic);
+//   4  reads every token's attention output and computes 16 output columns of
 //      x + O . W_o^T, summing sixteen k-partials in the order of the standalone output
 //      projection.
 // Every arithmetic step is that of the separate kernels, in the same order, so the layer
-// output equals the five-launch composition bit for bit.  Cross-workgroup data moves only
-// through agent-scope atomic stores/loads and tagged slots; every wait is bounded and a
-// wait that gives up sets the workspace's error word.
+// output equals the chain of separate launches bit for bit.
+//
+// Results that cross workgroups (the split partials, the attention output) travel as
+// 64-bit words (launch tag << 32 | 32-bit value) written with agent-scope atomic stores;
+// the reader polls the words themselves until each carries this launch's tag, so the
+// writer never waits for its stores to land and no separate "ready" flag is needed: one
+// memory round trip per hand-off.  The tag is the workspace's launch counter + 1 as left
+// by the selection that precedes this launch (which advances it once per launch), so it
+// differs from the previous layer step's.  Every wait is bounded; a wait that gives up
+// sets the workspace's error word.
 #include "attn_core.h"
 #include "dsa_common.h"
 #include "dsa_kernels.h"
-#include "select_core.h"
 
 namespace dsa {
 
@@ -46,47 +48,25 @@ constexpr int kXsS = kOpK + 8;                  // bf16 per attention-output row
 constexpr int kXqS = kOpK + 16;                 // bytes per W8A8 code row in LDS
 
 struct TailParams {
-  AttnParams ap;            // attention over the selection (ap.out: the bf16 output [T][1024])
+  AttnParams ap;            // attention over the selection (results as tagged words: tpart, tout)
   const uint8_t* w_o;       // [4096][1024] bf16, or e4m3 codes (W8A8)
   const float* w_o_scale;   // [4096] fp32 row scales (W8A8) or nullptr
   const uint16_t* x;        // [T][4096] residual input
   uint16_t* xout;           // [T][4096]
-  uint32_t* acnt;           // per-token split counters (stride 64 words)
-  uint64_t* idxg;           // per-token "indices published" tagged slots (stride 4)
-  uint64_t* outg;           // per-token "attention output published" tagged slots (stride 4)
+  uint64_t* trace;          // profiling builds: [grid][16] phase timestamps
 };
 
-// LDS of the phases after the selection (inside the selection's score area)
+// LDS of the launch
 struct TailShared {
   AttnShared<0, kSplitRows> att;
   alignas(16) uint16_t xs[kMaxT][kXsS];         // attention output (bf16)
   alignas(16) uint8_t xq[kMaxT][kXqS];          // W8A8: its e4m3 codes
   float red[kOpVW][16][16];                     // k-partials of the output tile
+  float merge[32 * (2 + kD)];                   // merge: one head's partials of every split
   float amax[kMaxT][16];
   float ascale[kMaxT];
   float ainv[kMaxT];
-  float2 ml[32 * kHq];                          // merge: (m, l) of every (split, head)
-  uint32_t flag;
 };
-
-// Wave 0 waits until slots[4 t] carries `tag` for every t < n (bounded), then the block.
-DSA_DEV void wait_slots(const uint64_t* slots, int n, uint32_t tag, uint32_t* ctl_words) {
-  if ((threadIdx.x >> 6) == 0) {
-    const int lane = threadIdx.x & 63;
-    const uint64_t* s = slots + 4 * (lane < n ? lane : n - 1);
-    uint64_t v = ald64(s);
-    const uint64_t t0 = __builtin_amdgcn_s_memrealtime();
-    while (__ballot((uint32_t)(v >> 32) != tag) != 0ull) {
-      __builtin_amdgcn_s_sleep(1);
-      if (__builtin_amdgcn_s_memrealtime() - t0 > kSpinLimit) {
-        if (lane == 0) ast(ctl_words + ctl::kError, 1u);
-        break;
-      }
-      v = ald64(s);
-    }
-  }
-  __syncthreads();
-}
 
 // The W_o units of output-projection block b this lane multiplies (k-partials 2w, 2w+1 of
 // the sixteen; lane group g = lane >> 4 takes units g, g + 4 of each 64-wide partial).
@@ -110,137 +90,140 @@ DSA_DEV void load_wo(const TailParams& tp, int b, WoFrags<F8>& wf) {
   }
 }
 
-// Merged attention output of token t (all 1024 elements, two per thread) from its ns
-// split partials, written as bf16 with agent-scope stores; the arithmetic and order of
-// merge_element (and of the standalone merge kernel).  The splits' (m, l) pairs go
-// through LDS (one load per thread); each thread keeps its two elements' 2 x ns values.
-DSA_DEV void merge_token(const TailParams& tp, int t, float2* ml_lds) {
-  const int ns = tp.ap.nsplit;
+// Merged attention output of (token t, head h) from its ns split partials (tagged words),
+// written as 64 tagged words of two bf16; the arithmetic and order of the standalone
+// merge kernel.  The ns x kTagPart words (m, l, acc[128] of each split) are polled into
+// LDS (thread tid takes words tid, tid + 512, ...), then thread d < 128 combines dim d
+// over the splits in split order.
+constexpr int kMergeWords = 32 * kTagPart;                                   // 4160
+constexpr int kMergePer = (kMergeWords + kSelThreads - 1) / kSelThreads;     // 9 per thread
+
+DSA_DEV void merge_head(const AttnParams& ap, int t, int h, float* vals /* LDS [ns][kTagPart] */, uint32_t tag,
+                        uint64_t* trace) {
+  (void)trace;
+  const int ns = ap.nsplit;
   const int tid = threadIdx.x;
-  const float* pt = tp.ap.part + (size_t)t * ns * kHq * kPartStride;
-  if (tid < ns * kHq) {                              // (split, head) = (tid / 8, tid % 8)
-    const uint64_t ml = ald64(reinterpret_cast<const uint64_t*>(pt + (size_t)tid * kPartStride));
-    ml_lds[tid] = make_float2(__uint_as_float((uint32_t)ml), __uint_as_float((uint32_t)(ml >> 32)));
-  }
-  const int e0 = 2 * tid;                            // elements e0, e0 + 1 (same head)
-  const int hh = e0 >> 7, d = e0 & (kD - 1);
-  float a0[32], a1[32];
+  const int n = ns * kTagPart;
+  const uint64_t* pt = ap.tpart + (size_t)t * ns * kHq * kTagPart;
+  uint32_t v[kMergePer];
+  poll_words<kMergePer>([&](int u) {
+    int i = tid + u * kSelThreads;
+    i = i < n ? i : n - 1;
+    const int j = i / kTagPart;
+    return pt + ((size_t)j * kHq + h) * kTagPart + (i - j * kTagPart);
+  }, tag, v, ap.ctl);
+  DSA_MARK(trace, 6);
 #pragma unroll
-  for (int j = 0; j < 32; ++j) {
-    const int js = j < ns ? j : ns - 1;
-    const uint64_t av = ald64(reinterpret_cast<const uint64_t*>(pt + ((size_t)js * kHq + hh) * kPartStride + 4 + d));
-    a0[j] = __uint_as_float((uint32_t)av);
-    a1[j] = __uint_as_float((uint32_t)(av >> 32));
+  for (int u = 0; u < kMergePer; ++u) {
+    const int i = tid + u * kSelThreads;
+    if (i < n) vals[i] = __uint_as_float(v[u]);
   }
   __syncthreads();
-  const float s2 = tp.ap.sink ? tp.ap.sink[hh] * 1.4426950408889634f : -__builtin_inff();
-  float M = -__builtin_inff();
-  for (int j = 0; j < ns; ++j) M = fmaxf(M, ml_lds[j * kHq + hh].x);
-  M = fmaxf(M, s2);
-  float den = 0.0f, o0 = 0.0f, o1 = 0.0f;
-  if (M != -__builtin_inff()) {
+  if (tid < kD) {
+    const int d = tid;
+    const float s2 = ap.sink ? ap.sink[h] * 1.4426950408889634f : -__builtin_inff();
+    // every split's (m, l, value) read from LDS up front (unrolled), then combined in order
+    float mj[32], lj[32], aj[32];
 #pragma unroll
     for (int j = 0; j < 32; ++j) {
-      if (j < ns) {
-        const float2 ml = ml_lds[j * kHq + hh];
-        const float sc = ml.x != -__builtin_inff() ? exp2f(ml.x - M) : 0.0f;
-        den = fmaf(ml.y, sc, den);
-        o0 = fmaf(a0[j], sc, o0);
-        o1 = fmaf(a1[j], sc, o1);
-      }
+      const int jc = j < ns ? j : ns - 1;
+      mj[j] = vals[jc * kTagPart];
+      lj[j] = vals[jc * kTagPart + 1];
+      aj[j] = vals[jc * kTagPart + tag_dim_word(d)];
     }
-    if (s2 != -__builtin_inff()) den += exp2f(s2 - M);
+    float M = -__builtin_inff();
+#pragma unroll
+    for (int j = 0; j < 32; ++j) M = j < ns ? fmaxf(M, mj[j]) : M;
+    M = fmaxf(M, s2);
+    float den = 0.0f, o = 0.0f;
+    if (M != -__builtin_inff()) {
+#pragma unroll
+      for (int j = 0; j < 32; ++j) {
+        if (j < ns) {
+          const float sc = mj[j] != -__builtin_inff() ? exp2f(mj[j] - M) : 0.0f;
+          den = fmaf(lj[j], sc, den);
+          o = fmaf(aj[j], sc, o);
+        }
+      }
+      if (s2 != -__builtin_inff()) den += exp2f(s2 - M);
+    }
+    const float r = den > 0.0f ? o / den : 0.0f;
+    // dims d, d + 1 sit in neighbouring lanes: the even lane stores the pair
+    const uint32_t b = (uint32_t)f32_to_bf16(r);
+    const uint32_t nb = (uint32_t)__shfl_down((int)b, 1, 64);
+    if ((d & 1) == 0)
+      ast64(ap.tout + (size_t)t * (kOpK / 2) + (h * kD + d) / 2, ((uint64_t)tag << 32) | b | (nb << 16));
   }
-  const float r0 = den > 0.0f ? o0 / den : 0.0f;
-  const float r1 = den > 0.0f ? o1 / den : 0.0f;
-  uint16_t* out = static_cast<uint16_t*>(tp.ap.out) + (size_t)t * kOpK + e0;
-  ast(reinterpret_cast<uint32_t*>(out), (uint32_t)f32_to_bf16(r0) | ((uint32_t)f32_to_bf16(r1) << 16));
+  DSA_MARK(trace, 7);
+  __syncthreads();
 }
 
 }  // namespace
 
-template <int RTW, bool F8>
-__global__ void __launch_bounds__(kSelThreads, 1) dsa_layer_tail_kernel(SelParams p, TailParams tp) {
-  __shared__ SelShared sh;
-  uint32_t epoch;
-  if (!select_body<0, 1, RTW, true>(p, sh, epoch)) return;     // poisoned workspace: nothing more
-  const uint32_t tag = epoch + 1u;
+template <bool F8>
+__global__ void __launch_bounds__(kSelThreads, 1) dsa_attn_oproj_kernel(TailParams tp) {
+  __shared__ TailShared ts;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
   const int wg = blockIdx.x;
-  const int nwg = p.nwg;
-  const int T = p.T;
-  const int ns = tp.ap.nsplit;
-  TailShared& ts = *reinterpret_cast<TailShared*>(&sh.sc[0][0]);
-  static_assert(sizeof(TailShared) <= sizeof(sh.sc), "tail phases fit the score area");
-
-  // ---- 1) resolver: publish token wg's indices (every thread's stores complete first)
-  if (wg < T) {
-    vm_wait_all();
-    __syncthreads();
-    if (tid == 0) ast64(tp.idxg + 4 * wg, ((uint64_t)tag << 32) | 1u);
-  }
-  // ---- 2) this workgroup's first output-projection block: W_o rows, residual, row scale
+  const int nwg = gridDim.x;
+  const AttnParams& ap = tp.ap;
+  const int T = ap.T;
+  const int ns = ap.nsplit;
+  uint64_t* trace = tp.trace;
+  (void)trace;
+  DSA_MARK(trace, 0);
+  // the launch tag (first needed when an item stores its partial, so the load's latency
+  // hides under the item); x_out is not written for a workspace whose error word is set
+  const uint64_t ctlw = ald64(reinterpret_cast<const uint64_t*>(ap.ctl + ctl::kEpoch));
+  const uint32_t tag = (uint32_t)ctlw + 1u;
+  const bool poisoned = (ctlw >> 32) != 0u;
+  DSA_MARK(trace, 1);
+  // ---- 1) attention items (token, split), round the workgroups; after the first item's
+  //      rows are in, this workgroup's first output-projection block (W_o rows, residual,
+  //      row scale) is requested: it streams in under the rest, behind the gather
   WoFrags<F8> wf;
   uint16_t xres = 0;
   float wsv = 1.0f;
   int b = wg;
-  if (b < kOpBlocks) {
-    load_wo<F8>(tp, b, wf);
-    const int r = tid >> 4, t = tid & 15;
-    if (tid < 256 && t < T) xres = tp.x[(size_t)t * kHidden + b * kOpRows + r];
-    if (F8) wsv = tp.w_o_scale[b * kOpRows + ((tid >> 4) & 15)];
-  }
-  // ---- 3) attention items: (t, 0) by resolver t, the others round the other workgroups
-  const int nrest = T * (ns - 1);
-  const int span = nwg > T ? nwg - T : nwg;
-  const int first = nwg > T ? wg - T : wg;
-  for (int it = (wg < T ? -1 : 0); ; ) {
-    int t, s;
-    if (it < 0) {
-      t = wg;
-      s = 0;
-    } else {
-      const int j = first + it * span;
-      if (first < 0 || j >= nrest) break;
-      t = j / (ns - 1);
-      s = 1 + j % (ns - 1);
+  auto request_wo = [&]() {
+    if (b < kOpBlocks) {
+      load_wo<F8>(tp, b, wf);
+      const int r = tid >> 4, t = tid & 15;
+      if (tid < 256 && t < T) xres = tp.x[(size_t)t * kHidden + b * kOpRows + r];
+      if (F8) wsv = tp.w_o_scale[b * kOpRows + ((tid >> 4) & 15)];
     }
-    if (!(s == 0 && t == wg)) wait_slots(tp.idxg + 4 * t, 1, tag, p.ctl);
-    attn_split<0, 0, kSplitRows, kSelThreads, true>(tp.ap, t, s, ts.att, nullptr);
-    vm_wait_all();
-    __syncthreads();
-    if (ns > 1) {
-      if (tid == 0) ts.flag = aadd(tp.acnt + 64 * t, 1u) == (uint32_t)(ns - 1) ? 1u : 0u;
-      __syncthreads();
-      if (ts.flag) {                  // the last split of token t: merge in split order
-        merge_token(tp, t, ts.ml);
-        if (tid == 0) ast(tp.acnt + 64 * t, 0u);
-        vm_wait_all();
-        __syncthreads();
-        if (tid == 0) ast64(tp.outg + 4 * t, ((uint64_t)tag << 32) | 1u);
-      }
-    } else if (tid == 0) {
-      ast64(tp.outg + 4 * t, ((uint64_t)tag << 32) | 1u);
+  };
+  bool requested = false;
+  for (int i = wg; i < T * ns; i += nwg) {
+    attn_split<0, 0, kSplitRows, kSelThreads, true>(ap, i / ns, i % ns, ts.att, nullptr, tag);
+    if (!requested) {
+      request_wo();
+      requested = true;
     }
     __syncthreads();
-    ++it;
   }
-  // ---- 4) output projection: every token's attention output into LDS (bf16; W8A8: codes)
-  wait_slots(tp.outg, T, tag, p.ctl);
+  if (!requested) request_wo();
+  DSA_MARK(trace, 2);
+  // ---- 3) (token, head) merges, round the workgroups from the last one down (the first
+  //      workgroups are the likeliest to hold a second attention item)
+  if (ns > 1) {
+    for (int q = nwg - 1 - wg; q < T * kHq; q += nwg) merge_head(ap, q / kHq, q % kHq, ts.merge, tag, trace);
+  }
+  DSA_MARK(trace, 3);
+  // ---- 4) output projection: every token's attention output into LDS (bf16; W8A8: codes):
+  //      word tid of each token holds elements 2 tid, 2 tid + 1
   {
-    const uint64_t* src = static_cast<const uint64_t*>(tp.ap.out);
-    constexpr int NQ = kMaxT * kOpK / 4 / kSelThreads;     // 64-bit words per thread (4)
+    static_assert(kOpK / 2 == kSelThreads, "one output word per thread and token");
+    uint32_t o[kMaxT];
+    poll_words<kMaxT>([&](int t) { return ap.tout + (size_t)(t < T ? t : T - 1) * (kOpK / 2) + tid; }, tag, o,
+                      ap.ctl);
 #pragma unroll
-    for (int u = 0; u < NQ; ++u) {
-      const int c = tid + u * kSelThreads;                  // word c: token c / 256, elements 4 (c % 256) ..
-      const int t = c / (kOpK / 4), k4 = (c % (kOpK / 4)) * 4;
-      const uint64_t v = t < T ? ald64(src + (size_t)t * (kOpK / 4) + k4 / 4) : 0ull;
-      *reinterpret_cast<uint64_t*>(&ts.xs[t][k4]) = v;
-    }
+    for (int t = 0; t < kMaxT; ++t) *reinterpret_cast<uint32_t*>(&ts.xs[t][2 * tid]) = t < T ? o[t] : 0u;
   }
   __syncthreads();
+  DSA_MARK(trace, 4);
   if constexpr (F8) {
     // per-token quantisation: amax over the token's 1024 values, scale and reciprocal, codes
     // of eight elements at a time (the standalone projection's quantiser)
@@ -312,39 +295,32 @@ __global__ void __launch_bounds__(kSelThreads, 1) dsa_layer_tail_kernel(SelParam
 #pragma unroll
       for (int w = 1; w < kOpVW; ++w) v += ts.red[w][r][c];
       if (F8) v *= ts.ascale[c & 7] * wsv;
-      if (c < T) tp.xout[(size_t)c * kHidden + b * kOpRows + r] = f32_to_bf16(v + bf16_to_f32(xres));
+      if (c < T && !poisoned) tp.xout[(size_t)c * kHidden + b * kOpRows + r] = f32_to_bf16(v + bf16_to_f32(xres));
     }
     __syncthreads();
   }
+  DSA_MARK(trace, 5);
 }
 
-hipError_t launch_dsa_layer_tail(const void* q_idx, const float* w_idx, const void* k_idx, const float* k_scale,
-                                 int T, int64_t L, int64_t pos0, int k, int32_t* idx, void* ctlp, void* seldata,
-                                 const void* q_att, const void* kcache, const void* vcache, float sm_scale,
-                                 const float* sink, void* o_buf, void* part, const void* w_o,
-                                 const float* w_o_scale, const void* x, void* xout, int num_cu, hipStream_t st) {
-  const SelGeometry g = select_geometry(T, L, pos0, k, num_cu);
-  SelParams p{};
-  p.q_idx = static_cast<const uint16_t*>(q_idx);
-  p.w_idx = w_idx;
-  p.k_idx = static_cast<const uint8_t*>(k_idx);
-  p.k_scale = k_scale;
-  p.T = T;
-  p.k = k;
-  p.L = L;
-  p.pos0 = pos0;
-  p.chunk = g.chunk;
-  p.nwg = g.nwg;
-  p.m = g.m;
-  p.n_part = g.n_part;
-  p.idx = idx;
-  p.count = nullptr;
-  uint8_t* w8 = static_cast<uint8_t*>(seldata);
-  uint32_t* ctl = static_cast<uint32_t*>(ctlp);
-  p.ctl = ctl;
-  p.cnt = reinterpret_cast<uint64_t*>(w8);
-  p.tauv = reinterpret_cast<uint64_t*>(w8 + (size_t)kMaxT * kMaxWG * 8);
-  p.cand = reinterpret_cast<uint64_t*>(w8 + (size_t)kMaxT * kMaxWG * 16);
+size_t layer_tail_tag_bytes(int k) {
+  return (size_t)kMaxT * attn_splits(0, k) * kHq * kTagPart * 8 + (size_t)kMaxT * (kOpK / 2) * 8;
+}
+
+static void* attn_oproj_fn(bool w8a8) {
+  return w8a8 ? (void*)dsa_attn_oproj_kernel<true> : (void*)dsa_attn_oproj_kernel<false>;
+}
+
+hipError_t attn_oproj_check_resident(bool w8a8, int num_cu) {
+  int64_t cap = 0;
+  hipError_t e = resident_capacity(attn_oproj_fn(w8a8), kSelThreads, num_cu, &cap);
+  if (e != hipSuccess) return e;
+  return cap < num_cu ? hipErrorCooperativeLaunchTooLarge : hipSuccess;
+}
+
+hipError_t launch_attn_oproj(const int32_t* idx, int T, int64_t L, int k, void* ctlp, const void* q_att,
+                             const void* kcache, const void* vcache, float sm_scale, const float* sink, void* tags,
+                             const void* w_o, const float* w_o_scale, const void* x, void* xout, int num_cu,
+                             hipStream_t st) {
   TailParams tp{};
   AttnParams& ap = tp.ap;
   ap.q = static_cast<const uint16_t*>(q_att);
@@ -356,42 +332,26 @@ hipError_t launch_dsa_layer_tail(const void* q_idx, const float* w_idx, const vo
   ap.L = L;
   ap.sm_log2 = sm_scale * 1.4426950408889634f;
   ap.sink = sink;
-  ap.out = o_buf;
-  ap.out_f32 = 0;
-  ap.part = static_cast<float*>(part);
   ap.nsplit = attn_splits(0, k);
+  uint64_t* tw = static_cast<uint64_t*>(tags);
+  ap.tpart = tw;
+  ap.tout = tw + (size_t)kMaxT * ap.nsplit * kHq * kTagPart;
+  ap.ctl = static_cast<uint32_t*>(ctlp);
   tp.w_o = static_cast<const uint8_t*>(w_o);
   tp.w_o_scale = w_o_scale;
   tp.x = static_cast<const uint16_t*>(x);
   tp.xout = static_cast<uint16_t*>(xout);
-  tp.acnt = ctl + ctl::kAttnCnt;
-  tp.idxg = reinterpret_cast<uint64_t*>(ctl + ctl::kIdxG);
-  tp.outg = reinterpret_cast<uint64_t*>(ctl + ctl::kOutG);
-  const int rt = (T + 1) / 2;
+#ifdef DSA_TRACE
+  tp.trace = dsa_trace_buffer() ? dsa_trace_buffer() + 1024 * 16 : nullptr;   // rows 1024.. of the buffer
+#endif
   const bool f8 = w_o_scale != nullptr;
-  void* fn = f8 ? (rt == 1 ? (void*)dsa_layer_tail_kernel<1, true> : rt == 2 ? (void*)dsa_layer_tail_kernel<2, true>
-                   : rt == 3 ? (void*)dsa_layer_tail_kernel<3, true> : (void*)dsa_layer_tail_kernel<4, true>)
-                : (rt == 1 ? (void*)dsa_layer_tail_kernel<1, false> : rt == 2 ? (void*)dsa_layer_tail_kernel<2, false>
-                   : rt == 3 ? (void*)dsa_layer_tail_kernel<3, false> : (void*)dsa_layer_tail_kernel<4, false>);
+  void* fn = attn_oproj_fn(f8);
   int64_t cap = 0;
   hipError_t e = resident_capacity(fn, kSelThreads, num_cu, &cap);
   if (e != hipSuccess) return e;
-  if (cap < g.nwg) return hipErrorCooperativeLaunchTooLarge;
-  void* args[] = {&p, &tp};
-  return hipLaunchKernel(fn, dim3(g.nwg), dim3(kSelThreads), args, 0, st);
-}
-
-hipError_t layer_tail_check_resident(int T, int64_t L, int64_t pos0, int k, bool w8a8, int num_cu) {
-  const SelGeometry g = select_geometry(T, L, pos0, k, num_cu);
-  const int rt = (T + 1) / 2;
-  void* fn = w8a8 ? (rt == 1 ? (void*)dsa_layer_tail_kernel<1, true> : rt == 2 ? (void*)dsa_layer_tail_kernel<2, true>
-                     : rt == 3 ? (void*)dsa_layer_tail_kernel<3, true> : (void*)dsa_layer_tail_kernel<4, true>)
-                  : (rt == 1 ? (void*)dsa_layer_tail_kernel<1, false> : rt == 2 ? (void*)dsa_layer_tail_kernel<2, false>
-                     : rt == 3 ? (void*)dsa_layer_tail_kernel<3, false> : (void*)dsa_layer_tail_kernel<4, false>);
-  int64_t cap = 0;
-  hipError_t e = resident_capacity(fn, kSelThreads, num_cu, &cap);
-  if (e != hipSuccess) return e;
-  return cap < g.nwg ? hipErrorCooperativeLaunchTooLarge : hipSuccess;
+  if (cap < num_cu) return hipErrorCooperativeLaunchTooLarge;
+  void* args[] = {&tp};
+  return hipLaunchKernel(fn, dim3(num_cu), dim3(kSelThreads), args, 0, st);
 }
 
 }  // namespace dsa

@@ -383,14 +383,6 @@ DSA_DEV uint32_t mth_largest_lanes_below(uint32_t v, int m, uint32_t known, int 
 // halves the bit search each workgroup runs before publishing its bound.
 constexpr int kTauBits = 16;
 
-// Stores of the selection's outputs: plain, or (COH) agent-scope atomic stores for use
-// inside a launch whose other workgroups read the indices.
-template <bool COH>
-DSA_DEV void put_i32(int32_t* a, int32_t v) {
-  if (COH) ast(reinterpret_cast<uint32_t*>(a), (uint32_t)v);
-  else *a = v;
-}
-
 constexpr int kRegPer = 16;                                  // candidates per lane
 constexpr uint32_t kRegCands = kSelThreads * kRegPer;        // register-resident limit
 
@@ -398,7 +390,7 @@ constexpr uint32_t kRegCands = kSelThreads * kRegPer;        // register-residen
 // (position order): wave w holds elements [w*R, (w+1)*R) as NB 64-element blocks (lane
 // = element), so ballots give position-ordered ranks.  Radix passes histogram the
 // registers; the compaction counts per wave in one pass and writes in a second.
-template <int NB, bool COH>
+template <int NB>
 DSA_DEV void resolve_regs(const SelParams& p, int t, SelShared& sh, const uint64_t* lc,
                           uint32_t nc, uint32_t kk, uint32_t kmin, uint32_t kmax,
                           uint32_t* hist, uint32_t* misc) {
@@ -571,7 +563,7 @@ DSA_DEV void resolve_regs(const SelParams& p, int t, SelShared& sh, const uint64
       const bool sel = ((uint32_t)i < nmine) & ((uint32_t)e[i] >= kstar);
       const uint64_t ms = __ballot(sel);
       const uint32_t oo = o + (uint32_t)__builtin_popcountll(ms & lt);
-      if (sel & (oo < kk)) put_i32<COH>(out + oo, (int32_t)(e[i] >> 32));
+      if (sel & (oo < kk)) out[oo] = (int32_t)(e[i] >> 32);
       o += (uint32_t)__builtin_popcountll(ms);
     }
   } else {
@@ -584,15 +576,15 @@ DSA_DEV void resolve_regs(const SelParams& p, int t, SelShared& sh, const uint64
       const bool sel = v & ((key > kstar) | (eq & (er + (uint32_t)__builtin_popcountll(me & lt) < take_eq)));
       const uint64_t ms = __ballot(sel);
       const uint32_t oo = o + (uint32_t)__builtin_popcountll(ms & lt);
-      if (sel & (oo < kk)) put_i32<COH>(out + oo, (int32_t)(e[i] >> 32));
+      if (sel & (oo < kk)) out[oo] = (int32_t)(e[i] >> 32);
       er += (uint32_t)__builtin_popcountll(me);
       o += (uint32_t)__builtin_popcountll(ms);
     }
   }
   DSA_MARK(p.trace, 12);
-  for (int i = (int)kk + tid; i < p.k; i += kSelThreads) put_i32<COH>(out + i, -1);
+  for (int i = (int)kk + tid; i < p.k; i += kSelThreads) out[i] = -1;
   if (tid == 0 && p.trace) p.trace[blockIdx.x * 16 + 13] = nc;
-  if (tid == 0 && p.count) put_i32<COH>(p.count + t, (int32_t)kk);
+  if (tid == 0 && p.count) p.count[t] = (int32_t)kk;
   __syncthreads();
 }
 
@@ -600,7 +592,6 @@ DSA_DEV void resolve_regs(const SelParams& p, int t, SelShared& sh, const uint64
 // every workgroup has published its candidates (after the second grid barrier).
 // Candidates arrive in position order; the selection is: every key above the cut key
 // K*, then the first `take_eq` (in position order) of the keys equal to K*.
-template <bool COH>
 DSA_DEV void resolve_token(const SelParams& p, int t, SelShared& sh, uint32_t epoch) {
   uint32_t* pre = reinterpret_cast<uint32_t*>(&sh.sc[0][0]);         // [nwg + 1]
   uint32_t* hist = pre + 1040;                                        // [4096] + [64] bin list
@@ -645,8 +636,8 @@ DSA_DEV void resolve_token(const SelParams& p, int t, SelShared& sh, uint32_t ep
     // is empty, the error word is set, and the launch counter stays as it is -- a
     // workgroup that has not run yet reads it later and tags with this launch
     int32_t* out = p.idx + (size_t)t * p.k;
-    for (int i = tid; i < p.k; i += kSelThreads) put_i32<COH>(out + i, -1);
-    if (tid == 0 && p.count) put_i32<COH>(p.count + t, 0);
+    for (int i = tid; i < p.k; i += kSelThreads) out[i] = -1;
+    if (tid == 0 && p.count) p.count[t] = 0;
     return;
   }
   DSA_MARK(p.trace, 8);
@@ -743,9 +734,9 @@ DSA_DEV void resolve_token(const SelParams& p, int t, SelShared& sh, uint32_t ep
     if (nc <= kRegCands) {
       // blocks of 64 candidates per wave: the register passes are unrolled to that many
       const uint32_t nb = (((nc + kSelWaves - 1) / kSelWaves + 63) & ~63u) / 64u;
-      if (nb <= 8u) resolve_regs<8, COH>(p, t, sh, lc, nc, kk, kmin, kmax, hist, misc);
-      else if (nb <= 12u) resolve_regs<12, COH>(p, t, sh, lc, nc, kk, kmin, kmax, hist, misc);
-      else resolve_regs<kRegPer, COH>(p, t, sh, lc, nc, kk, kmin, kmax, hist, misc);
+      if (nb <= 8u) resolve_regs<8>(p, t, sh, lc, nc, kk, kmin, kmax, hist, misc);
+      else if (nb <= 12u) resolve_regs<12>(p, t, sh, lc, nc, kk, kmin, kmax, hist, misc);
+      else resolve_regs<kRegPer>(p, t, sh, lc, nc, kk, kmin, kmax, hist, misc);
       return;
     }
   }
@@ -893,23 +884,22 @@ DSA_DEV void resolve_token(const SelParams& p, int t, SelShared& sh, uint32_t ep
       const bool sel = in & ((key > kstar) | (e & (er + (uint32_t)__builtin_popcountll(me & lt) < take_eq)));
       const uint64_t ms = __ballot(sel);
       const uint32_t oo = o + (uint32_t)__builtin_popcountll(ms & lt);
-      if (sel && oo < kk) put_i32<COH>(out + oo, (int32_t)(ev >> 32));
+      if (sel && oo < kk) out[oo] = (int32_t)(ev >> 32);
       er += (uint32_t)__builtin_popcountll(me);
       o += (uint32_t)__builtin_popcountll(ms);
     }
   }
   DSA_MARK(p.trace, 12);
-  for (int i = (int)kk + tid; i < p.k; i += kSelThreads) put_i32<COH>(out + i, -1);
+  for (int i = (int)kk + tid; i < p.k; i += kSelThreads) out[i] = -1;
   if (tid == 0 && p.trace) p.trace[blockIdx.x * 16 + 13] = nc;
-  if (tid == 0 && p.count) put_i32<COH>(p.count + t, (int32_t)kk);
+  if (tid == 0 && p.count) p.count[t] = (int32_t)kk;
   __syncthreads();
 }
 
 // The selection of one launch (all phases; workgroup t < T resolves token t).  Returns
 // false, having written empty selections, when the workspace's error word was already
 // set; otherwise true, with this launch's counter in `epoch_out` (slot tag = epoch + 1).
-// COH: the indices and counts are written with agent-scope atomic stores.
-template <int SRC, int KDT, int RTW, bool COH>
+template <int SRC, int KDT, int RTW>
 DSA_DEV bool select_body(const SelParams& p, SelShared& sh, uint32_t& epoch_out) {
   static_assert(RTW >= 1 && RTW <= 4, "a wave holds one to four row tiles");
   const int tid = threadIdx.x;
@@ -1045,8 +1035,8 @@ DSA_DEV bool select_body(const SelParams& p, SelShared& sh, uint32_t& epoch_out)
   if ((ctlw >> 32) != 0u) {
     if (wg < T) {
       int32_t* out = p.idx + (size_t)wg * p.k;
-      for (int i = tid; i < p.k; i += kSelThreads) put_i32<COH>(out + i, -1);
-      if (tid == 0 && p.count) put_i32<COH>(p.count + wg, 0);
+      for (int i = tid; i < p.k; i += kSelThreads) out[i] = -1;
+      if (tid == 0 && p.count) p.count[wg] = 0;
     }
     return false;
   }
@@ -1167,7 +1157,7 @@ DSA_DEV bool select_body(const SelParams& p, SelShared& sh, uint32_t& epoch_out)
   }
   DSA_MARK(p.trace, 7);
   // ---------------- P3: workgroup t selects token t once every count of the token is in
-  if (wg < T) resolve_token<COH>(p, wg, sh, epoch);
+  if (wg < T) resolve_token(p, wg, sh, epoch);
   DSA_MARK(p.trace, 15);
   return true;
 }

@@ -338,19 +338,18 @@ def test_dsa_layer_step_full_context(dsa, w8a8):
                                                  (777, 3, 64, False, True), (20000, 1, 2048, False, False),
                                                  (5000, 5, 300, True, True), (9000, 8, 2048, False, True),
                                                  (1 << 20, 8, 2048, False, True), (1 << 20, 8, 2048, True, False)])
-def test_fused_layer_equals_five_launch_composition(dsa, monkeypatch, L, T, top_k, w8a8, sink):
-    """The DSA layer as projection + one fused launch (selection, attention, split merge,
-    output projection) equals the five-launch chain bit for bit: outputs, indices, the
-    exported projection and every cache row."""
+def test_persistent_tail_equals_five_launch_composition(dsa, monkeypatch, L, T, top_k, w8a8, sink):
+    """The DSA layer with one persistent launch after the selection (attention, split
+    merge, output projection; DSA_LAYER_PERSISTENT_TAIL=1) equals the five-launch chain bit
+    for bit: outputs, indices, the exported projection and every cache row."""
     lay = synth.layer_inputs("dsa", 0, L, T, seed=L + T)
     x = synth.module_x(L + T, T)
     w8 = synth.w8a8_weights(lay) if w8a8 else None
     sk = up(synth.sink_logits(L, std=2.0)) if sink else None
-    monkeypatch.delenv("DSA_LAYER_UNFUSED", raising=False)
+    monkeypatch.setenv("DSA_LAYER_PERSISTENT_TAIL", "1")
     a = _run_layer(dsa, "dsa", lay, x, T, L - T, top_k=top_k, sink=sk, w8=w8)
-    monkeypatch.setenv("DSA_LAYER_UNFUSED", "1")
+    monkeypatch.delenv("DSA_LAYER_PERSISTENT_TAIL")
     b = _run_layer(dsa, "dsa", lay, x, T, L - T, top_k=top_k, sink=sk, w8=w8)
-    monkeypatch.delenv("DSA_LAYER_UNFUSED")
     for key in ("x_out", "qkv", "idx", "k", "v", "k_idx", "k_idx_scale"):
         assert np.array_equal(a[key], b[key]), key
     assert np.all((a["idx"] >= 0).sum(axis=1) == np.minimum(top_k, np.arange(L - T + 1, L + 1)))

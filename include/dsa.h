@@ -88,7 +88,8 @@ typedef enum {
   DSA_WS_SPARSE_ATTN = 3, /* dsa_sparse_attn */
   DSA_WS_SWA_ATTN = 4,    /* swa_attn */
   DSA_WS_LAYER_DSA = 5,   /* dsa_layer_step, kind = DSA */
-  DSA_WS_LAYER_SWA = 6    /* dsa_layer_step, kind = SWA */
+  DSA_WS_LAYER_SWA = 6,   /* dsa_layer_step, kind = SWA */
+  DSA_WS_MODULE = 7       /* dsa_module_step; k = largest top_k of its DSA layers (0: none) */
 } dsa_ws_kind_t;
 
 /*
@@ -261,6 +262,34 @@ dsa_status_t dsa_layer_step(const dsa_layer_config_t* cfg, const dsa_layer_weigh
                             const dsa_layer_cache_t* cache, const void* x_in, void* x_out,
                             int T, int64_t pos0, int32_t* idx_out, void* qkv_out, void* ws,
                             size_t ws_bytes, void* stream);
+
+/* ------------------------------------------------------------------ module step
+ * §The execution model (naive.ai/en/research): the stages of the decode loop are fused
+ * into larger kernels and the remaining boundaries are bridged on the device, without the
+ * host in between.
+ *
+ * n_layers (1 .. DSA_MAX_MODULE_LAYERS) decoder layers applied in order to one block of T
+ * tokens at pos0: layer i reads the output of layer i - 1 (x_in for layer 0) and the last
+ * writes x_out; layer i computes what dsa_layer_step computes for cfg[i], w[i], cache[i],
+ * and the result equals n_layers dsa_layer_step calls bit for bit.
+ * Consecutive SWA layers with bf16 weights and the same window (window + T - 1 <= 160),
+ * rms_eps, rope_theta, sm_scale and ring capacity run as ONE persistent launch per up to 8
+ * layers: 256 workgroups, one per compute unit, all resident, that hand each layer's
+ * Q/K/V and output to each other through launch-tagged words in the workspace.  When the
+ * device cannot hold them all at once (or with DSA_MODULE_NO_CHAIN=1 in the environment)
+ * those layers run one dsa_layer_step at a time instead.  The other layers run as in
+ * dsa_layer_step.
+ * idx_out [T][top_k] int32 (optional): the selection of the last DSA layer.
+ * ws: DSA_WS_MODULE sized for (T, pos0 + T, largest top_k), zero-filled before first use;
+ * like the other workspaces it carries launch counters and a sticky error word
+ * (dsa_workspace_status).  Every argument is checked, and every selection's co-residency,
+ * before anything is launched.
+ * --------------------------------------------------------------------------------- */
+#define DSA_MAX_MODULE_LAYERS 64
+
+dsa_status_t dsa_module_step(int n_layers, const dsa_layer_config_t* cfg, const dsa_layer_weights_t* w,
+                             const dsa_layer_cache_t* cache, const void* x_in, void* x_out, int T,
+                             int64_t pos0, int32_t* idx_out, void* ws, size_t ws_bytes, void* stream);
 
 /* ------------------------------------------------------------------- helpers */
 

@@ -35,6 +35,8 @@ of the block multiplies every pair by the shift's rotation), w_I not rotated, th
 block's own keys read back quantised, and the block's scores invariant under a shift
 within the quantiser bound.  Beyond the pinned stages and special cases with closed
 forms, the end-to-end layer step is unpinned (the pages print no worked example).
+``module_step`` (layers in order) is pinned by layers made the identity (zero output
+projection): the chain must hand each layer the previous layer's output.
 """
 from __future__ import annotations
 
@@ -463,3 +465,22 @@ def layer_step(kind: str, x_bits, gamma_bits, w_qkvi_bits, w_o_bits, cache: dict
     res["x_out"] = bf16_round_trip(out)
     res["x_out_f64"] = out
     return res
+
+
+def module_step(layers, x_bits, pos0: int, **kw):
+    """Decoder layers applied in order to one block of tokens (§The execution model: the
+    layers of a decode step run back to back, each on the previous layer's output).
+
+    ``layers``: list of dicts with keys kind, gamma, w_qkvi, w_o, cache (updated in place,
+    as in ``layer_step``) and optional top_k, window.  Each layer takes the bf16 output
+    of the one before it (``x_bits`` for the first).  Returns the last layer's output as
+    bf16 bits and the list of every layer's ``layer_step`` result.
+    """
+    x = np.asarray(x_bits, dtype=np.uint16)
+    results = []
+    for lay in layers:
+        r = layer_step(lay["kind"], x, lay["gamma"], lay["w_qkvi"], lay["w_o"], lay["cache"], pos0,
+                       top_k=lay.get("top_k", 2048), window=lay.get("window", 128), **kw)
+        results.append(r)
+        x = round_to_bf16(r["x_out_f64"])
+    return x, results

@@ -23,13 +23,14 @@ _lib = C.CDLL(LIB_PATH)
 
 # dtypes / kinds (include/dsa.h)
 BF16, FP8_E4M3, FP32 = 0, 1, 2
-WS_TOPK, WS_INDEX_TOPK, WS_SPARSE_ATTN, WS_SWA_ATTN, WS_LAYER_DSA, WS_LAYER_SWA = 1, 2, 3, 4, 5, 6
+WS_TOPK, WS_INDEX_TOPK, WS_SPARSE_ATTN, WS_SWA_ATTN, WS_LAYER_DSA, WS_LAYER_SWA, WS_MODULE = 1, 2, 3, 4, 5, 6, 7
+MAX_MODULE_LAYERS = 64
 LAYER_DSA, LAYER_SWA = 0, 1
 STATUS = {0: "DSA_OK", 1: "DSA_ERR_NULL", 2: "DSA_ERR_SHAPE", 3: "DSA_ERR_DTYPE", 4: "DSA_ERR_ALIGN",
           5: "DSA_ERR_WORKSPACE", 6: "DSA_ERR_LAUNCH", 7: "DSA_ERR_HIP"}
 
 EXPORTS = ("dsa_indexer_scores", "dsa_topk", "dsa_index_topk", "dsa_sparse_attn", "dsa_sparse_attn_static", "swa_attn",
-           "dsa_layer_step", "dsa_workspace_bytes", "dsa_workspace_init", "dsa_workspace_status",
+           "dsa_layer_step", "dsa_module_step", "dsa_workspace_bytes", "dsa_workspace_init", "dsa_workspace_status",
            "dsa_max_context", "dsa_status_string", "dsa_last_error")
 
 
@@ -69,6 +70,8 @@ _sig = {
     "swa_attn": [_P, _P, _P, _P, _P, _I, _L, _I, _L, _I, _F, _P, _P, _I, _P, _S, _P],
     "dsa_layer_step": [C.POINTER(LayerConfig), C.POINTER(LayerWeights), C.POINTER(LayerCache),
                        _P, _P, _I, _L, _P, _P, _P, _S, _P],
+    "dsa_module_step": [_I, C.POINTER(LayerConfig), C.POINTER(LayerWeights), C.POINTER(LayerCache),
+                        _P, _P, _I, _L, _P, _P, _S, _P],
     "dsa_workspace_init": [_P, _S, _P],
     "dsa_workspace_status": [_P, _S, _P],
 }
@@ -169,6 +172,20 @@ def dsa_layer_step(cfg: LayerConfig, weights: LayerWeights, cache: LayerCache, x
                              T, pos0, _ptr(idx_out), _ptr(qkv_out), _ptr(ws),
                              _nbytes(ws) if ws_bytes is None else ws_bytes, _stream(stream))
     return _check("dsa_layer_step", st, raise_on_error)
+
+
+def dsa_module_step(cfgs, weights, caches, x_in, x_out, T, pos0, idx_out=None, ws=None, ws_bytes=None,
+                    stream=None, raise_on_error=True):
+    """Layers cfgs[i], weights[i], caches[i] applied in order to the block (one call)."""
+    n = len(cfgs)
+    if len(weights) != n or len(caches) != n:
+        raise ValueError("dsa_module_step: one config, weight set and cache per layer")
+    ca = (LayerConfig * n)(*cfgs)
+    wa = (LayerWeights * n)(*weights)
+    ka = (LayerCache * n)(*caches)
+    st = _lib.dsa_module_step(n, ca, wa, ka, _ptr(x_in), _ptr(x_out), T, pos0, _ptr(idx_out), _ptr(ws),
+                              _nbytes(ws) if ws_bytes is None else ws_bytes, _stream(stream))
+    return _check("dsa_module_step", st, raise_on_error)
 
 
 def dsa_workspace_bytes(kind, T, L, k):

@@ -4,7 +4,7 @@ import os
 import subprocess
 
 HERE = os.path.dirname(os.path.abspath(__file__))
-SOURCES = ["capi.hip", "index_topk.hip", "attention.hip", "layer.hip", "swa_out.hip", "layer_dsa.hip"]
+SOURCES = ["capi.hip", "index_topk.hip", "attention.hip", "layer.hip", "swa_out.hip", "layer_dsa.hip", "swa_chain.hip"]
 LIB = os.path.join(HERE, "libdsa.so")
 READ_CEILING_SOURCES = ["read_ceiling.hip"]
 READ_CEILING_LIB = os.path.join(HERE, "libdsa_read_ceiling.so")

@@ -49,36 +49,6 @@ constexpr int kTagPart = 2 + kD;   // tagged words per (token, split, head): m, 
 // stores of a thread holding dims 4 j .. 4 j + 3 each cover 32 consecutive words.
 DSA_DEV int tag_dim_word(int d) { return 2 + (d & 3) * (kD / 4) + (d >> 2); }
 
-// N tagged words addr(0 .. N-1) loaded together, then the ones not yet carrying `tag`
-// reloaded until all do (bounded); the low halves into val.
-template <int N, typename F>
-DSA_DEV void poll_words(F addr, uint32_t tag, uint32_t (&val)[N], uint32_t* ctl_words) {
-  uint64_t v[N];
-#pragma unroll
-  for (int i = 0; i < N; ++i) v[i] = ald64(addr(i));
-  bool ok = true;
-#pragma unroll
-  for (int i = 0; i < N; ++i) ok = ok & ((uint32_t)(v[i] >> 32) == tag);
-  if (!ok) {
-    const uint64_t t0 = __builtin_amdgcn_s_memrealtime();
-    while (!ok) {
-      __builtin_amdgcn_s_sleep(1);
-      if (__builtin_amdgcn_s_memrealtime() - t0 > kSpinLimit) {
-        ast(ctl_words + ctl::kError, 1u);
-        break;
-      }
-#pragma unroll
-      for (int i = 0; i < N; ++i)
-        if ((uint32_t)(v[i] >> 32) != tag) v[i] = ald64(addr(i));
-      ok = true;
-#pragma unroll
-      for (int i = 0; i < N; ++i) ok = ok & ((uint32_t)(v[i] >> 32) == tag);
-    }
-  }
-#pragma unroll
-  for (int i = 0; i < N; ++i) val[i] = (uint32_t)v[i];
-}
-
 template <int KVDT, int ROWS>
 struct AttnShared {
   static constexpr int RB = KVDT == 0 ? 256 : 128;   // bytes per cache row

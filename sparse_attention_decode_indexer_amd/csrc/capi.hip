@@ -74,6 +74,70 @@ LayerWs layer_ws(int kind, int T, int64_t L, int k, int window, int ncu) {
   return w;
 }
 
+// Checks of one layer's configuration, weights and cache for a block of T tokens at pos0
+// (shared by the layer step and the module step).
+dsa_status_t check_layer(const dsa_layer_config_t* cfg, const dsa_layer_weights_t* w,
+                         const dsa_layer_cache_t* cache, int T, int64_t pos0, int ncu) {
+  if (!cfg || !w || !cache) return DSA_ERR_NULL;
+  if (!w->rms_gamma || !w->w_qkvi || !w->w_o || !cache->k || !cache->v) return DSA_ERR_NULL;
+  if (w->w_dtype != DSA_BF16 && w->w_dtype != DSA_FP8_E4M3) return DSA_ERR_DTYPE;
+  const bool w8a8 = w->w_dtype == DSA_FP8_E4M3;
+  if (w8a8 != (w->w_qkvi_scale != nullptr) || w8a8 != (w->w_o_scale != nullptr)) return DSA_ERR_DTYPE;
+  const bool dsa_kind = cfg->kind == DSA_LAYER_DSA;
+  if (!dsa_kind && cfg->kind != DSA_LAYER_SWA) return DSA_ERR_SHAPE;
+  if (dsa_kind && (!cache->k_idx || !cache->k_idx_scale)) return DSA_ERR_NULL;
+  if (cfg->hidden != dsa::kHidden) return DSA_ERR_SHAPE;
+  if (T < 1 || T > dsa::kMaxT || pos0 < 0) return DSA_ERR_SHAPE;
+  const int64_t L = pos0 + T;
+  if (dsa_kind) {
+    if (cfg->top_k < 1 || cfg->top_k > dsa::kMaxTopK) return DSA_ERR_SHAPE;
+    if (L > cache->capacity || L > dsa::select_max_context(ncu)) return DSA_ERR_SHAPE;
+  } else {
+    if (cfg->window < 1 || cfg->window > dsa::kMaxTopK) return DSA_ERR_SHAPE;
+    if (cache->capacity < (int64_t)cfg->window + T - 1 || cache->capacity > kMaxL) return DSA_ERR_SHAPE;
+  }
+  if (!aligned16(w->rms_gamma) || !aligned16(w->w_qkvi) || !aligned16(w->w_o) || !aligned16(cache->k) ||
+      !aligned16(cache->v) || (cache->k_idx && !aligned16(cache->k_idx)) || (cfg->sink && !aligned16(cfg->sink)))
+    return DSA_ERR_ALIGN;
+  return DSA_OK;
+}
+
+// ---- module-step workspace: the SWA chain's region (its own control block), two layer
+// outputs between launches, and a layer-step workspace for the layers that run one by one
+struct ModuleWs {
+  size_t chain, xa, xb, layer, layer_bytes, total;
+};
+
+ModuleWs module_ws(int T, int64_t L, int k, int ncu) {
+  ModuleWs m{};
+  size_t o = 0;
+  m.chain = o; o = align_up(o + dsa::swa_chain_workspace_bytes());
+  m.xa = o; o = align_up(o + (size_t)dsa::kMaxT * dsa::kHidden * 2);
+  m.xb = o; o = align_up(o + (size_t)dsa::kMaxT * dsa::kHidden * 2);
+  m.layer = o;
+  size_t lb = layer_ws(DSA_LAYER_SWA, T, L, 0, dsa::kMaxTopK, ncu).total;
+  if (k > 0) {
+    const size_t ld = layer_ws(DSA_LAYER_DSA, T, L, k, 0, ncu).total;
+    lb = ld > lb ? ld : lb;
+  }
+  m.layer_bytes = lb;
+  m.total = align_up(o + lb);
+  return m;
+}
+
+// Layer i joins an SWA chain that starts at layer c: bf16 weights, the same window,
+// norm, rotary and softmax constants and ring capacity, and a window that fits one
+// workgroup.
+bool chains_with(const dsa_layer_config_t* cfg, const dsa_layer_weights_t* w, const dsa_layer_cache_t* cache,
+                 int i, int c, int T) {
+  const dsa_layer_config_t& a = cfg[i];
+  const dsa_layer_config_t& z = cfg[c];
+  return a.kind == DSA_LAYER_SWA && w[i].w_dtype == DSA_BF16 && dsa::swa_chain_fits(T, a.window) &&
+         a.window == z.window && a.rms_eps == z.rms_eps && a.rope_theta == z.rope_theta &&
+         a.sm_scale == z.sm_scale && cache[i].capacity == cache[c].capacity;
+}
+
+
 // ---- scratch of the allocation-free attention entry point: the split partials of the
 // largest call (T = 8, k = 2048), one copy per GPU held until the process ends.  In host
 // code `scratch` names a host-side stand-in; its device address comes from
@@ -143,6 +207,8 @@ size_t dsa_workspace_bytes(int kind, int T, int64_t L, int k) {
       return layer_ws(DSA_LAYER_DSA, T, L, k, 0, ncu).total;
     case DSA_WS_LAYER_SWA:
       return layer_ws(DSA_LAYER_SWA, T, L, 0, k, ncu).total;
+    case DSA_WS_MODULE:
+      return module_ws(T, L, k, ncu).total;
   }
   return 0;
 }
@@ -315,34 +381,19 @@ dsa_status_t dsa_layer_step(const dsa_layer_config_t* cfg, const dsa_layer_weigh
                             int T, int64_t pos0, int32_t* idx_out, void* qkv_out, void* ws,
                             size_t ws_bytes, void* stream) {
   if (!cfg || !w || !cache || !x_in || !x_out) return DSA_ERR_NULL;
-  if (!w->rms_gamma || !w->w_qkvi || !w->w_o || !cache->k || !cache->v) return DSA_ERR_NULL;
-  if (w->w_dtype != DSA_BF16 && w->w_dtype != DSA_FP8_E4M3) return DSA_ERR_DTYPE;
+  const int ncu = device_cus();
+  if (dsa_status_t s = check_layer(cfg, w, cache, T, pos0, ncu)) return s;
   const bool w8a8 = w->w_dtype == DSA_FP8_E4M3;
-  if (w8a8 != (w->w_qkvi_scale != nullptr) || w8a8 != (w->w_o_scale != nullptr)) return DSA_ERR_DTYPE;
   const float* wq_scale = w8a8 ? w->w_qkvi_scale : nullptr;
   const float* wo_scale = w8a8 ? w->w_o_scale : nullptr;
   const bool dsa_kind = cfg->kind == DSA_LAYER_DSA;
-  if (!dsa_kind && cfg->kind != DSA_LAYER_SWA) return DSA_ERR_SHAPE;
-  if (dsa_kind && (!cache->k_idx || !cache->k_idx_scale)) return DSA_ERR_NULL;
-  if (cfg->hidden != dsa::kHidden) return DSA_ERR_SHAPE;
-  if (T < 1 || T > dsa::kMaxT || pos0 < 0) return DSA_ERR_SHAPE;
   if (x_in == x_out) return DSA_ERR_SHAPE;
-  const int ncu = device_cus();
+  if (!dsa_kind && idx_out) return DSA_ERR_SHAPE;
   int64_t L = pos0 + T;
-  if (dsa_kind) {
-    if (cfg->top_k < 1 || cfg->top_k > dsa::kMaxTopK) return DSA_ERR_SHAPE;
-    if (L > cache->capacity || L > dsa::select_max_context(ncu)) return DSA_ERR_SHAPE;
-  } else {
-    if (cfg->window < 1 || cfg->window > dsa::kMaxTopK) return DSA_ERR_SHAPE;
-    if (cache->capacity < (int64_t)cfg->window + T - 1 || cache->capacity > kMaxL) return DSA_ERR_SHAPE;
-    if (idx_out) return DSA_ERR_SHAPE;
-  }
   const LayerWs lw = layer_ws(cfg->kind, T, L, cfg->top_k, cfg->window, ncu);
   if (!ws || ws_bytes < lw.total) return DSA_ERR_WORKSPACE;
-  if (!aligned16(ws) || !aligned16(x_in) || !aligned16(x_out) || !aligned16(w->rms_gamma) ||
-      !aligned16(w->w_qkvi) || !aligned16(w->w_o) || !aligned16(cache->k) || !aligned16(cache->v) ||
-      (qkv_out && !aligned16(qkv_out)) || (idx_out && !aligned16(idx_out)) ||
-      (cache->k_idx && !aligned16(cache->k_idx)) || (cfg->sink && !aligned16(cfg->sink)))
+  if (!aligned16(ws) || !aligned16(x_in) || !aligned16(x_out) || (qkv_out && !aligned16(qkv_out)) ||
+      (idx_out && !aligned16(idx_out)))
     return DSA_ERR_ALIGN;
   // The DSA layer runs as projection, selection, then separate attention, split-merge and
   // output-projection launches (five in all).  The environment variable
@@ -399,6 +450,69 @@ dsa_status_t dsa_layer_step(const dsa_layer_config_t* cfg, const dsa_layer_weigh
   if (e != hipSuccess) return hip_fail(e, "dsa_layer_step: attention");
   e = dsa::launch_proj_out(attn_out, w->w_o, wo_scale, x_in, x_out, T, w8 + lw.proj, st);
   if (e != hipSuccess) return hip_fail(e, "dsa_layer_step: output projection");
+  return DSA_OK;
+}
+
+dsa_status_t dsa_module_step(int n_layers, const dsa_layer_config_t* cfg, const dsa_layer_weights_t* w,
+                             const dsa_layer_cache_t* cache, const void* x_in, void* x_out, int T, int64_t pos0,
+                             int32_t* idx_out, void* ws, size_t ws_bytes, void* stream) {
+  if (!cfg || !w || !cache || !x_in || !x_out) return DSA_ERR_NULL;
+  if (n_layers < 1 || n_layers > DSA_MAX_MODULE_LAYERS) return DSA_ERR_SHAPE;
+  if (x_in == x_out) return DSA_ERR_SHAPE;
+  const int ncu = device_cus();
+  int kmax = 0, last_dsa = -1;
+  for (int i = 0; i < n_layers; ++i) {
+    if (dsa_status_t s = check_layer(&cfg[i], &w[i], &cache[i], T, pos0, ncu)) return s;
+    if (cfg[i].kind == DSA_LAYER_DSA) {
+      kmax = cfg[i].top_k > kmax ? cfg[i].top_k : kmax;
+      last_dsa = i;
+    }
+  }
+  if (idx_out && last_dsa < 0) return DSA_ERR_SHAPE;
+  const int64_t L = pos0 + T;
+  const ModuleWs mw = module_ws(T, L, kmax, ncu);
+  if (!ws || ws_bytes < mw.total) return DSA_ERR_WORKSPACE;
+  if (!aligned16(ws) || !aligned16(x_in) || !aligned16(x_out) || (idx_out && !aligned16(idx_out)))
+    return DSA_ERR_ALIGN;
+  // nothing is launched (and no cache row written) unless every selection can run
+  for (int i = 0; i < n_layers; ++i)
+    if (cfg[i].kind == DSA_LAYER_DSA) {
+      hipError_t e = dsa::select_check_resident(0, 1, T, L, pos0, cfg[i].top_k, ncu);
+      if (e != hipSuccess) return hip_fail(e, "dsa_module_step: workgroups cannot all be resident");
+    }
+  // consecutive SWA layers run as one persistent launch when its workgroups can all be
+  // resident (else, and with DSA_MODULE_NO_CHAIN=1, one layer step at a time: same bits)
+  const char* nc = getenv("DSA_MODULE_NO_CHAIN");
+  const bool chain = !(nc && nc[0] == '1') && dsa::swa_chain_check_resident(ncu) == hipSuccess;
+  (void)hipGetLastError();
+  uint8_t* w8 = static_cast<uint8_t*>(ws);
+  void* buf[2] = {w8 + mw.xa, w8 + mw.xb};
+  hipStream_t st = (hipStream_t)stream;
+  const void* cur = x_in;
+  int sel = 0;
+  for (int i = 0; i < n_layers;) {
+    int j = i + 1;
+    if (chain && chains_with(cfg, w, cache, i, i, T))
+      while (j < n_layers && j - i < dsa::kMaxChain && chains_with(cfg, w, cache, j, i, T)) ++j;
+    void* out = j == n_layers ? x_out : buf[sel];
+    if (chain && chains_with(cfg, w, cache, i, i, T)) {
+      dsa::SwaChainLayer ls[dsa::kMaxChain];
+      for (int q = i; q < j; ++q)
+        ls[q - i] = dsa::SwaChainLayer{w[q].rms_gamma, w[q].w_qkvi, w[q].w_o, cache[q].k, cache[q].v, cfg[q].sink};
+      hipError_t e = dsa::launch_swa_chain(j - i, ls, cur, out, T, pos0, cfg[i].window, cfg[i].sm_scale,
+                                           cfg[i].rms_eps, cfg[i].rope_theta, cache[i].capacity, w8 + mw.chain, ncu,
+                                           st);
+      if (e != hipSuccess) return hip_fail(e, "dsa_module_step: SWA layers");
+    } else {
+      if (dsa_status_t s = dsa_layer_step(&cfg[i], &w[i], &cache[i], cur, out, T, pos0,
+                                          i == last_dsa ? idx_out : nullptr, nullptr, w8 + mw.layer,
+                                          mw.layer_bytes, stream))
+        return s;
+    }
+    cur = out;
+    sel ^= 1;
+    i = j;
+  }
   return DSA_OK;
 }
 

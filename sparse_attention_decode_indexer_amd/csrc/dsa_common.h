@@ -347,6 +347,39 @@ DSA_DEV uint32_t wait_tagged_one(const uint64_t* slot, uint32_t tag, uint32_t* c
   return (uint32_t)v;
 }
 
+// N tagged words addr(0 .. N-1) loaded together, then the ones not yet carrying `tag`
+// reloaded until all do; the low halves into val.  Bounded: the wait gives up after
+// kSpinLimit, or as soon as the workspace's error word is set (another wait of the launch
+// gave up), sets the error word and returns false.
+template <int N, typename F>
+DSA_DEV bool poll_words(F addr, uint32_t tag, uint32_t (&val)[N], uint32_t* ctl_words) {
+  uint64_t v[N];
+#pragma unroll
+  for (int i = 0; i < N; ++i) v[i] = ald64(addr(i));
+  bool ok = true;
+#pragma unroll
+  for (int i = 0; i < N; ++i) ok = ok & ((uint32_t)(v[i] >> 32) == tag);
+  if (!ok) {
+    const uint64_t t0 = __builtin_amdgcn_s_memrealtime();
+    while (!ok) {
+      __builtin_amdgcn_s_sleep(1);
+      if (__builtin_amdgcn_s_memrealtime() - t0 > kSpinLimit || ald(ctl_words + ctl::kError) != 0u) {
+        ast(ctl_words + ctl::kError, 1u);
+        break;
+      }
+#pragma unroll
+      for (int i = 0; i < N; ++i)
+        if ((uint32_t)(v[i] >> 32) != tag) v[i] = ald64(addr(i));
+      ok = true;
+#pragma unroll
+      for (int i = 0; i < N; ++i) ok = ok & ((uint32_t)(v[i] >> 32) == tag);
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < N; ++i) val[i] = (uint32_t)v[i];
+  return ok;
+}
+
 template <int N>
 DSA_DEV uint32_t wait_tagged_min(const uint64_t* slots, int n, uint32_t tag, uint32_t* ctl_words) {
   const int lane = threadIdx.x & 63;

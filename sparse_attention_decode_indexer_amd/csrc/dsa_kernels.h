@@ -62,6 +62,26 @@ hipError_t launch_swa_out(const void* q, const void* kring, const void* vring, i
                           const void* w_o, const float* w_o_scale, const void* x, void* xout,
                           hipStream_t st);
 
+// A run of up to kMaxChain consecutive SWA layers (bf16 weights, one window, W + T - 1 <=
+// 160) as one persistent launch of 256 workgroups; ws: swa_chain_workspace_bytes(), its
+// control block first.  hipErrorCooperativeLaunchTooLarge when the workgroups cannot all
+// be resident.
+constexpr int kMaxChain = 8;
+struct SwaChainLayer {
+  const void* gamma;
+  const void* w_qkv;
+  const void* w_o;
+  void* kring;
+  void* vring;
+  const float* sink;
+};
+size_t swa_chain_workspace_bytes();
+bool swa_chain_fits(int T, int window);
+hipError_t swa_chain_check_resident(int num_cu);
+hipError_t launch_swa_chain(int n, const SwaChainLayer* layers, const void* x_in, void* x_out, int T,
+                            int64_t pos0, int window, float sm_scale, float eps, float theta, int64_t ring_cap,
+                            void* ws, int num_cu, hipStream_t st);
+
 hipError_t launch_zero(void* p, size_t bytes, hipStream_t st);
 
 #ifdef DSA_TRACE

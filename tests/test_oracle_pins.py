@@ -683,3 +683,51 @@ def test_layer_step_w8a8_equals_bf16_step_when_lossless():
                       np.abs(wod))
     assert np.all(np.abs(a["x_out_f64"] - b["x_out_f64"]) <= bound)
     assert not np.array_equal(a["x_out_f64"], b["x_out_f64"])
+
+
+# ----------------------------------------------------------------------------- module step
+
+def _swa_stack(n, pos0, T, seed, zero_wo=()):
+    """n SWA layers of the module workload; layers in zero_wo get W_o = 0, which makes
+    them the identity on x (the output is the residual alone)."""
+    out = []
+    for i in range(n):
+        lay = synth.layer_inputs("swa", i, pos0 + T, T, seed=seed, ring_cap=256)
+        w_o = lay.w_o.copy()
+        if i in zero_wo:
+            w_o[:] = 0
+        out.append(dict(kind="swa", gamma=lay.gamma, w_qkvi=lay.w_qkvi, w_o=w_o,
+                        cache={"k": lay.k.copy(), "v": lay.v.copy(), "ring_cap": 256}))
+    return out
+
+
+def test_module_step_hands_each_layer_the_previous_output():
+    """Identity layers pin the chaining: with layer 0 the identity the module is layer 1
+    alone on x; with layer 1 the identity it is layer 0 alone (a chain that fed x_in to
+    every layer, or returned the first layer's output, fails one of the two)."""
+    pos0, T = 300, 4
+    x = synth.module_x(5, T)
+    got, _ = O.module_step(_swa_stack(2, pos0, T, 9, zero_wo={0}), x, pos0)
+    l1 = _swa_stack(2, pos0, T, 9)[1]
+    ref = O.layer_step("swa", x, l1["gamma"], l1["w_qkvi"], l1["w_o"], l1["cache"], pos0)
+    assert np.array_equal(got, O.round_to_bf16(ref["x_out_f64"]))
+    assert not np.array_equal(got, x)
+    got, _ = O.module_step(_swa_stack(2, pos0, T, 9, zero_wo={1}), x, pos0)
+    l0 = _swa_stack(2, pos0, T, 9)[0]
+    ref = O.layer_step("swa", x, l0["gamma"], l0["w_qkvi"], l0["w_o"], l0["cache"], pos0)
+    assert np.array_equal(got, O.round_to_bf16(ref["x_out_f64"]))
+
+
+def test_module_step_of_identity_layers_keeps_x_and_fills_every_cache():
+    pos0, T = 1000, 3
+    x = synth.module_x(6, T)
+    layers = _swa_stack(3, pos0, T, 4, zero_wo={0, 1, 2})
+    got, res = O.module_step(layers, x, pos0)
+    assert np.array_equal(got, x)
+    for lay, r in zip(layers, res):
+        for t in range(T):
+            slot = (pos0 + t) % 256
+            assert np.array_equal(lay["cache"]["k"][slot], O.round_to_bf16(r["qkv"][t, 1024:1152]))
+            assert np.array_equal(lay["cache"]["v"][slot], O.round_to_bf16(r["qkv"][t, 1152:1280]))
+    # the layers' own weights differ, so their new rows do too
+    assert not np.array_equal(layers[0]["cache"]["k"][pos0 % 256], layers[1]["cache"]["k"][pos0 % 256])

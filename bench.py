@@ -221,18 +221,50 @@ def main():
     dsa_us = [a.elapsed_time(b) * 1e3 for a, b in ev_dsa]
     log(f"[bench] {args.steps} module steps, direct launches: {ms_eager * 1e3:.1f} us/step "
         f"(host {t_host / args.steps * 1e6:.1f} us)")
-    ms_step = ms_eager
+    # The module entry point (dsa_module_step): one call per step, the same launches
+    # enqueued back to back -- the headline step time.  For reference the same call with
+    # DSA_MODULE_CHAIN=1 (the five SWA layers as one persistent launch).
+    ws_mod = dsa.workspace(dsa.WS_MODULE, T, L, K)
+    mod_args = []
+    for per in structs:
+        mod_args.append(([cfg_dsa if kind == "dsa" else cfg_swa for kind, _, _ in per],
+                         [w for _, w, _ in per], [c for _, _, c in per]))
+
+    def module_step(i, st=None):
+        cfgs, ws_l, cs = mod_args[i % len(mod_args)]
+        dsa.dsa_module_step(cfgs, ws_l, cs, x0, xs[-1], T, pos0, idx_out=idx, ws=ws_mod,
+                            stream=stream if st is None else st)
+
+    def time_module():
+        for i in range(args.warmup):
+            module_step(i)
+        torch.cuda.synchronize()
+        e_start.record(stream)
+        for i in range(args.steps):
+            module_step(args.warmup + i)
+        e_end.record(stream)
+        torch.cuda.synchronize()
+        return e_start.elapsed_time(e_end) / args.steps
+
+    ms_module = time_module()
+    os.environ["DSA_MODULE_CHAIN"] = "1"
+    ms_module_chain = time_module()
+    del os.environ["DSA_MODULE_CHAIN"]
+    log(f"[bench] {args.steps} module steps through dsa_module_step: {ms_module * 1e3:.1f} us/step "
+        f"(SWA layers as one persistent launch: {ms_module_chain * 1e3:.1f} us/step)")
+    ms_step = ms_module
     ms_graph = None
     if not args.eager:
-        # For reference: one HIP graph per input set holding a whole module step (19
-        # kernels), replayed as a serving loop would, one host launch per step.
+        # For reference: one HIP graph per input set holding a whole module step (one
+        # dsa_module_step call captured: 15 kernels), replayed as a serving loop would, one
+        # host launch per step.
         graphs = []
         cap = torch.cuda.Stream()
         cap.wait_stream(stream)
         for r in range(len(structs)):
             g = torch.cuda.CUDAGraph()
             with torch.cuda.graph(g, stream=cap):
-                step(r, st=torch.cuda.current_stream())
+                module_step(r, st=torch.cuda.current_stream())
             graphs.append(g)
         stream.wait_stream(cap)
         torch.cuda.synchronize()
@@ -420,6 +452,8 @@ def main():
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": round(ms_step, 5),
+        "ms_per_step_layer_calls": round(ms_eager, 5),
+        "ms_per_step_persistent_swa": round(ms_module_chain, 5),
         "ms_per_step_graph": None if ms_graph is None else round(ms_graph, 5),
         "higher_is_better": True,
         "scaling": "weak",
@@ -592,6 +626,8 @@ def read_ceiling(torch, dev, stream, dsa):
 
 
 KERNEL_SOURCES = ("sparse_attention_decode_indexer_amd/csrc/index_topk.hip",
+                  "sparse_attention_decode_indexer_amd/csrc/select_core.h",
+                  "sparse_attention_decode_indexer_amd/csrc/select_geometry.h",
                   "sparse_attention_decode_indexer_amd/csrc/dsa_common.h")
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "select_kernel_traffic_1m.txt")
 

@@ -272,13 +272,14 @@ dsa_status_t dsa_layer_step(const dsa_layer_config_t* cfg, const dsa_layer_weigh
  * tokens at pos0: layer i reads the output of layer i - 1 (x_in for layer 0) and the last
  * writes x_out; layer i computes what dsa_layer_step computes for cfg[i], w[i], cache[i],
  * and the result equals n_layers dsa_layer_step calls bit for bit.
- * Consecutive SWA layers with bf16 weights and the same window (window + T - 1 <= 160),
+ * The layers' launches are enqueued back to back with no host work between them (the
+ * call can be captured into a HIP graph).  With DSA_MODULE_CHAIN=1 in the environment,
+ * consecutive SWA layers with bf16 weights and the same window (window + T - 1 <= 160),
  * rms_eps, rope_theta, sm_scale and ring capacity run as ONE persistent launch per up to 8
- * layers: 256 workgroups, one per compute unit, all resident, that hand each layer's
- * Q/K/V and output to each other through launch-tagged words in the workspace.  When the
- * device cannot hold them all at once (or with DSA_MODULE_NO_CHAIN=1 in the environment)
- * those layers run one dsa_layer_step at a time instead.  The other layers run as in
- * dsa_layer_step.
+ * layers instead: 256 workgroups, one per compute unit, all resident, that hand each
+ * layer's Q/K/V and output to each other through launch-tagged words in the workspace
+ * (when the device cannot hold them all at once, those layers run one layer step at a
+ * time).  Both give the same bits; the persistent launch measured slower on MI355X.
  * idx_out [T][top_k] int32 (optional): the selection of the last DSA layer.
  * ws: DSA_WS_MODULE sized for (T, pos0 + T, largest top_k), zero-filled before first use;
  * like the other workspaces it carries launch counters and a sticky error word

@@ -99,8 +99,10 @@ __global__ void __launch_bounds__(swa::kThreads) swa_out_kernel(SoParams p) {
   }
   __syncthreads();
   DSA_MARK(p.trace, 2);
+  DSA_MARK_CLK(p.trace, 8);
   // ---- 2-4) attention of the block, 5) its output projection
   swa::attention(tid, l, p.pos0, W, T, p.sm_log2, p.sink != nullptr, sinkv, p.trace);
+  DSA_MARK_CLK(p.trace, 9);
   swa::oproj<F8>(tid, l, wf, wsv);
   DSA_MARK(p.trace, 6);
   {

@@ -2,8 +2,9 @@
 
 * Against the same layers called one dsa_layer_step at a time: the module's x_out, the
   last DSA layer's selection and every layer's cache or ring after the step are equal bit
-  for bit (runs of SWA layers go through the persistent multi-layer launch; a run longer
-  than eight layers is split over launches; DSA and W8A8 layers take the layer step).
+  for bit, both for the default path (the layer steps enqueued back to back) and with
+  DSA_MODULE_CHAIN=1 (runs of SWA layers through the persistent multi-layer launch; a run
+  longer than eight layers split over launches; DSA and W8A8 layers take the layer step).
 * Against the oracle's free-running composition of the layers (module_step): the module
   output within 2e-2 * max(1, |ref|) per element and 1e-2 relative in norm -- each layer
   adds fp32-accumulation and bf16-rounding differences that the next layer carries on.
@@ -27,6 +28,12 @@ CAP = 256
 def dsa():
     import sparse_attention_decode_indexer_amd as m
     return m
+
+
+@pytest.fixture
+def chain(monkeypatch):
+    """The persistent multi-layer SWA launch for the module calls of the test."""
+    monkeypatch.setenv("DSA_MODULE_CHAIN", "1")
 
 
 def _host_layers(kinds, L, T, seed, w8a8=()):
@@ -123,7 +130,7 @@ MODULE = ("swa",) * 5 + ("dsa",)
     (("swa",) * 2, (1 << 20), 8, 2048, 128),               # positions near 2^20, ring wrap
     (("swa",) * 3, 700, 4, 2048, 60),
 ])
-def test_module_equals_layer_by_layer(dsa, kinds, L, T, top_k, window):
+def test_module_equals_layer_by_layer(dsa, chain, kinds, L, T, top_k, window):
     pos0 = L - T
     host = _host_layers(kinds, L, T, seed=L + T)
     x = synth.module_x(L + 3, T)
@@ -132,7 +139,7 @@ def test_module_equals_layer_by_layer(dsa, kinds, L, T, top_k, window):
     _assert_same(a, b)
 
 
-def test_module_with_sinks_and_w8a8_equals_layer_by_layer(dsa):
+def test_module_with_sinks_and_w8a8_equals_layer_by_layer(dsa, chain):
     """Per-layer sinks (and none) through the chain; a W8A8 SWA layer breaks the run."""
     kinds = ("swa", "swa", "swa", "swa", "dsa")
     L, T = 2500, 8
@@ -144,7 +151,7 @@ def test_module_with_sinks_and_w8a8_equals_layer_by_layer(dsa):
     _assert_same(a, b)
 
 
-def test_module_two_calls_on_one_workspace(dsa):
+def test_module_two_calls_on_one_workspace(dsa, chain):
     """The second call (new launch counter, same workspace, a smaller block) is again equal
     to the layer-by-layer result."""
     kinds = ("swa",) * 4
@@ -157,7 +164,7 @@ def test_module_two_calls_on_one_workspace(dsa):
         _assert_same(a, b)
 
 
-def test_module_without_co_residency_runs_layer_by_layer(dsa, monkeypatch):
+def test_module_without_co_residency_runs_layer_by_layer(dsa, chain, monkeypatch):
     """With fewer resident workgroups than the chain needs (the DSA_RESIDENT_LIMIT hook),
     the SWA layers run one layer step at a time: the same bits."""
     kinds = ("swa",) * 3
@@ -170,10 +177,26 @@ def test_module_without_co_residency_runs_layer_by_layer(dsa, monkeypatch):
     _assert_same(a, b)
 
 
-@pytest.mark.parametrize("L,T", [(2000, 8), (300, 5)])
-def test_module_matches_oracle_composition(dsa, L, T):
+@pytest.mark.parametrize("persistent", [False, True])
+def test_default_module_equals_layer_by_layer(dsa, monkeypatch, persistent):
+    """The default path (layer steps enqueued back to back, outputs ping-ponged in the
+    workspace) on the module's layer mix; the persistent variant on the same inputs."""
+    if persistent:
+        monkeypatch.setenv("DSA_MODULE_CHAIN", "1")
+    L, T = 5000, 8
+    host = _host_layers(MODULE, L, T, seed=51)
+    x = synth.module_x(51, T)
+    a = _module(dsa, MODULE, host, x, T, L - T, 2048, 128)
+    b = _module(dsa, MODULE, host, x, T, L - T, 2048, 128, per_layer=True)
+    _assert_same(a, b)
+
+
+@pytest.mark.parametrize("L,T,persistent", [(2000, 8, True), (300, 5, True), (2000, 8, False)])
+def test_module_matches_oracle_composition(dsa, monkeypatch, L, T, persistent):
     """The module against the oracle's free-running composition of its six layers (top-k
     2048 >= L: the DSA layer attends its whole context, so its selection is unique)."""
+    if persistent:
+        monkeypatch.setenv("DSA_MODULE_CHAIN", "1")
     pos0 = L - T
     host = _host_layers(MODULE, L, T, seed=L)
     x = synth.module_x(L, T)

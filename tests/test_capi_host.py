@@ -132,7 +132,8 @@ def test_workspace_status_validation_without_device_access():
 def test_every_workspace_holds_the_control_block():
     import sparse_attention_decode_indexer_amd as dsa
     for kind, k in ((dsa.WS_TOPK, 64), (dsa.WS_INDEX_TOPK, 64), (dsa.WS_SPARSE_ATTN, 64),
-                    (dsa.WS_SWA_ATTN, 128), (dsa.WS_LAYER_DSA, 64), (dsa.WS_LAYER_SWA, 128)):
+                    (dsa.WS_SWA_ATTN, 128), (dsa.WS_LAYER_DSA, 64), (dsa.WS_LAYER_SWA, 128),
+                    (dsa.WS_MODULE, 64), (dsa.WS_MODULE, 0)):
         assert dsa.dsa_workspace_bytes(kind, 1, 4096, k) >= 16384, kind
 
 
@@ -165,3 +166,37 @@ def test_static_attention_validation_without_launch():
     assert a(FAKE, FAKE, FAKE, None, None, dsa.BF16, FAKE, 2049, 1, 100, 0.1, None, FAKE, dsa.FP32) == E["DSA_ERR_SHAPE"]
     assert a(FAKE, FAKE, FAKE, None, None, dsa.BF16, FAKE, 16, 9, 100, 0.1, None, FAKE, dsa.FP32) == E["DSA_ERR_SHAPE"]
     assert a(MIS, FAKE, FAKE, None, None, dsa.BF16, FAKE, 16, 1, 100, 0.1, None, FAKE, dsa.FP32) == E["DSA_ERR_ALIGN"]
+
+
+def test_module_step_validation_without_launch():
+    """dsa_module_step checks every layer (the layer step's checks), the layer count, the
+    aliasing of x_in and x_out, idx_out without a DSA layer and the workspace before any
+    launch; its workspace covers a DSA layer's and grows with top-k."""
+    import sparse_attention_decode_indexer_amd as dsa
+    E = {v: k for k, v in dsa.STATUS.items()}
+    swa = dsa.layer_config(dsa.LAYER_SWA)
+    dsa_cfg = dsa.layer_config(dsa.LAYER_DSA)
+    w = dsa.LayerWeights(FAKE, FAKE, FAKE)
+    ring = dsa.LayerCache(FAKE, FAKE, None, None, 256)
+    cache = dsa.LayerCache(FAKE, FAKE, FAKE, FAKE, 1000)
+    big = 1 << 40
+
+    def M(cfgs, caches, xo=FAKE + 0x1000, ws_bytes=big, idx=None, T=8, pos0=100):
+        return dsa.dsa_module_step(cfgs, [w] * len(cfgs), caches, FAKE, xo, T, pos0, idx_out=idx, ws=FAKE,
+                                   ws_bytes=ws_bytes, stream=0, raise_on_error=False)
+    assert M([swa], [ring], ws_bytes=16) == E["DSA_ERR_WORKSPACE"]
+    assert M([swa], [ring], xo=FAKE) == E["DSA_ERR_SHAPE"]                       # x_out aliases x_in
+    assert M([swa] * 65, [ring] * 65) == E["DSA_ERR_SHAPE"]                       # too many layers
+    assert M([swa], [ring], idx=FAKE) == E["DSA_ERR_SHAPE"]                       # no DSA layer to report
+    assert M([swa, dsa_cfg], [ring, dsa.LayerCache(FAKE, FAKE, None, FAKE, 1000)]) == E["DSA_ERR_NULL"]
+    assert M([swa, dsa_cfg], [ring, dsa.LayerCache(FAKE, FAKE, FAKE, FAKE, 100)]) == E["DSA_ERR_SHAPE"]
+    assert M([swa], [dsa.LayerCache(FAKE, FAKE, None, None, 100)]) == E["DSA_ERR_SHAPE"]   # ring too small
+    assert M([swa, dsa_cfg], [ring, dsa.LayerCache(FAKE, MIS, FAKE, FAKE, 1000)]) == E["DSA_ERR_ALIGN"]
+    assert M([swa, dsa_cfg], [ring, cache], T=9) == E["DSA_ERR_SHAPE"]
+    assert dsa.dsa_module_step([], [], [], FAKE, FAKE + 0x1000, 8, 100, ws=FAKE, ws_bytes=big, stream=0,
+                               raise_on_error=False) == E["DSA_ERR_SHAPE"]
+    m0 = dsa.dsa_workspace_bytes(dsa.WS_MODULE, 8, 1 << 20, 0)
+    m1 = dsa.dsa_workspace_bytes(dsa.WS_MODULE, 8, 1 << 20, 2048)
+    assert m1 > m0 > 0
+    assert m1 >= dsa.dsa_workspace_bytes(dsa.WS_LAYER_DSA, 8, 1 << 20, 2048)
+    assert M([swa, dsa_cfg], [ring, cache], ws_bytes=m0) == E["DSA_ERR_WORKSPACE"]

@@ -338,5 +338,233 @@ DSA_DEV void oproj(int tid, const Lds& l, const WoFrags<F8>& wf, float wsv) {
   __syncthreads();
 }
 
+
+// ----------------------------------------------------------------------------- token groups
+// The same steps for one group of G tokens (G = 2 or 4; group tg holds tokens G tg ..
+// G tg + G - 1, i.e. pairs 8 G tg .. 8 G tg + 8 G - 1), for a workgroup that produces output
+// columns of those tokens alone.  Every value is computed by the same instruction sequence
+// at the same MFMA tile position as in the whole-block functions above: the score tile of
+// pairs 32 q .. 32 q + 31 that holds the group (the other pairs' query rows zero), the P.V
+// tiles of 16 pairs, the output-projection tiles of 16 W_o rows x 16 token columns (the
+// other tokens' columns zero), partial sums added in the same order -- so the results are
+// equal bit for bit.
+// LDS: l.q holds the score tile's 32 query rows (column c = pair 32 q + c), l.s and l.scale
+// the group's 8 G rows (row = pair - 8 G tg).
+
+template <int G>
+DSA_DEV void attention_group(int tid, const Lds& l, int tg, int64_t pos0, int W, int T, float sm_log2,
+                             bool has_sink, float sinkv, uint64_t* trace) {
+  static_assert(G == 2 || G == 4, "two or four tokens per group");
+  constexpr int NP = 8 * G;                        // (token, head) rows of the group
+  (void)trace;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int U = W + T - 1;
+  const int p0 = NP * tg;                          // first pair of the group
+  const int c0 = p0 & 31;                          // its first column in the score tile
+  // ---- 2) scores: wave w < 5 takes rows 32 w .. 32 w + 31 against the tile's 32 columns;
+  //      the group's columns go to LDS
+  if (wave < kRows / 32) {
+    const uint8_t* ka = l.k + (wave * 32 + (lane & 31)) * kRowB + (lane >> 5) * 16;
+    const uint8_t* qa = l.q + (lane & 31) * kRowB + (lane >> 5) * 16;
+    f32x16_t acc = {};
+#pragma unroll
+    for (int ks = 0; ks < kD / 16; ++ks) {
+      Frag8 a, b0;
+      a.u = *reinterpret_cast<const uint4*>(ka + ks * 32);
+      b0.u = *reinterpret_cast<const uint4*>(qa + ks * 32);
+      acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a.v, b0.v, acc, 0, 0, 0);
+    }
+    const int pl = (lane & 31) - c0;
+    if (pl >= 0 && pl < NP) {
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        const int u = wave * 32 + 8 * (e >> 2) + 4 * (lane >> 5) + (e & 3);
+        l.s[pl][u] = acc[e] * sm_log2;
+      }
+    }
+  }
+  __syncthreads();
+  DSA_MARK(trace, 3);
+  // ---- 3) softmax of the group's rows (16 lanes per row)
+  if (tid < 16 * NP) {
+    const int pl = tid >> 4, j = tid & 15, t = (p0 + pl) >> 3;
+    const int64_t lo64 = (int64_t)(W - 1) - pos0;
+    const int lo = (int)(lo64 > t ? lo64 : t);
+    const int hi = (t + W - 1 < U - 1) ? t + W - 1 : U - 1;
+    const uint32_t span = (uint32_t)(hi - lo);
+    constexpr int NC = kRows / 32;
+    float z[2 * NC];
+    float m = -__builtin_inff();
+#pragma unroll
+    for (int c = 0; c < NC; ++c) {
+      const int u = 2 * j + 32 * c;
+      const float2 v2 = *reinterpret_cast<const float2*>(&l.s[pl][u]);
+      z[2 * c] = (uint32_t)(u - lo) <= span ? v2.x : -__builtin_inff();
+      z[2 * c + 1] = (uint32_t)(u + 1 - lo) <= span ? v2.y : -__builtin_inff();
+      m = fmaxf(m, fmaxf(z[2 * c], z[2 * c + 1]));
+    }
+    m = row16_max(m);
+    const float ms = m != -__builtin_inff() ? m : 0.0f;
+    float lsum = 0.0f;
+    uint32_t* ph = reinterpret_cast<uint32_t*>(&l.s[pl][0]);
+#pragma unroll
+    for (int c = 0; c < NC; ++c) {
+      const float q0 = __builtin_amdgcn_exp2f(z[2 * c] - ms);
+      const float q1 = __builtin_amdgcn_exp2f(z[2 * c + 1] - ms);
+      lsum += q0 + q1;
+      const uint32_t h2 = pack_bf16x2(q0, q1);
+      const uint32_t l2 = pack_bf16x2(q0 - __uint_as_float(h2 << 16), q1 - __uint_as_float(h2 & 0xffff0000u));
+      ph[j + 16 * c] = h2;
+      ph[kSStride / 2 + j + 16 * c] = l2;
+    }
+    lsum = row16_sum(lsum);
+    if (j == 0) {
+      const float sink2 = has_sink ? sinkv * 1.4426950408889634f : -__builtin_inff();
+      const float M = fmaxf(m, sink2);
+      float sc = 0.0f, den = 0.0f;
+      if (M != -__builtin_inff()) {
+        if (m != -__builtin_inff()) {
+          sc = exp2f(m - M);
+          den = lsum * sc;
+        }
+        if (sink2 != -__builtin_inff()) den += exp2f(sink2 - M);
+      }
+      l.scale[pl] = den > 0.0f ? sc / den : 0.0f;
+    }
+  }
+  __syncthreads();
+  DSA_MARK(trace, 4);
+  // ---- 4) O = P V: wave w < 4 takes dims 32 w .. +31 for the group's G / 2 tiles of 16
+  //      pairs x {hi, lo} parts, K = 160 rows in 10 steps (one wave per SIMD: spreading the
+  //      tiles over eight waves reads V twice and measured slower)
+  if (wave < 4) {
+    constexpr int MT = G / 2;
+    const int db = wave;
+    const int m = lane & 31;
+    const int poff = ((m >> 4) * kSStride + 8 * (lane >> 5)) * 2;
+    const int g = lane >> 4, q = lane & 15;
+    const uint8_t* vb = l.v + (8 * (g >> 1) + (q >> 2)) * kRowB + (32 * db + 16 * (g & 1) + 4 * (q & 3)) * 2;
+    f32x16_t acc[MT] = {};
+#pragma unroll
+    for (int ks = 0; ks < kRows / 16; ++ks) {
+      Frag8 a[MT], bv;
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt)
+        a[mt].u = *reinterpret_cast<const uint4*>(reinterpret_cast<const uint8_t*>(&l.s[16 * mt + (m & 15)][0]) +
+                                                  poff + ks * 32);
+      const uint2 lo4 = lds_tr16(vb + (16 * ks) * kRowB);
+      const uint2 hi4 = lds_tr16(vb + (16 * ks + 4) * kRowB);
+      bv.u = make_uint4(lo4.x, lo4.y, hi4.x, hi4.y);
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt)
+        acc[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[mt].v, bv.v, acc[mt], 0, 0, 0);
+    }
+    uint16_t* xs = reinterpret_cast<uint16_t*>(l.k);
+    const int dim = 32 * db + (lane & 31);
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) {
+      const int pb = 16 * mt + 4 * (lane >> 5);     // row within the group, element e < 4
+      const float4 s0 = *reinterpret_cast<const float4*>(&l.scale[pb]);
+      const float4 s1 = *reinterpret_cast<const float4*>(&l.scale[pb + 8]);
+      const float scl[8] = {s0.x, s0.y, s0.z, s0.w, s1.x, s1.y, s1.z, s1.w};
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const int pair = p0 + pb + 8 * (e >> 2) + (e & 3);
+        xs[(pair >> 3) * kXsStride + (pair & 7) * kD + dim] = f32_to_bf16((acc[mt][e] + acc[mt][e + 8]) * scl[e]);
+      }
+    }
+  }
+  __syncthreads();
+  DSA_MARK(trace, 5);
+}
+
+// Step 5 for the 128 / G output columns (128 / G) cb .. + 128 / G - 1 (W_o row blocks
+// (8 / G) cb + mt) and the token group tg.  Returns, for thread tid < 128, the sum of
+// column row (128 / G) cb + tid / G for token G tg + tid % G (sixteen wave partials in
+// wave order; W8A8: dequantised with the token's activation scale and wsv, the scale of
+// that W_o row).
+template <int G, bool F8>
+DSA_DEV float oproj_group(int tid, const Lds& l, int tg, const WoFrags<F8> (&wf)[8 / G], float wsv) {
+  constexpr int NMT = 8 / G;                       // W_o row tiles of 16
+  constexpr int Kw = kOK / kWaves;
+  constexpr int XQS = kOK + 16;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int kw0 = wave * Kw;
+  const uint16_t* xs = reinterpret_cast<const uint16_t*>(l.k);
+  uint8_t* xq = l.v;
+  if constexpr (F8) {
+    // per-token quantisation of the group's attention output: threads 0 .. 128 G - 1,
+    // token G tg + (tid >> 7), elements 8 (tid & 127) .. +7 (two waves per token)
+    if (tid < 128 * G) {
+      const int t = G * tg + (tid >> 7), kk = (tid & 127) * 8;
+      const uint4 y = *reinterpret_cast<const uint4*>(&xs[t * kXsStride + kk]);
+      const uint32_t y4[4] = {y.x, y.y, y.z, y.w};
+      const float m = row16_max(amax_bf16x8(y4));
+      if ((lane & 15) == 0) l.amax[t][(wave & 1) * 4 + (lane >> 4)] = m;
+    }
+    __syncthreads();
+    if (wave < G) {
+      const int t = G * tg + wave;
+      const float am = wave_max(lane < 8 ? l.amax[t][lane] : 0.0f);
+      if (lane == 0) {
+        l.ainv[t] = am > 0.0f ? 448.0f / am : 1.0f;
+        l.ascale[t] = am > 0.0f ? am / 448.0f : 1.0f;
+      }
+    }
+    __syncthreads();
+    if (tid < 128 * G) {
+      const int t = G * tg + (tid >> 7), kk = (tid & 127) * 8;
+      const uint4 y = *reinterpret_cast<const uint4*>(&xs[t * kXsStride + kk]);
+      const uint32_t y4[4] = {y.x, y.y, y.z, y.w};
+      *reinterpret_cast<uint2*>(xq + t * XQS + kk) = e4m3x8_scaled(y4, l.ainv[t]);
+    }
+    __syncthreads();
+  }
+  float (*red)[16 * NMT][G] = reinterpret_cast<float (*)[16 * NMT][G]>(l.k + kMaxT * kXsStride * 2);
+  {
+    const int tok = lane & 15;
+    const bool mine = tok / G == tg && tok < kMaxT;  // columns of other tokens are zero
+    f32x4_t acc[NMT] = {};
+#pragma unroll
+    for (int j = 0; j < WoFrags<F8>::NU; ++j) {
+      const int unit = 4 * j + (lane >> 4);
+      Frag8 bfr;
+      if (F8) bfr.u = *reinterpret_cast<const uint4*>(xq + (tok & 7) * XQS + kw0 + unit * 16);
+      else bfr.u = *reinterpret_cast<const uint4*>(&xs[(tok & 7) * kXsStride + kw0 + unit * 8]);
+      if (!mine) bfr.u = make_uint4(0u, 0u, 0u, 0u);
+#pragma unroll
+      for (int mt = 0; mt < NMT; ++mt) {
+        if constexpr (F8) {
+          const Frag8 a = wf[mt].f[j];
+          const long a0 = (long)(((uint64_t)a.u.y << 32) | a.u.x), a1 = (long)(((uint64_t)a.u.w << 32) | a.u.z);
+          const long b0 = (long)(((uint64_t)bfr.u.y << 32) | bfr.u.x), b1 = (long)(((uint64_t)bfr.u.w << 32) | bfr.u.z);
+          acc[mt] = __builtin_amdgcn_mfma_f32_16x16x32_fp8_fp8(a0, b0, acc[mt], 0, 0, 0);
+          acc[mt] = __builtin_amdgcn_mfma_f32_16x16x32_fp8_fp8(a1, b1, acc[mt], 0, 0, 0);
+        } else {
+          acc[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wf[mt].f[j].v, bfr.v, acc[mt], 0, 0, 0);
+        }
+      }
+    }
+    if (mine) {
+#pragma unroll
+      for (int mt = 0; mt < NMT; ++mt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) red[wave][16 * mt + 4 * (lane >> 4) + i][tok % G] = acc[mt][i];
+    }
+  }
+  __syncthreads();
+  float v = 0.0f;
+  if (tid < 128) {
+    const int r = tid / G, c = tid % G;
+    v = red[0][r][c];
+#pragma unroll
+    for (int w = 1; w < kWaves; ++w) v += red[w][r][c];
+    if (F8) v *= l.ascale[G * tg + c] * wsv;
+  }
+  return v;
+}
+
 }  // namespace swa
 }  // namespace dsa

@@ -539,6 +539,7 @@ DSA_DEV bool proj_body(int tid, const ProjParams& p, const ProjLayer& lp, int b,
       }
     }
   }
+  DSA_MARK(trace, 8);
   if (bi.seg != 4) return xok;
   // k_I: the last k_I block quantises the new rows (e4m3, per-row scale amax/448)
   vm_wait_all();

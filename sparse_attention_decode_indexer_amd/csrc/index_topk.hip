@@ -53,11 +53,11 @@ indexer_scores_kernel(const uint16_t* __restrict__ q_idx, const float* __restric
   }
 }
 
-template <int SRC, int KDT, int RTW>
+template <int SRC, int KDT, int RTW, bool SINGLE>
 __global__ void __launch_bounds__(kSelThreads, 1) select_kernel(SelParams p) {
   __shared__ SelShared sh;
   uint32_t epoch;
-  select_body<SRC, KDT, RTW>(p, sh, epoch);
+  select_body<SRC, KDT, RTW, SINGLE>(p, sh, epoch);
 }
 
 // ----------------------------------------------------------------------------- host launchers
@@ -103,15 +103,18 @@ extern "C" void dsa_trace_set(void* buf) { g_trace = static_cast<uint64_t*>(buf)
 uint64_t* dsa_trace_buffer() { return g_trace; }
 #endif
 
-static void* select_fn(int src, int kdt, int T) {
+static void* select_fn(int src, int kdt, int T, bool single) {
+  // one token over the whole context in one workgroup
+  if (single) return src == 1 ? (void*)select_kernel<1, 0, 1, true>
+                    : kdt == 0 ? (void*)select_kernel<0, 0, 1, true> : (void*)select_kernel<0, 1, 1, true>;
   // every wave scores all ceil(T/2) row tiles of its key tiles
   const int rt = row_tiles(T);
-  if (src == 1) return (void*)select_kernel<1, 0, 1>;
+  if (src == 1) return (void*)select_kernel<1, 0, 1, false>;
   if (kdt == 0)
-    return rt == 1 ? (void*)select_kernel<0, 0, 1> : rt == 2 ? (void*)select_kernel<0, 0, 2>
-         : rt == 3 ? (void*)select_kernel<0, 0, 3> : (void*)select_kernel<0, 0, 4>;
-  return rt == 1 ? (void*)select_kernel<0, 1, 1> : rt == 2 ? (void*)select_kernel<0, 1, 2>
-       : rt == 3 ? (void*)select_kernel<0, 1, 3> : (void*)select_kernel<0, 1, 4>;
+    return rt == 1 ? (void*)select_kernel<0, 0, 1, false> : rt == 2 ? (void*)select_kernel<0, 0, 2, false>
+         : rt == 3 ? (void*)select_kernel<0, 0, 3, false> : (void*)select_kernel<0, 0, 4, false>;
+  return rt == 1 ? (void*)select_kernel<0, 1, 1, false> : rt == 2 ? (void*)select_kernel<0, 1, 2, false>
+       : rt == 3 ? (void*)select_kernel<0, 1, 3, false> : (void*)select_kernel<0, 1, 4, false>;
 }
 
 // Workgroups `fn` can hold resident at once on the device (blocks per CU x CUs).  Test
@@ -131,9 +134,9 @@ hipError_t resident_capacity(const void* fn, int threads, int num_cu, int64_t* c
 }
 
 hipError_t select_check_resident(int src, int kdt, int T, int64_t L, int64_t pos0, int k, int num_cu) {
-  const SelGeometry g = select_geometry(T, L, pos0, k, num_cu);
+  const SelGeometry g = select_geometry(T, L, pos0, k, num_cu, select_single_max(src, kdt));
   int64_t cap = 0;
-  hipError_t e = resident_capacity(select_fn(src, kdt, T), kSelThreads, num_cu, &cap);
+  hipError_t e = resident_capacity(select_fn(src, kdt, T, g.single), kSelThreads, num_cu, &cap);
   if (e != hipSuccess) return e;
   return cap < g.nwg ? hipErrorCooperativeLaunchTooLarge : hipSuccess;
 }
@@ -142,7 +145,7 @@ hipError_t launch_select(int src, const void* q_idx, const float* w_idx, const v
                          const float* k_scale, int kdt, const float* scores, int64_t ld, int T,
                          int64_t L, int64_t pos0, int k, int32_t* idx, int32_t* count, void* ctlp,
                          void* data, int num_cu, hipStream_t st) {
-  SelGeometry g = select_geometry(T, L, pos0, k, num_cu);
+  SelGeometry g = select_geometry(T, L, pos0, k, num_cu, select_single_max(src, kdt));
   SelParams p{};
   p.q_idx = static_cast<const uint16_t*>(q_idx);
   p.w_idx = w_idx;
@@ -169,7 +172,7 @@ hipError_t launch_select(int src, const void* q_idx, const float* w_idx, const v
   p.tauv = reinterpret_cast<uint64_t*>(w8 + (size_t)kMaxT * kMaxWG * 8);
   p.cand = reinterpret_cast<uint64_t*>(w8 + (size_t)kMaxT * kMaxWG * 16);
   void* args[] = {&p};
-  void* fn = select_fn(src, kdt, T);
+  void* fn = select_fn(src, kdt, T, g.single);
   // every workgroup must be resident at once (one per CU by the LDS footprint)
   int64_t cap = 0;
   hipError_t e = resident_capacity(fn, kSelThreads, num_cu, &cap);

@@ -588,6 +588,32 @@ DSA_DEV void resolve_regs(const SelParams& p, int t, SelShared& sh, const uint64
   __syncthreads();
 }
 
+// Selection for a launch of one workgroup that holds every score of its single token
+// (row 0 of the chunk scores): every visible score is a candidate, in position order --
+// the candidates, and so the selection, of the path over several workgroups -- built in
+// LDS rows 4-5, with the radix histogram and scratch in rows 2-3, then the register
+// select.
+static_assert(2 * kMaxChunk * 4 >= (4096 + 64 + 16) * 4 && 2 * kMaxChunk * 4 >= kMaxChunk * 8, "single-workgroup LDS use");
+DSA_DEV void resolve_local(const SelParams& p, SelShared& sh, int nkeys) {
+  const int tid = threadIdx.x;
+  uint32_t* hist = reinterpret_cast<uint32_t*>(&sh.sc[2][0]);          // [4096] + [64] bin list
+  uint32_t* misc = hist + 4096 + 64;
+  uint64_t* lc = reinterpret_cast<uint64_t*>(&sh.sc[4][0]);            // [nc] (position, key)
+  const int64_t vis = p.pos0 + 1;
+  const uint32_t nc = (uint32_t)(vis < nkeys ? vis : nkeys);
+  const uint32_t kk = (uint32_t)p.k < nc ? (uint32_t)p.k : nc;
+  uint32_t kmin = 0xffffffffu, kmax = 0u;
+  for (int b2 = tid; b2 < 4096; b2 += kSelThreads) hist[b2] = 0u;
+  for (uint32_t g = tid; g < nc; g += kSelThreads) {
+    const uint32_t key = order_key(sh.sc[0][g]);
+    lc[g] = ((uint64_t)g << 32) | key;
+    kmin = min(kmin, key);
+    kmax = max(kmax, key);
+  }
+  __syncthreads();
+  resolve_regs<8>(p, 0, sh, lc, nc, kk, kmin, kmax, hist, misc);
+}
+
 // Exact selection of the kk best candidates of token t.  Runs in one workgroup after
 // every workgroup has published its candidates (after the second grid barrier).
 // Candidates arrive in position order; the selection is: every key above the cut key
@@ -899,7 +925,7 @@ DSA_DEV void resolve_token(const SelParams& p, int t, SelShared& sh, uint32_t ep
 // The selection of one launch (all phases; workgroup t < T resolves token t).  Returns
 // false, having written empty selections, when the workspace's error word was already
 // set; otherwise true, with this launch's counter in `epoch_out` (slot tag = epoch + 1).
-template <int SRC, int KDT, int RTW>
+template <int SRC, int KDT, int RTW, bool SINGLE = false>
 DSA_DEV bool select_body(const SelParams& p, SelShared& sh, uint32_t& epoch_out) {
   static_assert(RTW >= 1 && RTW <= 4, "a wave holds one to four row tiles");
   const int tid = threadIdx.x;
@@ -1041,6 +1067,13 @@ DSA_DEV bool select_body(const SelParams& p, SelShared& sh, uint32_t& epoch_out)
     return false;
   }
   if (wg >= T) DSA_MARK_CLK(p.trace, 13);     // core clock over P1 (profiling builds)
+  if constexpr (SINGLE) {
+    // one token, the whole context in this workgroup: select on chip.  The launch counter
+    // still advances once (the workgroup has read it), as every selection launch does.
+    if (tid == 0) ast(p.ctl + ctl::kEpoch, next_epoch(epoch));
+    resolve_local(p, sh, nkeys);
+    return true;
+  }
   // ---------------- tau bound.  Any split of the chunk's (visible) scores into at least
   // m non-empty groups gives one: the m-th largest group maximum is <= the m-th largest
   // score.  Computed scores use 64 groups per token: the keys at one position mod 32

@@ -6,6 +6,10 @@
 // whose chunk lies wholly before pos0 hold only keys visible to every token; each of
 // them publishes a lower bound of its m-th largest score with m * n_part >= min(k, L),
 // so at least k scores lie at or above the smallest published bound.
+// A single token whose whole context is short (T = 1, L <= single_max <= kMaxChunk) takes
+// one workgroup that holds every score and selects on chip, without a bound or any
+// hand-off.  One CU then streams every key alone, so single_max depends on the bytes per
+// key: select_single_max gives it per score source.
 #pragma once
 #include <stdint.h>
 
@@ -23,10 +27,26 @@ struct SelGeometry {
   int n_part;   // workgroups [0, n_part) publish a tau bound
   int m;        // tau rank (0: no bound)
   bool fits;    // chunk fits LDS and nwg fits the count arrays
+  bool single;  // one workgroup holds the whole context (T = 1, L <= single_max)
 };
 
-inline SelGeometry select_geometry(int T, int64_t L, int64_t pos0, int k, int num_cu) {
+// Longest context selected by one workgroup: src 1 = materialised fp32 scores, else the
+// indexer keys' storage (kdt 0 = bf16 rows of 128 bytes, 1 = e4m3 rows of 64 bytes plus
+// a scale).  Measured on MI355X: one workgroup beats the hand-off between workgroups up to
+// about 400 KB of keys; 0 turns the mode off.
+inline int64_t select_single_max(int src, int kdt) { return src == 1 || kdt == 1 ? kMaxChunk : 3072; }
+
+inline SelGeometry select_geometry(int T, int64_t L, int64_t pos0, int k, int num_cu, int64_t single_max) {
   SelGeometry g{};
+  if (T == 1 && L >= 1 && L <= single_max && L <= kMaxChunk) {
+    g.chunk = (int)((L + kSelThreads - 1) / kSelThreads * kSelThreads);
+    g.nwg = 1;
+    g.n_part = 0;
+    g.m = 0;
+    g.fits = true;
+    g.single = true;
+    return g;
+  }
   const int64_t per = (L + num_cu - 1) / num_cu;
   int64_t chunk = ((per + kSelThreads - 1) / kSelThreads) * kSelThreads;
   if (chunk < kSelThreads) chunk = kSelThreads;
@@ -48,9 +68,10 @@ inline SelGeometry select_geometry(int T, int64_t L, int64_t pos0, int k, int nu
 inline int64_t select_max_context(int num_cu) { return (int64_t)num_cu * kMaxChunk; }
 
 // candidate slots of a selection workspace sized for (T, L): one chunk per (token,
-// workgroup) for the largest block, so any pos0 and T <= kSelMaxT fit
+// workgroup) for the largest block, so any pos0 and T <= kSelMaxT fit (the geometry over
+// several workgroups: a single-workgroup launch uses no candidate slots)
 inline int64_t select_candidate_slots(int T, int64_t L, int k, int num_cu) {
-  const SelGeometry g = select_geometry(T, L, L - T, k, num_cu);
+  const SelGeometry g = select_geometry(T, L, L - T, k, num_cu, 0);
   return (int64_t)kSelMaxT * g.nwg * g.chunk;
 }
 

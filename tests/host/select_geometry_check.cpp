@@ -21,15 +21,19 @@ static long cases = 0;
     }                                                                        \
   } while (0)
 
-static void check(int T, int64_t L, int64_t pos0, int k, int ncu) {
+static void check(int T, int64_t L, int64_t pos0, int k, int ncu, int64_t single_max) {
   ++cases;
-  const SelGeometry g = select_geometry(T, L, pos0, k, ncu);
-  const SelGeometry gw = select_geometry(T, L, L - T, k, ncu);   // the geometry the workspace is sized for
+  const SelGeometry g = select_geometry(T, L, pos0, k, ncu, single_max);
+  const SelGeometry gw = select_geometry(T, L, L - T, k, ncu, single_max);   // the same block at its last position
   const int64_t ld = (L + 3) / 4 * 4;
   CHECK(g.chunk % kSelThreads == 0 && g.chunk >= kSelThreads, "T=%d L=%lld chunk=%d", T, (long long)L, g.chunk);
   CHECK((int64_t)g.nwg * g.chunk >= L && g.nwg >= T, "T=%d L=%lld nwg=%d", T, (long long)L, g.nwg);
   CHECK(g.chunk == gw.chunk && g.nwg == gw.nwg, "geometry depends on pos0: T=%d L=%lld", T, (long long)L);
   if (L <= select_max_context(ncu)) CHECK(g.fits, "T=%d L=%lld ncu=%d does not fit", T, (long long)L, ncu);
+  // one workgroup holding the whole context exactly when T = 1 and L <= single_max (and
+  // one chunk): its scores, candidates and histogram stay in LDS (static_asserts there)
+  CHECK(g.single == (T == 1 && L <= single_max && L <= kMaxChunk), "single T=%d L=%lld", T, (long long)L);
+  if (g.single) CHECK(g.nwg == 1 && g.m == 0 && g.chunk >= L && g.chunk <= kMaxChunk, "single geometry L=%lld", (long long)L);
   // tau: participating chunks lie wholly before pos0 and together hold >= min(k, L) bounds
   if (g.m > 0) {
     const int64_t kmax = k < L ? k : L;
@@ -80,14 +84,16 @@ int main() {
         if (T > L) continue;
         for (int k : ks) {
           const int64_t p[3] = {L - T, 0, (L - T) / 2};
-          for (int64_t pos0 : p) check(T, L, pos0, k, ncu);
+          for (int64_t pos0 : p)
+            for (int64_t sm : {(int64_t)0, select_single_max(0, 0), select_single_max(0, 1), select_single_max(1, 0)})
+              check(T, L, pos0, k, ncu, sm);
         }
       }
     }
     for (int64_t L : {(int64_t)65536, (int64_t)262144, (int64_t)1048576, (int64_t)ncu * kMaxChunk,
                       (int64_t)ncu * kMaxChunk - 1})
       for (int T : {1, 7, 8})
-        for (int k : {1, 2048}) check(T, L, L - T, k, ncu);
+        for (int k : {1, 2048}) check(T, L, L - T, k, ncu, select_single_max(0, 1));
   }
   printf("%s: %ld cases, %d failures\n", fails ? "FAILED" : "ok", cases, fails);
   return fails ? 1 : 0;

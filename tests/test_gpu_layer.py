@@ -118,7 +118,9 @@ def _check_dsa_output(dsa, g, lay, x, T, pos0, top_k, sink=None, w8=None):
     return tf
 
 
-@pytest.mark.parametrize("L,T,top_k", [(3000, 8, 2048), (40000, 8, 2048), (777, 3, 64)])
+# one decoded token over a short context (4096 and 1500 keys): one selection workgroup
+@pytest.mark.parametrize("L,T,top_k", [(3000, 8, 2048), (40000, 8, 2048), (777, 3, 64), (4096, 1, 2048),
+                                       (1500, 1, 512)])
 def test_dsa_layer_step_stages(dsa, L, T, top_k):
     pos0 = L - T
     lay = synth.layer_inputs("dsa", 0, L, T, seed=L)
@@ -337,7 +339,8 @@ def test_dsa_layer_step_full_context(dsa, w8a8):
 @pytest.mark.parametrize("L,T,top_k,w8a8,sink", [(3000, 8, 2048, False, False), (40000, 8, 2048, True, False),
                                                  (777, 3, 64, False, True), (20000, 1, 2048, False, False),
                                                  (5000, 5, 300, True, True), (9000, 8, 2048, False, True),
-                                                 (1 << 20, 8, 2048, False, True), (1 << 20, 8, 2048, True, False)])
+                                                 (1 << 20, 8, 2048, False, True), (1 << 20, 8, 2048, True, False),
+                                                 (2500, 1, 1024, False, True)])
 def test_persistent_tail_equals_five_launch_composition(dsa, monkeypatch, L, T, top_k, w8a8, sink):
     """The DSA layer with one persistent launch after the selection (attention, split
     merge, output projection; DSA_LAYER_PERSISTENT_TAIL=1) equals the five-launch chain bit

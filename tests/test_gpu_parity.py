@@ -232,6 +232,74 @@ def test_index_topk_matches_materialised_path_and_oracle(dsa, name, L, T, seed, 
         assert np.array_equal(fused, ridx)
 
 
+# One token whose context fits one workgroup's chunk (L <= 4096) is selected by a single
+# workgroup without any hand-off; L = 4097 is the first length over several workgroups.
+SINGLE_L = [1, 2, 33, 511, 512, 513, 2047, 2048, 2049, 3000, 4095, 4096, 4097]
+
+
+@pytest.mark.parametrize("L", SINGLE_L)
+@pytest.mark.parametrize("k,gen", [(2048, "normal"), (7, "ints"), (300, "ties"), (1, "equal")])
+def test_topk_single_token_short_context(dsa, L, k, gen):
+    g = np.random.default_rng(L * 31 + k)
+    if gen == "normal":
+        s = g.standard_normal((1, L)).astype(np.float32)
+    elif gen == "ints":
+        s = g.integers(-2, 3, (1, L)).astype(np.float32)
+    elif gen == "ties":
+        s = _with_cut_ties(g, g.random((1, L)), min(k, max(1, L - 1)), min(9, max(0, L - 1))) if L > 1 else \
+            np.zeros((1, 1), np.float32)
+    else:
+        s = np.where(g.random((1, L)) < 0.5, -0.0, 0.0).astype(np.float32)
+    idx, cnt = _gpu_topk(dsa, s, L - 1, k)
+    ridx, rcnt = O.topk_indices(s.astype(np.float64), L - 1, k)
+    assert np.array_equal(cnt, rcnt)
+    assert np.array_equal(idx, ridx)
+
+
+@pytest.mark.parametrize("L", SINGLE_L)
+@pytest.mark.parametrize("k,tie", [(2048, False), (2048, True), (100, False), (1, True)])
+def test_index_topk_single_token_short_context(dsa, L, k, tie):
+    """Integer-valued bf16 indexer inputs (exact scores): the fused selection of one token
+    equals the oracle's bit for bit, tie order included (one workgroup up to 3072 keys of
+    bf16, several beyond)."""
+    inp = synth.dsa_config("tiny", seed=L, L=L, T=1, tie_stress=tie)
+    idx = torch.full((1, k), -7, dtype=torch.int32, device=DEV)
+    cnt = torch.full((1,), -7, dtype=torch.int32, device=DEV)
+    ws = dsa.workspace(dsa.WS_INDEX_TOPK, 1, L, k)
+    dsa.dsa_index_topk(up(inp.q_idx), up(inp.w_idx), up(inp.k_idx), None, dsa.BF16, 1, L, inp.pos0, k, idx, cnt,
+                       ws)
+    torch.cuda.synchronize()
+    r, _ = _oracle_scores(inp)
+    ridx, rcnt = O.topk_indices(r, inp.pos0, k)
+    assert np.array_equal(down(cnt), rcnt)
+    assert np.array_equal(down(idx), ridx)
+    assert dsa.dsa_workspace_status(ws) == 0
+
+
+@pytest.mark.parametrize("L", SINGLE_L)
+@pytest.mark.parametrize("k", [2048, 64])
+def test_index_topk_single_token_short_context_fp8(dsa, L, k):
+    """e4m3 indexer keys (one workgroup up to 4096 keys): the fused selection equals top-k
+    of the GPU's own materialised scores bit for bit and the oracle's within the rounding
+    band."""
+    inp = synth.dsa_config("verify256k_fp8", seed=L, L=L, T=1)
+    idx = torch.full((1, k), -7, dtype=torch.int32, device=DEV)
+    cnt = torch.full((1,), -7, dtype=torch.int32, device=DEV)
+    ws = dsa.workspace(dsa.WS_INDEX_TOPK, 1, L, k)
+    dsa.dsa_index_topk(up(inp.q_idx), up(inp.w_idx), up(inp.k_idx), up(inp.k_idx_scale), dsa.FP8_E4M3, 1, L,
+                       inp.pos0, k, idx, cnt, ws)
+    torch.cuda.synchronize()
+    fused = down(idx)
+    g = _gpu_scores(dsa, inp)
+    ridx_same, rcnt = O.topk_indices(g.astype(np.float64), inp.pos0, k)
+    assert np.array_equal(fused, ridx_same)
+    assert np.array_equal(down(cnt), rcnt)
+    r, S = _oracle_scores(inp)
+    ridx, _ = O.topk_indices(r, inp.pos0, k)
+    ok, ndiff = tie_band_ok(fused, ridx, r, S, inp.pos0, k)
+    assert ok, f"selection differs outside the rounding band ({ndiff})"
+
+
 def test_index_topk_full_context_planted(dsa):
     inp = synth.dsa_config("verify1m", seed=0)
     T, L, k = inp.T, inp.L, inp.top_k

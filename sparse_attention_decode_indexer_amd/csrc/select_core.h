@@ -1029,6 +1029,17 @@ DSA_DEV bool select_body(const SelParams& p, SelShared& sh, uint32_t& epoch_out)
             acc = nxt;
           }
         }
+        // Issue order of the block's tiles (four row tiles): every MFMA is followed by up to
+        // five vector instructions, so one row tile's epilogue issues under the next row
+        // tile's matrix work.  Left to itself the compiler issues the first eight MFMAs of a
+        // tile back to back; this interleave measured 0.6 us faster per launch at 1M keys.
+        if constexpr (RTW == 4) {
+#pragma unroll
+          for (int g = 0; g < (4 + 4 * RTW) * PF; ++g) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // one MFMA
+            __builtin_amdgcn_sched_group_barrier(0x002, 5, 0);   // then up to five vector ALU
+          }
+        }
       }
     }
   } else {

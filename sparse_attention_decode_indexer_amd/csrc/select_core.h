@@ -386,6 +386,41 @@ constexpr int kTauBits = 16;
 constexpr int kRegPer = 16;                                  // candidates per lane
 constexpr uint32_t kRegCands = kSelThreads * kRegPer;        // register-resident limit
 
+// Boundary digit of a radix pass, by one wave: the largest digit d of the 4096-bin
+// histogram with count(digit >= d) >= need (1 <= need <= the histogram's total).  Lane l
+// sums bins [64 l, 64 l + 64) (reading its 16-byte chunks in a lane-rotated order, so the
+// lanes of one read hit different banks); a scan over the lanes finds the lane range
+// holding d, then one bin per lane of that range.  Writes d, the count of keys in digits
+// above d and the count of digit d to misc[0..2], and clears misc[4] (the small-bin list
+// counter).
+DSA_DEV void radix_digit_wave(const uint32_t* hist, uint32_t need, uint32_t* misc) {
+  const int lane = threadIdx.x & 63;
+  const uint4* hp = reinterpret_cast<const uint4*>(hist + 64 * lane);
+  uint32_t s = 0u;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    const uint4 q = hp[(i + lane) & 15];
+    s += (q.x + q.y) + (q.z + q.w);
+  }
+  const uint32_t inc = wave_incl_scan(s);
+  const uint32_t above = (uint32_t)__builtin_amdgcn_readlane((int)inc, 63) - inc;   // bins of higher lanes
+  // lanes whose range lies wholly below the boundary have `above` >= need; the first lane
+  // with above < need holds d (the last lane always qualifies: above = 0)
+  const int L = __builtin_amdgcn_readfirstlane(__builtin_ctzll(__ballot(above < need)));
+  const uint32_t sl = (uint32_t)__builtin_amdgcn_readlane((int)above, L);
+  const uint32_t h = hist[64 * L + lane];
+  const uint32_t pre = wave_incl_scan(h);
+  const uint32_t suf = (uint32_t)__builtin_amdgcn_readlane((int)pre, 63) - pre + h;          // bins >= this lane's
+  // the largest digit of the range whose count from it upward reaches need
+  const int dl = 63 - __builtin_clzll(__ballot(sl + suf >= need));
+  if (lane == dl) {
+    misc[0] = (uint32_t)(64 * L + dl);
+    misc[1] = sl + suf - h;
+    misc[2] = h;
+    misc[4] = 0u;
+  }
+}
+
 // Register-resident tail of the selection for nc <= kRegCands candidates already in LDS
 // (position order): wave w holds elements [w*R, (w+1)*R) as NB 64-element blocks (lane
 // = element), so ballots give position-ordered ranks.  Radix passes histogram the
@@ -441,31 +476,14 @@ DSA_DEV void resolve_regs(const SelParams& p, int t, SelShared& sh, const uint64
         if (((uint32_t)i < nmine) & ((key & pmask) == known)) atomicAdd(&hist[(key >> lo) & (nb - 1u)], 1u);
       }
       __syncthreads();
-      // largest digit d with count(digit >= d) >= need
-      constexpr int PER = 4096 / kSelThreads;
-      const int rb = kSelThreads - 1 - tid;           // reversed thread order
-      uint32_t loc = 0;
-#pragma unroll
-      for (int i = 0; i < PER; ++i) loc += hist[rb * PER + i];
-      uint32_t tot;
-      const uint32_t above = block_excl_scan<kSelThreads>(loc, sh.scan, &tot);
-      uint32_t run_c = above;
-#pragma unroll
-      for (int i = PER - 1; i >= 0; --i) {
-        const uint32_t h = hist[rb * PER + i];
-        if (run_c < need && run_c + h >= need) {
-          misc[0] = (uint32_t)(rb * PER + i);
-          misc[1] = run_c;
-        }
-        run_c += h;
-      }
+      // the boundary digit, found by wave 0 alone while the other waves wait at one barrier
+      if (wave == 0) radix_digit_wave(hist, need, misc);
       __syncthreads();
       const uint32_t d = misc[0];
       need -= misc[1];
       known |= d << lo;
       hi = lo;
-      const uint32_t in_bin = hist[d];
-      __syncthreads();
+      const uint32_t in_bin = misc[2];
       if (hi == 0) all_eq = need == in_bin;   // the last digit fixed every bit
       if (need == in_bin && hi > 0) {
         // the whole boundary bin is taken: the cut is its smallest key
@@ -481,15 +499,14 @@ DSA_DEV void resolve_regs(const SelParams& p, int t, SelShared& sh, const uint64
         all_eq = true;
         hi = 0;
       } else if (hi > 0 && in_bin <= 64u) {
-        // small boundary bin: gather its keys (any order) and let wave 0 take the
-        // need-th largest; `need` then counts the keys equal to it that are taken
-        if (tid == 0) misc[2] = 0u;
-        __syncthreads();
+        // small boundary bin: gather its keys (any order; misc[4] was cleared with the
+        // digit) and let wave 0 take the need-th largest; `need` then counts the keys
+        // equal to it that are taken
         const uint32_t pm = ~((1u << hi) - 1u);
 #pragma unroll
         for (int i = 0; i < NB; ++i) {
           const uint32_t key = (uint32_t)e[i];
-          if (((uint32_t)i < nmine) & ((key & pm) == known)) binl[atomicAdd(&misc[2], 1u)] = key;
+          if (((uint32_t)i < nmine) & ((key & pm) == known)) binl[atomicAdd(&misc[4], 1u)] = key;
         }
         __syncthreads();
         if (wave == 0) {
@@ -508,8 +525,7 @@ DSA_DEV void resolve_regs(const SelParams& p, int t, SelShared& sh, const uint64
         known = misc[0];
         need = misc[1];
         all_eq = misc[3] != 0u;
-        hi = 0;
-        __syncthreads();
+        hi = 0;                          // misc is not written again in this call
       }
     }
     kstar = known;

@@ -1176,22 +1176,30 @@ DSA_DEV bool select_body(const SelParams& p, SelShared& sh, uint32_t& epoch_out)
     const uint64_t lt = (1ull << lane) - 1ull;
     uint32_t off = 0;
     int s0 = 0;
-    // batches of 8 wholly visible segments: one compare per segment decides
+    // batches of 512 wholly visible positions: lane l takes positions 8 l .. 8 l + 7 of the
+    // batch, counts its candidates, and a wave scan of the counts gives each lane its first
+    // slot, so the candidates leave in position order from one short loop over each lane's
+    // own candidates (a branch per 64-position segment cost more than the work it skipped)
     for (; s0 + 8 <= nfull; s0 += 8) {
-      float v[8];
+      const float* rb = row + s0 * 64 + 8 * lane;
+      const float4 a0 = *reinterpret_cast<const float4*>(rb);
+      const float4 a1 = *reinterpret_cast<const float4*>(rb + 4);
+      const float sv[8] = {a0.x, a0.y, a0.z, a0.w, a1.x, a1.y, a1.z, a1.w};
+      uint32_t cm = 0u;
 #pragma unroll
-      for (int u = 0; u < 8; ++u) v[u] = row[(s0 + u) * 64 + lane];
-#pragma unroll
-      for (int u = 0; u < 8; ++u) {
-        const bool q = v[u] >= tauf;
-        const uint64_t m = __ballot(q);
-        if (m != 0ull) {                 // wave-uniform: most segments hold no candidate
-          if (q)
-            ast64(dst + off + (uint32_t)__builtin_popcountll(m & lt),
-                  ((uint64_t)(uint32_t)(c0 + (s0 + u) * 64 + lane) << 32) | order_key(v[u]));
-          off += (uint32_t)__builtin_popcountll(m);
-        }
+      for (int i = 0; i < 8; ++i) cm |= (sv[i] >= tauf ? 1u : 0u) << i;
+      const uint32_t c = (uint32_t)__builtin_popcount(cm);
+      const uint32_t inc = wave_incl_scan(c);
+      const uint32_t tot = (uint32_t)__builtin_amdgcn_readlane((int)inc, 63);
+      uint32_t o = off + inc - c;
+      const uint32_t pb = (uint32_t)(c0 + s0 * 64 + 8 * lane);
+      while (cm != 0u) {
+        const int i = __builtin_ctz(cm);
+        cm &= cm - 1u;
+        ast64(dst + o, ((uint64_t)(pb + (uint32_t)i) << 32) | order_key(rb[i]));
+        ++o;
       }
+      off += tot;
     }
     // the rest, up to the last visible position
     for (; s0 < nloop; s0 += 8) {

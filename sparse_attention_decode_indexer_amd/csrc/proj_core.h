@@ -182,7 +182,7 @@ DSA_DEV bool proj_body(int tid, const ProjParams& p, const ProjLayer& lp, int b,
   uint8_t* const xq = reinterpret_cast<uint8_t*>(&sh.xs[0][0]);
   const int kw0 = wave * Kw;
   const int T = p.T;
-  const int rpw = p.rpw;
+  constexpr int rpw = R8 ? 8 : 16;           // p.rpw (the launch's), known at compile time
   const int lrow = lane & 15;
   BlockInfo bi{};
   int wrow;
@@ -323,7 +323,7 @@ DSA_DEV bool proj_body(int tid, const ProjParams& p, const ProjLayer& lp, int b,
     // j = tid mod 512, of tokens 2u + tid / 512 (u = 0..3).  Per token: squares summed in
     // element pairs per thread; thread partials go through LDS (the activation area, not
     // yet in use) and wave t adds token t's: lane i takes threads 8i .. 8i+7 in order,
-    // then an xor butterfly over the wave.  y = bf16(x * (1 / sqrt(mean + eps)) * gamma).
+    // then an xor butterfly over the wave.  y = bf16((x * gamma) * (1 / sqrt(mean + eps))).
     static_assert(MODE != 0 || (kProjWaves >= kMaxT && NCH * kProjThreads == kMaxT * kRowThreads), "norm layout");
     float* scr = reinterpret_cast<float*>(&sh.xs[0][0]);          // [kMaxT][kRowThreads]
     const int j8 = tid % kRowThreads;
@@ -362,7 +362,15 @@ DSA_DEV bool proj_body(int tid, const ProjParams& p, const ProjLayer& lp, int b,
     DSA_MARK(trace, 7);
     // Rows of tokens >= T hold a copy of token T-1 (clamped loads): their products land
     // in MFMA columns that are never read.
+    // x * gamma is exact in fp32 (a product of two bf16): one dot of the x pair with the
+    // gamma pair whose other half is zero forms it, then one multiply by 1/rms
     const uint32_t g4[4] = {gv.x, gv.y, gv.z, gv.w};
+    bf16x2_t glo[4], ghi[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      glo[q] = __builtin_bit_cast(bf16x2_t, g4[q] & 0x0000ffffu);
+      ghi[q] = __builtin_bit_cast(bf16x2_t, g4[q] & 0xffff0000u);
+    }
 #pragma unroll
     for (int u = 0; u < NCH; ++u) {
       const int t = (tid + u * kProjThreads) / kRowThreads;
@@ -372,8 +380,9 @@ DSA_DEV bool proj_body(int tid, const ProjParams& p, const ProjLayer& lp, int b,
       amx[u] = 0.0f;
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
-        const float y0 = (__uint_as_float(x4[q] << 16) * r) * __uint_as_float(g4[q] << 16);
-        const float y1 = (__uint_as_float(x4[q] & 0xffff0000u) * r) * __uint_as_float(g4[q] & 0xffff0000u);
+        const bf16x2_t xv = __builtin_bit_cast(bf16x2_t, x4[q]);
+        const float y0 = __builtin_amdgcn_fdot2_f32_bf16(xv, glo[q], 0.0f, false) * r;
+        const float y1 = __builtin_amdgcn_fdot2_f32_bf16(xv, ghi[q], 0.0f, false) * r;
         o4[q] = pack_bf16x2(y0, y1);
         if (F8) amx[u] = fmaxf(amx[u], fmaxf(fabsf(y0), fabsf(y1)));
       }

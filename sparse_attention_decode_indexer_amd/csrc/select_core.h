@@ -161,11 +161,16 @@ DSA_DEV void load_qlin_frags(const uint16_t* ql, int rt0, Frag8 (&qf)[4]) {
   }
 }
 
-// Query block staged in LDS: qs [kMaxT][kHI][kDI] bf16 and wsh [kMaxT][kHI] fp32, rows of
+// Staged query rows are padded from 64 to 72 bf16 (144 bytes): the fragment loads of 16
+// heads at one column then fall in distinct banks instead of four.
+constexpr int kQsRow = kDI + 8;
+
+// Query block staged in LDS: qs [kMaxT][kHI][kQsRow] bf16 and wsh [kMaxT][kHI] fp32, rows of
 // tokens >= T zero.  The loaders below read it with the same lane mapping and produce
 // the same values as load_q_frags / load_w / build_qlin.
 template <int RTW>
 DSA_DEV void load_q_frags_lds(const uint16_t* qs, Frag8 (&qa)[RTW][4]) {
+  static_assert(kQsRow % 8 == 0, "16-byte aligned rows");
   const int l = threadIdx.x & 63;
   const int half = l >> 5;
   const int row = l & 31;
@@ -175,7 +180,7 @@ DSA_DEV void load_q_frags_lds(const uint16_t* qs, Frag8 (&qa)[RTW][4]) {
     const int hh = row & 15;
 #pragma unroll
     for (int j = 0; j < 4; ++j)
-      qa[r][j].u = *reinterpret_cast<const uint4*>(qs + (tt * kHI + hh) * kDI + half * 32 + 8 * j);
+      qa[r][j].u = *reinterpret_cast<const uint4*>(qs + (tt * kHI + hh) * kQsRow + half * 32 + 8 * j);
   }
 }
 
@@ -203,7 +208,7 @@ DSA_DEV void build_qlin_lds(const uint16_t* qs, const float* wsh, uint16_t* ql) 
     const int t = i / kDI, d = i % kDI;
     float acc = 0.0f;
 #pragma unroll
-    for (int h = 0; h < kHI; ++h) acc = fmaf(0.5f * wsh[t * kHI + h], bf16_to_f32(qs[(t * kHI + h) * kDI + d]), acc);
+    for (int h = 0; h < kHI; ++h) acc = fmaf(0.5f * wsh[t * kHI + h], bf16_to_f32(qs[(t * kHI + h) * kQsRow + d]), acc);
     const uint16_t hi = f32_to_bf16(acc);
     const float r1 = acc - bf16_to_f32(hi);
     const uint16_t mid = f32_to_bf16(r1);
@@ -979,8 +984,9 @@ DSA_DEV bool select_body(const SelParams& p, SelShared& sh, uint32_t& epoch_out)
     // The block's queries and head weights are staged in LDS (the score area is free
     // until the scan starts); their loads go out first, then the first key tiles (with
     // their row scales), whose latency overlaps the query set-up below.
-    uint16_t* qs = reinterpret_cast<uint16_t*>(&sh.sc[0][0]);        // [kMaxT][kHI][kDI]
-    float* wsh = &sh.sc[1][0];                                        // [kMaxT][kHI]
+    uint16_t* qs = reinterpret_cast<uint16_t*>(&sh.sc[0][0]);        // [kMaxT][kHI][kQsRow]
+    float* wsh = &sh.sc[2][0];                                        // [kMaxT][kHI]
+    static_assert(kMaxT * kHI * kQsRow * 2 <= 2 * kMaxChunk * 4, "padded query block fits two score rows");
     constexpr int QROW = kHI * kDI / 8;                               // uint4 per token
     constexpr int QPER = kMaxT * QROW / kSelThreads;
     static_assert(kMaxT * QROW % kSelThreads == 0 && kMaxT * kHI / 4 <= kSelThreads, "staging split");
@@ -1000,7 +1006,8 @@ DSA_DEV bool select_body(const SelParams& p, SelShared& sh, uint32_t& epoch_out)
 #pragma unroll
     for (int u = 0; u < QPER; ++u) {
       const int i = tid + u * kSelThreads;
-      reinterpret_cast<uint4*>(qs)[i] = (i / QROW < T) ? qv[u] : make_uint4(0u, 0u, 0u, 0u);
+      const int row = i / (kDI / 8), c8 = i % (kDI / 8);                // (token, head) row, 8-element chunk
+      *reinterpret_cast<uint4*>(qs + row * kQsRow + 8 * c8) = (i / QROW < T) ? qv[u] : make_uint4(0u, 0u, 0u, 0u);
     }
     if (tid < kMaxT * kHI / 4)
       reinterpret_cast<float4*>(wsh)[tid] = tw < T ? w4 : make_float4(0.0f, 0.0f, 0.0f, 0.0f);

@@ -336,7 +336,7 @@ struct SelParams {
 };
 
 struct SelShared {
-  float sc[kMaxT][kMaxChunk];        // chunk scores (P1/P2); resolver scratch (P3)
+  alignas(16) float sc[kMaxT][kMaxChunk];   // chunk scores (P1/P2); resolver scratch (P3); 16-byte reads
   float kscale[kMaxChunk];           // row scales of the chunk (e4m3 keys)
   uint16_t ql[3 * kMaxT * kDI];      // linear-part query, three bf16 parts
   uint32_t wcnt[2 * kSelWaves];      // resolver: per-wave counts

@@ -1174,57 +1174,44 @@ DSA_DEV bool select_body(const SelParams& p, SelShared& sh, uint32_t& epoch_out)
     const float tauf = tm ? key_to_float(tm) : -__builtin_inff();
     const int64_t lim64 = p.pos0 + t - c0;
     const int lim = (int)(lim64 < nkeys - 1 ? lim64 : nkeys - 1);      // last visible local index
-    const int nseg = p.chunk / 64;                                        // a multiple of 8
-    const int seg_vis = lim >= 0 ? ((lim >> 6) + 8) & ~7 : 0;            // segments up to lim, rounded to 8
-    const int nloop = seg_vis < nseg ? seg_vis : nseg;
-    const int nfull = (lim + 1) >> 6;                                     // segments wholly visible
     uint64_t* dst = p.cand + ((size_t)t * p.nwg + wg) * p.chunk;
+    // Lane l takes local positions 64 l .. 64 l + 63 (the chunk holds at most 64 x 64):
+    // sixteen 16-byte reads in a lane-rotated order (lanes of different l mod 16 hit
+    // different banks) give a 64-bit mask of its visible scores >= tau, one wave scan of
+    // the lanes' counts gives its first slot, and a short loop stores its candidates, so
+    // they leave in position order.  (The compares are independent, so the pass is short;
+    // a pass over 512-position batches with a wave scan each was bound by the latency of
+    // its dependent steps.)
     const float* row = sh.sc[t];
-    const uint64_t lt = (1ull << lane) - 1ull;
-    uint32_t off = 0;
-    int s0 = 0;
-    // batches of 512 wholly visible positions: lane l takes positions 8 l .. 8 l + 7 of the
-    // batch, counts its candidates, and a wave scan of the counts gives each lane its first
-    // slot, so the candidates leave in position order from one short loop over each lane's
-    // own candidates (a branch per 64-position segment cost more than the work it skipped)
-    for (; s0 + 8 <= nfull; s0 += 8) {
-      const float* rb = row + s0 * 64 + 8 * lane;
-      const float4 a0 = *reinterpret_cast<const float4*>(rb);
-      const float4 a1 = *reinterpret_cast<const float4*>(rb + 4);
-      const float sv[8] = {a0.x, a0.y, a0.z, a0.w, a1.x, a1.y, a1.z, a1.w};
-      uint32_t cm = 0u;
+    const int pb = 64 * lane;
+    const int nv = lim + 1 - pb;                                          // visible positions of this lane
+    uint32_t mlo = 0u, mhi = 0u;
+    if (nv > 0) {
+      const float4* r4 = reinterpret_cast<const float4*>(row + pb);
 #pragma unroll
-      for (int i = 0; i < 8; ++i) cm |= (sv[i] >= tauf ? 1u : 0u) << i;
-      const uint32_t c = (uint32_t)__builtin_popcount(cm);
-      const uint32_t inc = wave_incl_scan(c);
-      const uint32_t tot = (uint32_t)__builtin_amdgcn_readlane((int)inc, 63);
-      uint32_t o = off + inc - c;
-      const uint32_t pb = (uint32_t)(c0 + s0 * 64 + 8 * lane);
-      while (cm != 0u) {
-        const int i = __builtin_ctz(cm);
-        cm &= cm - 1u;
-        ast64(dst + o, ((uint64_t)(pb + (uint32_t)i) << 32) | order_key(rb[i]));
-        ++o;
+      for (int c = 0; c < 16; ++c) {
+        const int cc = (c + lane) & 15;
+        const float4 v = r4[cc];
+        const uint32_t nib = (v.x >= tauf ? 1u : 0u) | (v.y >= tauf ? 2u : 0u) | (v.z >= tauf ? 4u : 0u) |
+                             (v.w >= tauf ? 8u : 0u);
+        if (cc < 8) mlo |= nib << (4 * cc);
+        else mhi |= nib << (4 * (cc - 8));
       }
-      off += tot;
+      if (nv < 64) {                                                      // drop positions past lim
+        if (nv <= 32) { mlo &= nv == 32 ? 0xffffffffu : ((1u << nv) - 1u); mhi = 0u; }
+        else mhi &= (1u << (nv - 32)) - 1u;
+      }
     }
-    // the rest, up to the last visible position
-    for (; s0 < nloop; s0 += 8) {
-      float v[8];
-#pragma unroll
-      for (int u = 0; u < 8; ++u) v[u] = row[(s0 + u) * 64 + lane];
-#pragma unroll
-      for (int u = 0; u < 8; ++u) {
-        const int i = (s0 + u) * 64 + lane;
-        const bool q = (i <= lim) & (v[u] >= tauf);
-        const uint64_t m = __ballot(q);
-        if (m != 0ull) {
-          if (q)
-            ast64(dst + off + (uint32_t)__builtin_popcountll(m & lt),
-                  ((uint64_t)(uint32_t)(c0 + i) << 32) | order_key(v[u]));
-          off += (uint32_t)__builtin_popcountll(m);
-        }
-      }
+    const uint32_t cnt = (uint32_t)__builtin_popcount(mlo) + (uint32_t)__builtin_popcount(mhi);
+    const uint32_t inc = wave_incl_scan(cnt);
+    const uint32_t off = (uint32_t)__builtin_amdgcn_readlane((int)inc, 63);
+    uint32_t o = inc - cnt;
+    while ((mlo | mhi) != 0u) {
+      int i;
+      if (mlo != 0u) { i = __builtin_ctz(mlo); mlo &= mlo - 1u; }
+      else { i = 32 + __builtin_ctz(mhi); mhi &= mhi - 1u; }
+      ast64(dst + o, ((uint64_t)(uint32_t)(c0 + pb + i) << 32) | order_key(row[pb + i]));
+      ++o;
     }
     vm_wait_all();                       // candidates land before their count
     if (lane == 0) ast64(p.cnt + (size_t)t * p.nwg + wg, ((uint64_t)tag << 32) | off);

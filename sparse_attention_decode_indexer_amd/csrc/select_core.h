@@ -1185,7 +1185,7 @@ DSA_DEV bool select_body(const SelParams& p, SelShared& sh, uint32_t& epoch_out)
     const float* row = sh.sc[t];
     const int pb = 64 * lane;
     const int nv = lim + 1 - pb;                                          // visible positions of this lane
-    uint32_t mlo = 0u, mhi = 0u;
+    uint64_t mk = 0ull;
     if (nv > 0) {
       const float4* r4 = reinterpret_cast<const float4*>(row + pb);
 #pragma unroll
@@ -1194,14 +1194,11 @@ DSA_DEV bool select_body(const SelParams& p, SelShared& sh, uint32_t& epoch_out)
         const float4 v = r4[cc];
         const uint32_t nib = (v.x >= tauf ? 1u : 0u) | (v.y >= tauf ? 2u : 0u) | (v.z >= tauf ? 4u : 0u) |
                              (v.w >= tauf ? 8u : 0u);
-        if (cc < 8) mlo |= nib << (4 * cc);
-        else mhi |= nib << (4 * (cc - 8));
+        mk |= (uint64_t)nib << (4 * cc);
       }
-      if (nv < 64) {                                                      // drop positions past lim
-        if (nv <= 32) { mlo &= nv == 32 ? 0xffffffffu : ((1u << nv) - 1u); mhi = 0u; }
-        else mhi &= (1u << (nv - 32)) - 1u;
-      }
+      if (nv < 64) mk &= (1ull << nv) - 1ull;                             // drop positions past lim
     }
+    uint32_t mlo = (uint32_t)mk, mhi = (uint32_t)(mk >> 32);
     const uint32_t cnt = (uint32_t)__builtin_popcount(mlo) + (uint32_t)__builtin_popcount(mhi);
     const uint32_t inc = wave_incl_scan(cnt);
     const uint32_t off = (uint32_t)__builtin_amdgcn_readlane((int)inc, 63);

@@ -328,11 +328,9 @@ constexpr uint64_t kSpinLimit = 20000000ull;   // 0.2 s of the 100 MHz real-time
 // never 0 (the value of a cleared workspace).
 DSA_DEV uint32_t next_epoch(uint32_t e) { return (e + 1u) & 0x7fffffffu; }
 
-// Wave-wide wait for slots[0 .. n) (n >= 1, n <= 64 * N) to carry `tag`; returns the
-// minimum of their values.  A wait longer than kSpinLimit sets the sticky error word and
-// gives up, so a launch whose workgroups are not all resident ends instead of hanging.
 // Wait until one tagged slot carries `tag` and return its value (the wave polls one
-// address: one load per round).
+// address: one load per round).  A wait longer than kSpinLimit sets the sticky error word
+// and gives up, so a launch whose workgroups are not all resident ends instead of hanging.
 DSA_DEV uint32_t wait_tagged_one(const uint64_t* slot, uint32_t tag, uint32_t* ctl_words) {
   uint64_t v = ald64(slot);
   const uint64_t t0 = __builtin_amdgcn_s_memrealtime();
@@ -380,6 +378,9 @@ DSA_DEV bool poll_words(F addr, uint32_t tag, uint32_t (&val)[N], uint32_t* ctl_
   return ok;
 }
 
+// Wave-wide wait for slots[0 .. n) (n >= 1, n <= 64 * N) to carry `tag`; returns the
+// minimum of their values.  After the first round only the slots still without the tag
+// are read again.  Bounded like wait_tagged_one.
 template <int N>
 DSA_DEV uint32_t wait_tagged_min(const uint64_t* slots, int n, uint32_t tag, uint32_t* ctl_words) {
   const int lane = threadIdx.x & 63;
@@ -401,9 +402,9 @@ DSA_DEV uint32_t wait_tagged_min(const uint64_t* slots, int n, uint32_t tag, uin
       break;
     }
 #pragma unroll
-    for (int i = 0; i < N; ++i) {
+    for (int i = 0; i < N; ++i) {        // only the slots still without the tag
       const int w = lane + 64 * i;
-      v[i] = ald64(slots + (w < n ? w : n - 1));
+      if ((uint32_t)(v[i] >> 32) != tag) v[i] = ald64(slots + (w < n ? w : n - 1));
     }
   }
   uint32_t m = 0xffffffffu;

@@ -72,8 +72,16 @@ DSA_DEV void load_key_tile(const uint8_t* __restrict__ kbase, const float* __res
   }
 }
 
+// Rows of a score tile (2 tokens x 16 heads): row m holds token 2r + ((m >> 2) & 1) and
+// head (m & 3) + 4 p(m >> 3) with p = (0, 2, 1, 3).  A lane of half c then receives, as
+// its 16 accumulator elements (rows 8 (e >> 2) + 4 c + (e & 3)), all 16 heads of token
+// 2r + c: elements 0-7 heads 0-3 and 8-11, elements 8-15 heads 4-7 and 12-15.
+DSA_DEV int tile_row_token(int m) { return (m >> 2) & 1; }
+DSA_DEV int tile_row_head(int m) { return (m & 3) + 4 * (((m >> 3) & 1) * 2 + (m >> 4)); }
+
 // A operands of row tiles rt0 .. rt0+RTW-1, k-step j.  Lane l: row (l & 31) -> token
-// 2r + ((l&31)>>4), head (l & 15); dims 32*(l>>5) + 8j .. +8 (the key operand's dims).
+// 2r + tile_row_token(l & 31), head tile_row_head(l & 31); dims 32*(l>>5) + 8j .. +8 (the
+// key operand's dims).
 template <int RTW>
 DSA_DEV void load_q_frags(const uint16_t* __restrict__ q_idx, int T, int rt0, Frag8 (&qa)[RTW][4]) {
   const int l = threadIdx.x & 63;
@@ -81,9 +89,9 @@ DSA_DEV void load_q_frags(const uint16_t* __restrict__ q_idx, int T, int rt0, Fr
   const int row = l & 31;
 #pragma unroll
   for (int r = 0; r < RTW; ++r) {
-    const int tt = 2 * (rt0 + r) + (row >> 4);
+    const int tt = 2 * (rt0 + r) + tile_row_token(row);
     const int tc = tt < T ? tt : T - 1;          // clamped: loads stay unconditional
-    const int hh = row & 15;
+    const int hh = tile_row_head(row);
 #pragma unroll
     for (int j = 0; j < 4; ++j)
       qa[r][j].u = *reinterpret_cast<const uint4*>(q_idx + (tc * kHI + hh) * kDI + half * 32 + 8 * j);
@@ -94,7 +102,7 @@ DSA_DEV void load_q_frags(const uint16_t* __restrict__ q_idx, int T, int rt0, Fr
 }
 
 // Half head weights (w/2) of this lane's accumulator elements.  Element e of the 32x32 output holds
-// row 8*(e>>2) + 4*half + (e&3): token 2r + (e>>3), head 8*((e>>2)&1) + 4*half + (e&3).
+// row m = 8*(e>>2) + 4*half + (e&3): token 2r + half, head tile_row_head(m).
 template <int RTW>
 DSA_DEV void load_w(const float* __restrict__ w_idx, int T, int rt0, float (&wv)[RTW][16]) {
   const int half = (threadIdx.x & 63) >> 5;
@@ -102,8 +110,8 @@ DSA_DEV void load_w(const float* __restrict__ w_idx, int T, int rt0, float (&wv)
   for (int r = 0; r < RTW; ++r) {
 #pragma unroll
     for (int e = 0; e < 16; ++e) {
-      const int tt = 2 * (rt0 + r) + (e >> 3);
-      const int hh = 8 * ((e >> 2) & 1) + 4 * half + (e & 3);
+      const int tt = 2 * (rt0 + r) + half;
+      const int hh = tile_row_head(8 * (e >> 2) + 4 * half + (e & 3));
       const float v = w_idx[(tt < T ? tt : T - 1) * kHI + hh];
       wv[r][e] = (tt < T) ? 0.5f * v : 0.0f;
     }
@@ -176,8 +184,8 @@ DSA_DEV void load_q_frags_lds(const uint16_t* qs, Frag8 (&qa)[RTW][4]) {
   const int row = l & 31;
 #pragma unroll
   for (int r = 0; r < RTW; ++r) {
-    const int tt = 2 * r + (row >> 4);
-    const int hh = row & 15;
+    const int tt = 2 * r + tile_row_token(row);
+    const int hh = tile_row_head(row);
 #pragma unroll
     for (int j = 0; j < 4; ++j)
       qa[r][j].u = *reinterpret_cast<const uint4*>(qs + (tt * kHI + hh) * kQsRow + half * 32 + 8 * j);
@@ -191,8 +199,8 @@ DSA_DEV void load_w_lds(const float* wsh, float (&wv)[RTW][16]) {
   for (int r = 0; r < RTW; ++r) {
 #pragma unroll
     for (int g = 0; g < 4; ++g) {              // elements 4g .. 4g+3: four consecutive heads
-      const int tt = 2 * r + (g >> 1);
-      const int hh = 8 * (g & 1) + 4 * half;
+      const int tt = 2 * r + half;
+      const int hh = tile_row_head(8 * g);
       const float4 v = *reinterpret_cast<const float4*>(wsh + tt * kHI + hh);
       wv[r][4 * g + 0] = 0.5f * v.x;
       wv[r][4 * g + 1] = 0.5f * v.y;
@@ -238,10 +246,10 @@ DSA_DEV float key_to_float(uint32_t k) {
 DSA_DEV float relu_bits(float x) { return __int_as_float(max(__float_as_int(x), 0)); }
 
 // Building blocks of a tile's scores.  Their arithmetic and its order are fixed and the
-// same in every kernel that uses them: per head a = q_h . k (MFMA, fp32); per lane
-// sum_e (w/2)|a_e| over its 8 heads of each token of the row tile, in element order; the
-// two lanes of a (token pair, key) exchange and add; then + ((hi + mid) + lo) of the
-// linear tile; then x the row scale for e4m3 keys.
+// same in every kernel that uses them: per head a = q_h . k (MFMA, fp32); per lane, for
+// its token, sum_e (w/2)|a_e| over heads 0-3, 8-11 and over heads 4-7, 12-15, each in
+// element order, then the two added; then + ((hi + mid) + lo) of the linear tile; then x
+// the row scale for e4m3 keys.
 
 // e4m3 or bf16 key tile -> the four bf16 B operands (e4m3 -> bf16 is exact)
 template <int KDT>
@@ -282,11 +290,9 @@ DSA_DEV float row_score(const f32x16_t& acc, const float (&w)[16], float lin, fl
   for (int e = 0; e < 8; ++e) p0 = fmaf(w[e], fabsf(acc[e]), p0);
 #pragma unroll
   for (int e = 8; e < 16; ++e) p1 = fmaf(w[e], fabsf(acc[e]), p1);
-  // lanes l and l+32 hold the same (token pair, key) over complementary heads: one swap
-  // of p0's upper half with p1's lower half leaves token 2r's two partial sums side by
-  // side in lane l and token 2r+1's in lane l+32.
-  const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(p0), __float_as_uint(p1), false, false);
-  const float tot = __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
+  // the lane holds all 16 heads of one token (the tile's row order): heads 0-3, 8-11 in
+  // p0, heads 4-7, 12-15 in p1
+  const float tot = p0 + p1;
   const float v = tot + lin;
   return (KDT == 1) ? v * scale : v;
 }

@@ -72,6 +72,13 @@ DSA_DEV void load_key_tile(const uint8_t* __restrict__ kbase, const float* __res
   }
 }
 
+// Row scale of this lane's key in the tile at s0 (clamped like the keys)
+DSA_DEV float load_key_scale(const float* __restrict__ kscale, int64_t L, int64_t s0) {
+  int64_t s = s0 + (threadIdx.x & 31);
+  s = s < L ? s : L - 1;
+  return kscale[s];
+}
+
 // Rows of a score tile (2 tokens x 16 heads): row m holds token 2r + ((m >> 2) & 1) and
 // head (m & 3) + 4 p(m >> 3) with p = (0, 2, 1, 3).  A lane of half c then receives, as
 // its 16 accumulator elements (rows 8 (e >> 2) + 4 c + (e & 3)), all 16 heads of token
@@ -1043,7 +1050,7 @@ DSA_DEV bool select_body(const SelParams& p, SelShared& sh, uint32_t& epoch_out)
           const bool keep = j < nmine;
           Frag8 kb[4];
           keys_to_bf16<KDT>(buf[i], kb);
-          load_key_tile<KDT, true>(p.k_idx, p.k_scale, p.L, tile_of(j + PF), buf[i]);
+          load_key_tile<KDT, false>(p.k_idx, p.k_scale, p.L, tile_of(j + PF), buf[i]);
           const f32x16_t lacc = mma_k64(qf, kb);
           f32x16_t acc = mma_k64(qa[0], kb);
           float* row = keep ? &sh.sc[half][sl] : &sh.dump[lane];
@@ -1057,6 +1064,10 @@ DSA_DEV bool select_body(const SelParams& p, SelShared& sh, uint32_t& epoch_out)
             row[r * rstride] = o;
             acc = nxt;
           }
+          // the next scale of this slot is requested once the current one is used up, so
+          // the two never live at once (no copy at the loop's back edge, whose wait would
+          // drain every load in flight)
+          if constexpr (KDT == 1) buf[i].scale = load_key_scale(p.k_scale, p.L, tile_of(j + PF));
         }
         // Issue order of the block's tiles (four row tiles): every MFMA is followed by up to
         // five vector instructions, so one row tile's epilogue issues under the next row

@@ -57,6 +57,13 @@
  *     empty selections and nothing else, until dsa_workspace_init clears it.
  *     (Test hook: the environment variable DSA_RESIDENT_LIMIT=n makes the host check
  *     assume at most n resident workgroups.)
+ *   - Context length.  The selection cuts [0, L) into one chunk per compute unit.  Up to
+ *     4096 keys per chunk every score stays on chip; longer chunks (up to 65536 keys)
+ *     keep the scores past the first 4096 in the workspace, whose size
+ *     (dsa_workspace_bytes) grows by 32 bytes per such key.  The selection is the same
+ *     either way.  (Test hook: the environment variable DSA_NUM_CU=n, n below the
+ *     device's count, cuts the geometry for n compute units; workspaces must then be
+ *     sized with the same setting.)
  */
 #ifndef DSA_H_
 #define DSA_H_
@@ -306,8 +313,10 @@ dsa_status_t dsa_workspace_init(void* ws, size_t ws_bytes, void* stream);
  * stays set until dsa_workspace_init.  Blocking; not for use under graph capture. */
 dsa_status_t dsa_workspace_status(const void* ws, size_t ws_bytes, void* stream);
 
-/* Largest context length L the top-k calls accept on the current device
- * (4096 positions per compute unit: 1,048,576 on a 256-CU MI355X). */
+/* Largest context length L the top-k calls and dsa_layer_step accept on the current
+ * device: 65536 positions per compute unit (16,777,216 on a 256-CU MI355X).  Past 4096
+ * positions per compute unit (1,048,576 on MI355X) part of the scores is kept in the
+ * workspace instead of on chip. */
 int64_t dsa_max_context(void);
 
 const char* dsa_status_string(dsa_status_t s);

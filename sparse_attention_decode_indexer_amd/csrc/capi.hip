@@ -23,13 +23,20 @@ dsa_status_t hip_fail(hipError_t e, const char* what) {
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
+// CUs the launch geometry is cut for.  Test hook: the environment variable DSA_NUM_CU,
+// when set to a positive number below the device's count, stands in for a device with that
+// many CUs (the selection then cuts the context into fewer, longer chunks; residency is
+// still checked against the real device).
 int device_cus() {
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess) { (void)hipGetLastError(); return 256; }
-  int n = 0;
-  if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) {
+  int dev = 0, n = 0;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) {
     (void)hipGetLastError();
-    return 256;
+    n = 256;
+  }
+  if (const char* h = getenv("DSA_NUM_CU")) {
+    const long v = strtol(h, nullptr, 10);
+    if (v > 0 && v < n) n = (int)v;
   }
   return n;
 }

@@ -53,11 +53,11 @@ indexer_scores_kernel(const uint16_t* __restrict__ q_idx, const float* __restric
   }
 }
 
-template <int SRC, int KDT, int RTW, bool SINGLE>
+template <int SRC, int KDT, int RTW, bool SINGLE, bool SPILL = false>
 __global__ void __launch_bounds__(kSelThreads, 1) select_kernel(SelParams p) {
   __shared__ SelShared sh;
   uint32_t epoch;
-  select_body<SRC, KDT, RTW, SINGLE>(p, sh, epoch);
+  select_body<SRC, KDT, RTW, SINGLE, SPILL>(p, sh, epoch);
 }
 
 // ----------------------------------------------------------------------------- host launchers
@@ -89,7 +89,8 @@ hipError_t launch_indexer_scores(const void* q_idx, const float* w_idx, const vo
 // the candidate lists
 size_t select_data_bytes(int T, int64_t L, int k, int num_cu) {
   static_assert(kSelMaxT == kMaxT, "one verify-block limit");
-  return (size_t)kMaxT * kMaxWG * (8 + 8) + (size_t)select_candidate_slots(T, L, k, num_cu) * sizeof(uint64_t);
+  return (size_t)kMaxT * kMaxWG * (8 + 8) + (size_t)select_candidate_slots(T, L, k, num_cu) * sizeof(uint64_t) +
+         (size_t)select_spill_floats(T, L, k, num_cu) * sizeof(float);
 }
 
 size_t select_workspace_bytes(int T, int64_t L, int k, int num_cu) {
@@ -103,10 +104,14 @@ extern "C" void dsa_trace_set(void* buf) { g_trace = static_cast<uint64_t*>(buf)
 uint64_t* dsa_trace_buffer() { return g_trace; }
 #endif
 
-static void* select_fn(int src, int kdt, int T, bool single) {
+static void* select_fn(int src, int kdt, int T, bool single, bool spill) {
   // one token over the whole context in one workgroup
   if (single) return src == 1 ? (void*)select_kernel<1, 0, 1, true>
                     : kdt == 0 ? (void*)select_kernel<0, 0, 1, true> : (void*)select_kernel<0, 1, 1, true>;
+  // chunks longer than kMaxChunk keys (scores partly in the workspace): one instance per
+  // score source, scoring all four row tiles (rows of absent tokens are zero and unused)
+  if (spill) return src == 1 ? (void*)select_kernel<1, 0, 1, false, true>
+                   : kdt == 0 ? (void*)select_kernel<0, 0, 4, false, true> : (void*)select_kernel<0, 1, 4, false, true>;
   // every wave scores all ceil(T/2) row tiles of its key tiles
   const int rt = row_tiles(T);
   if (src == 1) return (void*)select_kernel<1, 0, 1, false>;
@@ -120,11 +125,15 @@ static void* select_fn(int src, int kdt, int T, bool single) {
 // Workgroups `fn` can hold resident at once on the device (blocks per CU x CUs).  Test
 // hook: the environment variable DSA_RESIDENT_LIMIT, when set to a positive number, caps
 // the result, standing in for CUs held by other work.
+// (The CU count is the device's own: a smaller num_cu only shapes the launch geometry.)
 hipError_t resident_capacity(const void* fn, int threads, int num_cu, int64_t* cap) {
   int per_cu = 0;
   hipError_t e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, fn, threads, 0);
   if (e != hipSuccess) return e;
-  int64_t c = (int64_t)per_cu * num_cu;
+  int dev = 0, ncu = 0;
+  if ((e = hipGetDevice(&dev)) != hipSuccess) return e;
+  if ((e = hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev)) != hipSuccess) return e;
+  int64_t c = (int64_t)per_cu * (ncu > num_cu ? ncu : num_cu);
   if (const char* lim = getenv("DSA_RESIDENT_LIMIT")) {
     const long v = strtol(lim, nullptr, 10);
     if (v > 0 && v < c) c = v;
@@ -136,7 +145,7 @@ hipError_t resident_capacity(const void* fn, int threads, int num_cu, int64_t* c
 hipError_t select_check_resident(int src, int kdt, int T, int64_t L, int64_t pos0, int k, int num_cu) {
   const SelGeometry g = select_geometry(T, L, pos0, k, num_cu, select_single_max(src, kdt));
   int64_t cap = 0;
-  hipError_t e = resident_capacity(select_fn(src, kdt, T, g.single), kSelThreads, num_cu, &cap);
+  hipError_t e = resident_capacity(select_fn(src, kdt, T, g.single, g.spill), kSelThreads, num_cu, &cap);
   if (e != hipSuccess) return e;
   return cap < g.nwg ? hipErrorCooperativeLaunchTooLarge : hipSuccess;
 }
@@ -171,8 +180,11 @@ hipError_t launch_select(int src, const void* q_idx, const float* w_idx, const v
   p.cnt = reinterpret_cast<uint64_t*>(w8);
   p.tauv = reinterpret_cast<uint64_t*>(w8 + (size_t)kMaxT * kMaxWG * 8);
   p.cand = reinterpret_cast<uint64_t*>(w8 + (size_t)kMaxT * kMaxWG * 16);
+  // spill rows after this launch's candidate slots (the workspace holds at least that many)
+  p.sstride = g.spill ? (int64_t)g.nwg * (g.chunk - kMaxChunk) : 0;
+  p.spill = g.spill ? reinterpret_cast<float*>(p.cand + (size_t)kSelMaxT * g.nwg * g.chunk) : nullptr;
   void* args[] = {&p};
-  void* fn = select_fn(src, kdt, T, g.single);
+  void* fn = select_fn(src, kdt, T, g.single, g.spill);
   // every workgroup must be resident at once (one per CU by the LDS footprint)
   int64_t cap = 0;
   hipError_t e = resident_capacity(fn, kSelThreads, num_cu, &cap);

@@ -31,6 +31,8 @@
 // independent of tau.  All cross-workgroup arithmetic is integer, so the result is
 // bitwise reproducible.
 #pragma once
+#include <type_traits>
+
 #include "dsa_common.h"
 #include "select_geometry.h"
 
@@ -333,7 +335,7 @@ struct SelParams {
   int k;
   int64_t L;
   int64_t pos0;
-  int chunk;             // keys per workgroup (multiple of 512, <= kMaxChunk)
+  int chunk;             // keys per workgroup (multiple of 512, <= kMaxSpillChunk)
   int nwg;               // workgroups (>= T)
   int m;                 // tau rank; 0 disables tau
   int n_part;            // workgroups [0, n_part) publish tau
@@ -346,6 +348,9 @@ struct SelParams {
   uint64_t* tauv;        // [T][kMaxWG] (launch tag << 32 | tau bound) per workgroup
   uint64_t* cand;        // [T][nwg][chunk] (position << 32 | order key)
   uint64_t* trace;       // profiling builds: [nwg][16] phase timestamps
+  float* spill;          // fused scan with chunk > kMaxChunk: scores of local positions
+                         // >= kMaxChunk, [kMaxT][nwg][chunk - kMaxChunk]
+  int64_t sstride;       // floats between the spill rows of consecutive tokens
 };
 
 struct SelShared {
@@ -959,8 +964,13 @@ DSA_DEV void resolve_token(const SelParams& p, int t, SelShared& sh, uint32_t ep
 // The selection of one launch (all phases; workgroup t < T resolves token t).  Returns
 // false, having written empty selections, when the workspace's error word was already
 // set; otherwise true, with this launch's counter in `epoch_out` (slot tag = epoch + 1).
-template <int SRC, int KDT, int RTW, bool SINGLE = false>
+// SPILL: chunks longer than kMaxChunk keys.  The first kMaxChunk scores of the chunk stay
+// in LDS; the fused scan writes the rest to the workspace's spill rows and the pass that
+// emits candidates reads them from there (loaded scores are read again from the input).
+// Every step is the same, so the selection is the one the exact top-k defines.
+template <int SRC, int KDT, int RTW, bool SINGLE = false, bool SPILL = false>
 DSA_DEV bool select_body(const SelParams& p, SelShared& sh, uint32_t& epoch_out) {
+  static_assert(!(SINGLE && SPILL), "one workgroup holds at most kMaxChunk keys");
   static_assert(RTW >= 1 && RTW <= 4, "a wave holds one to four row tiles");
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -1054,7 +1064,13 @@ DSA_DEV bool select_body(const SelParams& p, SelShared& sh, uint32_t& epoch_out)
           const f32x16_t lacc = mma_k64(qf, kb);
           f32x16_t acc = mma_k64(qa[0], kb);
           float* row = keep ? &sh.sc[half][sl] : &sh.dump[lane];
-          const int rstride = keep ? 2 * kMaxChunk : 0;  // floats between row tiles' rows
+          int rstride = keep ? 2 * kMaxChunk : 0;        // floats between row tiles' rows
+          if constexpr (SPILL) {
+            if (keep && sl >= kMaxChunk) {
+              row = p.spill + (size_t)half * p.sstride + (size_t)wg * (p.chunk - kMaxChunk) + (sl - kMaxChunk);
+              rstride = 2 * (int)p.sstride;                 // < 2^31: nwg * chunk <= kMaxWG * kMaxSpillChunk
+            }
+          }
 #pragma unroll
           for (int r = 0; r < RTW; ++r) {
             f32x16_t nxt = {};
@@ -1103,6 +1119,7 @@ DSA_DEV bool select_body(const SelParams& p, SelShared& sh, uint32_t& epoch_out)
   }
   const uint32_t epoch = (uint32_t)ctlw;
   const uint32_t tag = epoch + 1u;                       // this launch's slot tag
+  if constexpr (SPILL) __threadfence_block();            // spilled scores seen by every wave
   __syncthreads();
   DSA_MARK(p.trace, 2);
   // A workspace whose error word is set (an earlier launch on it gave up waiting) is not
@@ -1153,13 +1170,16 @@ DSA_DEV bool select_body(const SelParams& p, SelShared& sh, uint32_t& epoch_out)
     } else {
       for (int t = wave; t < T; t += kSelWaves) {
         uint32_t g = 0u;
-        for (int i0 = 0; i0 < nkeys; i0 += 512) {
+        // (a longer chunk's bound comes from its first kMaxChunk scores: any subset of
+        // the chunk's scores gives a valid one)
+        const int nkt = SPILL && nkeys > kMaxChunk ? kMaxChunk : nkeys;
+        for (int i0 = 0; i0 < nkt; i0 += 512) {
           float v[8];
 #pragma unroll
           for (int u = 0; u < 8; ++u) v[u] = sh.sc[t][(i0 + u * 64 + lane) & (kMaxChunk - 1)];
 #pragma unroll
           for (int u = 0; u < 8; ++u)
-            if (i0 + u * 64 + lane < nkeys) g = max(g, order_key_fast(v[u]));
+            if (i0 + u * 64 + lane < nkt) g = max(g, order_key_fast(v[u]));
         }
         const uint32_t tw = mth_largest_lanes_top<kTauBits>(g, p.m);
         if (lane == 0) ast64(p.tauv + (size_t)t * kMaxWG + wg, ((uint64_t)tag << 32) | tw);
@@ -1199,33 +1219,54 @@ DSA_DEV bool select_body(const SelParams& p, SelShared& sh, uint32_t& epoch_out)
     // they leave in position order.  (The compares are independent, so the pass is short;
     // a pass over 512-position batches with a wave scan each was bound by the latency of
     // its dependent steps.)
-    const float* row = sh.sc[t];
     const int pb = 64 * lane;
-    const int nv = lim + 1 - pb;                                          // visible positions of this lane
-    uint64_t mk = 0ull;
-    if (nv > 0) {
-      const float4* r4 = reinterpret_cast<const float4*>(row + pb);
+    // candidates among the kMaxChunk local positions sb .. held at `row`, visible up to
+    // local position sb + lims, stored from slot ob on; returns how many
+    auto emit = [&](auto guard, const float* row, int sb, int lims, uint32_t ob) -> uint32_t {
+      const int nv = lims + 1 - pb;                                       // visible positions of this lane
+      uint64_t mk = 0ull;
+      if (nv > 0) {
+        const float4* r4 = reinterpret_cast<const float4*>(row + pb);
 #pragma unroll
-      for (int c = 0; c < 16; ++c) {
-        const int cc = (c + lane) & 15;
-        const float4 v = r4[cc];
-        const uint32_t nib = (v.x >= tauf ? 1u : 0u) | (v.y >= tauf ? 2u : 0u) | (v.z >= tauf ? 4u : 0u) |
-                             (v.w >= tauf ? 8u : 0u);
-        mk |= (uint64_t)nib << (4 * cc);
+        for (int c = 0; c < 16; ++c) {
+          const int cc = (c + lane) & 15;
+          float4 v;
+          // guarded rows read no float4 that starts past the last visible position
+          if constexpr (decltype(guard)::value) {
+            const float ninf = -__builtin_inff();
+            v = 4 * cc < nv ? r4[cc] : make_float4(ninf, ninf, ninf, ninf);
+          } else {
+            v = r4[cc];
+          }
+          const uint32_t nib = (v.x >= tauf ? 1u : 0u) | (v.y >= tauf ? 2u : 0u) | (v.z >= tauf ? 4u : 0u) |
+                               (v.w >= tauf ? 8u : 0u);
+          mk |= (uint64_t)nib << (4 * cc);
+        }
+        if (nv < 64) mk &= (1ull << nv) - 1ull;                           // drop positions past lim
       }
-      if (nv < 64) mk &= (1ull << nv) - 1ull;                             // drop positions past lim
-    }
-    uint32_t mlo = (uint32_t)mk, mhi = (uint32_t)(mk >> 32);
-    const uint32_t cnt = (uint32_t)__builtin_popcount(mlo) + (uint32_t)__builtin_popcount(mhi);
-    const uint32_t inc = wave_incl_scan(cnt);
-    const uint32_t off = (uint32_t)__builtin_amdgcn_readlane((int)inc, 63);
-    uint32_t o = inc - cnt;
-    while ((mlo | mhi) != 0u) {
-      int i;
-      if (mlo != 0u) { i = __builtin_ctz(mlo); mlo &= mlo - 1u; }
-      else { i = 32 + __builtin_ctz(mhi); mhi &= mhi - 1u; }
-      ast64(dst + o, ((uint64_t)(uint32_t)(c0 + pb + i) << 32) | order_key(row[pb + i]));
-      ++o;
+      uint32_t mlo = (uint32_t)mk, mhi = (uint32_t)(mk >> 32);
+      const uint32_t cnt = (uint32_t)__builtin_popcount(mlo) + (uint32_t)__builtin_popcount(mhi);
+      const uint32_t inc = wave_incl_scan(cnt);
+      uint32_t o = ob + inc - cnt;
+      while ((mlo | mhi) != 0u) {
+        int i;
+        if (mlo != 0u) { i = __builtin_ctz(mlo); mlo &= mlo - 1u; }
+        else { i = 32 + __builtin_ctz(mhi); mhi &= mhi - 1u; }
+        ast64(dst + o, ((uint64_t)(uint32_t)(c0 + sb + pb + i) << 32) | order_key(row[pb + i]));
+        ++o;
+      }
+      return (uint32_t)__builtin_amdgcn_readlane((int)inc, 63);
+    };
+    uint32_t off = emit(std::false_type{}, sh.sc[t], 0, lim, 0u);
+    if constexpr (SPILL) {
+      // the chunk's later positions, kMaxChunk at a time, from the spill rows (fused scan)
+      // or the input rows (loaded scores), in position order after the LDS part
+      for (int sb = kMaxChunk; sb < nkeys; sb += kMaxChunk) {
+        const float* row = SRC == 0
+            ? p.spill + (size_t)t * p.sstride + (size_t)wg * (p.chunk - kMaxChunk) + (sb - kMaxChunk)
+            : p.scores + (size_t)t * p.ld + c0 + sb;
+        off += emit(std::true_type{}, row, sb, lim - sb, off);
+      }
     }
     vm_wait_all();                       // candidates land before their count
     if (lane == 0) ast64(p.cnt + (size_t)t * p.nwg + wg, ((uint64_t)tag << 32) | off);

@@ -6,6 +6,9 @@
 // whose chunk lies wholly before pos0 hold only keys visible to every token; each of
 // them publishes a lower bound of its m-th largest score with m * n_part >= min(k, L),
 // so at least k scores lie at or above the smallest published bound.
+// A chunk of up to kMaxChunk keys keeps its scores for every token in LDS; longer chunks
+// (contexts beyond kMaxChunk keys per CU) keep the first kMaxChunk there and the rest in
+// the workspace.
 // A single token whose whole context is short (T = 1, L <= single_max <= kMaxChunk) takes
 // one workgroup that holds every score and selects on chip, without a bound or any
 // hand-off.  One CU then streams every key alone, so single_max depends on the bytes per
@@ -16,7 +19,9 @@
 namespace dsa {
 
 constexpr int kSelThreads = 512;   // 8 waves; wave w scores key tiles w, w + 8, ... for all tokens
-constexpr int kMaxChunk = 4096;    // keys per workgroup held in LDS
+constexpr int kMaxChunk = 4096;    // keys per workgroup whose scores are held in LDS
+constexpr int kMaxSpillChunk = 65536;   // keys per workgroup when the scores past the first
+                                        // kMaxChunk of the chunk are kept in the workspace
 constexpr int kTauMaxM = 32;       // largest tau rank a workgroup searches (one per lane pair)
 constexpr int kMaxWG = 1024;       // slots per token in the count and tau arrays
 constexpr int kSelMaxT = 8;        // tokens of a verify block
@@ -26,8 +31,11 @@ struct SelGeometry {
   int nwg;      // workgroups
   int n_part;   // workgroups [0, n_part) publish a tau bound
   int m;        // tau rank (0: no bound)
-  bool fits;    // chunk fits LDS and nwg fits the count arrays
+  bool fits;    // chunk <= kMaxSpillChunk and nwg fits the count arrays
   bool single;  // one workgroup holds the whole context (T = 1, L <= single_max)
+  bool spill;   // chunk > kMaxChunk: scores past the first kMaxChunk keys of each chunk go
+                // to the workspace (fused scan) or are read again from the input (loaded
+                // scores)
 };
 
 // Longest context selected by one workgroup: src 1 = materialised fp32 scores, else the
@@ -54,7 +62,8 @@ inline SelGeometry select_geometry(int T, int64_t L, int64_t pos0, int k, int nu
   int64_t nwg = (L + chunk - 1) / chunk;
   if (nwg < T) nwg = T;
   g.nwg = (int)nwg;
-  g.fits = chunk <= kMaxChunk && nwg <= kMaxWG;
+  g.fits = chunk <= kMaxSpillChunk && nwg <= kMaxWG;
+  g.spill = chunk > kMaxChunk;
   g.n_part = (int)(pos0 / chunk);
   const int64_t kmax = (int64_t)k < L ? k : L;
   g.m = 0;
@@ -65,7 +74,10 @@ inline SelGeometry select_geometry(int T, int64_t L, int64_t pos0, int k, int nu
   return g;
 }
 
-inline int64_t select_max_context(int num_cu) { return (int64_t)num_cu * kMaxChunk; }
+// Longest context: one chunk of at most kMaxSpillChunk keys per CU (the workgroups are
+// resident one per CU).  Up to kMaxChunk keys per CU every score stays on chip.
+inline int64_t select_max_context(int num_cu) { return (int64_t)num_cu * kMaxSpillChunk; }
+inline int64_t select_lds_context(int num_cu) { return (int64_t)num_cu * kMaxChunk; }
 
 // candidate slots of a selection workspace sized for (T, L): one chunk per (token,
 // workgroup) for the largest block, so any pos0 and T <= kSelMaxT fit (the geometry over
@@ -73,6 +85,13 @@ inline int64_t select_max_context(int num_cu) { return (int64_t)num_cu * kMaxChu
 inline int64_t select_candidate_slots(int T, int64_t L, int k, int num_cu) {
   const SelGeometry g = select_geometry(T, L, L - T, k, num_cu, 0);
   return (int64_t)kSelMaxT * g.nwg * g.chunk;
+}
+
+// spilled scores of a selection workspace sized for (T, L): [kSelMaxT][nwg][chunk -
+// kMaxChunk] fp32, only when the chunks exceed kMaxChunk keys
+inline int64_t select_spill_floats(int T, int64_t L, int k, int num_cu) {
+  const SelGeometry g = select_geometry(T, L, L - T, k, num_cu, 0);
+  return g.spill ? (int64_t)kSelMaxT * g.nwg * (g.chunk - kMaxChunk) : 0;
 }
 
 }  // namespace dsa

@@ -41,6 +41,11 @@ static void check(int T, int64_t L, int64_t pos0, int k, int ncu, int64_t single
           T, (long long)L, (long long)pos0, k);
   }
   const int64_t cand_slots = select_candidate_slots(T, L, k, ncu);   // the workspace's candidate capacity
+  const int64_t spill_cap = select_spill_floats(T, L, k, ncu);       // and spill capacity
+  CHECK(g.spill == (g.chunk > kMaxChunk) && (g.spill ? spill_cap > 0 : spill_cap == 0), "spill T=%d L=%lld", T,
+        (long long)L);
+  // row offsets of the spill rows (r * 2 * sstride, r < 4) and candidate offsets stay in 32 bits
+  CHECK(7 * (int64_t)g.nwg * g.chunk < ((int64_t)1 << 31), "offsets T=%d L=%lld", T, (long long)L);
   for (int wg = 0; wg < g.nwg; ++wg) {
     const int64_t c0 = (int64_t)wg * g.chunk;
     int64_t nk64 = L - c0;
@@ -57,6 +62,31 @@ static void check(int T, int64_t L, int64_t pos0, int k, int ncu, int64_t single
       // candidate slots of (t, wg): at most nkeys written from (t * nwg + wg) * chunk
       const int64_t end = ((int64_t)t * g.nwg + wg) * g.chunk + nkeys;
       CHECK(end <= cand_slots, "candidates T=%d L=%lld wg=%d t=%d", T, (long long)L, wg, t);
+    }
+    // chunks longer than kMaxChunk: the fused scan writes local positions [kMaxChunk,
+    // roundup32(nkeys)) of all kSelMaxT token rows (four row tiles) to the spill rows at
+    // t * sstride + wg * (chunk - kMaxChunk) + (pos - kMaxChunk); the candidate pass reads,
+    // per kMaxChunk positions from sb, whole float4s up to the last visible position; the
+    // loaded-score source reads those from its own row t instead
+    if (g.spill && nkeys > kMaxChunk) {
+      const int64_t sstride = (int64_t)g.nwg * (g.chunk - kMaxChunk);
+      const int64_t seg = (int64_t)wg * (g.chunk - kMaxChunk);
+      const int64_t wr_hi = (nkeys + 31) / 32 * 32;
+      CHECK(wr_hi <= g.chunk, "spill rows T=%d L=%lld wg=%d", T, (long long)L, wg);
+      CHECK((kSelMaxT - 1) * sstride + seg + (wr_hi - 1 - kMaxChunk) < spill_cap, "spill writes T=%d L=%lld wg=%d",
+            T, (long long)L, wg);
+      for (int t = 0; t < T; ++t) {
+        int64_t lim = pos0 + t - c0;
+        lim = lim < nkeys - 1 ? lim : nkeys - 1;
+        for (int64_t sb = kMaxChunk; sb < nkeys; sb += kMaxChunk) {
+          const int64_t nvis = lim - sb + 1;
+          if (nvis <= 0) continue;
+          const int64_t rd = (nvis + 3) / 4 * 4;          // float4s starting before the last visible one
+          CHECK(sb - kMaxChunk + rd <= g.chunk - kMaxChunk && t * sstride + seg + (sb - kMaxChunk) + rd <= spill_cap,
+                "spill reads T=%d L=%lld wg=%d t=%d sb=%lld", T, (long long)L, wg, t, (long long)sb);
+          CHECK(c0 + sb + rd <= ld, "score row reads T=%d L=%lld wg=%d t=%d", T, (long long)L, wg, t);
+        }
+      }
     }
     // fused scan: wave w's tiles start at c0 + 32 (w + 8 j), rows past L clamped to L - 1
     const int ntiles = (nkeys + 31) / 32;
@@ -91,9 +121,18 @@ int main() {
       }
     }
     for (int64_t L : {(int64_t)65536, (int64_t)262144, (int64_t)1048576, (int64_t)ncu * kMaxChunk,
-                      (int64_t)ncu * kMaxChunk - 1})
+                      (int64_t)ncu * kMaxChunk - 1, (int64_t)ncu * kMaxChunk + 1, (int64_t)ncu * kMaxChunk + 777,
+                      (int64_t)ncu * 3 * kMaxChunk - 5, (int64_t)ncu * kMaxSpillChunk - 1,
+                      (int64_t)ncu * kMaxSpillChunk})
       for (int T : {1, 7, 8})
-        for (int k : {1, 2048}) check(T, L, L - T, k, ncu, select_single_max(0, 1));
+        for (int k : {1, 2048}) {
+          check(T, L, L - T, k, ncu, select_single_max(0, 1));
+          check(T, L, (L - T) / 3, k, ncu, select_single_max(0, 1));
+        }
+    // one past the longest context no longer fits
+    const SelGeometry gx = select_geometry(8, select_max_context(ncu) + 512, select_max_context(ncu) - 8 + 512, 2048,
+                                           ncu, 0);
+    CHECK(!gx.fits, "ncu=%d: a context past the limit fits", ncu);
   }
   printf("%s: %ld cases, %d failures\n", fails ? "FAILED" : "ok", cases, fails);
   return fails ? 1 : 0;

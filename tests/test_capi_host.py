@@ -45,6 +45,28 @@ def test_workspace_sizes_are_monotone_and_cover_candidates():
     assert dsa.dsa_workspace_bytes(dsa.WS_TOPK, 0, 100, 10) == 0
 
 
+def test_long_context_limit_and_spill_workspace(monkeypatch):
+    """Past 4096 keys per CU the selection keeps the rest of each chunk's scores in the
+    workspace: the context limit is 65536 keys per CU, and the workspace is the control
+    block, the count and bound slots, one candidate slot per key and chunk position of
+    each of 8 tokens, and the spilled scores (fp32, 8 tokens x workgroups x (chunk - 4096))."""
+    import sparse_attention_decode_indexer_amd as dsa
+    assert dsa.dsa_max_context() % 65536 == 0 and dsa.dsa_max_context() >= 65536
+    monkeypatch.setenv("DSA_NUM_CU", "4")          # geometry cut for 4 CUs
+    assert dsa.dsa_max_context() == 4 * 65536
+    L = 40000                                      # chunk = roundup(10000, 512) = 10240
+    ctl, slots = 16384, 8 * 1024 * 16
+
+    def ws(nwg, chunk):                            # nwg = max(chunks, T): one workgroup per token at least
+        return ctl + slots + 8 * nwg * chunk * 8 + (8 * nwg * (chunk - 4096) * 4 if chunk > 4096 else 0)
+
+    assert dsa.dsa_workspace_bytes(dsa.WS_INDEX_TOPK, 8, L, 2048) == ws(8, 10240)
+    assert dsa.dsa_workspace_bytes(dsa.WS_TOPK, 3, L, 100) == ws(4, 10240)
+    # up to 4096 keys per CU nothing spills
+    assert dsa.dsa_workspace_bytes(dsa.WS_INDEX_TOPK, 2, 16384, 2048) == ws(4, 4096)
+    assert dsa.dsa_workspace_bytes(dsa.WS_LAYER_DSA, 8, L, 2048) > ws(8, 10240)
+
+
 FAKE = 0x10000          # aligned, never dereferenced: every call below fails validation first
 MIS = 0x10004           # misaligned
 

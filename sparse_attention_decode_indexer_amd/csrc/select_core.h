@@ -1063,21 +1063,26 @@ DSA_DEV bool select_body(const SelParams& p, SelShared& sh, uint32_t& epoch_out)
           load_key_tile<KDT, false>(p.k_idx, p.k_scale, p.L, tile_of(j + PF), buf[i]);
           const f32x16_t lacc = mma_k64(qf, kb);
           f32x16_t acc = mma_k64(qa[0], kb);
-          float* row = keep ? &sh.sc[half][sl] : &sh.dump[lane];
-          int rstride = keep ? 2 * kMaxChunk : 0;        // floats between row tiles' rows
-          if constexpr (SPILL) {
-            if (keep && sl >= kMaxChunk) {
-              row = p.spill + (size_t)half * p.sstride + (size_t)wg * (p.chunk - kMaxChunk) + (sl - kMaxChunk);
-              rstride = 2 * (int)p.sstride;                 // < 2^31: nwg * chunk <= kMaxWG * kMaxSpillChunk
-            }
-          }
+          // SPILL: a tile lies wholly before or after local position kMaxChunk (a multiple
+          // of the tile), so the choice of LDS or spill row is uniform over the wave
+          const bool spill_tile = SPILL && keep && (wave + jc * kSelWaves) * kTile >= kMaxChunk;
+          float* row = keep && !spill_tile ? &sh.sc[half][sl] : &sh.dump[lane];
+          const int rstride = keep && !spill_tile ? 2 * kMaxChunk : 0;  // floats between row tiles' rows
+          float* grow = nullptr;
+          if constexpr (SPILL)
+            grow = p.spill + (size_t)half * p.sstride + (size_t)wg * (p.chunk - kMaxChunk) + (sl - kMaxChunk);
 #pragma unroll
           for (int r = 0; r < RTW; ++r) {
             f32x16_t nxt = {};
             if (r + 1 < RTW) nxt = mma_k64(qa[r + 1 < RTW ? r + 1 : r], kb);
             const float o = row_score<KDT>(acc, wv[r], (lacc[4 * r] + lacc[4 * r + 1]) + lacc[4 * r + 2], scale);
             gmax[r] = fmaxf(gmax[r], o);
-            row[r * rstride] = o;
+            if constexpr (SPILL) {
+              if (spill_tile) grow[(size_t)r * 2 * p.sstride] = o;
+              else row[r * rstride] = o;
+            } else {
+              row[r * rstride] = o;
+            }
             acc = nxt;
           }
           // the next scale of this slot is requested once the current one is used up, so
@@ -1154,10 +1159,15 @@ DSA_DEV bool select_body(const SelParams& p, SelShared& sh, uint32_t& epoch_out)
       // wave t then merges, per lane, the waves of one parity: 64 groups of the token
       constexpr int GPT = kSelWaves * 32;                           // group maxima per token
       float* gm = sh.kscale;                                        // [kMaxT][GPT]
+      // the thread's row and wave are formed again from an opaque copy of its index, so
+      // no value derived from it stays live (in a spill slot) across the scan
+      int tid_o = threadIdx.x;
+      asm volatile("" : "+v"(tid_o));
+      const int half_o = (tid_o >> 5) & 1, wave_o = tid_o >> 6;
 #pragma unroll
       for (int r = 0; r < RTW; ++r) {
-        const int tt = 2 * r + half;
-        if (tt < T) gm[tt * GPT + wave * 32 + (lane & 31)] = gmax[r];
+        const int tt = 2 * r + half_o;
+        if (tt < T) gm[tt * GPT + wave_o * 32 + (tid_o & 31)] = gmax[r];
       }
       __syncthreads();
       for (int t = wave; t < T; t += kSelWaves) {

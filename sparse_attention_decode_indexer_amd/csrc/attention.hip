@@ -11,7 +11,8 @@
 // One workgroup = one (token, split of 64 list entries).  It stages the split's K and V
 // rows in LDS with 16-byte coalesced loads, computes S = K q^T on the matrix cores,
 // runs the softmax of the split in fp32 (base-2 exponentials of log2e-scaled logits),
-// accumulates P V, and writes (m, l, acc) to the workspace.  A second, small kernel
+// forms P V on the matrix cores (P split exactly into three bf16 parts, fp32
+// accumulation), and writes (m, l, acc) to the workspace.  A second, small kernel
 // merges each token's splits in split order (the kernel boundary makes the partials
 // visible), so the result does not depend on timing.
 #include "attn_core.h"
@@ -123,7 +124,7 @@ hipError_t launch_attention(int mode, int kvdt, const void* q, const void* kc, c
   (void)num_cu;
   const dim3 grid(p.nsplit, T);
   if (mode == 0) {
-    // two P.V row groups (512 threads): each thread's P.V loop is half as long
+    // 512 threads: twice the staging loads in flight per workgroup
     if (kvdt == 0) hipLaunchKernelGGL((attn_kernel<0, 0, kSplitRows, 2 * kAttnThreads>), grid, dim3(2 * kAttnThreads), 0, st, p);
     else hipLaunchKernelGGL((attn_kernel<1, 0, kSplitRows, 2 * kAttnThreads>), grid, dim3(2 * kAttnThreads), 0, st, p);
   } else {

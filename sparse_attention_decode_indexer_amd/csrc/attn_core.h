@@ -53,12 +53,20 @@ template <int KVDT, int ROWS>
 struct AttnShared {
   static constexpr int RB = KVDT == 0 ? 256 : 128;   // bytes per cache row
   static constexpr int KSTRIDE = RB + 16;            // padded K row stride
+  static constexpr int VRB = kD * 2 + 16;            // staged V rows: bf16 (e4m3 converted), padded
+                                                     // so the transpose reads of 4 rows hit distinct banks
+  static constexpr int PSTR = ROWS + 8;              // bf16 per row of a P part (padded)
+  static constexpr int OXS = kD + 4;                 // floats per head of the P.V exchange
   int64_t rows[ROWS];
+  // K rows; after the scores: P in three bf16 parts [3][kHq][PSTR], then the P.V result
+  // [kHq][OXS] fp32
   alignas(16) uint8_t kst[ROWS * KSTRIDE];
-  alignas(16) uint8_t vst[ROWS * RB];
+  alignas(16) uint8_t vst[ROWS * VRB];
   float kscl[ROWS];
   float vscl[ROWS];
   float s[kHq][ROWS];
+  static_assert(3 * kHq * PSTR * 2 % 16 == 0 && 3 * kHq * PSTR * 2 + kHq * OXS * 4 <= ROWS * KSTRIDE,
+                "P parts and the P.V result fit the K staging area");
 };
 
 // out[t][h][d4 .. d4+3] = o / den (0 for an empty list), fp32 or bf16; COH (bf16 only):
@@ -85,17 +93,17 @@ DSA_DEV void store_out(const AttnParams& p, int t, int h, int d4, float (&o)[4],
   }
 }
 
-// One (token, split) of the attention by a workgroup of NT threads: the first 256 are
-// (head = tid / 32, 4 dims); with NT = 512 or 1024 the P.V product is split over 2 or 4
-// row groups whose partial sums are added in group order.  COH: the result (partial or
-// final output) is written as tagged words, for a launch whose other workgroups consume
-// it; the arithmetic is the same either way.
+// One (token, split) of the attention by a workgroup of NT threads: every thread stages
+// rows; the first 256 run the softmax and write the result as (head = tid / 32, 4 dims);
+// four waves form P.V on the matrix cores.  COH: the result (partial or final output) is
+// written as tagged words, for a launch whose other workgroups consume it; the arithmetic
+// is the same either way.
 template <int KVDT, int MODE, int ROWS, int NT, bool COH>
 DSA_DEV void attn_split(const AttnParams& p, int t, int split, AttnShared<KVDT, ROWS>& sh, uint64_t* trace,
                         uint32_t tag = 0u) {
   static_assert(ROWS % 64 == 0 && ROWS <= NT && NT % kAttnThreads == 0, "64-row blocks, one list entry per thread");
   constexpr int NW = NT / 64;                 // waves
-  constexpr int G = NT / kAttnThreads;        // P.V row groups
+  static_assert(NW >= kD / 32, "four waves for the P.V tiles");
   using SH = AttnShared<KVDT, ROWS>;
   constexpr int RB = SH::RB;
   const int tid = threadIdx.x;
@@ -145,8 +153,28 @@ DSA_DEV void attn_split(const AttnParams& p, int t, int split, AttnShared<KVDT, 
       const int c = tid + u * NT;
       const int row = c / CPR, col = c % CPR;
       const bool ok = sh.rows[row] >= 0;
-      *reinterpret_cast<uint4*>(&sh.kst[row * SH::KSTRIDE + col * 16]) = ok ? kv[u] : make_uint4(0u, 0u, 0u, 0u);
-      *reinterpret_cast<uint4*>(&sh.vst[row * RB + col * 16]) = ok ? vv[u] : make_uint4(0u, 0u, 0u, 0u);
+      // component-wise selects (a select of two uint4 objects went through scratch)
+      auto keep = [ok](const uint4& v) {
+        return make_uint4(ok ? v.x : 0u, ok ? v.y : 0u, ok ? v.z : 0u, ok ? v.w : 0u);
+      };
+      *reinterpret_cast<uint4*>(&sh.kst[row * SH::KSTRIDE + col * 16]) = keep(kv[u]);
+      if constexpr (KVDT == 0) {
+        *reinterpret_cast<uint4*>(&sh.vst[row * SH::VRB + col * 16]) = keep(vv[u]);
+      } else {
+        // sixteen e4m3 codes -> sixteen bf16 (exact), the P.V operand's format
+        const uint32_t cw[4] = {vv[u].x, vv[u].y, vv[u].z, vv[u].w};
+        uint32_t bw[8];
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+          const bf16x2_t a = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)cw[w], 1.0f, false);
+          const bf16x2_t b = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)cw[w], 1.0f, true);
+          bw[2 * w] = __builtin_bit_cast(uint32_t, a);
+          bw[2 * w + 1] = __builtin_bit_cast(uint32_t, b);
+        }
+        *reinterpret_cast<uint4*>(&sh.vst[row * SH::VRB + col * 32]) = keep(make_uint4(bw[0], bw[1], bw[2], bw[3]));
+        *reinterpret_cast<uint4*>(&sh.vst[row * SH::VRB + col * 32 + 16]) =
+            keep(make_uint4(bw[4], bw[5], bw[6], bw[7]));
+      }
     }
   }
   // ---- q^T operand (heads on the N side): lane l -> head l%16 (< 8 real), dims kb*32 + (l/16)*8
@@ -203,8 +231,7 @@ DSA_DEV void attn_split(const AttnParams& p, int t, int split, AttnShared<KVDT, 
   constexpr int RPT = ROWS / 32;
   const int h = (tid >> 5) & (kHq - 1);
   const int jj = tid & 31;
-  const int grp = tid / kAttnThreads;         // P.V row group
-  const bool lead = grp == 0;
+  const bool lead = tid < kAttnThreads;       // the softmax and result threads
   float m = -__builtin_inff(), l = 0.0f;
   if (lead) {
     float z[RPT];
@@ -240,58 +267,57 @@ DSA_DEV void attn_split(const AttnParams& p, int t, int split, AttnShared<KVDT, 
       const float l1 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(l), 32));
       l = (lane & 32) ? l1 : l0;
     }
+    // P in three bf16 parts, P = hi + mid + lo exactly (8 + 8 + 8 significant bits of
+    // the fp32 value; each residual is exact in fp32), the A operand of the P.V product
+    uint16_t* pp = reinterpret_cast<uint16_t*>(sh.kst);
 #pragma unroll
     for (int i = 0; i < RPT; ++i) {
       if (KVDT == 1) pz[i] *= sh.vscl[jj + 32 * i];
-      sh.s[h][jj + 32 * i] = pz[i];
+      const uint16_t b0 = f32_to_bf16(pz[i]);
+      const float r1 = pz[i] - bf16_to_f32(b0);
+      const uint16_t b1 = f32_to_bf16(r1);
+      const uint16_t b2 = f32_to_bf16(r1 - bf16_to_f32(b1));
+      const int j = jj + 32 * i;
+      pp[(0 * kHq + h) * SH::PSTR + j] = b0;
+      pp[(1 * kHq + h) * SH::PSTR + j] = b1;
+      pp[(2 * kHq + h) * SH::PSTR + j] = b2;
     }
   }
   __syncthreads();
   DSA_MARK(trace, 4);
-  // ---- acc[h][d4..d4+3] = sum_j p[h][j] * V[j][d4..d4+3]
-  const int d4 = jj * 4;
-  float acc[4] = {0.0f, 0.0f, 0.0f, 0.0f};
-  // rows in groups of 8: the group's LDS reads are issued together
-  constexpr int PVU = 8;
-  constexpr int RG = ROWS / G;                // rows per group
-  for (int j0 = grp * RG; j0 < (grp + 1) * RG; j0 += PVU) {
-    float pj[PVU];
-    float v[PVU][4];
+  // ---- O = P V on the matrix cores: wave w < 4 takes dims 32 w .. +31 as one 32 x 32 tile
+  //      whose rows are (part, head) = (m >> 3, m & 7) for m < 24 (rows 24-31 zero),
+  //      K = the split's rows in steps of 16; V through the LDS transpose path.  The
+  //      products are exact and accumulate in fp32; the three parts of each head are added
+  //      (hi + mid) + lo and the result goes through LDS to the softmax's thread layout.
+  float* ox = reinterpret_cast<float*>(sh.kst + 3 * kHq * SH::PSTR * 2);   // [kHq][OXS]
+  if (wave < kD / 32) {
+    const int m = lane & 31;
+    const uint8_t* pa = sh.kst + (m * SH::PSTR + 8 * (lane >> 5)) * 2;
+    const int g = lane >> 4, q = lane & 15;
+    const uint8_t* vb = sh.vst + (8 * (g >> 1) + (q >> 2)) * SH::VRB + (32 * wave + 16 * (g & 1) + 4 * (q & 3)) * 2;
+    f32x16_t pv = {};
 #pragma unroll
-    for (int u = 0; u < PVU; ++u) {
-      const int j = j0 + u;
-      pj[u] = sh.s[h][j];
-      if constexpr (KVDT == 0) {
-        const uint2 raw = *reinterpret_cast<const uint2*>(&sh.vst[j * RB + d4 * 2]);
-        v[u][0] = __uint_as_float(raw.x << 16);
-        v[u][1] = __uint_as_float(raw.x & 0xffff0000u);
-        v[u][2] = __uint_as_float(raw.y << 16);
-        v[u][3] = __uint_as_float(raw.y & 0xffff0000u);
-      } else {
-        const uint32_t raw = *reinterpret_cast<const uint32_t*>(&sh.vst[j * RB + d4]);
-        auto lo = __builtin_amdgcn_cvt_pk_f32_fp8((int)raw, false);
-        auto hi = __builtin_amdgcn_cvt_pk_f32_fp8((int)raw, true);
-        v[u][0] = lo[0]; v[u][1] = lo[1]; v[u][2] = hi[0]; v[u][3] = hi[1];
-      }
+    for (int ks = 0; ks < ROWS / 16; ++ks) {
+      Frag8 a, bv;
+      a.u = make_uint4(0u, 0u, 0u, 0u);
+      if (m < 3 * kHq) a.u = *reinterpret_cast<const uint4*>(pa + ks * 32);
+      const uint2 lo4 = lds_tr16(vb + (16 * ks) * SH::VRB);
+      const uint2 hi4 = lds_tr16(vb + (16 * ks + 4) * SH::VRB);
+      bv.u = make_uint4(lo4.x, lo4.y, hi4.x, hi4.y);
+      pv = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a.v, bv.v, pv, 0, 0, 0);
     }
+    // lane l, element e < 4: head 4 (l >> 5) + e, part 0; elements e + 4, e + 8: parts 1, 2
+    const int dim = 32 * wave + (lane & 31);
 #pragma unroll
-    for (int u = 0; u < PVU; ++u) {
-#pragma unroll
-      for (int i = 0; i < 4; ++i) acc[i] = fmaf(pj[u], v[u][i], acc[i]);
-    }
+    for (int e = 0; e < 4; ++e) ox[(4 * (lane >> 5) + e) * SH::OXS + dim] = (pv[e] + pv[e + 4]) + pv[e + 8];
   }
-  if constexpr (G > 1) {
-    // group partials through LDS (the K staging area is free now), added in group order
-    float* pv = reinterpret_cast<float*>(sh.kst);                     // [G][kHq][kD]
-    *reinterpret_cast<float4*>(&pv[(grp * kHq + h) * kD + d4]) = make_float4(acc[0], acc[1], acc[2], acc[3]);
-    __syncthreads();
-    if (lead) {
-#pragma unroll
-      for (int g = 1; g < G; ++g) {
-        const float4 q4 = *reinterpret_cast<const float4*>(&pv[(g * kHq + h) * kD + d4]);
-        acc[0] += q4.x; acc[1] += q4.y; acc[2] += q4.z; acc[3] += q4.w;
-      }
-    }
+  __syncthreads();
+  const int d4 = jj * 4;
+  float acc[4];
+  {
+    const float4 o4 = *reinterpret_cast<const float4*>(&ox[h * SH::OXS + d4]);
+    acc[0] = o4.x; acc[1] = o4.y; acc[2] = o4.z; acc[3] = o4.w;
   }
   DSA_MARK(trace, 5);
   float sink2 = -__builtin_inff();

@@ -29,6 +29,20 @@ union Frag8 {           // eight bf16 = one MFMA A/B operand of the K=16/K=32 sh
   uint32_t w[4];
 };
 
+typedef short v4i16 __attribute__((ext_vector_type(4)));
+
+// Four 16-bit values through the LDS transpose path: within each 16-lane group, lane q
+// supplies the 8 bytes at its address and receives element (q & 3) of the values
+// supplied by lanes (q >> 2) + 4i, i = 0..3.  With lane q of group g pointing at row
+// r0 + (q >> 2), columns c0 + 16 (g & 1) + 4 (q & 3) .. +3 of a row-major bf16 matrix,
+// lane l receives rows r0 .. r0 + 3 of column c0 + (l & 31): the K-major layout of a
+// 32x32x16 MFMA B operand (the next four rows come from a second read 4 rows further).
+DSA_DEV uint2 lds_tr16(const uint8_t* addr) {
+  const v4i16 r = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (__attribute__((address_space(3))) v4i16*)(reinterpret_cast<uintptr_t>(addr)));
+  return __builtin_bit_cast(uint2, r);
+}
+
 // ----------------------------------------------------------------------------- formats
 
 DSA_DEV float bf16_to_f32(uint16_t b) { return __uint_as_float((uint32_t)b << 16); }

@@ -102,16 +102,6 @@ DSA_DEV void store_window(int tid, const Lds& l, const uint4 (&kv)[kWinNCH], con
   }
 }
 
-typedef short v4i16 __attribute__((ext_vector_type(4)));
-
-// Four 16-bit values through the LDS transpose path: within each 16-lane group, lane q
-// supplies the 8 bytes at its address and receives element (q & 3) of the values
-// supplied by lanes (q >> 2) + 4i, i = 0..3.
-DSA_DEV uint2 lds_tr16(const uint8_t* addr) {
-  const v4i16 r = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-      (__attribute__((address_space(3))) v4i16*)(reinterpret_cast<uintptr_t>(addr)));
-  return __builtin_bit_cast(uint2, r);
-}
 
 // The functions take the thread's index as an argument (a caller running them in a loop
 // can keep the compiler from hoisting index arithmetic out of it).

@@ -782,13 +782,28 @@ DSA_DEV void resolve_token(const SelParams& p, int t, SelShared& sh, uint32_t ep
           vlong |= n[u] > 64u;
         }
         if (__ballot(vlong) != 0ull) {
+          // longer runs (short contexts without a bound: every visible score of a chunk is
+          // a candidate) in rounds of eight loads per lane issued before any is used, so a
+          // 512-candidate run takes two round trips instead of fourteen
+          constexpr int LB = 8;
 #pragma unroll 1
           for (int u = 0; u < UP; ++u) {
-            for (uint32_t j = 64u + el; j < n[u]; j += 32u) {
-              const uint64_t x = ald64(base + so[u] + j);
-              lc[b0[u] + j] = x;
-              kmin = min(kmin, (uint32_t)x);
-              kmax = max(kmax, (uint32_t)x);
+            for (uint32_t j0 = 64u; j0 < n[u]; j0 += 32u * LB) {
+              uint64_t x[LB];
+#pragma unroll
+              for (int i = 0; i < LB; ++i) {
+                const uint32_t j = j0 + el + 32u * i;
+                x[i] = ald64(base + so[u] + (j < n[u] ? j : 0u));
+              }
+#pragma unroll
+              for (int i = 0; i < LB; ++i) {
+                const uint32_t j = j0 + el + 32u * i;
+                if (j < n[u]) {
+                  lc[b0[u] + j] = x[i];
+                  kmin = min(kmin, (uint32_t)x[i]);
+                  kmax = max(kmax, (uint32_t)x[i]);
+                }
+              }
             }
           }
         }

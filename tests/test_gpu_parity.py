@@ -260,8 +260,8 @@ def test_topk_single_token_short_context(dsa, L, k, gen):
 @pytest.mark.parametrize("k,tie", [(2048, False), (2048, True), (100, False), (1, True)])
 def test_index_topk_single_token_short_context(dsa, L, k, tie):
     """Integer-valued bf16 indexer inputs (exact scores): the fused selection of one token
-    equals the oracle's bit for bit, tie order included (one workgroup up to 3072 keys of
-    bf16, several beyond)."""
+    equals the oracle's bit for bit, tie order included (one workgroup up to 4096 keys,
+    several beyond)."""
     inp = synth.dsa_config("tiny", seed=L, L=L, T=1, tie_stress=tie)
     idx = torch.full((1, k), -7, dtype=torch.int32, device=DEV)
     cnt = torch.full((1,), -7, dtype=torch.int32, device=DEV)

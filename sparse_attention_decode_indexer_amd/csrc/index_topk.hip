@@ -18,15 +18,10 @@ __global__ void __launch_bounds__(kScoreThreads)
 indexer_scores_kernel(const uint16_t* __restrict__ q_idx, const float* __restrict__ w_idx,
                       const uint8_t* __restrict__ k_idx, const float* __restrict__ k_scale,
                       int T, int64_t L, int64_t pos0, float* __restrict__ scores, int64_t ld) {
-  __shared__ uint16_t ql[3 * kMaxT * kDI];
-  build_qlin<kScoreThreads>(q_idx, w_idx, T, ql);
   Frag8 qa[RT][4];
   float wv[RT][16];
   load_q_frags<RT>(q_idx, T, 0, qa);
   load_w<RT>(w_idx, T, 0, wv);
-  __syncthreads();
-  Frag8 qf[4];
-  load_qlin_frags<RT>(ql, 0, qf);
   const int lane = threadIdx.x & 63;
   const int half = lane >> 5;
   const int wave = threadIdx.x >> 6;
@@ -43,7 +38,7 @@ indexer_scores_kernel(const uint16_t* __restrict__ q_idx, const float* __restric
     const int64_t tile = tile0 + i;
     if (tile >= ntiles) break;
     float out[RT];
-    score_tile<KDT, RT>(buf[i], qa, qf, wv, out);
+    score_tile<KDT, RT>(buf[i], qa, wv, out);
     const int64_t s = tile * kTile + (lane & 31);
 #pragma unroll
     for (int r = 0; r < RT; ++r) {

@@ -11,8 +11,8 @@
 // MFMA mapping (v_mfma_f32_32x32x16_bf16): one row tile = 2 tokens x 16 heads = 32 MFMA
 // rows; the 32 MFMA columns are 32 consecutive keys; K = 64 indexer dims in 4 steps.
 // A block of 8 tokens therefore fills 128 rows with no padding.  The epilogue does
-// relu -> x w -> fixed-order head sum in registers (8 heads per lane, then one exchange
-// with the lane 32 away) and, for e4m3 keys, one multiply by the row scale.
+// relu -> x w -> fixed-order head sum in registers (each lane holds the 16 heads of one
+// token) and, for e4m3 keys, one multiply by the row scale.
 //
 // Selection is one launch of one workgroup per chunk of C keys, all resident at once:
 //   P1  scores of the chunk (computed, or read from memory) stay in LDS; each
@@ -110,7 +110,7 @@ DSA_DEV void load_q_frags(const uint16_t* __restrict__ q_idx, int T, int rt0, Fr
   }
 }
 
-// Half head weights (w/2) of this lane's accumulator elements.  Element e of the 32x32 output holds
+// Head weights of this lane's accumulator elements.  Element e of the 32x32 output holds
 // row m = 8*(e>>2) + 4*half + (e&3): token 2r + half, head tile_row_head(m).
 template <int RTW>
 DSA_DEV void load_w(const float* __restrict__ w_idx, int T, int rt0, float (&wv)[RTW][16]) {
@@ -122,59 +122,8 @@ DSA_DEV void load_w(const float* __restrict__ w_idx, int T, int rt0, float (&wv)
       const int tt = 2 * (rt0 + r) + half;
       const int hh = tile_row_head(8 * (e >> 2) + 4 * half + (e & 3));
       const float v = w_idx[(tt < T ? tt : T - 1) * kHI + hh];
-      wv[r][e] = (tt < T) ? 0.5f * v : 0.0f;
+      wv[r][e] = (tt < T) ? v : 0.0f;
     }
-  }
-}
-
-// Linear part of the score.  relu(x) = (x + |x|) / 2, so
-//   I[t,s] = sum_h (w_h/2) |q_h . k_s|  +  k_s . qlin_t,   qlin_t = sum_h (w_h/2) q_h.
-// qlin is formed once per launch in fp32 (fixed order h = 0..15) and stored as three
-// bf16 parts hi + mid + lo (each the round-to-nearest-even of the remainder), which
-// carry its 24 bits; the key contraction with the parts runs on the matrix cores.
-// ql: [3][kMaxT][kDI] bf16 in LDS; rows of tokens >= T are zero.
-template <int NT>
-DSA_DEV void build_qlin(const uint16_t* __restrict__ q_idx, const float* __restrict__ w_idx, int T,
-                        uint16_t* ql) {
-  for (int i = threadIdx.x; i < kMaxT * kDI; i += NT) {
-    const int t = i / kDI, d = i % kDI;
-    const int tc = t < T ? t : T - 1;
-    float wq[kHI], qv[kHI];
-#pragma unroll
-    for (int h = 0; h < kHI; ++h) {
-      wq[h] = w_idx[tc * kHI + h];
-      qv[h] = bf16_to_f32(q_idx[(tc * kHI + h) * kDI + d]);
-    }
-    float acc = 0.0f;
-#pragma unroll
-    for (int h = 0; h < kHI; ++h) acc = fmaf(0.5f * wq[h], qv[h], acc);
-    acc = (t < T) ? acc : 0.0f;
-    const uint16_t hi = f32_to_bf16(acc);
-    const float r1 = acc - bf16_to_f32(hi);
-    const uint16_t mid = f32_to_bf16(r1);
-    const uint16_t lo = f32_to_bf16(r1 - bf16_to_f32(mid));
-    ql[(0 * kMaxT + t) * kDI + d] = hi;
-    ql[(1 * kMaxT + t) * kDI + d] = mid;
-    ql[(2 * kMaxT + t) * kDI + d] = lo;
-  }
-}
-
-// A operand of the linear tile for row tiles rt0 .. rt0+RTW-1: row 8r + 4c + p holds part
-// p (< 3) of qlin for token 2(rt0+r) + c, so accumulator element 4r + p of a lane in half c
-// is part p of the token whose score that lane ends up holding.  Other rows are zero.
-template <int RTW>
-DSA_DEV void load_qlin_frags(const uint16_t* ql, int rt0, Frag8 (&qf)[4]) {
-  const int l = threadIdx.x & 63;
-  const int half = l >> 5;
-  const int row = l & 31;
-  const int r = row >> 3, c = (row >> 2) & 1, pp = row & 3;
-  const int t = 2 * (rt0 + r) + c;
-  const bool ok = (r < RTW) & (pp < 3) & (t < kMaxT);
-  const int pc = pp < 3 ? pp : 2, tcl = t < kMaxT ? t : kMaxT - 1;
-#pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const uint4 v = *reinterpret_cast<const uint4*>(ql + (pc * kMaxT + tcl) * kDI + half * 32 + 8 * j);
-    qf[j].u = ok ? v : make_uint4(0u, 0u, 0u, 0u);
   }
 }
 
@@ -184,7 +133,7 @@ constexpr int kQsRow = kDI + 8;
 
 // Query block staged in LDS: qs [kMaxT][kHI][kQsRow] bf16 and wsh [kMaxT][kHI] fp32, rows of
 // tokens >= T zero.  The loaders below read it with the same lane mapping and produce
-// the same values as load_q_frags / load_w / build_qlin.
+// the same values as load_q_frags / load_w.
 template <int RTW>
 DSA_DEV void load_q_frags_lds(const uint16_t* qs, Frag8 (&qa)[RTW][4]) {
   static_assert(kQsRow % 8 == 0, "16-byte aligned rows");
@@ -211,28 +160,11 @@ DSA_DEV void load_w_lds(const float* wsh, float (&wv)[RTW][16]) {
       const int tt = 2 * r + half;
       const int hh = tile_row_head(8 * g);
       const float4 v = *reinterpret_cast<const float4*>(wsh + tt * kHI + hh);
-      wv[r][4 * g + 0] = 0.5f * v.x;
-      wv[r][4 * g + 1] = 0.5f * v.y;
-      wv[r][4 * g + 2] = 0.5f * v.z;
-      wv[r][4 * g + 3] = 0.5f * v.w;
+      wv[r][4 * g + 0] = v.x;
+      wv[r][4 * g + 1] = v.y;
+      wv[r][4 * g + 2] = v.z;
+      wv[r][4 * g + 3] = v.w;
     }
-  }
-}
-
-template <int NT>
-DSA_DEV void build_qlin_lds(const uint16_t* qs, const float* wsh, uint16_t* ql) {
-  for (int i = threadIdx.x; i < kMaxT * kDI; i += NT) {
-    const int t = i / kDI, d = i % kDI;
-    float acc = 0.0f;
-#pragma unroll
-    for (int h = 0; h < kHI; ++h) acc = fmaf(0.5f * wsh[t * kHI + h], bf16_to_f32(qs[(t * kHI + h) * kQsRow + d]), acc);
-    const uint16_t hi = f32_to_bf16(acc);
-    const float r1 = acc - bf16_to_f32(hi);
-    const uint16_t mid = f32_to_bf16(r1);
-    const uint16_t lo = f32_to_bf16(r1 - bf16_to_f32(mid));
-    ql[(0 * kMaxT + t) * kDI + d] = hi;
-    ql[(1 * kMaxT + t) * kDI + d] = mid;
-    ql[(2 * kMaxT + t) * kDI + d] = lo;
   }
 }
 
@@ -256,9 +188,8 @@ DSA_DEV float relu_bits(float x) { return __int_as_float(max(__float_as_int(x), 
 
 // Building blocks of a tile's scores.  Their arithmetic and its order are fixed and the
 // same in every kernel that uses them: per head a = q_h . k (MFMA, fp32); per lane, for
-// its token, sum_e (w/2)|a_e| over heads 0-3, 8-11 and over heads 4-7, 12-15, each in
-// element order, then the two added; then + ((hi + mid) + lo) of the linear tile; then x
-// the row scale for e4m3 keys.
+// its token, sum_e w_e relu(a_e) over heads 0-3, 8-11 and over heads 4-7, 12-15, each in
+// element order, then the two added; then x the row scale for e4m3 keys.
 
 // e4m3 or bf16 key tile -> the four bf16 B operands (e4m3 -> bf16 is exact)
 template <int KDT>
@@ -287,37 +218,31 @@ DSA_DEV f32x16_t mma_k64(const Frag8 (&a)[4], const Frag8 (&kb)[4]) {
   return acc;
 }
 
-// linear part of row tile r (accumulator elements 4r .. 4r+2 of the linear tile)
-template <int R>
-DSA_DEV float lin_part(const f32x16_t& lacc) { return (lacc[4 * R] + lacc[4 * R + 1]) + lacc[4 * R + 2]; }
-
 // score of token 2r + (lane>>5) for key lane & 31 from the row tile's accumulator
 template <int KDT>
-DSA_DEV float row_score(const f32x16_t& acc, const float (&w)[16], float lin, float scale) {
+DSA_DEV float row_score(const f32x16_t& acc, const float (&w)[16], float scale) {
   float p0 = 0.0f, p1 = 0.0f;
 #pragma unroll
-  for (int e = 0; e < 8; ++e) p0 = fmaf(w[e], fabsf(acc[e]), p0);
+  for (int e = 0; e < 8; ++e) p0 = fmaf(w[e], relu_bits(acc[e]), p0);
 #pragma unroll
-  for (int e = 8; e < 16; ++e) p1 = fmaf(w[e], fabsf(acc[e]), p1);
+  for (int e = 8; e < 16; ++e) p1 = fmaf(w[e], relu_bits(acc[e]), p1);
   // the lane holds all 16 heads of one token (the tile's row order): heads 0-3, 8-11 in
   // p0, heads 4-7, 12-15 in p1
-  const float tot = p0 + p1;
-  const float v = tot + lin;
+  const float v = p0 + p1;
   return (KDT == 1) ? v * scale : v;
 }
 
 // Scores of one 32-key tile for RTW row tiles: out[r] is the score of token
 // 2(rt0+r) + (lane>>5) for key s0 + (lane & 31).
 template <int KDT, int RTW>
-DSA_DEV void score_tile(const KeyTile<KDT>& kt, const Frag8 (&qa)[RTW][4], const Frag8 (&qf)[4],
-                        const float (&wv)[RTW][16], float (&out)[RTW]) {
+DSA_DEV void score_tile(const KeyTile<KDT>& kt, const Frag8 (&qa)[RTW][4], const float (&wv)[RTW][16],
+                        float (&out)[RTW]) {
   Frag8 kb[4];
   keys_to_bf16<KDT>(kt, kb);
-  const f32x16_t lacc = mma_k64(qf, kb);
-  out[0] = row_score<KDT>(mma_k64(qa[0], kb), wv[0], lin_part<0>(lacc), kt.scale);
-  if constexpr (RTW > 1) out[1] = row_score<KDT>(mma_k64(qa[1], kb), wv[1], lin_part<1>(lacc), kt.scale);
-  if constexpr (RTW > 2) out[2] = row_score<KDT>(mma_k64(qa[2], kb), wv[2], lin_part<2>(lacc), kt.scale);
-  if constexpr (RTW > 3) out[3] = row_score<KDT>(mma_k64(qa[3], kb), wv[3], lin_part<3>(lacc), kt.scale);
+  out[0] = row_score<KDT>(mma_k64(qa[0], kb), wv[0], kt.scale);
+  if constexpr (RTW > 1) out[1] = row_score<KDT>(mma_k64(qa[1], kb), wv[1], kt.scale);
+  if constexpr (RTW > 2) out[2] = row_score<KDT>(mma_k64(qa[2], kb), wv[2], kt.scale);
+  if constexpr (RTW > 3) out[3] = row_score<KDT>(mma_k64(qa[3], kb), wv[3], kt.scale);
 }
 
 // ----------------------------------------------------------------------------- selection
@@ -356,7 +281,6 @@ struct SelParams {
 struct SelShared {
   alignas(16) float sc[kMaxT][kMaxChunk];   // chunk scores (P1/P2); resolver scratch (P3); 16-byte reads
   float kscale[kMaxChunk];           // row scales of the chunk (e4m3 keys)
-  uint16_t ql[3 * kMaxT * kDI];      // linear-part query, three bf16 parts
   uint32_t wcnt[2 * kSelWaves];      // resolver: per-wave counts
   float dump[64];                    // target of scores that are not kept (clamped tiles)
   uint32_t scan[32];
@@ -1054,10 +978,7 @@ DSA_DEV bool select_body(const SelParams& p, SelShared& sh, uint32_t& epoch_out)
     float wv[RTW][16];
     load_q_frags_lds<RTW>(qs, qa);
     load_w_lds<RTW>(wsh, wv);
-    build_qlin_lds<kSelThreads>(qs, wsh, sh.ql);
-    __syncthreads();
-    Frag8 qf[4];
-    load_qlin_frags<RTW>(sh.ql, 0, qf);
+    __syncthreads();                     // the staged block is read; the scan overwrites it
     ctlw = ald64(reinterpret_cast<const uint64_t*>(p.ctl + ctl::kEpoch));
     DSA_MARK(p.trace, 1);
     DSA_MARK_CLK(p.trace, 14);
@@ -1076,7 +997,6 @@ DSA_DEV bool select_body(const SelParams& p, SelShared& sh, uint32_t& epoch_out)
           Frag8 kb[4];
           keys_to_bf16<KDT>(buf[i], kb);
           load_key_tile<KDT, false>(p.k_idx, p.k_scale, p.L, tile_of(j + PF), buf[i]);
-          const f32x16_t lacc = mma_k64(qf, kb);
           f32x16_t acc = mma_k64(qa[0], kb);
           // SPILL: a tile lies wholly before or after local position kMaxChunk (a multiple
           // of the tile), so the choice of LDS or spill row is uniform over the wave
@@ -1090,7 +1010,7 @@ DSA_DEV bool select_body(const SelParams& p, SelShared& sh, uint32_t& epoch_out)
           for (int r = 0; r < RTW; ++r) {
             f32x16_t nxt = {};
             if (r + 1 < RTW) nxt = mma_k64(qa[r + 1 < RTW ? r + 1 : r], kb);
-            const float o = row_score<KDT>(acc, wv[r], (lacc[4 * r] + lacc[4 * r + 1]) + lacc[4 * r + 2], scale);
+            const float o = row_score<KDT>(acc, wv[r], scale);
             gmax[r] = fmaxf(gmax[r], o);
             if constexpr (SPILL) {
               if (spill_tile) grow[(size_t)r * 2 * p.sstride] = o;
@@ -1106,14 +1026,13 @@ DSA_DEV bool select_body(const SelParams& p, SelShared& sh, uint32_t& epoch_out)
           if constexpr (KDT == 1) buf[i].scale = load_key_scale(p.k_scale, p.L, tile_of(j + PF));
         }
         // Issue order of the block's tiles (four row tiles): every MFMA is followed by up to
-        // five vector instructions, so one row tile's epilogue issues under the next row
-        // tile's matrix work.  Left to itself the compiler issues the first eight MFMAs of a
-        // tile back to back; this interleave measured 0.6 us faster per launch at 1M keys.
+        // ten vector instructions, so one row tile's epilogue issues under the next row
+        // tile's matrix work.  Left to itself the compiler issues a tile's MFMAs back to back.
         if constexpr (RTW == 4) {
 #pragma unroll
-          for (int g = 0; g < (4 + 4 * RTW) * PF; ++g) {
+          for (int g = 0; g < 4 * RTW * PF; ++g) {
             __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // one MFMA
-            __builtin_amdgcn_sched_group_barrier(0x002, 5, 0);   // then up to five vector ALU
+            __builtin_amdgcn_sched_group_barrier(0x002, 10, 0);  // then up to ten vector ALU
           }
         }
       }

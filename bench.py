@@ -498,6 +498,13 @@ CONFIGS = (
     ("verify256k_fp8", "config2: L=262144, T=8, e4m3 indexer keys and e4m3 K/V with row scales"),
     ("verify1m", "config3: L=1048576, T=8, e4m3 indexer keys with 1% planted rows, bf16 K/V"),
 )
+# Beyond the workload list (timed on the GPU only): the config3 recipe at twice its
+# context, where each workgroup's chunk exceeds the 4096 keys whose scores stay on chip
+# (8192 keys per CU on 256 CUs) and the rest of the scores go through the workspace.
+EXTRA_CONFIGS = (
+    ("context2m", "verify1m", 1 << 21,
+     "L=2097152, T=8, config3's recipe at twice the context (scores past 4096 keys per CU kept in the workspace)"),
+)
 
 
 def config_timings(args, dsa, torch, np, synth, dev, stream):
@@ -508,8 +515,9 @@ def config_timings(args, dsa, torch, np, synth, dev, stream):
     import math
     out = {}
     sm = 1.0 / math.sqrt(128)
-    for name, label in CONFIGS:
-        inp = synth.dsa_config(name, seed=args.seed)
+    runs = [(name, name, None, label) for name, label in CONFIGS] + list(EXTRA_CONFIGS)
+    for name, recipe, Lx, label in runs:
+        inp = synth.dsa_config(recipe, seed=args.seed, L=Lx)
         T, Lc, K = inp.T, inp.L, inp.top_k
         fp8k = inp.k_idx_dtype == "fp8"
         fp8v = inp.kv_dtype == "fp8"

@@ -15,8 +15,8 @@
 //      into registers at once, so they stream in under the attention;
 //   2  takes (token, split) attention items in turn: stages the split's 64 selected rows
 //      and writes its partial (the code of the standalone attention, attn_core.h);
-//   3  takes (token, head) merges in turn: combines the token's split partials in split
-//      order (the standalone merge's arithmetic);
+//   3  takes (token, head, 32-dim slice) merges in turn: combines the token's split
+//      partials in split order (the standalone merge's arithmetic);
 //   4  reads every token's attention output and computes 16 output columns of
 //      x + O . W_o^T, summing sixteen k-partials in the order of the standalone output
 //      projection.
@@ -62,7 +62,7 @@ struct TailShared {
   alignas(16) uint16_t xs[kMaxT][kXsS];         // attention output (bf16)
   alignas(16) uint8_t xq[kMaxT][kXqS];          // W8A8: its e4m3 codes
   float red[kOpVW][16][16];                     // k-partials of the output tile
-  float merge[32 * (2 + kD)];                   // merge: one head's partials of every split
+  float merge[32 * (2 + 32)];                   // merge: one 32-dim slice's partials of every split
   float amax[kMaxT][16];
   float ascale[kMaxT];
   float ainv[kMaxT];
@@ -90,46 +90,51 @@ DSA_DEV void load_wo(const TailParams& tp, int b, WoFrags<F8>& wf) {
   }
 }
 
-// Merged attention output of (token t, head h) from its ns split partials (tagged words),
-// written as 64 tagged words of two bf16; the arithmetic and order of the standalone
-// merge kernel.  The ns x kTagPart words (m, l, acc[128] of each split) are polled into
-// LDS (thread tid takes words tid, tid + 512, ...), then thread d < 128 combines dim d
-// over the splits in split order.
-constexpr int kMergeWords = 32 * kTagPart;                                   // 4160
-constexpr int kMergePer = (kMergeWords + kSelThreads - 1) / kSelThreads;     // 9 per thread
+// Merged attention output of 32 dims (quarter qtr) of (token t, head h) from its ns split
+// partials (tagged words), written as 16 tagged words of two bf16; the arithmetic and order
+// of the standalone merge kernel.  The ns x (2 + 32) words (m, l and the slice's values of
+// each split) are polled into LDS (thread tid takes words tid, tid + 512, ...), then thread
+// d < 32 combines its dim over the splits in split order.  (A whole head per workgroup --
+// 4160 words polled by 64 of the workgroups -- took 2.8 us; the chain's merge kernel cuts
+// the same work in these 256 slices.)
+constexpr int kSliceD = 32;                                                  // dims per merge slice
+constexpr int kSliceW = 2 + kSliceD;                                         // words per split
+constexpr int kSlicePer = (32 * kSliceW + kSelThreads - 1) / kSelThreads;    // 3 per thread
 
-DSA_DEV void merge_head(const AttnParams& ap, int t, int h, float* vals /* LDS [ns][kTagPart] */, uint32_t tag,
-                        uint64_t* trace) {
+DSA_DEV void merge_slice(const AttnParams& ap, int t, int h, int qtr, float* vals /* LDS [ns][kSliceW] */,
+                         uint32_t tag, uint64_t* trace) {
   (void)trace;
   const int ns = ap.nsplit;
   const int tid = threadIdx.x;
-  const int n = ns * kTagPart;
+  const int n = ns * kSliceW;
+  const int d0 = kSliceD * qtr;
   const uint64_t* pt = ap.tpart + (size_t)t * ns * kHq * kTagPart;
-  uint32_t v[kMergePer];
-  poll_words<kMergePer>([&](int u) {
+  uint32_t v[kSlicePer];
+  poll_words<kSlicePer>([&](int u) {
     int i = tid + u * kSelThreads;
     i = i < n ? i : n - 1;
-    const int j = i / kTagPart;
-    return pt + ((size_t)j * kHq + h) * kTagPart + (i - j * kTagPart);
+    const int j = i / kSliceW, w = i - j * kSliceW;
+    const int word = w < 2 ? w : tag_dim_word(d0 + (w - 2));
+    return pt + ((size_t)j * kHq + h) * kTagPart + word;
   }, tag, v, ap.ctl);
   DSA_MARK(trace, 6);
 #pragma unroll
-  for (int u = 0; u < kMergePer; ++u) {
+  for (int u = 0; u < kSlicePer; ++u) {
     const int i = tid + u * kSelThreads;
     if (i < n) vals[i] = __uint_as_float(v[u]);
   }
   __syncthreads();
-  if (tid < kD) {
-    const int d = tid;
+  if (tid < kSliceD) {
+    const int d = d0 + tid;
     const float s2 = ap.sink ? ap.sink[h] * 1.4426950408889634f : -__builtin_inff();
     // every split's (m, l, value) read from LDS up front (unrolled), then combined in order
     float mj[32], lj[32], aj[32];
 #pragma unroll
     for (int j = 0; j < 32; ++j) {
       const int jc = j < ns ? j : ns - 1;
-      mj[j] = vals[jc * kTagPart];
-      lj[j] = vals[jc * kTagPart + 1];
-      aj[j] = vals[jc * kTagPart + tag_dim_word(d)];
+      mj[j] = vals[jc * kSliceW];
+      lj[j] = vals[jc * kSliceW + 1];
+      aj[j] = vals[jc * kSliceW + 2 + tid];
     }
     float M = -__builtin_inff();
 #pragma unroll
@@ -206,10 +211,12 @@ __global__ void __launch_bounds__(kSelThreads, 1) dsa_attn_oproj_kernel(TailPara
   }
   if (!requested) request_wo();
   DSA_MARK(trace, 2);
-  // ---- 3) (token, head) merges, round the workgroups from the last one down (the first
-  //      workgroups are the likeliest to hold a second attention item)
+  // ---- 3) (token, head, 32-dim quarter) merges, round the workgroups from the last one
+  //      down (the first workgroups are the likeliest to hold a second attention item)
   if (ns > 1) {
-    for (int q = nwg - 1 - wg; q < T * kHq; q += nwg) merge_head(ap, q / kHq, q % kHq, ts.merge, tag, trace);
+    constexpr int QPH = kD / kSliceD;                               // slices per head
+    for (int q = nwg - 1 - wg; q < T * kHq * QPH; q += nwg)
+      merge_slice(ap, q / (kHq * QPH), (q / QPH) % kHq, q % QPH, ts.merge, tag, trace);
   }
   DSA_MARK(trace, 3);
   // ---- 4) output projection: every token's attention output into LDS (bf16; W8A8: codes):

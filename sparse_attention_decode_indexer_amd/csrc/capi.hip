@@ -406,7 +406,7 @@ dsa_status_t dsa_layer_step(const dsa_layer_config_t* cfg, const dsa_layer_weigh
   // output-projection launches (five in all).  The environment variable
   // DSA_LAYER_PERSISTENT_TAIL=1 selects one persistent launch for everything after the
   // selection instead (three in all); it gives the same result bit for bit and measured
-  // about 1 us slower per DSA layer on MI355X (1.5 us per module step), where a hand-off
+  // about 0.8 us slower per DSA layer on MI355X (0.9 us per module step), where a hand-off
   // between workgroups through memory costs about as much as a launch boundary.
   const char* pt = getenv("DSA_LAYER_PERSISTENT_TAIL");
   const bool fused = pt && pt[0] == '1';

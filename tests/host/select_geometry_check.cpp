@@ -134,6 +134,15 @@ int main() {
                                            ncu, 0);
     CHECK(!gx.fits, "ncu=%d: a context past the limit fits", ncu);
   }
+  // the long-chunk shapes the GPU tests run with the geometry cut for a few CUs
+  for (int ncu : {1, 2, 3, 4})
+    for (int64_t L : {(int64_t)4097, (int64_t)8193, (int64_t)12345, (int64_t)20000, (int64_t)25000, (int64_t)30000,
+                      (int64_t)33333, (int64_t)40000, (int64_t)50000, (int64_t)50001, (int64_t)65536, (int64_t)70000,
+                      (int64_t)131072})
+      for (int T = 1; T <= 8; ++T)
+        for (int k : {1000, 2048})
+          for (int64_t pos0 : {L - T, L / 2, L / 3})
+            if (L <= select_max_context(ncu)) check(T, L, pos0, k, ncu, select_single_max(0, 1));
   printf("%s: %ld cases, %d failures\n", fails ? "FAILED" : "ok", cases, fails);
   return fails ? 1 : 0;
 }

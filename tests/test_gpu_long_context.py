@@ -80,6 +80,13 @@ CASES = [
     ("verify64k", 30000, 5, 0, False, 2, "end"),
     ("verify256k_fp8", 50000, 8, 1, False, 4, "end"),
     ("verify1m", 70000, 8, 3, False, 4, "mid"),
+    # edges: one key past the LDS part (4608-key chunk, 511 masked spill slots); the longest
+    # chunk (65536 keys) with an empty second workgroup; a T = 1 longest chunk on e4m3 keys;
+    # a ragged context whose tokens outnumber the chunks (five empty workgroups, no bound)
+    ("tiny", 4097, 1, 4, False, 1, "end"),
+    ("tiny", 65536, 2, 5, True, 1, "end"),
+    ("verify256k_fp8", 65536, 1, 7, False, 1, "end"),
+    ("verify64k", 12345, 7, 6, False, 2, "mid"),
 ]
 
 
@@ -128,6 +135,10 @@ TOPK_CASES = [
     ("ints", 4, 25000, 1000, "mid", lambda g, T, L: g.integers(-3, 30, (T, L)).astype(np.float32)),
     ("late-runs", 3, 33333, 2048, "end",
      lambda g, T, L: np.where(np.arange(L) > 9000, 5 + g.random((T, L)), g.random((T, L))).astype(np.float32)),
+    # one position past the LDS part of the first chunk (4608-key chunks)
+    ("edge-8193", 1, 8193, 2048, "end", lambda g, T, L: g.standard_normal((T, L)).astype(np.float32)),
+    # the longest chunks (65536 positions) at the context limit of two CUs, six empty workgroups
+    ("longest", 8, 131072, 2048, "end", lambda g, T, L: g.standard_normal((T, L)).astype(np.float32)),
 ]
 
 
